@@ -1,0 +1,73 @@
+"""Exact-arithmetic brute force for tiny inputs.  TEST INFRASTRUCTURE ONLY.
+
+A second statement of the kernscope "Numerical contract" (sections "RMSNorm"
+and "Fused residual-add RMSNorm") that shares nothing with ``ks_oracle.c``:
+the sum of squares, the mean and eps are exact rationals, the square root is
+taken to 80 significant digits, and the result is rounded ONCE to the output
+format (round to nearest, ties to even) by integer arithmetic on the rational.
+Only the fused form's fp32 residual sum is rounded to fp32 first, because the
+contract defines s as an fp32 value.
+
+It is meant for a few hundred elements at most (pure Python).
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal, localcontext
+from fractions import Fraction
+
+# (significand bits incl. the implicit one, smallest normal exponent, largest finite value)
+FORMATS = {
+    "float32": (24, -126, (2 - Fraction(1, 2**23)) * Fraction(2) ** 127),
+    "float16": (11, -14, Fraction(65504)),
+    "bfloat16": (8, -126, (2 - Fraction(1, 2**7)) * Fraction(2) ** 127),
+}
+
+
+def round_to(q: Fraction, fmt: str) -> float:
+    """Nearest value of ``fmt`` to the rational q, ties to even; +-inf past the largest finite."""
+    prec, emin, max_finite = FORMATS[fmt]
+    if q == 0:
+        return 0.0
+    neg = q < 0
+    a = -q if neg else q
+    lead = a.numerator.bit_length() - a.denominator.bit_length()  # 2^lead <= a < 2^(lead+2)
+    if Fraction(2) ** (lead + 1) <= a:
+        lead += 1
+    elif Fraction(2) ** lead > a:
+        lead -= 1
+    lead = max(lead, emin)
+    qexp = lead - (prec - 1)
+    n = round(a / Fraction(2) ** qexp)  # Fraction rounding: half to even
+    v = n * Fraction(2) ** qexp
+    if v > max_finite:
+        return -math.inf if neg else math.inf
+    out = float(v)  # exact: v has at most 24 significant bits
+    return -out if neg else out
+
+
+def _inv_sqrt(m: Fraction) -> Fraction:
+    with localcontext() as ctx:
+        ctx.prec = 80
+        d = Decimal(m.numerator) / Decimal(m.denominator)
+        return Fraction(1 / d.sqrt())
+
+
+def rms_norm(x: list[list[float]], w: list[float], eps32: float, fmt: str) -> list[list[float]]:
+    """Rows x (exact values of the stored elements), weight w, eps already rounded to fp32."""
+    out = []
+    hidden = len(w)
+    for row in x:
+        assert len(row) == hidden
+        m = sum(Fraction(v) ** 2 for v in row) / hidden + Fraction(eps32)
+        inv = _inv_sqrt(m)
+        out.append([round_to(Fraction(v) * Fraction(wj) * inv, fmt) for v, wj in zip(row, w)])
+    return out
+
+
+def fused_add_rms_norm(x: list[list[float]], r: list[list[float]], w: list[float], eps32: float,
+                       fmt: str) -> tuple[list[list[float]], list[list[float]]]:
+    """Returns (x_out, residual_out) as values."""
+    s = [[round_to(Fraction(a) + Fraction(b), "float32") for a, b in zip(xr, rr)] for xr, rr in zip(x, r)]
+    residual = [[round_to(Fraction(v), fmt) for v in row] for row in s]
+    return rms_norm(s, w, eps32, fmt), residual

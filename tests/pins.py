@@ -1,0 +1,322 @@
+"""Checks that pin the CPU oracle to facts fixed outside the oracle itself.
+
+Each check takes an oracle library handle (``oracle.load()`` or a build of a
+deliberately broken copy) and raises AssertionError when the oracle
+disagrees.  Sources of truth:
+
+- closed forms and invariants that follow from the kernscope contract
+  ("Numerical contract": RMSNorm, Fused residual-add RMSNorm);
+- an exact-rational brute force (``oracle/brute64.py``, tiny inputs);
+- library routines that compute the same thing by a different route: torch
+  and numpy casts, torch's fp32 evaluation of the formula.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import brute64
+from compare import bits, check_bitexact, check_normalised, stats, ulp_distance
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "constant_rows.txt")
+DT = {"float32": torch.float32, "float16": torch.float16, "bfloat16": torch.bfloat16}
+
+
+def read_constant_rows():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            fmt, c, eps, h, expected, margin = line.split()
+            rows.append((fmt, float(c), float(eps), int(h), int(expected, 16), float(margin)))
+    return rows
+
+
+def _pattern_tensor(pattern: int, dtype: torch.dtype, n: int) -> torch.Tensor:
+    if dtype == torch.float32:
+        return torch.full((n,), pattern, dtype=torch.int64).to(torch.int32).view(torch.float32)
+    signed = pattern - (1 << 16) if pattern >= (1 << 15) else pattern
+    return torch.full((n,), signed, dtype=torch.int16).view(dtype)
+
+
+# --------------------------------------------------------------------------
+# P-a: constant rows against the closed form c / sqrt(c^2 + eps)
+# --------------------------------------------------------------------------
+def pin_constant_rows(lib) -> None:
+    for fmt, c, eps, h, expected, margin in read_constant_rows():
+        dt = DT[fmt]
+        x = torch.full((2, h), c, dtype=dt)
+        w = torch.ones(h, dtype=dt)
+        want = _pattern_tensor(expected, dt, h).expand(2, h)
+        y = oracle.rms_norm(x, w, eps, lib=lib)
+        if fmt == "float32":
+            assert int(ulp_distance(y, want).max()) <= 4, (fmt, c, eps, h)
+        else:
+            check_bitexact(y, want)
+        # fused: x + residual = c exactly (two halves), residual_out must be c
+        half = torch.full((2, h), c / 2, dtype=dt)
+        xo, ro = oracle.fused_add_rms_norm(half, half.clone(), w, eps, lib=lib)
+        check_bitexact(ro, x)
+        if fmt == "float32":
+            assert int(ulp_distance(xo, want).max()) <= 4, (fmt, c, eps, h)
+        else:
+            check_bitexact(xo, want)
+
+
+# --------------------------------------------------------------------------
+# P-b: unit weight gives output RMS sqrt(ms / (ms + eps))
+# --------------------------------------------------------------------------
+def pin_unit_weight_rms(lib) -> None:
+    for dtype, seed in (("bfloat16", 11), ("float16", 12), ("float32", 13)):
+        inp = workloads.random_case((16, 512), dtype, seed)
+        x = inp["x"]
+        w = torch.ones(512, dtype=x.dtype)
+        for eps in (1e-6, 0.5):
+            y = oracle.rms_norm(x, w, eps, lib=lib).double()
+            ms = x.double().pow(2).mean(-1)
+            want = torch.sqrt(ms / (ms + float(np.float32(eps))))
+            got = y.pow(2).mean(-1).sqrt()
+            rel = ((got - want).abs() / want).max().item()
+            assert rel < 2.0 ** -8, (dtype, eps, rel)
+
+
+# --------------------------------------------------------------------------
+# P-c: exact-rational brute force on tiny inputs
+# --------------------------------------------------------------------------
+BRUTE_SHAPES = [(5,), (2, 3, 5), (3, 1000), (4, 1), (3, 2), (2, 3), (2, 8), (2, 64)]
+
+
+def _values(t: torch.Tensor) -> list:
+    t = t.float().reshape(-1, t.shape[-1])
+    return [[float(v) for v in row] for row in t]
+
+
+def _from_values(vals: list, dtype: torch.dtype, shape) -> torch.Tensor:
+    return torch.tensor(vals, dtype=torch.float64).to(torch.float32).to(dtype).reshape(shape)
+
+
+def pin_brute_force(lib) -> None:
+    for dtype in ("bfloat16", "float16", "float32"):
+        for i, shape in enumerate(BRUTE_SHAPES):
+            inp = workloads.random_case(shape, dtype, 100 + i, residual=workloads.normal(0, 0.7))
+            x, r, w = inp["x"], inp["residual"], inp["weight"]
+            eps = 1e-6 if i % 2 == 0 else 1e-5
+            eps32 = float(np.float32(eps))
+            want = _from_values(brute64.rms_norm(_values(x), [float(v) for v in w.float()], eps32, dtype),
+                                x.dtype, shape)
+            got = oracle.rms_norm(x, w, eps, lib=lib)
+            _check_brute(got, want, dtype, shape)
+            bx, br = brute64.fused_add_rms_norm(_values(x), _values(r), [float(v) for v in w.float()], eps32, dtype)
+            gx, gr = oracle.fused_add_rms_norm(x, r, w, eps, lib=lib)
+            check_bitexact(gr, _from_values(br, x.dtype, shape))
+            _check_brute(gx, _from_values(bx, x.dtype, shape), dtype, shape)
+
+
+def _check_brute(got: torch.Tensor, want: torch.Tensor, dtype: str, shape) -> None:
+    d = int(ulp_distance(got, want).max())
+    # 16-bit outputs: at most 1 ulp.  fp32 outputs: the oracle rounds about six
+    # times in fp32 against one rounding for the brute force, so a few ulps.
+    limit = 4 if dtype == "float32" else 1
+    assert d <= limit, (dtype, shape, d)
+
+
+# --------------------------------------------------------------------------
+# P-d: power-of-two scaling;  P-e: sign symmetry
+# --------------------------------------------------------------------------
+def pin_scaling_and_sign(lib) -> None:
+    for dtype in ("bfloat16", "float16", "float32"):
+        inp = workloads.random_case((8, 300), dtype, 21)
+        x, r, w = inp["x"], inp["residual"], inp["weight"]
+        # keep |x| >= 2^-6 so that neither scaled inputs nor scaled outputs reach
+        # the fp16 subnormal range, where power-of-two scaling stops being exact
+        x = (torch.sign(x.float()) * x.float().abs().clamp_min(2.0 ** -6)).to(x.dtype)
+        eps = 1e-6
+        eps32 = float(np.float32(eps))
+        y = oracle.rms_norm(x, w, eps, lib=lib)
+        for k in (-3, 2):
+            xs = (x.float() * 2.0 ** k).to(x.dtype)   # exact: power-of-two scaling in range
+            ys = oracle.rms_norm(xs, w, eps32 * 4.0 ** k, lib=lib)
+            check_bitexact(ys, y)
+            ws = (w.float() * 2.0 ** k).to(w.dtype)
+            yw = oracle.rms_norm(x, ws, eps, lib=lib)
+            check_bitexact(yw, (y.float() * 2.0 ** k).to(y.dtype))
+        check_bitexact(oracle.rms_norm(-x, w, eps, lib=lib), -y)
+        # fused: (x, r) -> (-x, -r) flips both outputs.  Compared by value: where
+        # x = -r the IEEE sum is +0 for both signs, so only the zero's sign differs.
+        gx, gr = oracle.fused_add_rms_norm(x, r, w, eps, lib=lib)
+        nx, nr = oracle.fused_add_rms_norm(-x, -r, w, eps, lib=lib)
+        assert int(ulp_distance(nx, -gx).max()) == 0
+        assert int(ulp_distance(nr, -gr).max()) == 0
+
+
+# --------------------------------------------------------------------------
+# P-f: fused residual closed form;  P-g: zero residual reduces to rms_norm
+# --------------------------------------------------------------------------
+def pin_fused_residual(lib) -> None:
+    for dtype in ("bfloat16", "float16", "float32"):
+        inp = workloads.random_case((32, 1000), dtype, 31, residual=workloads.normal(0, 3))
+        x, r, w = inp["x"], inp["residual"], inp["weight"]
+        _, ro = oracle.fused_add_rms_norm(x, r, w, 1e-6, lib=lib)
+        check_bitexact(ro, (x.float() + r.float()).to(x.dtype))   # torch fp32 add + RNE cast
+        zx, zr = oracle.fused_add_rms_norm(x, torch.zeros_like(x), w, 1e-6, lib=lib)
+        check_bitexact(zr, x)
+        check_bitexact(zx, oracle.rms_norm(x, w, 1e-6, lib=lib))
+
+
+# --------------------------------------------------------------------------
+# P-h: each row is independent of the batch around it
+# --------------------------------------------------------------------------
+def pin_batch_invariance(lib) -> None:
+    inp = workloads.random_case((9, 777), "bfloat16", 41)
+    x, r, w = inp["x"], inp["residual"], inp["weight"]
+    y = oracle.rms_norm(x, w, 1e-6, lib=lib)
+    gx, gr = oracle.fused_add_rms_norm(x, r, w, 1e-6, lib=lib)
+    for i in (0, 4, 8):
+        check_bitexact(oracle.rms_norm(x[i:i + 1].contiguous(), w, 1e-6, lib=lib), y[i:i + 1])
+        ox, orr = oracle.fused_add_rms_norm(x[i:i + 1].contiguous(), r[i:i + 1].contiguous(), w, 1e-6, lib=lib)
+        check_bitexact(ox, gx[i:i + 1])
+        check_bitexact(orr, gr[i:i + 1])
+
+
+# --------------------------------------------------------------------------
+# P-i: casts against torch (bf16) and numpy (fp16)
+# --------------------------------------------------------------------------
+def _fp32_from_bits(b: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(b.astype(np.uint32).view(np.int32)).view(torch.float32)
+
+
+def cast_test_patterns(dtype: torch.dtype) -> torch.Tensor:
+    """fp32 inputs for the rounding test: every 16-bit prefix with tie and near-tie tails,
+    plus every midpoint between neighbouring 16-bit values and its fp32 neighbours."""
+    rng = np.random.default_rng(7)
+    if dtype == torch.bfloat16:
+        hi = np.arange(1 << 16, dtype=np.uint64) << 16
+        lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint64)
+        pats = (hi[:, None] | lows[None, :]).reshape(-1)
+        extra = rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64)
+    else:
+        hi = np.arange(1 << 19, dtype=np.uint64) << 13
+        lows = np.array([0, 1, 0xFFF, 0x1000, 0x1001, 0x1FFF], dtype=np.uint64)
+        pats = (hi[:, None] | lows[None, :]).reshape(-1)
+        # around the fp16 subnormal and overflow ranges, where the rounding bit moves
+        sub = rng.integers(0, 1 << 23, size=1 << 20, dtype=np.uint64)
+        ex = rng.integers(100, 114, size=1 << 20, dtype=np.uint64)
+        extra = (ex << 23) | sub | (rng.integers(0, 2, size=1 << 20, dtype=np.uint64) << 31)
+    vals = _fp32_from_bits(np.concatenate([pats, extra]))
+    # midpoints between consecutive positive finite 16-bit values, and their neighbours
+    b = torch.arange(0, 0x7C00 if dtype == torch.float16 else 0x7F80, dtype=torch.int32)
+    v0 = b.to(torch.int16).view(dtype).double()
+    v1 = (b + 1).to(torch.int16).view(dtype).double()
+    mid = ((v0 + v1) / 2).float()    # exact in fp32 for both formats
+    up = torch.nextafter(mid, torch.tensor(float("inf")))
+    dn = torch.nextafter(mid, torch.tensor(float("-inf")))
+    allv = torch.cat([vals, mid, up, dn])
+    return torch.cat([allv, -allv])
+
+
+def pin_casts(lib) -> None:
+    # widening: every 16-bit pattern
+    allbits = torch.arange(-(1 << 15), 1 << 15, dtype=torch.int32).to(torch.int16)
+    for dtype in (torch.bfloat16, torch.float16):
+        got = oracle.widen(allbits, dtype, lib=lib)
+        ref = allbits.view(dtype).float()
+        same = (got.view(torch.int32) == ref.view(torch.int32)) | (torch.isnan(got) & torch.isnan(ref))
+        assert bool(same.all()), f"widen {dtype}: {int((~same).sum())} patterns differ"
+    # rounding
+    for dtype in (torch.bfloat16, torch.float16):
+        v = cast_test_patterns(dtype)
+        got = oracle.round_f32(v, dtype, lib=lib)
+        if dtype == torch.bfloat16:
+            ref = v.to(torch.bfloat16).view(torch.int16)
+        else:
+            with np.errstate(over="ignore"):   # overflow to inf is the expected result
+                ref = torch.from_numpy(v.numpy().astype(np.float16).view(np.int16))
+        gv, rv = got.view(dtype).float(), ref.view(dtype).float()
+        same = (got == ref) | (torch.isnan(gv) & torch.isnan(rv))
+        if not bool(same.all()):
+            i = int(torch.nonzero(~same)[0])
+            raise AssertionError(f"round {dtype}: {int((~same).sum())} of {v.numel()} differ; "
+                                 f"first {v[i].item()!r}: {int(got[i]) & 0xFFFF:#06x} vs {int(ref[i]) & 0xFFFF:#06x}")
+
+
+# --------------------------------------------------------------------------
+# P-j: torch's fp32 evaluation of the formula (a different summation order)
+# --------------------------------------------------------------------------
+def torch_fp32_rms_norm(x: torch.Tensor, w: torch.Tensor, eps: float) -> torch.Tensor:
+    x32 = x.float()
+    scale = torch.rsqrt(x32.pow(2).mean(-1, keepdim=True) + np.float32(eps))
+    return (x32 * scale * w.float()).to(x.dtype)
+
+
+def pin_library_formula(lib) -> None:
+    for name in ("C2", "C3", "C3b"):
+        wl = workloads.WORKLOADS[name]
+        inp = workloads.make_inputs(wl, rows=256)
+        x, r, w = inp["x"], inp["residual"], inp["weight"]
+        y = oracle.rms_norm(x, w, wl.eps, lib=lib)
+        check_normalised(y, torch_fp32_rms_norm(x, w, wl.eps), min_exact_rate=0.999)
+        f = torch.nn.functional.rms_norm(x.float(), (wl.hidden,), w.float(), wl.eps).to(x.dtype)
+        check_normalised(y, f, min_exact_rate=0.999)
+        # fused: normalise the fp32 sum
+        gx, _ = oracle.fused_add_rms_norm(x, r, w, wl.eps, lib=lib)
+        s = x.float() + r.float()
+        ref = (s * torch.rsqrt(s.pow(2).mean(-1, keepdim=True) + np.float32(wl.eps)) * w.float()).to(x.dtype)
+        check_normalised(gx, ref, min_exact_rate=0.999)
+    # fp32 dtype against torch with the page's fp32 tolerance
+    inp = workloads.random_case((64, 4096), "float32", 51)
+    y = oracle.rms_norm(inp["x"], inp["weight"], 1e-6, lib=lib)
+    check_normalised(y, torch_fp32_rms_norm(inp["x"], inp["weight"], 1e-6))
+
+
+# --------------------------------------------------------------------------
+# P-k: the contract normalises the UNROUNDED fp32 sum; the exact-match gate
+# separates that from normalising the stored (rounded) residual
+# --------------------------------------------------------------------------
+def pin_unrounded_sum(lib) -> None:
+    wl = workloads.WORKLOADS["C2"]
+    inp = workloads.make_inputs(wl, rows=128)
+    x, r, w = inp["x"], inp["residual"], inp["weight"]
+    gx, gr = oracle.fused_add_rms_norm(x, r, w, wl.eps, lib=lib)
+    wrong = oracle.rms_norm(gr, w, wl.eps, lib=lib)      # normalising the rounded sum
+    st = stats(gx, wrong)
+    assert st.max_ulp <= 2, st                              # a ulp bound alone barely tells them apart
+    assert st.exact_rate < 0.95, st                         # the exact-match gate does
+    s = x.float() + r.float()
+    ref = (s * torch.rsqrt(s.pow(2).mean(-1, keepdim=True) + np.float32(wl.eps)) * w.float()).to(x.dtype)
+    assert stats(gx, ref).exact_rate > stats(wrong, ref).exact_rate
+
+
+# --------------------------------------------------------------------------
+# zeros, and empty batches
+# --------------------------------------------------------------------------
+def pin_zeros_and_empty(lib) -> None:
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
+        x = torch.zeros(3, 64, dtype=dtype)
+        w = torch.ones(64, dtype=dtype)
+        y = oracle.rms_norm(x, w, 1e-6, lib=lib)
+        assert bool((bits(y) == 0).all())
+        e = torch.zeros(0, 64, dtype=dtype)
+        assert oracle.rms_norm(e, w, 1e-6, lib=lib).shape == (0, 64)
+        ex, er = oracle.fused_add_rms_norm(e, e.clone(), w, 1e-6, lib=lib)
+        assert ex.shape == er.shape == (0, 64)
+
+
+ALL_PINS = [
+    pin_constant_rows, pin_unit_weight_rms, pin_brute_force, pin_scaling_and_sign, pin_fused_residual,
+    pin_batch_invariance, pin_casts, pin_library_formula, pin_unrounded_sum, pin_zeros_and_empty,
+]
+
+
+def first_failure(lib) -> str | None:
+    """Run every pin; return the name and message of the first that fails, else None."""
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, ZeroDivisionError, OverflowError) as exc:
+            return f"{pin.__name__}: {exc}"[:300]
+    return None

@@ -1,0 +1,55 @@
+"""Plausible mistakes planted in a COPY of the oracle, on the CPU, must each
+fail at least one pin: evidence that the pins would catch such an error in the
+real oracle (a dropped term, a wrong index or sign, a wrong rounding)."""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ks_oracle.c")
+
+# (name, original text, planted text, occurrence index to replace or None for all)
+MUTANTS = [
+    ("eps_dropped", "float d = mean + eps;", "float d = mean;"),
+    ("eps_outside_sqrt", "return (float)(1.0 / sqrt((double)d));",
+     "return (float)(1.0 / (sqrt((double)mean) + (double)eps));"),
+    ("sqrt_dropped", "return (float)(1.0 / sqrt((double)d));", "return (float)(1.0 / (double)d);"),
+    ("mean_off_by_one", "float mean = ss / (float)hidden;", "float mean = ss / (float)(hidden + 1);"),
+    ("abs_not_square", "sum_sq += v * v;  /* each square is exact in double */",
+     "sum_sq += fabs(v);"),
+    ("weight_dropped", "float u = t * load_elem(dtype, w, j);\n            store_elem(dtype, out",
+     "float u = t;\n            store_elem(dtype, out"),
+    ("weight_reversed", "float u = t * load_elem(dtype, w, j);\n            store_elem(dtype, out",
+     "float u = t * load_elem(dtype, w, hidden - 1 - j);\n            store_elem(dtype, out"),
+    ("fused_sub", "s[j] = load_elem(dtype, x, base + j) + load_elem(dtype, residual, base + j);",
+     "s[j] = load_elem(dtype, x, base + j) - load_elem(dtype, residual, base + j);"),
+    ("fused_residual_is_x", "store_elem(dtype, residual, base + j, s[j]);",
+     "store_elem(dtype, residual, base + j, load_elem(dtype, x, base + j));"),
+    ("fused_normalises_rounded_sum", "float t = s[j] * scale;",
+     "float t = load_elem(dtype, residual, base + j) * scale;"),
+    ("fused_no_weight", "float u = t * load_elem(dtype, w, j);\n            store_elem(dtype, x,",
+     "float u = t;\n            store_elem(dtype, x,"),
+    ("round_truncates", "double r = nearbyint(n);", "double r = trunc(n);"),
+    ("round_ties_away", "double r = nearbyint(n);", "double r = round(n);"),
+    ("no_subnormals", "    if (lead < f->emin)\n        lead = f->emin;          /* subnormal range: fixed quantum */",
+     "    if (lead < f->emin)\n        return copysign(0.0, a);"),
+    ("bias_off_by_one", "int bias = 1 - f->emin;\n    int frac_bits = f->prec - 1;",
+     "int bias = 2 - f->emin;\n    int frac_bits = f->prec - 1;"),
+    ("widen_bias_off_by_one", "int bias = 1 - f->emin;\n    uint32_t exp_all_ones",
+     "int bias = -f->emin;\n    uint32_t exp_all_ones"),
+    ("scale_in_fp32_sqrt_of_mean_only", "float d = mean + eps;               /* fp32 add */",
+     "float d = mean + eps * 0.5f;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique or missing"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.load(oracle.build(str(mutated), str(tmp_path / "libmutant.so")))
+    failure = pins.first_failure(lib)
+    assert failure is not None, f"mutant {name} passed every pin"

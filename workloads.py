@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module draws random numbers and nothing else: it holds none of the
+normalisation's arithmetic, so both the CPU oracle and the GPU path can take
+their inputs from it without sharing any of the method.
+
+Recipe: one ``numpy.random.default_rng(seed)`` stream per tensor; values are
+drawn in fp32, scaled and shifted in fp32, optional outliers are applied in
+fp32, and the result is rounded ONCE to the storage dtype by torch's CPU cast
+(round to nearest, ties to even).  Both sides therefore see identical bits.
+
+The shapes and distributions are the ones the benchmark pages use for this
+operator: random-normal activations with hidden sizes 1024, 1536, 4096, 8192
+and 16384, and row counts from one decode token up to long prefills.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"float32": torch.float32, "float16": torch.float16, "bfloat16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Dist:
+    """A value distribution: ``normal`` (mean, std) or ``uniform`` (low, high)."""
+
+    kind: str
+    a: float
+    b: float
+
+    def draw(self, rng: np.random.Generator, n: int) -> np.ndarray:
+        if self.kind == "normal":
+            return rng.standard_normal(n, dtype=np.float32) * np.float32(self.b) + np.float32(self.a)
+        if self.kind == "uniform":
+            return rng.random(n, dtype=np.float32) * np.float32(self.b - self.a) + np.float32(self.a)
+        raise ValueError(self.kind)
+
+    def __str__(self) -> str:
+        return f"N({self.a:g},{self.b:g})" if self.kind == "normal" else f"U({self.a:g},{self.b:g})"
+
+
+def normal(mean: float, std: float) -> Dist:
+    return Dist("normal", mean, std)
+
+
+def uniform(low: float, high: float) -> Dist:
+    return Dist("uniform", low, high)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    ops: tuple[str, ...]
+    dtype: str
+    rows: int
+    hidden: int
+    x: Dist
+    weight: Dist
+    eps: float
+    seed_x: int
+    seed_w: int
+    residual: Dist | None = None
+    seed_r: int | None = None
+    outlier_frac: float = 0.0
+    outlier_scale: float = 1.0
+    seed_outlier: int | None = None
+    note: str = field(default="", compare=False)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    def describe(self) -> str:
+        ops = " + ".join(self.ops)
+        parts = [f"{ops} {self.dtype} [{self.rows},{self.hidden}]", f"x ~{self.x}"]
+        if self.outlier_frac:
+            parts[-1] += f" with {self.outlier_frac:.0%} of elements x{self.outlier_scale:g}"
+        if self.residual is not None and "fused_add_rms_norm" in self.ops:
+            parts.append(f"residual ~{self.residual}")
+        parts.append(f"weight ~{self.weight}")
+        parts.append(f"eps={self.eps:g}")
+        return ", ".join(parts)
+
+
+RMS, FUSED = "rms_norm", "fused_add_rms_norm"
+
+WORKLOADS: dict[str, Workload] = {
+    # small case the oracle finishes in milliseconds
+    "C1": Workload("C1", (RMS,), "bfloat16", 128, 1024, normal(0, 1), normal(1, 0.1), 1e-6, 1001, 1003),
+    "C2": Workload("C2", (RMS, FUSED), "bfloat16", 512, 4096, normal(0, 1), normal(1, 0.1), 1e-6, 2001, 2003,
+                   residual=normal(0, 1), seed_r=2002),
+    "C3": Workload("C3", (RMS, FUSED), "float16", 2048, 4096, normal(0, 1), uniform(0.5, 1.5), 1e-5, 3001, 3003,
+                   residual=normal(0, 0.5), seed_r=3002, outlier_frac=0.01, outlier_scale=100.0,
+                   seed_outlier=3004),
+    # the headline shape in bf16 (same distributions as C3)
+    "C3b": Workload("C3b", (RMS, FUSED), "bfloat16", 2048, 4096, normal(0, 1), uniform(0.5, 1.5), 1e-5, 3101,
+                    3103, residual=normal(0, 0.5), seed_r=3102, outlier_frac=0.01, outlier_scale=100.0,
+                    seed_outlier=3104),
+    # decode-shaped, launch-bound
+    "C4a": Workload("C4a", (FUSED,), "bfloat16", 4, 1536, normal(0, 1), normal(1, 0.1), 1e-6, 4001, 4003,
+                    residual=normal(0, 1), seed_r=4002),
+    "C4b": Workload("C4b", (FUSED,), "bfloat16", 1, 8192, normal(0, 1), normal(1, 0.1), 1e-6, 4101, 4103,
+                    residual=normal(0, 1), seed_r=4102),
+    # large prefill (wide rows); the residual distribution is not stated, taken as that of x
+    "C5f": Workload("C5f", (FUSED,), "bfloat16", 32768, 8192, normal(0, 2), normal(1, 0.1), 1e-6, 5001, 5003,
+                    residual=normal(0, 2), seed_r=5002),
+    "C5r": Workload("C5r", (RMS,), "bfloat16", 8192, 16384, normal(0, 2), normal(1, 0.1), 1e-6, 5101, 5103),
+}
+
+
+def _to_dtype(values: np.ndarray, dtype: torch.dtype, shape: tuple[int, ...]) -> torch.Tensor:
+    return torch.from_numpy(values).reshape(shape).to(dtype)
+
+
+def make_inputs(wl: Workload, rows: int | None = None) -> dict[str, torch.Tensor]:
+    """CPU tensors ``x``, ``weight`` and (if the workload has one) ``residual`` in the workload's dtype.
+
+    ``rows`` may truncate the batch (the first rows of the full draw are NOT
+    reproduced then: a shorter draw is a different sample); default is the
+    workload's own row count.
+    """
+    rows = wl.rows if rows is None else rows
+    n = rows * wl.hidden
+    x = wl.x.draw(np.random.default_rng(wl.seed_x), n)
+    if wl.outlier_frac:
+        k = int(round(wl.outlier_frac * n))
+        idx = np.random.default_rng(wl.seed_outlier).choice(n, size=k, replace=False)
+        x[idx] *= np.float32(wl.outlier_scale)
+    out = {
+        "x": _to_dtype(x, wl.torch_dtype, (rows, wl.hidden)),
+        "weight": _to_dtype(wl.weight.draw(np.random.default_rng(wl.seed_w), wl.hidden), wl.torch_dtype,
+                            (wl.hidden,)),
+    }
+    if wl.residual is not None:
+        r = wl.residual.draw(np.random.default_rng(wl.seed_r), n)
+        out["residual"] = _to_dtype(r, wl.torch_dtype, (rows, wl.hidden))
+    return out
+
+
+def random_case(shape: tuple[int, ...], dtype: str, seed: int, x: Dist = normal(0, 1),
+                residual: Dist = normal(0, 1), weight: Dist = normal(1, 0.1)) -> dict[str, torch.Tensor]:
+    """Inputs of any shape (..., H) for edge-case tests."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    hidden = shape[-1]
+    tdt = DTYPES[dtype]
+    rng = np.random.default_rng(seed)
+    return {
+        "x": _to_dtype(x.draw(rng, n), tdt, shape),
+        "residual": _to_dtype(residual.draw(rng, n), tdt, shape),
+        "weight": _to_dtype(weight.draw(rng, hidden), tdt, (hidden,)),
+    }
