@@ -1,0 +1,310 @@
+"""Benchmark: RMSNorm and fused residual-add RMSNorm on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b]
+
+One step is one pass of the whole path over one batch: ks_rms_norm on the
+batch, then ks_fused_add_rms_norm on it (both at 2048 x 4096 bf16 by
+default; x ~ N(0,1) with 1% of elements x100, residual ~ N(0,0.5), weight ~
+U(0.5,1.5), eps = 1e-5).  The inputs are resident in HBM before timing.
+
+Cache state: the 256 MiB Infinity Cache and the L2s would hold a 64 MiB
+working set, so the steps rotate over enough copies of the batch (1 GiB by
+default) that every step reads data last touched more than a cache's worth
+of traffic ago.  Numbers are therefore HBM numbers, not cache numbers.
+
+Timing:
+  * whole job (``value``): the K steps are captured once into a HIP graph
+    (no host launch overhead inside the region) and replayed, bracketed by a
+    synchronize and events on the launch stream;
+  * per kernel (``per_op``, ``roofline``): a second pass launches each kernel
+    with start/stop events that HIP records at the kernel's own boundaries
+    (hipExtLaunchKernelGGL), and averages them.
+Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
+writes out, (2 R H + H) elements; the fused form reads x and residual and
+writes both, (4 R H + H) elements.
+
+Before any timing the outputs are checked against the CPU oracle; on a
+mismatch nothing is timed (exit status 1).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "HBM GB/s (% of MI355X peak) + µs/call, rms_norm & fused_add @2048x4096 bf16"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+DTYPE_TAG = {"bfloat16": "bf16", "float16": "fp16", "float32": "fp32"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "rmsnorm_row_normalisation_amd", "csrc", f)
+                  for f in ("ks_device.hpp", "ks_launch.hpp", "ks_internal.h", "ks_api.cpp")]
+
+
+def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
+    per_row = 2 if op == "rms_norm" else 4
+    return (per_row * rows * hidden + hidden) * esize
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse() -> argparse.Namespace:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="C3b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--rotate-mib", type=int, default=1024, help="total size of the rotating input copies")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-only", action="store_true", help="skip the graph pass (debugging)")
+    return ap.parse_args()
+
+
+def fail(msg: str, code: int = 1):
+    print(json.dumps({"metric": METRIC, "error": msg}), flush=True)
+    sys.exit(code)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parity_gate(wl, inp, ks, oracle_mod) -> dict:
+    """Full-size GPU vs oracle check before any timing."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from compare import check_bitexact, check_normalised
+
+    out = {}
+    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    if "rms_norm" in wl.ops:
+        y = ks.rms_norm(x, w, wl.eps)
+        torch.cuda.synchronize()
+        ref = oracle_mod.rms_norm(inp["x"], inp["weight"], wl.eps)
+        st = check_normalised(y.cpu(), ref, 0.999)
+        out["rms_norm"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
+    if "fused_add_rms_norm" in wl.ops:
+        xf, rf = inp["x"].cuda(), inp["residual"].cuda()
+        ks.fused_add_rms_norm(xf, rf, w, wl.eps)
+        torch.cuda.synchronize()
+        rx, rr = oracle_mod.fused_add_rms_norm(inp["x"], inp["residual"], inp["weight"], wl.eps)
+        check_bitexact(rf.cpu(), rr)
+        st = check_normalised(xf.cpu(), rx, 0.999)
+        out["fused_add_rms_norm"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6),
+                                     "residual": "bit-exact"}
+    return out
+
+
+def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
+    """The oracle as it stands, single-threaded on a host core, on whole steps of the workload."""
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        if "rms_norm" in wl.ops:
+            oracle_mod.rms_norm(inp["x"], inp["weight"], wl.eps)
+        if "fused_add_rms_norm" in wl.ops:
+            oracle_mod.fused_add_rms_norm(inp["x"], inp["residual"], inp["weight"], wl.eps)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(steps * step_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full steps ({' + '.join(wl.ops)} on the whole [{wl.rows},{wl.hidden}] batch) "
+                      f"in {el:.1f} s, single thread",
+            "us_per_step": round(el / steps * 1e6, 1), "host_cpus": os.cpu_count(),
+            "host_cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def load_traffic(workload: str) -> dict | None:
+    """Counter-derived HBM bytes per launch, if taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return data.get("workloads", {}).get(workload)
+
+
+def main() -> None:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(rows shard across GPUs with no communication; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        fail("no HIP device visible")
+
+    import oracle
+    import rmsnorm_row_normalisation_amd as ks
+
+    wl = workloads.WORKLOADS[args.workload]
+    esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
+    op_bytes = {op: algorithmic_bytes(op, wl.rows, wl.hidden, esize) for op in wl.ops}
+    step_bytes = sum(op_bytes.values())
+    dev = torch.cuda.get_device_properties(0)
+    log("device", dev.name, getattr(dev, "gcnArchName", "?"), "CUs", dev.multi_processor_count)
+
+    log("generating inputs", wl.describe())
+    inp = workloads.make_inputs(wl)
+    try:
+        parity = parity_gate(wl, inp, ks, oracle)
+    except AssertionError as exc:
+        fail(f"parity gate failed, nothing timed: {exc}")
+    log("parity", parity)
+
+    # rotating copies of the batch, resident in HBM
+    per_set = 0
+    if "rms_norm" in wl.ops:
+        per_set += 2 * wl.rows * wl.hidden * esize
+    if "fused_add_rms_norm" in wl.ops:
+        per_set += 2 * wl.rows * wl.hidden * esize
+    nsets = max(1, -(-args.rotate_mib * (1 << 20) // per_set))
+    x0, r0 = inp["x"].cuda(), inp.get("residual")
+    r0 = r0.cuda() if r0 is not None else None
+    w = inp["weight"].cuda()
+    sets = []
+    for _ in range(nsets):
+        s = {}
+        if "rms_norm" in wl.ops:
+            s["x"] = x0.clone()
+            s["out"] = torch.empty_like(x0)
+        if "fused_add_rms_norm" in wl.ops:
+            s["fx"] = x0.clone()
+            s["fr"] = r0.clone()
+        sets.append(s)
+    torch.cuda.synchronize()
+    log(f"{nsets} rotating sets, {nsets * per_set / 2**20:.0f} MiB")
+
+    stream = torch.cuda.Stream()
+
+    def step(i: int, timing: dict | None = None):
+        s = sets[i % nsets]
+        if "rms_norm" in wl.ops:
+            ks.rms_norm(s["x"], w, wl.eps, out=s["out"], timing=timing["rms_norm"][i] if timing else None)
+        if "fused_add_rms_norm" in wl.ops:
+            ks.fused_add_rms_norm(s["fx"], s["fr"], w, wl.eps,
+                                  timing=timing["fused_add_rms_norm"][i] if timing else None)
+
+    steps = max(nsets, -(-args.steps // nsets) * nsets)     # whole rotations
+    result = {}
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+
+        # ---- pass 1: whole job, HIP graph replay ----
+        if not args.eager_only:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(nsets):
+                    step(i)
+            graph.replay()                       # one untimed replay
+            torch.cuda.synchronize()
+            reps = steps // nsets
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            ms = ev0.elapsed_time(ev1)
+            result["graph"] = {"ms_total": ms, "wall_s": wall, "steps": steps}
+            log(f"graph pass: {steps} steps in {ms:.3f} ms (wall {wall * 1e3:.3f} ms)")
+
+        # ---- pass 2: per-kernel durations, events at the kernel boundaries ----
+        timing = {op: [ks.Timing(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(steps)] for op in wl.ops}
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            step(i, timing)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        eager_ms = ev0.elapsed_time(ev1)
+        per_op = {}
+        for op in wl.ops:
+            durs = sorted(t.start.elapsed_time(t.stop) * 1e3 for t in timing[op])   # microseconds
+            avg = sum(durs) / len(durs)
+            p50 = durs[len(durs) // 2]
+            gbps = op_bytes[op] / (avg * 1e-6) / 1e9
+            per_op[op] = {"us_per_call": round(avg, 3), "us_p50": round(p50, 3),
+                          "us_min": round(durs[0], 3), "us_p95": round(durs[int(0.95 * (len(durs) - 1))], 3),
+                          "bytes": op_bytes[op], "gbps": round(gbps, 1),
+                          "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                          "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden).as_dict()}
+        log(f"eager pass: {steps} steps in {eager_ms:.3f} ms (wall {wall * 1e3:.3f} ms)", per_op)
+
+    if "graph" in result:
+        ms_per_step = result["graph"]["ms_total"] / steps
+        timing_mode = "hip graph replay of the K steps"
+    else:
+        ms_per_step = eager_ms / steps
+        timing_mode = "eager launches"
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    dominant = max(wl.ops, key=lambda op: per_op[op]["us_per_call"])
+    traffic = load_traffic(args.workload)
+    roofline = {"bound": "hbm", "kernel": dominant,
+                "achieved": per_op[dominant]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(per_op[dominant]["gbps"] / HBM_PEAK_GBPS, 4),
+                "traffic": (traffic or {}).get(dominant)}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_TAG[wl.dtype], "data": "synthetic",
+        "config": {"workload": wl.describe(), "ops": list(wl.ops), "rows": wl.rows, "hidden": wl.hidden,
+                   "eps": wl.eps, "timing": timing_mode,
+                   "cache": f"cold: {nsets} rotating copies ({nsets * per_set / 2**20:.0f} MiB)"},
+        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "per_op": per_op,
+        "roofline": roofline,
+        "parity": parity,
+        "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", "?"), "cus": dev.multi_processor_count},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(wl, inp, oracle, args.cpu_seconds, step_bytes)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

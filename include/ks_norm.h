@@ -1,0 +1,165 @@
+/*
+ * ks_norm: RMSNorm row normalisation and fused residual-add RMSNorm for
+ * AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operations are the ones defined in the kernscope README, section
+ * "Numerical contract" (subsections "RMSNorm" and "Fused residual-add
+ * RMSNorm"), with the input rules of its "Inputs" section.  The C-ABI
+ * convention (a status code from every entry point, device pointers, an
+ * explicit stream) follows the kernel-set README ("What it is", last line of
+ * the operator table).
+ *
+ * Common conventions
+ * ------------------
+ * Layout     x, out and residual are dense row-major [rows, hidden] arrays
+ *            (row stride = hidden elements); weight is a dense [hidden] array.
+ *            All buffers hold the same dtype.  There are no stride arguments.
+ * Memory     Every pointer is a device pointer owned by the caller.  The
+ *            library never allocates, frees, copies or synchronises.  weight
+ *            is only read.  Any alignment is accepted; 16-byte aligned
+ *            buffers with hidden * sizeof(element) a multiple of 16 take the
+ *            vector path, others a narrower path with identical results.
+ * Streams    Work is enqueued on `stream` (0 = the default stream) and the
+ *            call returns without waiting.  Calls that overlap in time on
+ *            the same buffers race, as with any asynchronous kernel.
+ * Arithmetic Per row: widen to fp32; sum of squares in fp32; mean = sum / H
+ *            (IEEE division); scale = rsqrt(mean + eps) (eps rounded to fp32;
+ *            the rsqrt is correctly rounded); y = (v * scale) * fp32(weight);
+ *            output rounded to the dtype with round-to-nearest-even.  The
+ *            reduction order depends only on hidden and dtype, so a row's
+ *            result does not depend on how many rows are in the batch.
+ * Errors     Checked in this order, before any HIP call:
+ *              KS_ERROR_UNSUPPORTED_DTYPE  dtype is not one of ks_dtype_t;
+ *              KS_ERROR_INVALID_VALUE      rows < 0; hidden <= 0 or
+ *                                          hidden > 2^24; rows * hidden *
+ *                                          element size > 2^62; eps not
+ *                                          finite or eps <= 0; a NULL
+ *                                          pointer while rows > 0; a bad plan;
+ *              KS_ERROR_OVERLAP            forbidden aliasing (per call);
+ *            then rows == 0 returns KS_SUCCESS without touching HIP.
+ *            KS_ERROR_HIP reports a failed launch (e.g. no device); the HIP
+ *            error code is kept per thread in ks_last_hip_error().
+ */
+#ifndef KS_NORM_H
+#define KS_NORM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KS_SUCCESS = 0,
+    KS_ERROR_INVALID_VALUE = 1,
+    KS_ERROR_UNSUPPORTED_DTYPE = 2,
+    KS_ERROR_OVERLAP = 3,
+    KS_ERROR_HIP = 4
+} ks_status_t;
+
+typedef enum {
+    KS_DTYPE_FLOAT32 = 0,
+    KS_DTYPE_FLOAT16 = 1,
+    KS_DTYPE_BFLOAT16 = 2
+} ks_dtype_t;
+
+typedef enum {
+    KS_OP_RMS_NORM = 0,
+    KS_OP_FUSED_ADD_RMS_NORM = 1
+} ks_op_t;
+
+/* How a launch maps rows onto threads.
+ *   KS_PATH_VECTOR   each thread holds `vectors_per_thread` 16-byte pieces of
+ *                    its row in registers; `threads_per_row` threads share a
+ *                    row; the row is read once and written once.
+ *   KS_PATH_GENERIC  `threads_per_row` threads stride over the row with
+ *                    `elems_per_access`-element accesses, in two passes (sum,
+ *                    then normalise and store); used for unaligned buffers,
+ *                    row sizes that are not a multiple of 16 bytes, and rows
+ *                    wider than the vector path holds. */
+typedef enum {
+    KS_PATH_VECTOR = 0,
+    KS_PATH_GENERIC = 1
+} ks_path_t;
+
+typedef struct {
+    int32_t path;               /* ks_path_t */
+    int32_t threads_per_row;    /* 8, 16, 32, 64, 128, 256, 512 or 1024 */
+    int32_t vectors_per_thread; /* vector path: 1..8; generic path: 0 */
+    int32_t elems_per_access;   /* generic path: 1 or 16 / element size; vector path: 16 / element size */
+    int32_t rows_per_block;     /* rows handled by one workgroup */
+    int32_t block_threads;      /* workgroup size */
+} ks_plan_t;
+
+/*
+ * RMSNorm (kernscope README, "Numerical contract" > "RMSNorm"):
+ *   out[r, :] = cast( fp32(x[r, :]) * rsqrt(mean(fp32(x[r, :])^2) + eps) * fp32(weight) )
+ * out     [rows, hidden] output.  It may be exactly x (in place); any other
+ *         overlap of out with x or weight is KS_ERROR_OVERLAP.
+ * x       [rows, hidden] input, read only (unless out == x).
+ * weight  [hidden], read only.
+ */
+ks_status_t ks_rms_norm(void *out, const void *x, const void *weight,
+                        int64_t rows, int64_t hidden, float eps,
+                        ks_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Fused residual-add RMSNorm (kernscope README, "Numerical contract" >
+ * "Fused residual-add RMSNorm"), in place, from the input snapshots:
+ *   s        = fp32(x) + fp32(residual)
+ *   residual = cast(s)
+ *   x        = cast( s * rsqrt(mean(s^2) + eps) * fp32(weight) )
+ * Normalisation uses the unrounded fp32 s.
+ * x, residual  [rows, hidden], read and overwritten.
+ * weight       [hidden], read only.
+ * x, residual and weight must not overlap (KS_ERROR_OVERLAP), as the
+ * README's "Inputs" section requires.
+ */
+ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight,
+                                  int64_t rows, int64_t hidden, float eps,
+                                  ks_dtype_t dtype, hipStream_t stream);
+
+/*
+ * The launch plan the two calls above would use for this hidden size and
+ * dtype (a pure function of op, dtype, hidden and alignment; never of rows).
+ * `aligned` != 0 means all buffers are 16-byte aligned.  No HIP call.
+ * Returns KS_ERROR_INVALID_VALUE for a NULL plan or a bad hidden size.
+ */
+ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t hidden, int aligned,
+                        ks_plan_t *plan);
+
+/*
+ * Variants of the two operations with an explicit plan and optional timing.
+ * plan         NULL = the plan ks_get_plan returns.  Otherwise it must name a
+ *              compiled configuration that covers the row and whose path fits
+ *              the buffers' alignment; else KS_ERROR_INVALID_VALUE.  Results
+ *              are identical in value to the default plan's up to the
+ *              reduction order.
+ * start, stop  NULL, or two events that HIP records at the start and the end
+ *              of the kernel itself (hipExtLaunchKernelGGL), for timing.
+ */
+ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight,
+                           int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
+                           const ks_plan_t *plan, hipEvent_t start, hipEvent_t stop,
+                           hipStream_t stream);
+
+ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight,
+                                     int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
+                                     const ks_plan_t *plan, hipEvent_t start, hipEvent_t stop,
+                                     hipStream_t stream);
+
+/* Static description of a status code. */
+const char *ks_status_string(ks_status_t status);
+
+/* hipError_t behind the calling thread's last KS_ERROR_HIP (0 if none). */
+int ks_last_hip_error(void);
+
+/* Library version string, e.g. "ks_norm 0.1.0 gfx950". */
+const char *ks_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KS_NORM_H */

@@ -1,0 +1,26 @@
+"""RMSNorm row normalisation and fused residual-add RMSNorm for MI355X (gfx950).
+
+The computation lives in ``libks_norm.so`` (hand-written HIP kernels behind a
+C ABI, ``include/ks_norm.h``); this package is its thin Python binding.
+"""
+from .binding import (  # noqa: F401
+    KS_DTYPE,
+    KsError,
+    KsTypeError,
+    KsValueError,
+    Plan,
+    Timing,
+    fused_add_rms_norm,
+    get_plan,
+    ks_fused_add_rms_norm,
+    ks_fused_add_rms_norm_ex,
+    ks_get_plan,
+    ks_rms_norm,
+    ks_rms_norm_ex,
+    ks_version,
+    lib,
+    library_path,
+    rms_norm,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,225 @@
+"""ctypes binding of libks_norm.so: argument marshalling only.
+
+The ``ks_*`` functions mirror the C ABI in ``include/ks_norm.h`` one to one
+(raw device pointers as ints).  ``rms_norm`` and ``fused_add_rms_norm`` are
+the tensor-level calls with the kernscope API shape (README, "API contract"
+and "Inputs"): they check devices, dtypes, shapes, contiguity and
+``requires_grad`` (the accelerator kernels are inference-only), then pass the
+tensors' device pointers and torch's current HIP stream to the library.
+Every step of the computation runs in the library's kernels; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(_PKG, "libks_norm.so")
+
+KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP = range(5)
+KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM = 0, 1
+KS_PATH_VECTOR, KS_PATH_GENERIC = 0, 1
+
+
+class KsError(RuntimeError):
+    """A non-success ks_status_t."""
+
+    def __init__(self, status: int, message: str, hip_error: int = 0):
+        super().__init__(message)
+        self.status = status
+        self.hip_error = hip_error
+
+
+class KsValueError(KsError, ValueError):
+    pass
+
+
+class KsTypeError(KsError, TypeError):
+    pass
+
+
+class Plan(ctypes.Structure):
+    """ks_plan_t."""
+
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("threads_per_row", ctypes.c_int32),
+        ("vectors_per_thread", ctypes.c_int32),
+        ("elems_per_access", ctypes.c_int32),
+        ("rows_per_block", ctypes.c_int32),
+        ("block_threads", ctypes.c_int32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "Plan":
+        return cls(**{k: int(d[k]) for k, _ in cls._fields_})
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def library_path() -> str:
+    return os.environ.get("KS_NORM_LIB", DEFAULT_LIB)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m rmsnorm_row_normalisation_amd.build` "
+                               "(or __graft_entry__.build()) first")
+        h = ctypes.CDLL(path)
+        i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+        h.ks_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
+        h.ks_fused_add_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
+        h.ks_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp]
+        h.ks_fused_add_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp]
+        h.ks_get_plan.argtypes = [i32, i32, i64, i32, ctypes.POINTER(Plan)]
+        h.ks_status_string.argtypes = [i32]
+        h.ks_status_string.restype = ctypes.c_char_p
+        h.ks_last_hip_error.argtypes = []
+        h.ks_version.restype = ctypes.c_char_p
+        for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
+                     "ks_get_plan", "ks_last_hip_error"):
+            getattr(h, name).restype = ctypes.c_int
+        _lib = h
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status == KS_SUCCESS:
+        return
+    msg = f"{what}: {lib().ks_status_string(status).decode()}"
+    if status == KS_ERROR_UNSUPPORTED_DTYPE:
+        raise KsTypeError(status, msg)
+    if status in (KS_ERROR_INVALID_VALUE, KS_ERROR_OVERLAP):
+        raise KsValueError(status, msg)
+    hip = int(lib().ks_last_hip_error())
+    raise KsError(status, f"{msg} (hipError {hip})", hip)
+
+
+# ---------------------------------------------------------------------------
+# Raw C-ABI mirrors (device pointers as ints; return the status code).
+# ---------------------------------------------------------------------------
+def ks_rms_norm(out: int, x: int, weight: int, rows: int, hidden: int, eps: float, dtype: int,
+                stream: int) -> int:
+    return lib().ks_rms_norm(out, x, weight, rows, hidden, eps, dtype, stream)
+
+
+def ks_fused_add_rms_norm(x: int, residual: int, weight: int, rows: int, hidden: int, eps: float, dtype: int,
+                          stream: int) -> int:
+    return lib().ks_fused_add_rms_norm(x, residual, weight, rows, hidden, eps, dtype, stream)
+
+
+def ks_rms_norm_ex(out: int, x: int, weight: int, rows: int, hidden: int, eps: float, dtype: int,
+                   plan: Plan | None, start: int | None, stop: int | None, stream: int) -> int:
+    return lib().ks_rms_norm_ex(out, x, weight, rows, hidden, eps, dtype,
+                                ctypes.byref(plan) if plan is not None else None, start, stop, stream)
+
+
+def ks_fused_add_rms_norm_ex(x: int, residual: int, weight: int, rows: int, hidden: int, eps: float, dtype: int,
+                             plan: Plan | None, start: int | None, stop: int | None, stream: int) -> int:
+    return lib().ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype,
+                                          ctypes.byref(plan) if plan is not None else None, start, stop, stream)
+
+
+def ks_get_plan(op: int, dtype: int, hidden: int, aligned: bool = True) -> Plan:
+    plan = Plan()
+    _check(lib().ks_get_plan(op, dtype, hidden, int(bool(aligned)), ctypes.byref(plan)), "ks_get_plan")
+    return plan
+
+
+def ks_version() -> str:
+    return lib().ks_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# Tensor-level API.
+# ---------------------------------------------------------------------------
+@dataclass
+class Timing:
+    """Two HIP events (``torch.cuda.Event(enable_timing=True)``) that the library
+    records at the start and the end of the kernel itself."""
+
+    start: torch.cuda.Event
+    stop: torch.cuda.Event
+
+    def handles(self) -> tuple[int, int]:
+        return int(self.start.cuda_event), int(self.stop.cuda_event)
+
+
+def _check_tensors(op: str, x: torch.Tensor, weight: torch.Tensor, *others: torch.Tensor) -> tuple[int, int]:
+    if x.dtype not in KS_DTYPE:
+        raise TypeError(f"{op}: unsupported dtype {x.dtype}")
+    for t in (weight, *others):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{op}: all tensors must share dtype {x.dtype}, got {t.dtype}")
+        if t.device != x.device:
+            raise ValueError(f"{op}: all tensors must be on {x.device}, got {t.device}")
+    if x.device.type != "cuda":
+        raise ValueError(f"{op}: tensors must be on a HIP device, got {x.device}")
+    for t in (x, weight, *others):
+        if not t.is_contiguous():
+            raise ValueError(f"{op}: tensors must be contiguous")
+        if t.requires_grad:
+            raise ValueError(f"{op}: inference-only kernel; got a tensor that requires grad")
+    if x.dim() == 0 or x.shape[-1] == 0:
+        raise ValueError(f"{op}: the last dimension must be nonempty")
+    hidden = x.shape[-1]
+    if weight.shape != (hidden,):
+        raise ValueError(f"{op}: weight must have shape ({hidden},), got {tuple(weight.shape)}")
+    return x.numel() // hidden, hidden
+
+
+def _stream(x: torch.Tensor) -> int:
+    return int(torch.cuda.current_stream(x.device).cuda_stream)
+
+
+def _events(timing: Timing | None) -> tuple[int | None, int | None]:
+    return timing.handles() if timing is not None else (None, None)
+
+
+def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *, out: torch.Tensor | None = None,
+             plan: Plan | None = None, timing: Timing | None = None) -> torch.Tensor:
+    """RMSNorm over the last dimension; returns ``out`` (a new tensor unless given; may be ``x``)."""
+    rows, hidden = _check_tensors("rms_norm", x, weight)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_tensors("rms_norm", out, weight)
+        if out.shape != x.shape:
+            raise ValueError("rms_norm: out must have the shape of x")
+    start, stop = _events(timing)
+    with torch.cuda.device(x.device):
+        st = ks_rms_norm_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(), rows, hidden, float(eps),
+                            KS_DTYPE[x.dtype], plan, start, stop, _stream(x))
+    _check(st, "ks_rms_norm")
+    return out
+
+
+def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
+                       plan: Plan | None = None, timing: Timing | None = None) -> None:
+    """In place: residual <- cast(x + residual); x <- RMSNorm of the fp32 sum.  Returns None."""
+    rows, hidden = _check_tensors("fused_add_rms_norm", x, weight, residual)
+    if residual.shape != x.shape:
+        raise ValueError("fused_add_rms_norm: residual must have the shape of x")
+    start, stop = _events(timing)
+    with torch.cuda.device(x.device):
+        st = ks_fused_add_rms_norm_ex(x.data_ptr(), residual.data_ptr(), weight.data_ptr(), rows, hidden,
+                                      float(eps), KS_DTYPE[x.dtype], plan, start, stop, _stream(x))
+    _check(st, "ks_fused_add_rms_norm")
+
+
+def get_plan(op: str, dtype: torch.dtype, hidden: int, aligned: bool = True) -> Plan:
+    code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM}[op]
+    return ks_get_plan(code, KS_DTYPE[dtype], hidden, aligned)

@@ -1,0 +1,381 @@
+// Device code for RMSNorm and fused residual-add RMSNorm on gfx950 (CDNA4).
+//
+// Operation (kernscope README, "Numerical contract"): per row, widen to fp32,
+// sum of squares in fp32, scale = rsqrt(sum / H + eps), y = (v * scale) *
+// fp32(w), round to the storage dtype.  The fused form first forms the fp32
+// sum s = x + residual, stores cast(s) to residual, and normalises the
+// unrounded s into x.
+//
+// Two kernel families:
+//   vec_kernel      a team of kTpr lanes owns a row; each lane keeps kVpt
+//                   16-byte pieces of it in VGPRs, so every byte of x (and
+//                   residual) is read from HBM once and written once.  Loads
+//                   and stores are raw buffer instructions on one descriptor
+//                   per workgroup; pieces past the end of the row get an
+//                   out-of-range offset, so they read as zero and their
+//                   stores are dropped by the hardware range check.
+//   generic_kernel  a team of kTpr lanes strides over the row with kEpa
+//                   elements per access, in two passes (sum, then normalise
+//                   and store).  Serves unaligned buffers, rows whose byte
+//                   size is not a multiple of 16, and rows wider than the
+//                   vector kernel holds in registers.
+//
+// Reduction: per-lane fp32 FMA chain in a fixed order, then a fixed tree
+// across the team (DPP within rows of 16 lanes, cross-row swaps, and an LDS
+// combine in wave order when a row spans several waves).  The tree depends
+// only on the plan, and the plan only on (op, dtype, hidden), so a row's
+// result never depends on the batch it is in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ks {
+
+using u32x4 = unsigned int __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw (unswizzled, stride 0) buffer descriptor on gfx9-family
+// parts, gfx950 included: 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+// A byte offset past every buffer this library builds (all are < 2^31 bytes):
+// loads there return zero and stores there are discarded.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+struct Params {
+    void *y;          // rms_norm: out;   fused: x (written)
+    const void *x;    // rms_norm: x;     fused: x (read; same buffer as y)
+    void *res;        // fused: residual (read, then written); rms_norm: unused
+    const void *w;    // weight [hidden]
+    int64_t rows;
+    int32_t hidden;
+    float eps;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// ---------------------------------------------------------------------------
+// Element packing: a 16-byte piece holds kElems values of T.
+// ---------------------------------------------------------------------------
+template <typename T> struct Pack;
+
+template <> struct Pack<float> {
+    static constexpr int kElems = 4;
+    __device__ static __forceinline__ float get(const u32x4 &v, int e) { return __uint_as_float(v[e]); }
+    __device__ static __forceinline__ u32x4 put(const float *f)
+    {
+        u32x4 r;
+        r.x = __float_as_uint(f[0]);
+        r.y = __float_as_uint(f[1]);
+        r.z = __float_as_uint(f[2]);
+        r.w = __float_as_uint(f[3]);
+        return r;
+    }
+};
+
+// bfloat16 is the upper half of binary32: widening is a 16-bit shift, exact.
+template <> struct Pack<__bf16> {
+    static constexpr int kElems = 8;
+    __device__ static __forceinline__ float get(const u32x4 &v, int e)
+    {
+        unsigned w = v[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    // round to nearest even (v_cvt_pk_bf16_f32 under the default rounding mode)
+    __device__ static __forceinline__ unsigned two(float a, float b)
+    {
+        unsigned lo = __builtin_bit_cast(unsigned short, (__bf16)a);
+        unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)b);
+        return lo | (hi << 16);
+    }
+    __device__ static __forceinline__ u32x4 put(const float *f)
+    {
+        u32x4 r;
+        r.x = two(f[0], f[1]);
+        r.y = two(f[2], f[3]);
+        r.z = two(f[4], f[5]);
+        r.w = two(f[6], f[7]);
+        return r;
+    }
+};
+
+template <> struct Pack<_Float16> {
+    static constexpr int kElems = 8;
+    __device__ static __forceinline__ float get(const u32x4 &v, int e)
+    {
+        unsigned w = v[e >> 1];
+        unsigned short h = (unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu));
+        return (float)__builtin_bit_cast(_Float16, h);   // exact widening
+    }
+    // round to nearest even (v_cvt_f16_f32 under the default rounding mode)
+    __device__ static __forceinline__ unsigned two(float a, float b)
+    {
+        unsigned lo = __builtin_bit_cast(unsigned short, (_Float16)a);
+        unsigned hi = __builtin_bit_cast(unsigned short, (_Float16)b);
+        return lo | (hi << 16);
+    }
+    __device__ static __forceinline__ u32x4 put(const float *f)
+    {
+        u32x4 r;
+        r.x = two(f[0], f[1]);
+        r.y = two(f[2], f[3]);
+        r.z = two(f[4], f[5]);
+        r.w = two(f[6], f[7]);
+        return r;
+    }
+};
+
+// Scalar element access for the unaligned generic path.
+template <typename T> struct Scalar;
+template <> struct Scalar<float> {
+    __device__ static __forceinline__ float get(const void *p, int64_t i) { return ((const float *)p)[i]; }
+    __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((float *)p)[i] = v; }
+};
+template <> struct Scalar<__bf16> {
+    __device__ static __forceinline__ float get(const void *p, int64_t i)
+    {
+        return __uint_as_float((unsigned)((const unsigned short *)p)[i] << 16);
+    }
+    __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((__bf16 *)p)[i] = (__bf16)v; }
+};
+template <> struct Scalar<_Float16> {
+    __device__ static __forceinline__ float get(const void *p, int64_t i) { return (float)((const _Float16 *)p)[i]; }
+    __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((_Float16 *)p)[i] = (_Float16)v; }
+};
+
+// ---------------------------------------------------------------------------
+// Reductions.  Every lane of a team ends with the bitwise same sum: each step
+// adds a value to its partner's value, and fp32 addition is commutative.
+// ---------------------------------------------------------------------------
+template <int kCtrl> __device__ __forceinline__ float dpp_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of kWidth lanes (kWidth in 8, 16, 32, 64).
+template <int kWidth> __device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(kWidth == 8 || kWidth == 16 || kWidth == 32 || kWidth == 64, "group width");
+    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+    v = dpp_add<0x141>(v);   // row_half_mirror: groups of 8
+    if constexpr (kWidth >= 16)
+        v = dpp_add<0x140>(v);   // row_mirror: rows of 16
+    if constexpr (kWidth >= 32)
+        v += __shfl_xor(v, 16, 64);
+    if constexpr (kWidth >= 64)
+        v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Sum over a team of kTpr lanes inside a block of kBlock threads.  Teams wider
+// than a wave combine their waves' sums through LDS in wave order.  Every
+// thread of the block must call this (it may contain a barrier).
+template <int kTpr, int kBlock> __device__ __forceinline__ float team_sum(float v)
+{
+    if constexpr (kTpr <= 64) {
+        return group_sum<kTpr>(v);
+    } else {
+        constexpr int kWaves = kBlock / 64;
+        constexpr int kWavesPerTeam = kTpr / 64;
+        __shared__ float part[kWaves];
+        const int wave = threadIdx.x >> 6;
+        const float wsum = group_sum<64>(v);
+        if ((threadIdx.x & 63) == 0)
+            part[wave] = wsum;
+        __syncthreads();
+        const int first = (wave / kWavesPerTeam) * kWavesPerTeam;
+        float t = part[first];
+#pragma unroll
+        for (int i = 1; i < kWavesPerTeam; ++i)
+            t += part[first + i];
+        return t;
+    }
+}
+
+// rsqrt(sum / H + eps) with fp32 mean and add, and a correctly rounded
+// reciprocal square root (IEEE double sqrt and divide, one rounding to fp32).
+__device__ __forceinline__ float row_scale(float sum_sq, int32_t hidden, float eps)
+{
+    const float mean = sum_sq / (float)hidden;
+    const float d = mean + eps;
+    return (float)(1.0 / __builtin_sqrt((double)d));
+}
+
+// ---------------------------------------------------------------------------
+// Vector kernel: row held in VGPRs.
+// ---------------------------------------------------------------------------
+template <typename T, bool kFused, int kTpr, int kVpt, int kBlock, int kCpol>
+__global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
+{
+    constexpr int kE = Pack<T>::kElems;
+    constexpr int kRpb = kBlock / kTpr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;   // position inside the row's team
+    const int team = tid / kTpr;   // row inside the block
+    const int64_t row0 = (int64_t)blockIdx.x * kRpb;
+    const int64_t left = p.rows - row0;
+    const uint32_t nrows = left < kRpb ? (uint32_t)left : (uint32_t)kRpb;
+    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)sizeof(T);
+    const uint32_t blk_bytes = nrows * row_bytes;          // rows past the batch are out of range
+    const size_t base = (size_t)row0 * row_bytes;
+
+    const auto rx = make_rsrc((const char *)p.x + base, blk_bytes);
+    const auto ry = make_rsrc((char *)p.y + base, blk_bytes);
+    const auto rw = make_rsrc(p.w, row_bytes);
+
+    uint32_t off[kVpt], woff[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        const uint32_t c = (uint32_t)(k * kTpr + lane) * 16u;
+        const bool in_row = c < row_bytes;
+        off[k] = in_row ? (uint32_t)team * row_bytes + c : kOutOfRange;
+        woff[k] = in_row ? c : kOutOfRange;
+    }
+
+    u32x4 xv[kVpt], wv[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kCpol);
+
+    float sum_sq = 0.0f;
+    if constexpr (!kFused) {
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            wv[k] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[k], 0, 0);
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const float v = Pack<T>::get(xv[k], e);
+                sum_sq = __builtin_fmaf(v, v, sum_sq);
+            }
+        const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq), p.hidden, p.eps);
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            float o[kE];
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const float t = Pack<T>::get(xv[k], e) * scale;
+                o[e] = t * Pack<T>::get(wv[k], e);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kCpol);
+        }
+    } else {
+        const auto rr = make_rsrc((char *)p.res + base, blk_bytes);
+        u32x4 rv[kVpt];
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            rv[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, off[k], 0, kCpol);
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            wv[k] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[k], 0, 0);
+        float s[kVpt][kE];
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                s[k][e] = Pack<T>::get(xv[k], e) + Pack<T>::get(rv[k], e);
+                sum_sq = __builtin_fmaf(s[k][e], s[k][e], sum_sq);
+            }
+            // this lane has read every element it will write: store the
+            // rounded residual now, so the writes start before the reduction
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(s[k]), rr, off[k], 0, kCpol);
+        }
+        const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq), p.hidden, p.eps);
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            float o[kE];
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const float t = s[k][e] * scale;
+                o[e] = t * Pack<T>::get(wv[k], e);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kCpol);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel: two passes over the row, kEpa elements per access.
+// kEpa == 1: scalar accesses (any alignment); kEpa == 16 / sizeof(T): 16-byte
+// accesses (aligned buffers, row bytes a multiple of 16).
+// ---------------------------------------------------------------------------
+template <typename T, bool kFused, int kTpr, int kEpa, int kBlock>
+__global__ __launch_bounds__(kBlock) void generic_kernel(Params p)
+{
+    constexpr int kRpb = kBlock / kTpr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;
+    const int team = tid / kTpr;
+    const int64_t row = (int64_t)blockIdx.x * kRpb + team;
+    const bool active = row < p.rows;   // no early return: team_sum may hold a barrier
+    const int64_t H = p.hidden;
+    const int64_t base = active ? row * H : 0;
+    constexpr int64_t kStride = (int64_t)kTpr * kEpa;
+
+    float sum_sq = 0.0f;
+    if (active) {
+        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+            if constexpr (kEpa == 1) {
+                float v = Scalar<T>::get(p.x, base + j);
+                if constexpr (kFused)
+                    v = v + Scalar<T>::get(p.res, base + j);
+                sum_sq = __builtin_fmaf(v, v, sum_sq);
+            } else {
+                const u32x4 xv = *(const u32x4 *)((const T *)p.x + base + j);
+                u32x4 rv;
+                if constexpr (kFused)
+                    rv = *(const u32x4 *)((const T *)p.res + base + j);
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e) {
+                    float v = Pack<T>::get(xv, e);
+                    if constexpr (kFused)
+                        v = v + Pack<T>::get(rv, e);
+                    sum_sq = __builtin_fmaf(v, v, sum_sq);
+                }
+            }
+        }
+    }
+    const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq), p.hidden, p.eps);
+    if (!active)
+        return;
+    // Second pass: each element is read again and written by the same lane that
+    // read it in the first pass, so in-place updates are safe.
+    for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+        if constexpr (kEpa == 1) {
+            float v = Scalar<T>::get(p.x, base + j);
+            if constexpr (kFused) {
+                v = v + Scalar<T>::get(p.res, base + j);
+                Scalar<T>::put(p.res, base + j, v);
+            }
+            const float t = v * scale;
+            Scalar<T>::put(p.y, base + j, t * Scalar<T>::get(p.w, j));
+        } else {
+            const u32x4 xv = *(const u32x4 *)((const T *)p.x + base + j);
+            const u32x4 wv = *(const u32x4 *)((const T *)p.w + j);
+            float v[kEpa], o[kEpa];
+            if constexpr (kFused) {
+                const u32x4 rv = *(const u32x4 *)((const T *)p.res + base + j);
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e)
+                    v[e] = Pack<T>::get(xv, e) + Pack<T>::get(rv, e);
+                *(u32x4 *)((T *)p.res + base + j) = Pack<T>::put(v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e)
+                    v[e] = Pack<T>::get(xv, e);
+            }
+#pragma unroll
+            for (int e = 0; e < kEpa; ++e) {
+                const float t = v[e] * scale;
+                o[e] = t * Pack<T>::get(wv, e);
+            }
+            *(u32x4 *)((T *)p.y + base + j) = Pack<T>::put(o);
+        }
+    }
+}
+
+}  // namespace ks

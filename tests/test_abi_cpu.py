@@ -1,0 +1,226 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function its header declares, and rejects every invalid call with the right
+status before making any HIP call.  No compute call is made here: every call
+below either fails validation or has rows == 0.
+
+Validation rules: kernscope README, "Inputs" (nonempty last dimension, finite
+positive eps, shared dtype, no overlap between x, residual and weight for the
+fused form); status codes and pointer convention as in include/ks_norm.h.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import rmsnorm_row_normalisation_amd as ks
+from rmsnorm_row_normalisation_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+F32, F16, BF16 = 0, 1, 2
+OK, INVALID, DTYPE, OVERLAP, HIP = range(5)
+A = 0x10000000          # fake, 16-byte aligned device addresses: only compared, never dereferenced
+MB = 1 << 20
+
+
+def header_functions() -> set[str]:
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(ks_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ks.lib()
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert {"ks_rms_norm", "ks_fused_add_rms_norm", "ks_status_string"} <= declared
+    nm = subprocess.run(["nm", "-D", "--defined-only", ks.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(ks_[a-z0-9_]+)\b", nm))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    for code in range(5):
+        s = lib.ks_status_string(code).decode()
+        assert s.startswith("KS_")
+    assert lib.ks_status_string(99).decode().startswith("unknown")
+    assert "gfx950" in ks.ks_version()
+    assert lib.ks_last_hip_error() == 0
+
+
+def rms(out, x, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None, start=None, stop=None):
+    return b.ks_rms_norm_ex(out, x, w, rows, hidden, eps, dtype, plan, start, stop, 0)
+
+
+def fused(x, r, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None, start=None, stop=None):
+    return b.ks_fused_add_rms_norm_ex(x, r, w, rows, hidden, eps, dtype, plan, start, stop, 0)
+
+
+@pytest.mark.parametrize("call", [rms, fused])
+def test_invalid_values(call):
+    x, y, w = A, A + 64 * MB, A + 128 * MB
+    assert call(y, x, w, 4, 4096, dtype=7) == DTYPE
+    assert call(y, x, w, 4, 4096, dtype=-1) == DTYPE
+    assert call(y, x, w, -1, 4096) == INVALID
+    assert call(y, x, w, 2**31, 4096) == INVALID
+    assert call(y, x, w, 4, 0) == INVALID
+    assert call(y, x, w, 4, -5) == INVALID
+    assert call(y, x, w, 4, 2**24 + 1) == INVALID
+    for eps in (0.0, -1e-6, float("nan"), float("inf"), -float("inf")):
+        assert call(y, x, w, 4, 4096, eps=eps) == INVALID
+    assert call(None, x, w, 4, 4096) == INVALID
+    assert call(y, None, w, 4, 4096) == INVALID
+    assert call(y, x, None, 4, 4096) == INVALID
+    assert call(y, x, w, 4, 4096, start=A) == INVALID     # one event without the other
+    # dtype is checked before sizes
+    assert call(y, x, w, -1, 0, dtype=9) == DTYPE
+
+
+@pytest.mark.parametrize("call", [rms, fused])
+def test_empty_batch_is_a_no_op(call):
+    # rows == 0: success without any HIP call, NULL pointers allowed
+    assert call(None, None, None, 0, 4096) == OK
+    assert call(A, A + MB, A + 2 * MB, 0, 4096) == OK
+    # but a bad eps or dtype is still an error
+    assert call(None, None, None, 0, 4096, eps=0.0) == INVALID
+    assert call(None, None, None, 0, 4096, dtype=5) == DTYPE
+
+
+def test_overlap_rules():
+    rows, hidden = 8, 1024
+    nbytes = rows * hidden * 2
+    x = A
+    # rms_norm: out partially overlapping x, or overlapping weight
+    assert rms(x + 2, x, A + 8 * MB, rows, hidden) == OVERLAP
+    assert rms(x + nbytes - 2, x, A + 8 * MB, rows, hidden) == OVERLAP
+    assert rms(A + 4 * MB, x, A + 4 * MB + 100, rows, hidden) == OVERLAP
+    # fused: x, residual and weight pairwise disjoint
+    assert fused(x, x, A + 8 * MB, rows, hidden) == OVERLAP
+    assert fused(x, x + nbytes - 2, A + 8 * MB, rows, hidden) == OVERLAP
+    assert fused(x, A + 4 * MB, x + 64, rows, hidden) == OVERLAP
+    assert fused(x, A + 4 * MB, A + 4 * MB + nbytes - 2, rows, hidden) == OVERLAP
+
+
+def _plan(**kw):
+    d = dict(path=0, threads_per_row=64, vectors_per_thread=8, elems_per_access=8, rows_per_block=4,
+             block_threads=256)
+    d.update(kw)
+    return b.Plan.from_dict(d)
+
+
+def test_explicit_plans_are_checked():
+    # a plan that does not fit is rejected before anything else happens
+    y, x, w = A + 64 * MB, A, A + 128 * MB
+    assert rms(y, x, w, 0, 4096, plan=_plan()) == OK              # 64 lanes x 8 x 16 B = 8 KiB row
+    assert rms(y, x, w, 4, 8192, plan=_plan()) == INVALID         # 16 KiB row does not fit
+    assert rms(y, x, w, 4, 4096, plan=_plan(threads_per_row=48)) == INVALID
+    assert rms(y, x, w, 4, 4096, plan=_plan(vectors_per_thread=9)) == INVALID
+    assert rms(y, x, w, 4, 4096, plan=_plan(rows_per_block=2)) == INVALID
+    assert rms(y, x, w, 4, 4096, plan=_plan(elems_per_access=4)) == INVALID
+    assert rms(y, x, w, 4, 4096, plan=_plan(path=7)) == INVALID
+    assert rms(y, x, w, 0, 4096, plan=_plan(threads_per_row=1024, vectors_per_thread=4, rows_per_block=1,
+                                            block_threads=1024)) == OK
+    assert rms(y, x, w, 4, 4096, plan=_plan(threads_per_row=1024, vectors_per_thread=5, rows_per_block=1,
+                                            block_threads=1024)) == INVALID
+    # the vector path needs 16-byte aligned buffers
+    assert rms(y + 2, x, w, 4, 4096, plan=_plan()) == INVALID
+    # generic plans
+    g = dict(path=1, vectors_per_thread=0, elems_per_access=1)
+    assert rms(y + 2, x, w, 0, 4095, plan=_plan(threads_per_row=256, rows_per_block=1, **g)) == OK
+    assert rms(y, x, w, 0, 4096, plan=_plan(threads_per_row=64, rows_per_block=4, **{**g, "elems_per_access": 8})) == OK
+    assert rms(y, x, w, 4, 4095, plan=_plan(threads_per_row=64, rows_per_block=4,
+                                            **{**g, "elems_per_access": 8})) == INVALID
+    assert rms(y, x, w, 4, 4096, plan=_plan(threads_per_row=32, rows_per_block=8, **g)) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# Launch policy: host launch heuristics tested on the CPU, as the kernel pages
+# recommend for launch-parameter selection.
+# ---------------------------------------------------------------------------
+EXPECTED = {
+    # (op, dtype, hidden): (path, threads_per_row, vectors_per_thread, rows_per_block)
+    ("rms_norm", torch.bfloat16, 1024): (0, 16, 8, 16),       # C1
+    ("rms_norm", torch.bfloat16, 4096): (0, 64, 8, 4),        # C2 / C3b headline
+    ("fused_add_rms_norm", torch.bfloat16, 4096): (0, 64, 8, 4),
+    ("rms_norm", torch.float16, 4096): (0, 64, 8, 4),         # C3
+    ("fused_add_rms_norm", torch.bfloat16, 1536): (0, 32, 6, 8),   # C4a
+    ("fused_add_rms_norm", torch.bfloat16, 8192): (0, 128, 8, 2),  # C4b, C5f
+    ("rms_norm", torch.bfloat16, 16384): (0, 256, 8, 1),      # C5r
+    ("rms_norm", torch.float32, 4096): (0, 128, 8, 2),
+    ("rms_norm", torch.bfloat16, 5): (1, 8, 0, 32),           # odd sizes: generic scalar path
+    ("rms_norm", torch.bfloat16, 1000): (0, 16, 8, 16),      # 2000-byte rows are 16-byte multiples
+    ("rms_norm", torch.bfloat16, 1001): (1, 64, 0, 4),
+    ("rms_norm", torch.bfloat16, 65536): (1, 1024, 0, 1),    # wider than the vector path holds
+}
+
+
+@pytest.mark.parametrize("key", list(EXPECTED), ids=[f"{k[0]}-{k[1]}-{k[2]}" for k in EXPECTED])
+def test_policy_table(key):
+    op, dtype, hidden = key
+    p = ks.get_plan(op, dtype, hidden).as_dict()
+    assert (p["path"], p["threads_per_row"], p["vectors_per_thread"], p["rows_per_block"]) == EXPECTED[key]
+
+
+def test_policy_covers_every_row_and_is_accepted():
+    hiddens = list(range(1, 300)) + [511, 512, 1000, 1023, 1024, 1536, 2048, 2880, 4095, 4096, 5120, 8192,
+                                     12288, 16384, 20480, 32768, 32769, 65536, 131072, 2**24]
+    for dtype, code, es in ((torch.float32, F32, 4), (torch.float16, F16, 2), (torch.bfloat16, BF16, 2)):
+        for op in ("rms_norm", "fused_add_rms_norm"):
+            for hidden in hiddens:
+                for aligned in (True, False):
+                    p = ks.get_plan(op, dtype, hidden, aligned)
+                    d = p.as_dict()
+                    assert d["block_threads"] % 64 == 0 and d["block_threads"] <= 1024
+                    assert d["rows_per_block"] * d["threads_per_row"] == d["block_threads"]
+                    if d["path"] == 0:
+                        assert aligned and (hidden * es) % 16 == 0
+                        assert d["threads_per_row"] * d["vectors_per_thread"] * 16 >= hidden * es
+                        # the last piece of a row starts inside the row: no team is mostly padding
+                        assert (d["threads_per_row"] * (d["vectors_per_thread"] - 1)) * 16 < hidden * es
+                    # the library accepts its own plan (rows == 0: no launch)
+                    call = rms if op == "rms_norm" else fused
+                    base = A if aligned else A + 2
+                    assert call(base, base + 256 * MB, base + 512 * MB, 0, hidden, dtype=code, plan=p) == OK
+
+
+def test_tensor_api_rejects_bad_tensors():
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    w = torch.ones(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ks.rms_norm(x, w)                                   # not on a HIP device
+    with pytest.raises(TypeError):
+        ks.rms_norm(x, w.float())
+    with pytest.raises(TypeError):
+        ks.rms_norm(x.to(torch.int32), w)
+    with pytest.raises(ValueError):
+        ks.rms_norm(x.t(), torch.ones(4, dtype=torch.bfloat16))   # not contiguous
+    with pytest.raises(ValueError):
+        ks.fused_add_rms_norm(x, x.clone()[:, :4].contiguous(), w)
+
+
+def test_library_missing_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setenv("KS_NORM_LIB", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        b.lib()
+
+
+def test_ctypes_signatures_match_header():
+    # every ABI function has its argument count fixed in the binding
+    h = ks.lib()
+    for name in ("ks_rms_norm", "ks_fused_add_rms_norm"):
+        assert len(getattr(h, name).argtypes) == 8
+    for name in ("ks_rms_norm_ex", "ks_fused_add_rms_norm_ex"):
+        assert len(getattr(h, name).argtypes) == 11
+    assert ctypes.sizeof(b.Plan) == 24

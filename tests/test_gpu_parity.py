@@ -1,0 +1,237 @@
+"""Parity of the HIP path with the CPU oracle, element by element, on cuda:0.
+
+Bar: the fused residual output is bit-exact; normalised outputs are within
+1 ulp of the dtype (|difference| <= 1e-6 near zero; fp32 within rtol = atol
+= 1e-6) and, on large cases, identical on at least 99.9% of elements.
+
+Cases: every benchmark workload of the operator pages (128x1024, 512x4096,
+2048x4096 in fp16 with outliers and in bf16, decode 4x1536 and 1x8192, and the
+large prefills 32768x8192 and 8192x16384, those two checked on sampled rows),
+the kernscope edge shapes, ragged row counts, unaligned buffers, every
+compiled launch plan, and the invariants that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_row_normalisation_amd as ks
+import workloads
+from compare import check_bitexact, check_normalised, ulp_distance
+from gpu_cases import all_plans, check_case, check_outputs, gpu_run, oracle_run, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["bfloat16", "float16", "float32"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ---------------------------------------------------------------------------
+# the benchmark workloads at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C3b", "C4a", "C4b"])
+def test_workload_full(name):
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    for op in wl.ops:
+        st = check_case(name, op, inp, wl.eps)
+        say(name, op, st)
+
+
+@pytest.mark.parametrize("name", ["C5f", "C5r"])
+def test_workload_large_sampled(name):
+    """Full-size launch; the oracle checks 48 sampled rows plus the first and last."""
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(wl)
+    rows = np.random.default_rng(77).choice(wl.rows, size=48, replace=False)
+    rows = np.unique(np.concatenate([rows, [0, wl.rows - 1]]))
+    idx = torch.from_numpy(rows)
+    for op in wl.ops:
+        say(name, op, "full launch", (wl.rows, wl.hidden))
+        y, r = gpu_run(op, inp, wl.eps)
+        sub = {k: (v[idx].contiguous() if v.dim() == 2 else v) for k, v in inp.items()}
+        ref = oracle_run(op, sub, wl.eps)
+        st = check_outputs(op, (y[idx].contiguous(), r[idx].contiguous() if r is not None else None), ref,
+                           exact_rate=True)
+        say(name, op, st)
+
+
+# ---------------------------------------------------------------------------
+# edge shapes from the kernscope test list, odd and wide hidden sizes, ragged
+# row counts (not multiples of any rows-per-workgroup)
+# ---------------------------------------------------------------------------
+EDGE_SHAPES = [(5,), (2, 3, 5), (3, 1000), (512, 1024), (1, 1), (3, 2), (7, 3), (9, 8), (5, 63), (5, 64),
+               (13, 65), (3, 127), (17, 1001), (130, 1536), (33, 2880), (7, 4095), (7, 4096), (7, 4097),
+               (3, 5120), (5, 8191), (3, 12288), (2, 20000), (3, 32768), (2, 40000), (2, 65536), (1, 70000)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(shape, dtype):
+    inp = workloads.random_case(shape, dtype, seed=sum(shape) + len(dtype))
+    for op in ("rms_norm", "fused_add_rms_norm"):
+        check_case("edge", op, inp, 1e-6)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 5, 17, 63, 129, 1000, 4097])
+def test_ragged_row_counts(rows):
+    inp = workloads.random_case((rows, 4096), "bfloat16", seed=rows)
+    for op in ("rms_norm", "fused_add_rms_norm"):
+        check_case("ragged", op, inp, 1e-5)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("hidden", [1000, 1024, 4096, 4097])
+def test_unaligned_buffers(hidden, dtype):
+    """Tensors starting one element into an allocation (offset views): the generic path."""
+    inp = workloads.random_case((37, hidden), dtype, seed=hidden + 5)
+    for op in ("rms_norm", "fused_add_rms_norm"):
+        check_case("unaligned", op, inp, 1e-6, offset=1)
+
+
+def test_empty_and_zero():
+    w = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    e = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    assert ks.rms_norm(e, w).shape == (0, 64)
+    ks.fused_add_rms_norm(e, e.clone(), w)
+    e3 = torch.empty(4, 0, 64, dtype=torch.bfloat16, device="cuda")
+    assert ks.rms_norm(e3, w).shape == (4, 0, 64)
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
+        x = torch.zeros(33, 4096, dtype=dtype, device="cuda")
+        y = ks.rms_norm(x, torch.ones(4096, dtype=dtype, device="cuda"))
+        torch.cuda.synchronize()
+        assert bool((y == 0).all())
+
+
+# ---------------------------------------------------------------------------
+# every compiled plan gives the oracle's result
+# ---------------------------------------------------------------------------
+PLAN_CASES = [("bfloat16", 4096), ("float16", 1536), ("float32", 2048), ("bfloat16", 8192), ("bfloat16", 16384),
+              ("bfloat16", 264)]
+
+
+@pytest.mark.parametrize("dtype,hidden", PLAN_CASES, ids=[f"{d}-{h}" for d, h in PLAN_CASES])
+def test_every_plan(dtype, hidden):
+    inp = workloads.random_case((70, hidden), dtype, seed=hidden)
+    refs = {op: oracle_run(op, inp, 1e-6) for op in ("rms_norm", "fused_add_rms_norm")}
+    plans = all_plans(inp["x"].dtype, hidden)
+    assert len(plans) >= 8
+    for plan in plans:
+        for op in ("rms_norm", "fused_add_rms_norm"):
+            say("plan", op, dtype, hidden, plan.as_dict())
+            got = gpu_run(op, inp, 1e-6, plan=plan)
+            check_outputs(op, got, refs[op], exact_rate=True)
+
+
+# ---------------------------------------------------------------------------
+# invariants that hold at any size
+# ---------------------------------------------------------------------------
+def test_constant_rows_closed_form():
+    import pins
+
+    for fmt, c, eps, h, expected, _margin in pins.read_constant_rows():
+        dt = pins.DT[fmt]
+        x = torch.full((3, h), c, dtype=dt)
+        w = torch.ones(h, dtype=dt)
+        want = pins._pattern_tensor(expected, dt, h).expand(3, h).contiguous()
+        say("constant", fmt, c, eps, h)
+        y, _ = gpu_run("rms_norm", {"x": x, "weight": w}, eps)
+        half = torch.full((3, h), c / 2, dtype=dt)
+        fx, fr = gpu_run("fused_add_rms_norm", {"x": half, "residual": half.clone(), "weight": w}, eps)
+        check_bitexact(fr, x)
+        if fmt == "float32":
+            assert int(ulp_distance(y, want).max()) <= 4
+            assert int(ulp_distance(fx, want).max()) <= 4
+        else:
+            check_bitexact(y, want)
+            check_bitexact(fx, want)
+
+
+def test_batch_invariance():
+    """A row's result does not depend on the batch around it (the plan is a function of hidden only)."""
+    for dtype, hidden in (("bfloat16", 4096), ("float16", 1536), ("bfloat16", 16384), ("bfloat16", 1001)):
+        inp = workloads.random_case((300, hidden), dtype, seed=9)
+        full = {op: gpu_run(op, inp, 1e-6) for op in ("rms_norm", "fused_add_rms_norm")}
+        for lo, hi in ((0, 1), (17, 18), (299, 300), (5, 12), (100, 227)):
+            sub = {k: (v[lo:hi].contiguous() if v.dim() == 2 else v) for k, v in inp.items()}
+            for op in ("rms_norm", "fused_add_rms_norm"):
+                y, r = gpu_run(op, sub, 1e-6)
+                check_bitexact(y, full[op][0][lo:hi])
+                if r is not None:
+                    check_bitexact(r, full[op][1][lo:hi])
+
+
+def test_scaling_sign_and_zero_residual():
+    for dtype in DTYPES:
+        inp = workloads.random_case((64, 4096), dtype, seed=3)
+        x = inp["x"]
+        x = (torch.sign(x.float()) * x.float().abs().clamp_min(2.0 ** -6)).to(x.dtype)
+        w, r = inp["weight"], inp["residual"]
+        eps32 = float(np.float32(1e-6))
+        y, _ = gpu_run("rms_norm", {"x": x, "weight": w}, 1e-6)
+        ys, _ = gpu_run("rms_norm", {"x": (x.float() * 4).to(x.dtype), "weight": w}, eps32 * 16)
+        check_bitexact(ys, y)
+        yw, _ = gpu_run("rms_norm", {"x": x, "weight": (w.float() * 0.5).to(w.dtype)}, 1e-6)
+        check_bitexact(yw, (y.float() * 0.5).to(y.dtype))
+        yn, _ = gpu_run("rms_norm", {"x": -x, "weight": w}, 1e-6)
+        check_bitexact(yn, -y)
+        zx, zr = gpu_run("fused_add_rms_norm", {"x": x, "residual": torch.zeros_like(x), "weight": w}, 1e-6)
+        check_bitexact(zr, x)
+        check_bitexact(zx, y)
+        fx, fr = gpu_run("fused_add_rms_norm", {"x": x, "residual": r, "weight": w}, 1e-6)
+        check_bitexact(fr, (x.float() + r.float()).to(x.dtype))
+
+
+def test_in_place_rms_norm_and_streams():
+    inp = workloads.random_case((257, 4096), "bfloat16", seed=12)
+    ref = oracle.rms_norm(inp["x"], inp["weight"], 1e-6)
+    x = inp["x"].cuda()
+    w = inp["weight"].cuda()
+    out = ks.rms_norm(x, w, 1e-6, out=x)          # out == x: in place
+    assert out.data_ptr() == x.data_ptr()
+    torch.cuda.synchronize()
+    check_normalised(x.cpu(), ref, 0.999)
+    s = torch.cuda.Stream()
+    got = gpu_run("rms_norm", inp, 1e-6, stream=s)
+    check_normalised(got[0], ref, 0.999)
+
+
+def test_timing_events_record_the_kernel():
+    inp = workloads.random_case((2048, 4096), "bfloat16", seed=4)
+    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    t = ks.Timing(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    y = ks.rms_norm(x, w, 1e-6, timing=t)
+    torch.cuda.synchronize()
+    ms = t.start.elapsed_time(t.stop)
+    assert 0.0 < ms < 100.0
+    check_normalised(y.cpu(), oracle.rms_norm(inp["x"], inp["weight"], 1e-6), 0.999)
+
+
+def test_special_values():
+    """IEEE propagation (no fast-math, no flush to zero): an infinite element makes the
+    row's scale zero, subnormal outputs survive, overflow goes to infinity."""
+    h = 256
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
+        x = torch.randn(6, h, generator=torch.Generator().manual_seed(1)).to(dtype)
+        w = torch.ones(h, dtype=dtype)
+        x[0, 3] = float("inf")
+        x[1, 7] = float("nan")
+        x[2] = 0.0
+        tiny = {torch.bfloat16: 1e-39, torch.float16: 1e-7, torch.float32: 1e-44}[dtype]
+        w_tiny = torch.full((h,), tiny, dtype=dtype)
+        for weight in (w, w_tiny):
+            y, _ = gpu_run("rms_norm", {"x": x, "weight": weight}, 1e-6)
+            ref = oracle.rms_norm(x, weight, 1e-6)
+            d = ulp_distance(y, ref)
+            assert int(d.max()) <= 1, (dtype, int(d.max()))
+        big = torch.full((2, h), {torch.bfloat16: 3e38, torch.float16: 60000.0, torch.float32: 3e38}[dtype],
+                         dtype=dtype)
+        bw = torch.full((h,), 4.0, dtype=dtype)
+        fx, fr = gpu_run("fused_add_rms_norm", {"x": big, "residual": big.clone(), "weight": bw}, 1e-6)
+        rx, rr = oracle.fused_add_rms_norm(big, big.clone(), bw, 1e-6)
+        check_bitexact(fr, rr)
+        assert int(ulp_distance(fx, rx).max()) <= 1
