@@ -13,12 +13,15 @@ default) that every step reads data last touched more than a cache's worth
 of traffic ago.  Numbers are therefore HBM numbers, not cache numbers.
 
 Timing:
-  * whole job (``value``): the K steps are captured once into a HIP graph
-    (no host launch overhead inside the region) and replayed, bracketed by a
-    synchronize and events on the launch stream;
-  * per kernel (``per_op``, ``roofline``): a second pass launches each kernel
-    with start/stop events that HIP records at the kernel's own boundaries
-    (hipExtLaunchKernelGGL), and averages them.
+  * whole job (``value``): one rotation of steps over the copies is captured
+    into a HIP graph (no host launch overhead inside the timed region) and
+    replayed until K steps have run, between a synchronize and two events on
+    the launch stream;
+  * per kernel (``per_op``, ``roofline``): the same, with a graph holding only
+    that op's launches, back to back; the average launch period includes the
+    short gap between consecutive kernels, so it is an upper bound on the
+    kernel's own duration (rocprofv3's kernel trace of the same run gives the
+    duration alone).
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
 writes both, (4 R H + H) elements.
@@ -73,7 +76,6 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--rotate-mib", type=int, default=1024, help="total size of the rotating input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager-only", action="store_true", help="skip the graph pass (debugging)")
     return ap.parse_args()
 
 
@@ -206,76 +208,58 @@ def main() -> None:
 
     stream = torch.cuda.Stream()
 
-    def step(i: int, timing: dict | None = None):
+    def launch(op: str, i: int):
         s = sets[i % nsets]
-        if "rms_norm" in wl.ops:
-            ks.rms_norm(s["x"], w, wl.eps, out=s["out"], timing=timing["rms_norm"][i] if timing else None)
-        if "fused_add_rms_norm" in wl.ops:
-            ks.fused_add_rms_norm(s["fx"], s["fr"], w, wl.eps,
-                                  timing=timing["fused_add_rms_norm"][i] if timing else None)
+        if op == "rms_norm":
+            ks.rms_norm(s["x"], w, wl.eps, out=s["out"])
+        else:
+            ks.fused_add_rms_norm(s["fx"], s["fr"], w, wl.eps)
 
-    steps = max(nsets, -(-args.steps // nsets) * nsets)     # whole rotations
-    result = {}
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
+    def timed_graph(ops: tuple[str, ...], reps: int) -> float:
+        """Capture one rotation (nsets steps of `ops`) into a HIP graph, replay it
+        `reps` times between two events on the launch stream; returns milliseconds."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(nsets):
+                for op in ops:
+                    launch(op, i)
+        graph.replay()                                   # untimed
         torch.cuda.synchronize()
-
-        # ---- pass 1: whole job, HIP graph replay ----
-        if not args.eager_only:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                for i in range(nsets):
-                    step(i)
-            graph.replay()                       # one untimed replay
-            torch.cuda.synchronize()
-            reps = steps // nsets
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            ev0.record(stream)
-            for _ in range(reps):
-                graph.replay()
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - t0
-            ms = ev0.elapsed_time(ev1)
-            result["graph"] = {"ms_total": ms, "wall_s": wall, "steps": steps}
-            log(f"graph pass: {steps} steps in {ms:.3f} ms (wall {wall * 1e3:.3f} ms)")
-
-        # ---- pass 2: per-kernel durations, events at the kernel boundaries ----
-        timing = {op: [ks.Timing(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(steps)] for op in wl.ops}
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         ev0.record(stream)
-        for i in range(steps):
-            step(i, timing)
+        for _ in range(reps):
+            graph.replay()
         ev1.record(stream)
         torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
+    reps = max(1, -(-args.steps // nsets))
+    steps = reps * nsets                                   # whole rotations over the copies
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            for op in wl.ops:
+                launch(op, i)
+        torch.cuda.synchronize()
+        # whole job: every step runs all ops of the path
+        t0 = time.perf_counter()
+        total_ms = timed_graph(wl.ops, reps)
         wall = time.perf_counter() - t0
-        eager_ms = ev0.elapsed_time(ev1)
+        log(f"whole-step graph: {steps} steps in {total_ms:.3f} ms")
+        # per kernel: back-to-back launches of one op
         per_op = {}
         for op in wl.ops:
-            durs = sorted(t.start.elapsed_time(t.stop) * 1e3 for t in timing[op])   # microseconds
-            avg = sum(durs) / len(durs)
-            p50 = durs[len(durs) // 2]
-            gbps = op_bytes[op] / (avg * 1e-6) / 1e9
-            per_op[op] = {"us_per_call": round(avg, 3), "us_p50": round(p50, 3),
-                          "us_min": round(durs[0], 3), "us_p95": round(durs[int(0.95 * (len(durs) - 1))], 3),
-                          "bytes": op_bytes[op], "gbps": round(gbps, 1),
+            ms = timed_graph((op,), reps)
+            us = ms * 1e3 / steps
+            gbps = op_bytes[op] / (us * 1e-6) / 1e9
+            per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
                           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                          "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden).as_dict()}
-        log(f"eager pass: {steps} steps in {eager_ms:.3f} ms (wall {wall * 1e3:.3f} ms)", per_op)
+                          "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden, wl.rows).as_dict()}
+        log("per op", per_op)
 
-    if "graph" in result:
-        ms_per_step = result["graph"]["ms_total"] / steps
-        timing_mode = "hip graph replay of the K steps"
-    else:
-        ms_per_step = eager_ms / steps
-        timing_mode = "eager launches"
+    ms_per_step = total_ms / steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    timing_mode = (f"HIP graph replay, {reps} replays of {nsets} steps; per op: graphs of back-to-back "
+                   "launches of that op")
 
     dominant = max(wl.ops, key=lambda op: per_op[op]["us_per_call"])
     traffic = load_traffic(args.workload)

@@ -90,6 +90,12 @@ typedef struct {
     int32_t elems_per_access;   /* generic path: 1 or 16 / element size; vector path: 16 / element size */
     int32_t rows_per_block;     /* rows handled by one workgroup */
     int32_t block_threads;      /* workgroup size */
+    /* Vector path only (0 on the generic path).  Memory hints that change
+     * speed, never results; compiled combinations (load_nt, store_nt,
+     * weight_lds): (0,0,0), (1,1,0), (0,1,0), (1,1,1). */
+    int32_t load_nt;            /* x / residual loads marked non-temporal */
+    int32_t store_nt;           /* out / x / residual stores marked non-temporal */
+    int32_t weight_lds;         /* weight staged once per workgroup in LDS */
 } ks_plan_t;
 
 /*
@@ -121,33 +127,31 @@ ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight,
                                   ks_dtype_t dtype, hipStream_t stream);
 
 /*
- * The launch plan the two calls above would use for this hidden size and
- * dtype (a pure function of op, dtype, hidden and alignment; never of rows).
- * `aligned` != 0 means all buffers are 16-byte aligned.  No HIP call.
- * Returns KS_ERROR_INVALID_VALUE for a NULL plan or a bad hidden size.
+ * The launch plan the two calls above use.  The way a row is split across
+ * threads (path, threads_per_row, vectors_per_thread, elems_per_access), and
+ * with it the summation order, is a function of op, dtype, hidden and
+ * alignment only; the memory hints may also depend on rows.  `aligned` != 0
+ * means all buffers are 16-byte aligned.  No HIP call.  Returns
+ * KS_ERROR_INVALID_VALUE for a NULL plan, rows < 0 or a bad hidden size.
  */
-ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t hidden, int aligned,
+ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned,
                         ks_plan_t *plan);
 
 /*
- * Variants of the two operations with an explicit plan and optional timing.
- * plan         NULL = the plan ks_get_plan returns.  Otherwise it must name a
- *              compiled configuration that covers the row and whose path fits
- *              the buffers' alignment; else KS_ERROR_INVALID_VALUE.  Results
- *              are identical in value to the default plan's up to the
- *              reduction order.
- * start, stop  NULL, or two events that HIP records at the start and the end
- *              of the kernel itself (hipExtLaunchKernelGGL), for timing.
+ * The two operations with an explicit launch plan (for tuning and for
+ * testing every compiled kernel).
+ * plan  NULL = the plan ks_get_plan returns.  Otherwise it must name a
+ *       compiled configuration that covers the row and whose path fits the
+ *       buffers' alignment; else KS_ERROR_INVALID_VALUE.  Every plan computes
+ *       the same contract; plans differ only in the fp32 summation order.
  */
 ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight,
                            int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
-                           const ks_plan_t *plan, hipEvent_t start, hipEvent_t stop,
-                           hipStream_t stream);
+                           const ks_plan_t *plan, hipStream_t stream);
 
 ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight,
                                      int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
-                                     const ks_plan_t *plan, hipEvent_t start, hipEvent_t stop,
-                                     hipStream_t stream);
+                                     const ks_plan_t *plan, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *ks_status_string(ks_status_t status);

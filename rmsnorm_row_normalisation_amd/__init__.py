@@ -9,7 +9,6 @@ from .binding import (  # noqa: F401
     KsTypeError,
     KsValueError,
     Plan,
-    Timing,
     fused_add_rms_norm,
     get_plan,
     ks_fused_add_rms_norm,

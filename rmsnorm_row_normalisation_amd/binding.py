@@ -13,8 +13,6 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass
-
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +51,9 @@ class Plan(ctypes.Structure):
         ("elems_per_access", ctypes.c_int32),
         ("rows_per_block", ctypes.c_int32),
         ("block_threads", ctypes.c_int32),
+        ("load_nt", ctypes.c_int32),
+        ("store_nt", ctypes.c_int32),
+        ("weight_lds", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -60,7 +61,7 @@ class Plan(ctypes.Structure):
 
     @classmethod
     def from_dict(cls, d: dict) -> "Plan":
-        return cls(**{k: int(d[k]) for k, _ in cls._fields_})
+        return cls(**{k: int(d.get(k, 0)) for k, _ in cls._fields_})
 
 
 _lib: ctypes.CDLL | None = None
@@ -82,9 +83,9 @@ def lib() -> ctypes.CDLL:
         i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
         h.ks_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
         h.ks_fused_add_rms_norm.argtypes = [vp, vp, vp, i64, i64, f32, i32, vp]
-        h.ks_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp]
-        h.ks_fused_add_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp, vp, vp]
-        h.ks_get_plan.argtypes = [i32, i32, i64, i32, ctypes.POINTER(Plan)]
+        h.ks_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
+        h.ks_fused_add_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
+        h.ks_get_plan.argtypes = [i32, i32, i64, i64, i32, ctypes.POINTER(Plan)]
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
         h.ks_last_hip_error.argtypes = []
@@ -122,20 +123,20 @@ def ks_fused_add_rms_norm(x: int, residual: int, weight: int, rows: int, hidden:
 
 
 def ks_rms_norm_ex(out: int, x: int, weight: int, rows: int, hidden: int, eps: float, dtype: int,
-                   plan: Plan | None, start: int | None, stop: int | None, stream: int) -> int:
+                   plan: Plan | None, stream: int) -> int:
     return lib().ks_rms_norm_ex(out, x, weight, rows, hidden, eps, dtype,
-                                ctypes.byref(plan) if plan is not None else None, start, stop, stream)
+                                ctypes.byref(plan) if plan is not None else None, stream)
 
 
 def ks_fused_add_rms_norm_ex(x: int, residual: int, weight: int, rows: int, hidden: int, eps: float, dtype: int,
-                             plan: Plan | None, start: int | None, stop: int | None, stream: int) -> int:
+                             plan: Plan | None, stream: int) -> int:
     return lib().ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype,
-                                          ctypes.byref(plan) if plan is not None else None, start, stop, stream)
+                                          ctypes.byref(plan) if plan is not None else None, stream)
 
 
-def ks_get_plan(op: int, dtype: int, hidden: int, aligned: bool = True) -> Plan:
+def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True) -> Plan:
     plan = Plan()
-    _check(lib().ks_get_plan(op, dtype, hidden, int(bool(aligned)), ctypes.byref(plan)), "ks_get_plan")
+    _check(lib().ks_get_plan(op, dtype, rows, hidden, int(bool(aligned)), ctypes.byref(plan)), "ks_get_plan")
     return plan
 
 
@@ -146,18 +147,6 @@ def ks_version() -> str:
 # ---------------------------------------------------------------------------
 # Tensor-level API.
 # ---------------------------------------------------------------------------
-@dataclass
-class Timing:
-    """Two HIP events (``torch.cuda.Event(enable_timing=True)``) that the library
-    records at the start and the end of the kernel itself."""
-
-    start: torch.cuda.Event
-    stop: torch.cuda.Event
-
-    def handles(self) -> tuple[int, int]:
-        return int(self.start.cuda_event), int(self.stop.cuda_event)
-
-
 def _check_tensors(op: str, x: torch.Tensor, weight: torch.Tensor, *others: torch.Tensor) -> tuple[int, int]:
     if x.dtype not in KS_DTYPE:
         raise TypeError(f"{op}: unsupported dtype {x.dtype}")
@@ -185,12 +174,8 @@ def _stream(x: torch.Tensor) -> int:
     return int(torch.cuda.current_stream(x.device).cuda_stream)
 
 
-def _events(timing: Timing | None) -> tuple[int | None, int | None]:
-    return timing.handles() if timing is not None else (None, None)
-
-
 def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *, out: torch.Tensor | None = None,
-             plan: Plan | None = None, timing: Timing | None = None) -> torch.Tensor:
+             plan: Plan | None = None) -> torch.Tensor:
     """RMSNorm over the last dimension; returns ``out`` (a new tensor unless given; may be ``x``)."""
     rows, hidden = _check_tensors("rms_norm", x, weight)
     if out is None:
@@ -199,27 +184,26 @@ def rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *, out: t
         _check_tensors("rms_norm", out, weight)
         if out.shape != x.shape:
             raise ValueError("rms_norm: out must have the shape of x")
-    start, stop = _events(timing)
     with torch.cuda.device(x.device):
         st = ks_rms_norm_ex(out.data_ptr(), x.data_ptr(), weight.data_ptr(), rows, hidden, float(eps),
-                            KS_DTYPE[x.dtype], plan, start, stop, _stream(x))
+                            KS_DTYPE[x.dtype], plan, _stream(x))
     _check(st, "ks_rms_norm")
     return out
 
 
 def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
-                       plan: Plan | None = None, timing: Timing | None = None) -> None:
+                       plan: Plan | None = None) -> None:
     """In place: residual <- cast(x + residual); x <- RMSNorm of the fp32 sum.  Returns None."""
     rows, hidden = _check_tensors("fused_add_rms_norm", x, weight, residual)
     if residual.shape != x.shape:
         raise ValueError("fused_add_rms_norm: residual must have the shape of x")
-    start, stop = _events(timing)
     with torch.cuda.device(x.device):
         st = ks_fused_add_rms_norm_ex(x.data_ptr(), residual.data_ptr(), weight.data_ptr(), rows, hidden,
-                                      float(eps), KS_DTYPE[x.dtype], plan, start, stop, _stream(x))
+                                      float(eps), KS_DTYPE[x.dtype], plan, _stream(x))
     _check(st, "ks_fused_add_rms_norm")
 
 
-def get_plan(op: str, dtype: torch.dtype, hidden: int, aligned: bool = True) -> Plan:
+def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: bool = True) -> Plan:
+    """The plan the library picks for this op, dtype, row size and batch (ks_get_plan)."""
     code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM}[op]
-    return ks_get_plan(code, KS_DTYPE[dtype], hidden, aligned)
+    return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned)

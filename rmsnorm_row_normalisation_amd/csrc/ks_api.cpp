@@ -46,18 +46,38 @@ bool overlaps(const void *a, int64_t n, const void *b, int64_t m)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The launch policy: a function of op, dtype, hidden and alignment only.
+// The launch policy.
 //
-// Vector path (aligned buffers, row bytes a multiple of 16): the smallest
-// power-of-two team of 8..1024 lanes that holds the row with at most 8
-// sixteen-byte pieces per lane (4 for 1024-lane teams).  A small team keeps
-// many rows in flight per workgroup; a full row per lane group keeps every
-// byte read once.  Rows too wide for that use the generic path with 16-byte
-// accesses.  Everything else uses the generic path with scalar accesses and a
-// team sized to the row.
-ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned)
+// Row split (sets the summation order, so a function of op, dtype, hidden and
+// alignment only): on the vector path (aligned buffers, row bytes a multiple
+// of 16) the smallest power-of-two team of 8..1024 lanes that holds the row
+// with at most 8 sixteen-byte pieces per lane (4 for 1024-lane teams); rows
+// too wide for that take the generic path with 16-byte accesses; everything
+// else takes the generic path with scalar accesses and a team sized to the
+// row.
+//
+// Memory hints (speed only): stores are marked non-temporal (the data is not
+// re-read by this kernel); loads too, except for rms_norm over batches larger
+// than the last-level cache, where default loads measured faster; the fused
+// kernel stages the weight in LDS when a workgroup holds several rows.
+void choose_hints(ks_op_t op, int64_t rows, int64_t row_bytes, ks_plan_t *plan)
 {
-    (void)op;
+    if (plan->path != KS_PATH_VECTOR)
+        return;
+    const int64_t batch_bytes = rows * row_bytes;
+    constexpr int64_t kLargeBatch = int64_t(64) << 20;
+    plan->store_nt = 1;
+    if (op == KS_OP_RMS_NORM) {
+        plan->load_nt = batch_bytes >= kLargeBatch ? 0 : 1;
+        plan->weight_lds = 0;
+    } else {
+        plan->load_nt = 1;
+        plan->weight_lds = plan->rows_per_block >= 2 ? 1 : 0;
+    }
+}
+
+ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned)
+{
     ks_plan_t plan;
     memset(&plan, 0, sizeof(plan));
     const int64_t esize = elem_size(dtype);
@@ -74,6 +94,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned)
                 plan.elems_per_access = vec_elems;
                 plan.block_threads = ks::block_threads_for(tpr);
                 plan.rows_per_block = plan.block_threads / tpr;
+                choose_hints(op, rows, row_bytes, &plan);
                 return plan;
             }
         }
@@ -91,6 +112,15 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned)
     return plan;
 }
 
+// Whether the hint combination is one of the compiled variants.
+bool hints_compiled(const ks_plan_t &p)
+{
+    const int key = (p.load_nt ? 4 : 0) | (p.store_nt ? 2 : 0) | (p.weight_lds ? 1 : 0);
+    if ((p.load_nt | p.store_nt | p.weight_lds) & ~1)
+        return false;
+    return key == 0 || key == 6 || key == 2 || key == 7;
+}
+
 // Whether an explicit plan names a compiled kernel that covers this row and
 // suits the buffers' alignment.
 bool plan_fits(const ks_plan_t &p, ks_dtype_t dtype, int64_t hidden, bool aligned)
@@ -100,7 +130,7 @@ bool plan_fits(const ks_plan_t &p, ks_dtype_t dtype, int64_t hidden, bool aligne
     const int vec_elems = (int)(16 / esize);
     const bool vec_ok = aligned && row_bytes % 16 == 0;
     if (p.path == KS_PATH_VECTOR) {
-        if (!vec_ok || !is_pow2_team(p.threads_per_row))
+        if (!vec_ok || !is_pow2_team(p.threads_per_row) || !hints_compiled(p))
             return false;
         const int maxv = p.threads_per_row == ks::kMaxTpr ? ks::kMaxVptAt1024 : ks::kMaxVpt;
         if (p.vectors_per_thread < 1 || p.vectors_per_thread > maxv)
@@ -114,7 +144,7 @@ bool plan_fits(const ks_plan_t &p, ks_dtype_t dtype, int64_t hidden, bool aligne
         const int t = p.threads_per_row;
         if (t != 8 && t != 64 && t != 256 && t != 1024)
             return false;
-        if (p.vectors_per_thread != 0)
+        if (p.vectors_per_thread != 0 || p.load_nt != 0 || p.store_nt != 0 || p.weight_lds != 0)
             return false;
         if (p.elems_per_access != 1 && !(p.elems_per_access == vec_elems && vec_ok))
             return false;
@@ -127,10 +157,17 @@ bool plan_fits(const ks_plan_t &p, ks_dtype_t dtype, int64_t hidden, bool aligne
 ks_status_t launch(ks::Launch &l, ks_dtype_t dtype)
 {
     hipError_t err;
+    const bool vec = l.plan.path == KS_PATH_VECTOR;
     switch (dtype) {
-    case KS_DTYPE_FLOAT32: err = ks::launch_f32(l); break;
-    case KS_DTYPE_FLOAT16: err = ks::launch_f16(l); break;
-    default: err = ks::launch_bf16(l); break;
+    case KS_DTYPE_FLOAT32:
+        err = !vec ? ks::launch_generic_f32(l) : l.fused ? ks::launch_vec_f32_fused(l) : ks::launch_vec_f32_rms(l);
+        break;
+    case KS_DTYPE_FLOAT16:
+        err = !vec ? ks::launch_generic_f16(l) : l.fused ? ks::launch_vec_f16_fused(l) : ks::launch_vec_f16_rms(l);
+        break;
+    default:
+        err = !vec ? ks::launch_generic_bf16(l) : l.fused ? ks::launch_vec_bf16_fused(l) : ks::launch_vec_bf16_rms(l);
+        break;
     }
     if (err != hipSuccess) {
         g_last_hip_error = (int)err;
@@ -139,11 +176,11 @@ ks_status_t launch(ks::Launch &l, ks_dtype_t dtype)
     return KS_SUCCESS;
 }
 
-ks_status_t select_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned,
-                        ks_plan_t *out)
+ks_status_t select_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden,
+                        bool aligned, ks_plan_t *out)
 {
     if (requested == nullptr) {
-        *out = policy(op, dtype, hidden, aligned);
+        *out = policy(op, dtype, rows, hidden, aligned);
         return KS_SUCCESS;
     }
     if (!plan_fits(*requested, dtype, hidden, aligned))
@@ -152,26 +189,21 @@ ks_status_t select_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype
     return KS_SUCCESS;
 }
 
-bool events_ok(hipEvent_t start, hipEvent_t stop) { return (start == nullptr) == (stop == nullptr); }
-
 }  // namespace
 
 extern "C" {
 
 ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t rows, int64_t hidden, float eps,
-                           ks_dtype_t dtype, const ks_plan_t *plan, hipEvent_t start, hipEvent_t stop,
-                           hipStream_t stream)
+                           ks_dtype_t dtype, const ks_plan_t *plan, hipStream_t stream)
 {
     ks_status_t st = check_sizes(dtype, rows, hidden, eps);
     if (st != KS_SUCCESS)
         return st;
-    if (!events_ok(start, stop))
-        return KS_ERROR_INVALID_VALUE;
     if (rows > 0 && (out == nullptr || x == nullptr || weight == nullptr))
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(out) && aligned16(x) && aligned16(weight);
-    ks::Launch l{out, x, nullptr, weight, rows, (int32_t)hidden, eps, false, {}, start, stop, stream};
-    st = select_plan(plan, KS_OP_RMS_NORM, dtype, hidden, aligned, &l.plan);
+    ks::Launch l{out, x, nullptr, weight, rows, (int32_t)hidden, eps, false, {}, stream};
+    st = select_plan(plan, KS_OP_RMS_NORM, dtype, rows, hidden, aligned, &l.plan);
     if (st != KS_SUCCESS || rows == 0)
         return st;
     const int64_t es = elem_size(dtype);
@@ -186,23 +218,20 @@ ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t
 ks_status_t ks_rms_norm(void *out, const void *x, const void *weight, int64_t rows, int64_t hidden, float eps,
                         ks_dtype_t dtype, hipStream_t stream)
 {
-    return ks_rms_norm_ex(out, x, weight, rows, hidden, eps, dtype, nullptr, nullptr, nullptr, stream);
+    return ks_rms_norm_ex(out, x, weight, rows, hidden, eps, dtype, nullptr, stream);
 }
 
 ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight, int64_t rows, int64_t hidden,
-                                     float eps, ks_dtype_t dtype, const ks_plan_t *plan, hipEvent_t start,
-                                     hipEvent_t stop, hipStream_t stream)
+                                     float eps, ks_dtype_t dtype, const ks_plan_t *plan, hipStream_t stream)
 {
     ks_status_t st = check_sizes(dtype, rows, hidden, eps);
     if (st != KS_SUCCESS)
         return st;
-    if (!events_ok(start, stop))
-        return KS_ERROR_INVALID_VALUE;
     if (rows > 0 && (x == nullptr || residual == nullptr || weight == nullptr))
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(x) && aligned16(residual) && aligned16(weight);
-    ks::Launch l{x, x, residual, weight, rows, (int32_t)hidden, eps, true, {}, start, stop, stream};
-    st = select_plan(plan, KS_OP_FUSED_ADD_RMS_NORM, dtype, hidden, aligned, &l.plan);
+    ks::Launch l{x, x, residual, weight, rows, (int32_t)hidden, eps, true, {}, stream};
+    st = select_plan(plan, KS_OP_FUSED_ADD_RMS_NORM, dtype, rows, hidden, aligned, &l.plan);
     if (st != KS_SUCCESS || rows == 0)
         return st;
     const int64_t es = elem_size(dtype);
@@ -216,18 +245,17 @@ ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight
 ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight, int64_t rows, int64_t hidden,
                                   float eps, ks_dtype_t dtype, hipStream_t stream)
 {
-    return ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype, nullptr, nullptr, nullptr,
-                                    stream);
+    return ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype, nullptr, stream);
 }
 
-ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t hidden, int aligned, ks_plan_t *plan)
+ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned, ks_plan_t *plan)
 {
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
-    if (plan == nullptr || hidden <= 0 || hidden > kMaxHidden ||
+    if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
         (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM))
         return KS_ERROR_INVALID_VALUE;
-    *plan = policy(op, dtype, hidden, aligned != 0);
+    *plan = policy(op, dtype, rows, hidden, aligned != 0);
     return KS_SUCCESS;
 }
 

@@ -20,11 +20,10 @@
 //                   size is not a multiple of 16, and rows wider than the
 //                   vector kernel holds in registers.
 //
-// Reduction: per-lane fp32 FMA chain in a fixed order, then a fixed tree
-// across the team (DPP within rows of 16 lanes, cross-row swaps, and an LDS
-// combine in wave order when a row spans several waves).  The tree depends
-// only on the plan, and the plan only on (op, dtype, hidden), so a row's
-// result never depends on the batch it is in.
+// Reduction: the vector kernel sums every row in one canonical order that is
+// the same for every launch shape (see "Reductions" below), so its results do
+// not depend on the plan or on the batch a row is in.  The generic kernel's
+// order depends on its plan, which depends only on (op, dtype, hidden).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -146,53 +145,95 @@ template <> struct Scalar<_Float16> {
 };
 
 // ---------------------------------------------------------------------------
-// Reductions.  Every lane of a team ends with the bitwise same sum: each step
-// adds a value to its partner's value, and fp32 addition is commutative.
+// Reductions.
+//
+// The vector kernel sums a row in one canonical order that does not depend on
+// the launch shape: each 16-byte piece p (bytes [16p, 16p + 16) of the row) is
+// summed element by element in index order (an FMA chain), then the piece
+// sums are combined by folding in half: with n the row's piece count rounded
+// up to a power of two (missing pieces are zero), s[p] += s[p + n/2] for all
+// p < n/2, then n /= 2, until one value is left.  A lane holding pieces
+// lane + k * kTpr performs the levels with n/2 >= kTpr locally (k with
+// k + n/(2 kTpr)), the levels 64 <= n/2 < kTpr across waves through LDS, and
+// the last levels as an XOR butterfly inside the wave.  Every power-of-two
+// team size therefore produces the bitwise same sum, so plans may differ
+// between batch sizes without changing any result.  Each step adds two
+// values; fp32 addition is commutative, so partner lanes agree bitwise.
 // ---------------------------------------------------------------------------
 template <int kCtrl> __device__ __forceinline__ float dpp_add(float v)
 {
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
 }
 
-// Sum over aligned groups of kWidth lanes (kWidth in 8, 16, 32, 64).
-template <int kWidth> __device__ __forceinline__ float group_sum(float v)
+// v + (v of lane ^ kMask), kMask a power of two below 64.
+template <int kMask> __device__ __forceinline__ float xor_add(float v)
 {
-    static_assert(kWidth == 8 || kWidth == 16 || kWidth == 32 || kWidth == 64, "group width");
-    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
-    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]: quads
-    v = dpp_add<0x141>(v);   // row_half_mirror: groups of 8
-    if constexpr (kWidth >= 16)
-        v = dpp_add<0x140>(v);   // row_mirror: rows of 16
-    if constexpr (kWidth >= 32)
-        v += __shfl_xor(v, 16, 64);
-    if constexpr (kWidth >= 64)
-        v += __shfl_xor(v, 32, 64);
+    if constexpr (kMask == 1)
+        return dpp_add<0xB1>(v);                     // quad_perm [1,0,3,2]
+    else if constexpr (kMask == 2)
+        return dpp_add<0x4E>(v);                     // quad_perm [2,3,0,1]
+    else if constexpr (kMask <= 16)                  // ds_swizzle bit mode: lane ^ kMask within 32 lanes
+        return v + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (kMask << 10)));
+    else
+        return v + __shfl_xor(v, kMask, 64);
+}
+
+// Butterfly over aligned groups of kWidth lanes, masks kWidth/2 down to 1.
+template <int kWidth> __device__ __forceinline__ float butterfly(float v)
+{
+    if constexpr (kWidth >= 2) {
+        v = xor_add<kWidth / 2>(v);
+        v = butterfly<kWidth / 2>(v);
+    }
     return v;
 }
 
-// Sum over a team of kTpr lanes inside a block of kBlock threads.  Teams wider
-// than a wave combine their waves' sums through LDS in wave order.  Every
-// thread of the block must call this (it may contain a barrier).
-template <int kTpr, int kBlock> __device__ __forceinline__ float team_sum(float v)
+// Local folding of kSlots partial sums (kSlots rounded up to a power of two,
+// missing slots count as zero); returns the fold of all of them.
+template <int kSlots> __device__ __forceinline__ float local_fold(float *part)
+{
+    constexpr int kP2 = kSlots <= 1 ? 1 : kSlots <= 2 ? 2 : kSlots <= 4 ? 4 : 8;
+    static_assert(kSlots <= 8, "at most 8 slots per lane");
+#pragma unroll
+    for (int n = kP2; n > 1; n /= 2)
+#pragma unroll
+        for (int k = 0; k < n / 2; ++k)
+            if (k + n / 2 < kSlots)
+                part[k] = part[k] + part[k + n / 2];
+    return part[0];
+}
+
+// Finish the canonical fold across a team of kTpr lanes (kTpr a power of two)
+// in a block of kBlock threads.  Every thread of the block must call this.
+template <int kTpr, int kBlock> __device__ __forceinline__ float team_fold(float v)
 {
     if constexpr (kTpr <= 64) {
-        return group_sum<kTpr>(v);
+        return butterfly<kTpr>(v);
     } else {
-        constexpr int kWaves = kBlock / 64;
-        constexpr int kWavesPerTeam = kTpr / 64;
-        __shared__ float part[kWaves];
-        const int wave = threadIdx.x >> 6;
-        const float wsum = group_sum<64>(v);
-        if ((threadIdx.x & 63) == 0)
-            part[wave] = wsum;
+        constexpr int kWaves = kTpr / 64;            // waves per row
+        __shared__ float lanes[kBlock];
+        lanes[threadIdx.x] = v;
         __syncthreads();
-        const int first = (wave / kWavesPerTeam) * kWavesPerTeam;
-        float t = part[first];
+        const int lane = threadIdx.x & 63;
+        const int first = (threadIdx.x / kTpr) * kTpr;
+        float a[kWaves];
 #pragma unroll
-        for (int i = 1; i < kWavesPerTeam; ++i)
-            t += part[first + i];
-        return t;
+        for (int j = 0; j < kWaves; ++j)
+            a[j] = lanes[first + j * 64 + lane];
+#pragma unroll
+        for (int n = kWaves; n > 1; n /= 2)
+#pragma unroll
+            for (int j = 0; j < n / 2; ++j)
+                a[j] = a[j] + a[j + n / 2];
+        return butterfly<64>(a[0]);
     }
+}
+
+// Sum over a team of kTpr lanes (generic path: any order that depends only on
+// the plan).  Every thread of the block must call this.
+template <int kTpr, int kBlock> __device__ __forceinline__ float team_sum(float v)
+{
+    return team_fold<kTpr, kBlock>(v);
 }
 
 // rsqrt(sum / H + eps) with fp32 mean and add, and a correctly rounded
@@ -206,8 +247,14 @@ __device__ __forceinline__ float row_scale(float sum_sq, int32_t hidden, float e
 
 // ---------------------------------------------------------------------------
 // Vector kernel: row held in VGPRs.
+//
+// kLoadCpol / kStoreCpol: cache-policy bits of the streamed x / residual /
+// out accesses (0 = default, 2 = non-temporal).  kWeightLds: the workgroup
+// first stages the weight row in LDS (one HBM/L2 read per workgroup instead
+// of one per row); needs row_bytes of dynamic LDS.
 // ---------------------------------------------------------------------------
-template <typename T, bool kFused, int kTpr, int kVpt, int kBlock, int kCpol>
+template <typename T, bool kFused, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol,
+          bool kWeightLds>
 __global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
 {
     constexpr int kE = Pack<T>::kElems;
@@ -226,33 +273,70 @@ __global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
     const auto ry = make_rsrc((char *)p.y + base, blk_bytes);
     const auto rw = make_rsrc(p.w, row_bytes);
 
-    uint32_t off[kVpt], woff[kVpt];
+    uint32_t off[kVpt];
+    bool in_row[kVpt];
 #pragma unroll
     for (int k = 0; k < kVpt; ++k) {
         const uint32_t c = (uint32_t)(k * kTpr + lane) * 16u;
-        const bool in_row = c < row_bytes;
-        off[k] = in_row ? (uint32_t)team * row_bytes + c : kOutOfRange;
-        woff[k] = in_row ? c : kOutOfRange;
+        in_row[k] = c < row_bytes;
+        off[k] = in_row[k] ? (uint32_t)team * row_bytes + c : kOutOfRange;
+    }
+
+    // weight staging loads go out first, so waiting for them does not wait for x
+    constexpr int kStage = kWeightLds ? 1 : 0;
+    extern __shared__ u32x4 wlds[];
+    u32x4 wst[kStage ? (kVpt * kTpr + kBlock - 1) / kBlock : 1];
+    if constexpr (kWeightLds) {
+#pragma unroll
+        for (int i = 0; i < (kVpt * kTpr + kBlock - 1) / kBlock; ++i) {
+            const uint32_t c = (uint32_t)(i * kBlock + tid) * 16u;
+            wst[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, c < row_bytes ? c : kOutOfRange, 0, 0);
+        }
     }
 
     u32x4 xv[kVpt], wv[kVpt];
 #pragma unroll
     for (int k = 0; k < kVpt; ++k)
-        xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kCpol);
+        xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kLoadCpol);
+    u32x4 rv[kFused ? kVpt : 1];
+    const auto rr = make_rsrc((char *)p.res + base, kFused ? blk_bytes : 0u);
+    if constexpr (kFused) {
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            rv[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, off[k], 0, kLoadCpol);
+    }
 
-    float sum_sq = 0.0f;
+    if constexpr (kWeightLds) {
+#pragma unroll
+        for (int i = 0; i < (kVpt * kTpr + kBlock - 1) / kBlock; ++i) {
+            const int v = i * kBlock + tid;
+            if (v < kVpt * kTpr)
+                wlds[v] = wst[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            wv[k] = wlds[k * kTpr + lane];     // pieces past the row hold zeros
+    } else {
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            wv[k] = __builtin_amdgcn_raw_buffer_load_b128(rw, in_row[k] ? (uint32_t)(k * kTpr + lane) * 16u
+                                                                          : kOutOfRange, 0, 0);
+    }
+
+    float part[kVpt];   // per-piece sums of squares, elements in index order
     if constexpr (!kFused) {
 #pragma unroll
-        for (int k = 0; k < kVpt; ++k)
-            wv[k] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[k], 0, 0);
-#pragma unroll
-        for (int k = 0; k < kVpt; ++k)
+        for (int k = 0; k < kVpt; ++k) {
+            float a = 0.0f;
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
                 const float v = Pack<T>::get(xv[k], e);
-                sum_sq = __builtin_fmaf(v, v, sum_sq);
+                a = __builtin_fmaf(v, v, a);
             }
-        const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq), p.hidden, p.eps);
+            part[k] = a;
+        }
+        const float scale = row_scale(team_fold<kTpr, kBlock>(local_fold<kVpt>(part)), p.hidden, p.eps);
 #pragma unroll
         for (int k = 0; k < kVpt; ++k) {
             float o[kE];
@@ -261,30 +345,24 @@ __global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
                 const float t = Pack<T>::get(xv[k], e) * scale;
                 o[e] = t * Pack<T>::get(wv[k], e);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kStoreCpol);
         }
     } else {
-        const auto rr = make_rsrc((char *)p.res + base, blk_bytes);
-        u32x4 rv[kVpt];
-#pragma unroll
-        for (int k = 0; k < kVpt; ++k)
-            rv[k] = __builtin_amdgcn_raw_buffer_load_b128(rr, off[k], 0, kCpol);
-#pragma unroll
-        for (int k = 0; k < kVpt; ++k)
-            wv[k] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[k], 0, 0);
         float s[kVpt][kE];
 #pragma unroll
         for (int k = 0; k < kVpt; ++k) {
+            float a = 0.0f;
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
                 s[k][e] = Pack<T>::get(xv[k], e) + Pack<T>::get(rv[k], e);
-                sum_sq = __builtin_fmaf(s[k][e], s[k][e], sum_sq);
+                a = __builtin_fmaf(s[k][e], s[k][e], a);
             }
+            part[k] = a;
             // this lane has read every element it will write: store the
             // rounded residual now, so the writes start before the reduction
-            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(s[k]), rr, off[k], 0, kCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(s[k]), rr, off[k], 0, kStoreCpol);
         }
-        const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq), p.hidden, p.eps);
+        const float scale = row_scale(team_fold<kTpr, kBlock>(local_fold<kVpt>(part)), p.hidden, p.eps);
 #pragma unroll
         for (int k = 0; k < kVpt; ++k) {
             float o[kE];
@@ -293,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
                 const float t = s[k][e] * scale;
                 o[e] = t * Pack<T>::get(wv[k], e);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kCpol);
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kStoreCpol);
         }
     }
 }

@@ -21,20 +21,24 @@ struct Launch {
     float eps;
     bool fused;
     ks_plan_t plan;
-    hipEvent_t start;
-    hipEvent_t stop;
     hipStream_t stream;
 };
 
-// Cache-policy bits for the streamed (x, residual, out) buffer accesses.
-// 0 = default; 2 = non-temporal.  Weight accesses always use the default.
-constexpr int kStreamCpol = 0;
+// Cache-policy bits of a buffer instruction that marks it non-temporal.
+constexpr int kNonTemporal = 2;
 
-// Launch the kernel the plan names for one dtype.  Returns hipErrorInvalidValue
-// when no kernel was compiled for the plan (plan_fits rules that out).
-hipError_t launch_f32(const Launch &l);
-hipError_t launch_f16(const Launch &l);
-hipError_t launch_bf16(const Launch &l);
+// Launch the kernel the plan names, one function per path, dtype and op (each
+// in its own translation unit so they compile in parallel).  Return
+// hipErrorInvalidValue when no kernel was compiled for the plan (plan_fits
+// rules that out before a launch).
+#define KS_DECLARE_LAUNCH(dt)                          \
+    hipError_t launch_vec_##dt##_rms(const Launch &l);   \
+    hipError_t launch_vec_##dt##_fused(const Launch &l); \
+    hipError_t launch_generic_##dt(const Launch &l);
+KS_DECLARE_LAUNCH(f32)
+KS_DECLARE_LAUNCH(f16)
+KS_DECLARE_LAUNCH(bf16)
+#undef KS_DECLARE_LAUNCH
 
 // Vector path limits: threads per row 8..1024 (powers of two), vectors per
 // thread 1..8 (1..4 when a row spans 1024 threads, to stay within the VGPR

@@ -2,7 +2,6 @@
 // per-dtype translation unit includes this once and defines its launch_*.
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "ks_device.hpp"
@@ -11,36 +10,48 @@
 namespace ks {
 
 template <typename Kernel>
-hipError_t run(Kernel kernel, const Launch &l, int block)
+hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
 {
     Params p{l.y, l.x, l.res, l.w, l.rows, l.hidden, l.eps};
     const int64_t rpb = block / l.plan.threads_per_row;
     const dim3 grid((unsigned)((l.rows + rpb - 1) / rpb));
-    if (l.start != nullptr)
-        hipExtLaunchKernelGGL(kernel, grid, dim3(block), 0, l.stream, l.start, l.stop, 0, p);
-    else
-        hipLaunchKernelGGL(kernel, grid, dim3(block), 0, l.stream, p);
+    hipLaunchKernelGGL(kernel, grid, dim3(block), lds_bytes, l.stream, p);
     return hipGetLastError();
+}
+
+// The compiled memory-hint variants of one launch shape.
+template <typename T, bool F, int TPR, int V>
+hipError_t vec_one(const Launch &l)
+{
+    constexpr int B = TPR < 256 ? 256 : TPR;
+    const ks_plan_t &p = l.plan;
+    if (!p.load_nt && !p.store_nt && !p.weight_lds)
+        return run(vec_kernel<T, F, TPR, V, B, 0, 0, false>, l, B);
+    if (p.load_nt && p.store_nt && !p.weight_lds)
+        return run(vec_kernel<T, F, TPR, V, B, kNonTemporal, kNonTemporal, false>, l, B);
+    if (!p.load_nt && p.store_nt && !p.weight_lds)
+        return run(vec_kernel<T, F, TPR, V, B, 0, kNonTemporal, false>, l, B);
+    if (p.load_nt && p.store_nt && p.weight_lds)
+        return run(vec_kernel<T, F, TPR, V, B, kNonTemporal, kNonTemporal, true>, l, B, (size_t)V * TPR * 16);
+    return hipErrorInvalidValue;
 }
 
 template <typename T, bool F, int TPR>
 hipError_t vec_by_vpt(const Launch &l)
 {
-    constexpr int B = TPR < 256 ? 256 : TPR;
-    constexpr int C = kStreamCpol;
     switch (l.plan.vectors_per_thread) {
-    case 1: return run(vec_kernel<T, F, TPR, 1, B, C>, l, B);
-    case 2: return run(vec_kernel<T, F, TPR, 2, B, C>, l, B);
-    case 3: return run(vec_kernel<T, F, TPR, 3, B, C>, l, B);
-    case 4: return run(vec_kernel<T, F, TPR, 4, B, C>, l, B);
+    case 1: return vec_one<T, F, TPR, 1>(l);
+    case 2: return vec_one<T, F, TPR, 2>(l);
+    case 3: return vec_one<T, F, TPR, 3>(l);
+    case 4: return vec_one<T, F, TPR, 4>(l);
     default: break;
     }
     if constexpr (TPR < kMaxTpr) {
         switch (l.plan.vectors_per_thread) {
-        case 5: return run(vec_kernel<T, F, TPR, 5, B, C>, l, B);
-        case 6: return run(vec_kernel<T, F, TPR, 6, B, C>, l, B);
-        case 7: return run(vec_kernel<T, F, TPR, 7, B, C>, l, B);
-        case 8: return run(vec_kernel<T, F, TPR, 8, B, C>, l, B);
+        case 5: return vec_one<T, F, TPR, 5>(l);
+        case 6: return vec_one<T, F, TPR, 6>(l);
+        case 7: return vec_one<T, F, TPR, 7>(l);
+        case 8: return vec_one<T, F, TPR, 8>(l);
         default: break;
         }
     }
@@ -75,18 +86,14 @@ hipError_t generic_by_tpr(const Launch &l)
     }
 }
 
-template <typename T>
-hipError_t launch_typed(const Launch &l)
+template <typename T, bool F>
+hipError_t launch_generic_typed(const Launch &l)
 {
     constexpr int kVecElems = Pack<T>::kElems;
-    if (l.plan.path == KS_PATH_VECTOR)
-        return l.fused ? vec_by_tpr<T, true>(l) : vec_by_tpr<T, false>(l);
-    if (l.plan.path == KS_PATH_GENERIC) {
-        if (l.plan.elems_per_access == 1)
-            return l.fused ? generic_by_tpr<T, true, 1>(l) : generic_by_tpr<T, false, 1>(l);
-        if (l.plan.elems_per_access == kVecElems)
-            return l.fused ? generic_by_tpr<T, true, kVecElems>(l) : generic_by_tpr<T, false, kVecElems>(l);
-    }
+    if (l.plan.elems_per_access == 1)
+        return generic_by_tpr<T, F, 1>(l);
+    if (l.plan.elems_per_access == kVecElems)
+        return generic_by_tpr<T, F, kVecElems>(l);
     return hipErrorInvalidValue;
 }
 

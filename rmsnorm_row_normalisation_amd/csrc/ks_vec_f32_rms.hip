@@ -1,0 +1,8 @@
+// Vector-path kernels for float, RMSNorm.
+#include "ks_launch.hpp"
+
+namespace ks {
+
+hipError_t launch_vec_f32_rms(const Launch &l) { return vec_by_tpr<float, false>(l); }
+
+}  // namespace ks

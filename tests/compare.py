@@ -4,9 +4,9 @@ The gates follow the parity bar for this operator: the fused residual output
 is bit-exact; normalised outputs are within 1 ulp of the output dtype (or
 |difference| <= 1e-6 near zero) for fp16/bf16, and within rtol = atol = 1e-6
 for fp32 (kernscope README, "Numerical tolerances" table, FP32 row).  Large
-cases must also match bit for bit on at least 99.9% of elements, because a
-1-ulp bound alone cannot tell normalising the unrounded residual sum from
-normalising its rounded copy.
+16-bit cases must also match bit for bit on at least 99.9% of elements,
+because a 1-ulp bound alone cannot tell normalising the unrounded residual
+sum from normalising its rounded copy.
 """
 from __future__ import annotations
 
@@ -86,7 +86,10 @@ def check_normalised(out: torch.Tensor, ref: torch.Tensor, min_exact_rate: float
         near_zero = (o.float() - r.float()).abs() <= 1e-6
         bad = (d > 1) & ~near_zero
         assert not bool(bad.any()), f"more than 1 ulp apart: {st}"
-    if min_exact_rate is not None:
+    # The exact-match gate is for 16-bit outputs, where an fp32 pipeline lands on
+    # the same rounded value almost always.  fp32 outputs carry the fp32 pipeline's
+    # own few-ulp differences (summation order) and are judged by rtol/atol alone.
+    if min_exact_rate is not None and o.dtype != torch.float32:
         assert st.exact_rate >= min_exact_rate, f"exact-match rate below {min_exact_rate}: {st}"
     return st
 

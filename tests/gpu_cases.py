@@ -80,6 +80,9 @@ def check_case(name: str, op: str, inp: dict, eps: float, plan=None, offset: int
     return check_outputs(op, got, ref, exact_rate)
 
 
+HINTS = ((0, 0, 0), (1, 1, 0), (0, 1, 0), (1, 1, 1))   # compiled (load_nt, store_nt, weight_lds)
+
+
 def all_plans(dtype: torch.dtype, hidden: int, aligned: bool = True) -> list:
     """Every compiled plan that covers rows of this size (the library rejects the rest)."""
     es = torch.empty(0, dtype=dtype).element_size()
@@ -93,9 +96,10 @@ def all_plans(dtype: torch.dtype, hidden: int, aligned: bool = True) -> list:
             for vpt in range(1, maxv + 1):
                 if tpr * vpt * 16 >= row_bytes:
                     block = max(256, tpr)
-                    plans.append(ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt,
-                                         elems_per_access=vec_elems, rows_per_block=block // tpr,
-                                         block_threads=block))
+                    for lnt, snt, wlds in HINTS:
+                        plans.append(ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt,
+                                             elems_per_access=vec_elems, rows_per_block=block // tpr,
+                                             block_threads=block, load_nt=lnt, store_nt=snt, weight_lds=wlds))
             tpr *= 2
     for tpr in (8, 64, 256, 1024):
         block = 1024 if tpr == 1024 else 256

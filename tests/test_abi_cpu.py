@@ -59,12 +59,12 @@ def test_status_strings_and_version(lib):
     assert lib.ks_last_hip_error() == 0
 
 
-def rms(out, x, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None, start=None, stop=None):
-    return b.ks_rms_norm_ex(out, x, w, rows, hidden, eps, dtype, plan, start, stop, 0)
+def rms(out, x, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None):
+    return b.ks_rms_norm_ex(out, x, w, rows, hidden, eps, dtype, plan, 0)
 
 
-def fused(x, r, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None, start=None, stop=None):
-    return b.ks_fused_add_rms_norm_ex(x, r, w, rows, hidden, eps, dtype, plan, start, stop, 0)
+def fused(x, r, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None):
+    return b.ks_fused_add_rms_norm_ex(x, r, w, rows, hidden, eps, dtype, plan, 0)
 
 
 @pytest.mark.parametrize("call", [rms, fused])
@@ -82,7 +82,6 @@ def test_invalid_values(call):
     assert call(None, x, w, 4, 4096) == INVALID
     assert call(y, None, w, 4, 4096) == INVALID
     assert call(y, x, None, 4, 4096) == INVALID
-    assert call(y, x, w, 4, 4096, start=A) == INVALID     # one event without the other
     # dtype is checked before sizes
     assert call(y, x, w, -1, 0, dtype=9) == DTYPE
 
@@ -142,6 +141,11 @@ def test_explicit_plans_are_checked():
     assert rms(y, x, w, 4, 4095, plan=_plan(threads_per_row=64, rows_per_block=4,
                                             **{**g, "elems_per_access": 8})) == INVALID
     assert rms(y, x, w, 4, 4096, plan=_plan(threads_per_row=32, rows_per_block=8, **g)) == INVALID
+    # memory hints: only the compiled combinations, and none on the generic path
+    for lnt, snt, wl, ok in ((0, 0, 0, OK), (1, 1, 0, OK), (0, 1, 0, OK), (1, 1, 1, OK), (1, 0, 0, INVALID),
+                             (0, 0, 1, INVALID), (2, 1, 0, INVALID), (0, 1, 1, INVALID)):
+        assert rms(y, x, w, 0, 4096, plan=_plan(load_nt=lnt, store_nt=snt, weight_lds=wl)) == ok
+    assert rms(y, x, w, 0, 4095, plan=_plan(threads_per_row=256, rows_per_block=1, store_nt=1, **g)) == INVALID
 
 
 # ---------------------------------------------------------------------------
@@ -168,8 +172,27 @@ EXPECTED = {
 @pytest.mark.parametrize("key", list(EXPECTED), ids=[f"{k[0]}-{k[1]}-{k[2]}" for k in EXPECTED])
 def test_policy_table(key):
     op, dtype, hidden = key
-    p = ks.get_plan(op, dtype, hidden).as_dict()
-    assert (p["path"], p["threads_per_row"], p["vectors_per_thread"], p["rows_per_block"]) == EXPECTED[key]
+    for rows in (1, 2048, 32768):
+        p = ks.get_plan(op, dtype, hidden, rows).as_dict()
+        assert (p["path"], p["threads_per_row"], p["vectors_per_thread"], p["rows_per_block"]) == EXPECTED[key]
+
+
+def test_memory_hints():
+    """Hints follow the measured rules; the row split never depends on rows."""
+    small = ks.get_plan("rms_norm", torch.bfloat16, 4096, 2048).as_dict()
+    big = ks.get_plan("rms_norm", torch.bfloat16, 16384, 8192).as_dict()
+    assert (small["load_nt"], small["store_nt"], small["weight_lds"]) == (1, 1, 0)
+    assert (big["load_nt"], big["store_nt"], big["weight_lds"]) == (0, 1, 0)
+    f = ks.get_plan("fused_add_rms_norm", torch.bfloat16, 4096, 2048).as_dict()
+    assert (f["load_nt"], f["store_nt"], f["weight_lds"]) == (1, 1, 1)
+    g = ks.get_plan("rms_norm", torch.bfloat16, 1001, 64).as_dict()
+    assert (g["path"], g["load_nt"], g["store_nt"], g["weight_lds"]) == (1, 0, 0, 0)
+    for hidden in (1024, 4096, 8192, 16384):
+        for op in ("rms_norm", "fused_add_rms_norm"):
+            shapes = {tuple(ks.get_plan(op, torch.bfloat16, hidden, rows).as_dict()[k]
+                            for k in ("path", "threads_per_row", "vectors_per_thread", "elems_per_access"))
+                      for rows in (0, 1, 7, 2048, 65536, 2**31 - 1)}
+            assert len(shapes) == 1
 
 
 def test_policy_covers_every_row_and_is_accepted():
@@ -179,7 +202,7 @@ def test_policy_covers_every_row_and_is_accepted():
         for op in ("rms_norm", "fused_add_rms_norm"):
             for hidden in hiddens:
                 for aligned in (True, False):
-                    p = ks.get_plan(op, dtype, hidden, aligned)
+                    p = ks.get_plan(op, dtype, hidden, 4096, aligned)
                     d = p.as_dict()
                     assert d["block_threads"] % 64 == 0 and d["block_threads"] <= 1024
                     assert d["rows_per_block"] * d["threads_per_row"] == d["block_threads"]
@@ -222,5 +245,5 @@ def test_ctypes_signatures_match_header():
     for name in ("ks_rms_norm", "ks_fused_add_rms_norm"):
         assert len(getattr(h, name).argtypes) == 8
     for name in ("ks_rms_norm_ex", "ks_fused_add_rms_norm_ex"):
-        assert len(getattr(h, name).argtypes) == 11
-    assert ctypes.sizeof(b.Plan) == 24
+        assert len(getattr(h, name).argtypes) == 9
+    assert ctypes.sizeof(b.Plan) == 36
