@@ -76,6 +76,10 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--rotate-mib", type=int, default=1024, help="total size of the rotating input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run device-to-device copies of MIB MiB (the counter calibration run) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="turn four rocprofv3 --pmc output directories into profiles/hbm_traffic.json and exit")
     return ap.parse_args()
 
 
@@ -156,14 +160,100 @@ def load_traffic(workload: str) -> dict | None:
     return data.get("workloads", {}).get(workload)
 
 
+COPY_REPS = 5
+
+
+def copy_calibration(mib: int) -> None:
+    """Plain device-to-device copies of a known size: the reference the HBM
+    counters are scaled by (bytes read = bytes written = MIB MiB per copy)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": COPY_REPS}), flush=True)
+
+
+def _counter_rows(directory: str) -> list[dict]:
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    return rows
+
+
+def _per_kernel_kib(directory: str, counter: str) -> dict[str, list[float]]:
+    out: dict[str, list[float]] = {}
+    for r in _counter_rows(directory):
+        if r.get("Counter_Name") != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> None:
+    """Counter-derived HBM bytes per launch of each kernel, scaled so that the
+    calibration copy reads and writes exactly its own size."""
+    fetch = _per_kernel_kib(fetch_dir, "FETCH_SIZE")
+    write = _per_kernel_kib(write_dir, "WRITE_SIZE")
+    cf = _per_kernel_kib(copy_fetch_dir, "FETCH_SIZE")
+    cw = _per_kernel_kib(copy_write_dir, "WRITE_SIZE")
+
+    def copy_kib(d: dict) -> float:
+        vals = [v for k, vs in d.items() if "copy" in k.lower() for v in vs]
+        vals.sort()
+        return vals[len(vals) // 2]          # median over the calibration copies
+
+    calib_bytes = None
+    for line in open(os.path.join(copy_fetch_dir, "calibration.json")) if os.path.exists(
+            os.path.join(copy_fetch_dir, "calibration.json")) else []:
+        calib_bytes = json.loads(line)["copy_calibration_bytes"]
+    calib_bytes = calib_bytes or (256 << 20)
+    fetch_scale = calib_bytes / (copy_kib(cf) * 1024)
+    write_scale = calib_bytes / (copy_kib(cw) * 1024)
+    wl = workloads.WORKLOADS["C3b"]
+    esize = 2
+    kernels = {}
+    for name in fetch:
+        if "ks::" not in name or "rms_norm" not in name:
+            continue
+        op = "fused_add_rms_norm" if "fused_add_rms_norm" in name else "rms_norm"
+        f = sorted(fetch[name])[len(fetch[name]) // 2] * 1024 * fetch_scale
+        w = sorted(write.get(name, [0.0]))[len(write.get(name, [0.0])) // 2] * 1024 * write_scale
+        alg = algorithmic_bytes(op, wl.rows, wl.hidden, esize)
+        kernels[name] = {"op": op, "dispatches": len(fetch[name]), "fetch_bytes": round(f),
+                         "write_bytes": round(w), "traffic_bytes": round(f + w), "algorithmic_bytes": alg,
+                         "traffic_over_algorithmic": round((f + w) / alg, 4)}
+    data = {"kernel_source_hash": kernel_source_hash(), "fetch_scale": round(fetch_scale, 5),
+            "write_scale": round(write_scale, 5), "calibration_copy_bytes": calib_bytes, "kernels": kernels,
+            "workloads": {"C3b": {k["op"]: k["traffic_bytes"] for k in kernels.values()}}}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+    print(json.dumps(data, indent=1))
+
+
 def main() -> None:
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(rows shard across GPUs with no communication; see the design notes).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         fail("no HIP device visible")
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import oracle
     import rmsnorm_row_normalisation_amd as ks

@@ -26,8 +26,9 @@
  *            (IEEE division); scale = rsqrt(mean + eps) (eps rounded to fp32;
  *            the rsqrt is correctly rounded); y = (v * scale) * fp32(weight);
  *            output rounded to the dtype with round-to-nearest-even.  The
- *            reduction order depends only on hidden and dtype, so a row's
- *            result does not depend on how many rows are in the batch.
+ *            summation order depends only on hidden, dtype and alignment, so
+ *            a row's result does not depend on how many rows are in the
+ *            batch.
  * Errors     Checked in this order, before any HIP call:
  *              KS_ERROR_UNSUPPORTED_DTYPE  dtype is not one of ks_dtype_t;
  *              KS_ERROR_INVALID_VALUE      rows < 0; hidden <= 0 or
@@ -127,12 +128,13 @@ ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight,
                                   ks_dtype_t dtype, hipStream_t stream);
 
 /*
- * The launch plan the two calls above use.  The way a row is split across
- * threads (path, threads_per_row, vectors_per_thread, elems_per_access), and
- * with it the summation order, is a function of op, dtype, hidden and
- * alignment only; the memory hints may also depend on rows.  `aligned` != 0
- * means all buffers are 16-byte aligned.  No HIP call.  Returns
- * KS_ERROR_INVALID_VALUE for a NULL plan, rows < 0 or a bad hidden size.
+ * The launch plan the two calls above use for this op, dtype, batch and row
+ * size.  All vector-path plans sum a row in one canonical order, so the plan
+ * may change with `rows` while every row's result stays the same; the path
+ * (vector or generic) depends only on dtype, hidden and alignment.
+ * `aligned` != 0 means all buffers are 16-byte aligned.  No HIP call.
+ * Returns KS_ERROR_INVALID_VALUE for a NULL plan, a bad row count or hidden
+ * size, or an unknown op.
  */
 ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned,
                         ks_plan_t *plan);

@@ -7,14 +7,14 @@
 // unrounded s into x.
 //
 // Two kernel families:
-//   vec_kernel      a team of kTpr lanes owns a row; each lane keeps kVpt
+//   *_vec           a team of kTpr lanes owns a row; each lane keeps kVpt
 //                   16-byte pieces of it in VGPRs, so every byte of x (and
 //                   residual) is read from HBM once and written once.  Loads
 //                   and stores are raw buffer instructions on one descriptor
 //                   per workgroup; pieces past the end of the row get an
 //                   out-of-range offset, so they read as zero and their
 //                   stores are dropped by the hardware range check.
-//   generic_kernel  a team of kTpr lanes strides over the row with kEpa
+//   *_generic       a team of kTpr lanes strides over the row with kEpa
 //                   elements per access, in two passes (sum, then normalise
 //                   and store).  Serves unaligned buffers, rows whose byte
 //                   size is not a multiple of 16, and rows wider than the
@@ -55,12 +55,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// Storage dtype tags (kernel names carry them, e.g. rms_norm_vec<ks::bf16, ...>).
+struct f32 {};
+struct f16 {};
+struct bf16 {};
+
 // ---------------------------------------------------------------------------
 // Element packing: a 16-byte piece holds kElems values of T.
 // ---------------------------------------------------------------------------
 template <typename T> struct Pack;
 
-template <> struct Pack<float> {
+template <> struct Pack<f32> {
+    static constexpr int kBytes = 4;
     static constexpr int kElems = 4;
     __device__ static __forceinline__ float get(const u32x4 &v, int e) { return __uint_as_float(v[e]); }
     __device__ static __forceinline__ u32x4 put(const float *f)
@@ -75,7 +81,8 @@ template <> struct Pack<float> {
 };
 
 // bfloat16 is the upper half of binary32: widening is a 16-bit shift, exact.
-template <> struct Pack<__bf16> {
+template <> struct Pack<bf16> {
+    static constexpr int kBytes = 2;
     static constexpr int kElems = 8;
     __device__ static __forceinline__ float get(const u32x4 &v, int e)
     {
@@ -100,7 +107,8 @@ template <> struct Pack<__bf16> {
     }
 };
 
-template <> struct Pack<_Float16> {
+template <> struct Pack<f16> {
+    static constexpr int kBytes = 2;
     static constexpr int kElems = 8;
     __device__ static __forceinline__ float get(const u32x4 &v, int e)
     {
@@ -128,18 +136,18 @@ template <> struct Pack<_Float16> {
 
 // Scalar element access for the unaligned generic path.
 template <typename T> struct Scalar;
-template <> struct Scalar<float> {
+template <> struct Scalar<f32> {
     __device__ static __forceinline__ float get(const void *p, int64_t i) { return ((const float *)p)[i]; }
     __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((float *)p)[i] = v; }
 };
-template <> struct Scalar<__bf16> {
+template <> struct Scalar<bf16> {
     __device__ static __forceinline__ float get(const void *p, int64_t i)
     {
         return __uint_as_float((unsigned)((const unsigned short *)p)[i] << 16);
     }
     __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((__bf16 *)p)[i] = (__bf16)v; }
 };
-template <> struct Scalar<_Float16> {
+template <> struct Scalar<f16> {
     __device__ static __forceinline__ float get(const void *p, int64_t i) { return (float)((const _Float16 *)p)[i]; }
     __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((_Float16 *)p)[i] = (_Float16)v; }
 };
@@ -255,7 +263,7 @@ __device__ __forceinline__ float row_scale(float sum_sq, int32_t hidden, float e
 // ---------------------------------------------------------------------------
 template <typename T, bool kFused, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol,
           bool kWeightLds>
-__global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
+__device__ __forceinline__ void vec_body(const Params &p)
 {
     constexpr int kE = Pack<T>::kElems;
     constexpr int kRpb = kBlock / kTpr;
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
     const int64_t row0 = (int64_t)blockIdx.x * kRpb;
     const int64_t left = p.rows - row0;
     const uint32_t nrows = left < kRpb ? (uint32_t)left : (uint32_t)kRpb;
-    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)sizeof(T);
+    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)Pack<T>::kBytes;
     const uint32_t blk_bytes = nrows * row_bytes;          // rows past the batch are out of range
     const size_t base = (size_t)row0 * row_bytes;
 
@@ -382,7 +390,7 @@ __global__ __launch_bounds__(kBlock) void vec_kernel(Params p)
 // accesses (aligned buffers, row bytes a multiple of 16).
 // ---------------------------------------------------------------------------
 template <typename T, bool kFused, int kTpr, int kEpa, int kBlock>
-__global__ __launch_bounds__(kBlock) void generic_kernel(Params p)
+__device__ __forceinline__ void generic_body(const Params &p)
 {
     constexpr int kRpb = kBlock / kTpr;
     const int tid = threadIdx.x;
@@ -403,10 +411,10 @@ __global__ __launch_bounds__(kBlock) void generic_kernel(Params p)
                     v = v + Scalar<T>::get(p.res, base + j);
                 sum_sq = __builtin_fmaf(v, v, sum_sq);
             } else {
-                const u32x4 xv = *(const u32x4 *)((const T *)p.x + base + j);
+                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
                 u32x4 rv;
                 if constexpr (kFused)
-                    rv = *(const u32x4 *)((const T *)p.res + base + j);
+                    rv = *(const u32x4 *)((const char *)p.res + (base + j) * Pack<T>::kBytes);
 #pragma unroll
                 for (int e = 0; e < kEpa; ++e) {
                     float v = Pack<T>::get(xv, e);
@@ -432,15 +440,15 @@ __global__ __launch_bounds__(kBlock) void generic_kernel(Params p)
             const float t = v * scale;
             Scalar<T>::put(p.y, base + j, t * Scalar<T>::get(p.w, j));
         } else {
-            const u32x4 xv = *(const u32x4 *)((const T *)p.x + base + j);
-            const u32x4 wv = *(const u32x4 *)((const T *)p.w + j);
+            const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+            const u32x4 wv = *(const u32x4 *)((const char *)p.w + j * Pack<T>::kBytes);
             float v[kEpa], o[kEpa];
             if constexpr (kFused) {
-                const u32x4 rv = *(const u32x4 *)((const T *)p.res + base + j);
+                const u32x4 rv = *(const u32x4 *)((const char *)p.res + (base + j) * Pack<T>::kBytes);
 #pragma unroll
                 for (int e = 0; e < kEpa; ++e)
                     v[e] = Pack<T>::get(xv, e) + Pack<T>::get(rv, e);
-                *(u32x4 *)((T *)p.res + base + j) = Pack<T>::put(v);
+                *(u32x4 *)((char *)p.res + (base + j) * Pack<T>::kBytes) = Pack<T>::put(v);
             } else {
 #pragma unroll
                 for (int e = 0; e < kEpa; ++e)
@@ -451,9 +459,36 @@ __global__ __launch_bounds__(kBlock) void generic_kernel(Params p)
                 const float t = v[e] * scale;
                 o[e] = t * Pack<T>::get(wv, e);
             }
-            *(u32x4 *)((T *)p.y + base + j) = Pack<T>::put(o);
+            *(u32x4 *)((char *)p.y + (base + j) * Pack<T>::kBytes) = Pack<T>::put(o);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel entry points, one name per operation and path.
+// ---------------------------------------------------------------------------
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
+__global__ __launch_bounds__(kBlock) void rms_norm_vec(Params p)
+{
+    vec_body<T, false, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
+}
+
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
+__global__ __launch_bounds__(kBlock) void fused_add_rms_norm_vec(Params p)
+{
+    vec_body<T, true, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
+}
+
+template <typename T, int kTpr, int kEpa, int kBlock>
+__global__ __launch_bounds__(kBlock) void rms_norm_generic(Params p)
+{
+    generic_body<T, false, kTpr, kEpa, kBlock>(p);
+}
+
+template <typename T, int kTpr, int kEpa, int kBlock>
+__global__ __launch_bounds__(kBlock) void fused_add_rms_norm_generic(Params p)
+{
+    generic_body<T, true, kTpr, kEpa, kBlock>(p);
 }
 
 }  // namespace ks

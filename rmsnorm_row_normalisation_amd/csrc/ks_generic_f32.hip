@@ -1,11 +1,11 @@
-// Generic-path kernels for float, both operations.
+// Generic-path kernels for float32, both operations.
 #include "ks_launch.hpp"
 
 namespace ks {
 
 hipError_t launch_generic_f32(const Launch &l)
 {
-    return l.fused ? launch_generic_typed<float, true>(l) : launch_generic_typed<float, false>(l);
+    return l.fused ? launch_generic_typed<f32, true>(l) : launch_generic_typed<f32, false>(l);
 }
 
 }  // namespace ks

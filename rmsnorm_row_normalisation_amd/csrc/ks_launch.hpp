@@ -19,20 +19,40 @@ hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
     return hipGetLastError();
 }
 
+// The kernel entry point of one op.
+template <bool F, typename T, int TPR, int V, int B, int LC, int SC, bool WL>
+constexpr auto vec_entry()
+{
+    if constexpr (F)
+        return fused_add_rms_norm_vec<T, TPR, V, B, LC, SC, WL>;
+    else
+        return rms_norm_vec<T, TPR, V, B, LC, SC, WL>;
+}
+
+template <bool F, typename T, int TPR, int EPA, int B>
+constexpr auto generic_entry()
+{
+    if constexpr (F)
+        return fused_add_rms_norm_generic<T, TPR, EPA, B>;
+    else
+        return rms_norm_generic<T, TPR, EPA, B>;
+}
+
 // The compiled memory-hint variants of one launch shape.
 template <typename T, bool F, int TPR, int V>
 hipError_t vec_one(const Launch &l)
 {
     constexpr int B = TPR < 256 ? 256 : TPR;
+    constexpr int NT = kNonTemporal;
     const ks_plan_t &p = l.plan;
     if (!p.load_nt && !p.store_nt && !p.weight_lds)
-        return run(vec_kernel<T, F, TPR, V, B, 0, 0, false>, l, B);
+        return run(vec_entry<F, T, TPR, V, B, 0, 0, false>(), l, B);
     if (p.load_nt && p.store_nt && !p.weight_lds)
-        return run(vec_kernel<T, F, TPR, V, B, kNonTemporal, kNonTemporal, false>, l, B);
+        return run(vec_entry<F, T, TPR, V, B, NT, NT, false>(), l, B);
     if (!p.load_nt && p.store_nt && !p.weight_lds)
-        return run(vec_kernel<T, F, TPR, V, B, 0, kNonTemporal, false>, l, B);
+        return run(vec_entry<F, T, TPR, V, B, 0, NT, false>(), l, B);
     if (p.load_nt && p.store_nt && p.weight_lds)
-        return run(vec_kernel<T, F, TPR, V, B, kNonTemporal, kNonTemporal, true>, l, B, (size_t)V * TPR * 16);
+        return run(vec_entry<F, T, TPR, V, B, NT, NT, true>(), l, B, (size_t)V * TPR * 16);
     return hipErrorInvalidValue;
 }
 
@@ -78,10 +98,10 @@ template <typename T, bool F, int EPA>
 hipError_t generic_by_tpr(const Launch &l)
 {
     switch (l.plan.threads_per_row) {
-    case 8: return run(generic_kernel<T, F, 8, EPA, 256>, l, 256);
-    case 64: return run(generic_kernel<T, F, 64, EPA, 256>, l, 256);
-    case 256: return run(generic_kernel<T, F, 256, EPA, 256>, l, 256);
-    case 1024: return run(generic_kernel<T, F, 1024, EPA, 1024>, l, 1024);
+    case 8: return run(generic_entry<F, T, 8, EPA, 256>(), l, 256);
+    case 64: return run(generic_entry<F, T, 64, EPA, 256>(), l, 256);
+    case 256: return run(generic_entry<F, T, 256, EPA, 256>(), l, 256);
+    case 1024: return run(generic_entry<F, T, 1024, EPA, 1024>(), l, 1024);
     default: return hipErrorInvalidValue;
     }
 }

@@ -1,8 +1,8 @@
-// Vector-path kernels for __bf16, RMSNorm.
+// Vector-path kernels for bfloat16, RMSNorm.
 #include "ks_launch.hpp"
 
 namespace ks {
 
-hipError_t launch_vec_bf16_rms(const Launch &l) { return vec_by_tpr<__bf16, false>(l); }
+hipError_t launch_vec_bf16_rms(const Launch &l) { return vec_by_tpr<bf16, false>(l); }
 
 }  // namespace ks

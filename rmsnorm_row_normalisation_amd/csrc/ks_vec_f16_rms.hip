@@ -1,8 +1,8 @@
-// Vector-path kernels for _Float16, RMSNorm.
+// Vector-path kernels for float16, RMSNorm.
 #include "ks_launch.hpp"
 
 namespace ks {
 
-hipError_t launch_vec_f16_rms(const Launch &l) { return vec_by_tpr<_Float16, false>(l); }
+hipError_t launch_vec_f16_rms(const Launch &l) { return vec_by_tpr<f16, false>(l); }
 
 }  // namespace ks

@@ -1,8 +1,8 @@
-// Vector-path kernels for float, RMSNorm.
+// Vector-path kernels for float32, RMSNorm.
 #include "ks_launch.hpp"
 
 namespace ks {
 
-hipError_t launch_vec_f32_rms(const Launch &l) { return vec_by_tpr<float, false>(l); }
+hipError_t launch_vec_f32_rms(const Launch &l) { return vec_by_tpr<f32, false>(l); }
 
 }  // namespace ks

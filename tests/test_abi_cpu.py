@@ -153,46 +153,72 @@ def test_explicit_plans_are_checked():
 # recommend for launch-parameter selection.
 # ---------------------------------------------------------------------------
 EXPECTED = {
-    # (op, dtype, hidden): (path, threads_per_row, vectors_per_thread, rows_per_block)
-    ("rms_norm", torch.bfloat16, 1024): (0, 16, 8, 16),       # C1
-    ("rms_norm", torch.bfloat16, 4096): (0, 64, 8, 4),        # C2 / C3b headline
-    ("fused_add_rms_norm", torch.bfloat16, 4096): (0, 64, 8, 4),
-    ("rms_norm", torch.float16, 4096): (0, 64, 8, 4),         # C3
-    ("fused_add_rms_norm", torch.bfloat16, 1536): (0, 32, 6, 8),   # C4a
-    ("fused_add_rms_norm", torch.bfloat16, 8192): (0, 128, 8, 2),  # C4b, C5f
-    ("rms_norm", torch.bfloat16, 16384): (0, 256, 8, 1),      # C5r
-    ("rms_norm", torch.float32, 4096): (0, 128, 8, 2),
-    ("rms_norm", torch.bfloat16, 5): (1, 8, 0, 32),           # odd sizes: generic scalar path
-    ("rms_norm", torch.bfloat16, 1000): (0, 16, 8, 16),      # 2000-byte rows are 16-byte multiples
-    ("rms_norm", torch.bfloat16, 1001): (1, 64, 0, 4),
-    ("rms_norm", torch.bfloat16, 65536): (1, 1024, 0, 1),    # wider than the vector path holds
+    # (op, dtype, hidden, rows): (path, threads_per_row, vectors_per_thread, rows_per_block, weight_lds)
+    ("rms_norm", torch.bfloat16, 1024, 128): (0, 128, 1, 2, 0),          # 128x1024
+    ("rms_norm", torch.bfloat16, 4096, 512): (0, 256, 2, 1, 0),          # 512x4096
+    ("fused_add_rms_norm", torch.bfloat16, 4096, 512): (0, 256, 2, 1, 1),
+    ("rms_norm", torch.bfloat16, 4096, 2048): (0, 64, 8, 4, 0),          # 2048x4096
+    ("fused_add_rms_norm", torch.bfloat16, 4096, 2048): (0, 64, 8, 4, 1),
+    ("rms_norm", torch.float16, 4096, 2048): (0, 64, 8, 4, 0),
+    ("fused_add_rms_norm", torch.bfloat16, 1536, 4): (0, 256, 1, 1, 0),  # decode 4x1536
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 1): (0, 512, 2, 1, 0),  # decode 1x8192
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 32768): (0, 256, 4, 1, 1),   # prefill 32768x8192
+    ("rms_norm", torch.bfloat16, 16384, 8192): (0, 512, 4, 1, 0),        # prefill 8192x16384
+    ("rms_norm", torch.float32, 4096, 2048): (0, 128, 8, 2, 0),
+    ("rms_norm", torch.bfloat16, 5, 3): (1, 8, 0, 32, 0),                # odd sizes: generic scalar path
+    ("rms_norm", torch.bfloat16, 1000, 3): (0, 128, 1, 2, 0),            # 2000-byte rows are 16-byte multiples
+    ("rms_norm", torch.bfloat16, 1001, 3): (1, 64, 0, 4, 0),
+    ("rms_norm", torch.bfloat16, 32768, 4): (0, 512, 8, 1, 0),           # 64 KiB rows: widest vector plan
+    ("rms_norm", torch.bfloat16, 32776, 4): (1, 1024, 0, 1, 0),          # wider: generic 16-byte path
 }
 
 
-@pytest.mark.parametrize("key", list(EXPECTED), ids=[f"{k[0]}-{k[1]}-{k[2]}" for k in EXPECTED])
+@pytest.mark.parametrize("key", list(EXPECTED), ids=[f"{k[0]}-{k[1]}-{k[2]}x{k[3]}" for k in EXPECTED])
 def test_policy_table(key):
-    op, dtype, hidden = key
-    for rows in (1, 2048, 32768):
-        p = ks.get_plan(op, dtype, hidden, rows).as_dict()
-        assert (p["path"], p["threads_per_row"], p["vectors_per_thread"], p["rows_per_block"]) == EXPECTED[key]
+    op, dtype, hidden, rows = key
+    p = ks.get_plan(op, dtype, hidden, rows).as_dict()
+    got = (p["path"], p["threads_per_row"], p["vectors_per_thread"], p["rows_per_block"], p["weight_lds"])
+    assert got == EXPECTED[key]
+    if p["path"] == 0:
+        assert p["load_nt"] == 1 and p["store_nt"] == 1
+    else:
+        assert p["load_nt"] == p["store_nt"] == p["weight_lds"] == 0
+
+
+def test_policy_rule():
+    """The vector plan follows the stated rule: about 131072 lanes of work,
+    pieces per lane a power of two in [1, 8] (at most 4 from 4M pieces), team a
+    power of two in [8, 512]; the path itself never depends on rows."""
+    for hidden in (8, 64, 1024, 1536, 4096, 5120, 8192, 16384, 32768):
+        nvec = hidden * 2 // 16
+        paths = set()
+        for rows in (0, 1, 3, 64, 512, 2048, 8192, 65536, 2**20):
+            p = ks.get_plan("rms_norm", torch.bfloat16, hidden, rows).as_dict()
+            paths.add(p["path"])
+            pieces = rows * nvec
+            target = 1
+            while target * 131072 < pieces:
+                target *= 2
+            target = min(target, 4 if pieces >= 2**22 else 8)
+            tpr = 1
+            while tpr * target < nvec:
+                tpr *= 2
+            tpr = min(max(tpr, 8), 512)
+            assert p["threads_per_row"] == tpr, (hidden, rows, p)
+            assert p["vectors_per_thread"] == -(-nvec // tpr)
+        assert paths == {0}
 
 
 def test_memory_hints():
-    """Hints follow the measured rules; the row split never depends on rows."""
-    small = ks.get_plan("rms_norm", torch.bfloat16, 4096, 2048).as_dict()
-    big = ks.get_plan("rms_norm", torch.bfloat16, 16384, 8192).as_dict()
+    """Hints follow the measured rules."""
+    small = ks.get_plan("fused_add_rms_norm", torch.bfloat16, 4096, 4).as_dict()
+    big = ks.get_plan("fused_add_rms_norm", torch.bfloat16, 4096, 512).as_dict()
     assert (small["load_nt"], small["store_nt"], small["weight_lds"]) == (1, 1, 0)
-    assert (big["load_nt"], big["store_nt"], big["weight_lds"]) == (0, 1, 0)
-    f = ks.get_plan("fused_add_rms_norm", torch.bfloat16, 4096, 2048).as_dict()
-    assert (f["load_nt"], f["store_nt"], f["weight_lds"]) == (1, 1, 1)
+    assert (big["load_nt"], big["store_nt"], big["weight_lds"]) == (1, 1, 1)
+    r = ks.get_plan("rms_norm", torch.bfloat16, 16384, 8192).as_dict()
+    assert (r["load_nt"], r["store_nt"], r["weight_lds"]) == (1, 1, 0)
     g = ks.get_plan("rms_norm", torch.bfloat16, 1001, 64).as_dict()
     assert (g["path"], g["load_nt"], g["store_nt"], g["weight_lds"]) == (1, 0, 0, 0)
-    for hidden in (1024, 4096, 8192, 16384):
-        for op in ("rms_norm", "fused_add_rms_norm"):
-            shapes = {tuple(ks.get_plan(op, torch.bfloat16, hidden, rows).as_dict()[k]
-                            for k in ("path", "threads_per_row", "vectors_per_thread", "elems_per_access"))
-                      for rows in (0, 1, 7, 2048, 65536, 2**31 - 1)}
-            assert len(shapes) == 1
 
 
 def test_policy_covers_every_row_and_is_accepted():
@@ -209,8 +235,9 @@ def test_policy_covers_every_row_and_is_accepted():
                     if d["path"] == 0:
                         assert aligned and (hidden * es) % 16 == 0
                         assert d["threads_per_row"] * d["vectors_per_thread"] * 16 >= hidden * es
-                        # the last piece of a row starts inside the row: no team is mostly padding
-                        assert (d["threads_per_row"] * (d["vectors_per_thread"] - 1)) * 16 < hidden * es
+                        # at most half of a team's pieces are padding
+                        assert d["threads_per_row"] * d["vectors_per_thread"] * 16 < 2 * hidden * es or \
+                            d["threads_per_row"] == 8
                     # the library accepts its own plan (rows == 0: no launch)
                     call = rms if op == "rms_norm" else fused
                     base = A if aligned else A + 2
