@@ -1,6 +1,7 @@
 """Benchmark: RMSNorm and fused residual-add RMSNorm on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b]
+    python bench.py --sweep-workloads [--out FILE]      # every workload, one table
 
 One step is one pass of the whole path over one batch: ks_rms_norm on the
 batch, then ks_fused_add_rms_norm on it (both at 2048 x 4096 bf16 by
@@ -21,13 +22,17 @@ Timing:
     that op's launches, back to back; the average launch period includes the
     short gap between consecutive kernels, so it is an upper bound on the
     kernel's own duration (rocprofv3's kernel trace of the same run gives the
-    duration alone).
+    duration alone);
+  * ``copy_reference``: the HIP runtime's own device-to-device copy of one
+    batch-sized tensor, timed the same way: what a plain read+write stream of
+    that size achieves on this GPU.
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
 writes both, (4 R H + H) elements.
 
-Before any timing the outputs are checked against the CPU oracle; on a
-mismatch nothing is timed (exit status 1).
+Before any timing the outputs are checked against the CPU oracle (all rows, or
+sampled rows for batches over 2^24 elements); on a mismatch nothing is timed
+(exit status 1).
 """
 from __future__ import annotations
 
@@ -36,9 +41,11 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +59,10 @@ DTYPE_TAG = {"bfloat16": "bf16", "float16": "fp16", "float32": "fp32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rmsnorm_row_normalisation_amd", "csrc", f)
                   for f in ("ks_device.hpp", "ks_launch.hpp", "ks_internal.h", "ks_api.cpp")]
+FULL_PARITY_ELEMS = 1 << 24     # above this, the parity gate checks sampled rows
+SAMPLED_ROWS = 64
+COPY_REPS = 5
+MAX_SETS = 1024
 
 
 def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
@@ -60,10 +71,14 @@ def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -76,6 +91,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--rotate-mib", type=int, default=1024, help="total size of the rotating input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-workloads", action="store_true",
+                    help="measure every workload (per op) and print a markdown table instead of the bench line")
+    ap.add_argument("--out", default=None, help="with --sweep-workloads: also write the table to this file")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run device-to-device copies of MIB MiB (the counter calibration run) and exit")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -92,31 +110,158 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------------------
+# parity gate
+# ---------------------------------------------------------------------------
 def parity_gate(wl, inp, ks, oracle_mod) -> dict:
-    """Full-size GPU vs oracle check before any timing."""
+    """GPU vs oracle on the full batch (or on sampled rows of a large one) before any timing."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from compare import check_bitexact, check_normalised
 
-    out = {}
-    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    if wl.rows * wl.hidden <= FULL_PARITY_ELEMS:
+        idx = None
+    else:
+        idx = torch.from_numpy(np.unique(np.concatenate([
+            np.random.default_rng(77).choice(wl.rows, size=SAMPLED_ROWS, replace=False), [0, wl.rows - 1]])))
+
+    def pick(t):
+        return t if idx is None else t[idx].contiguous()
+
+    def ref_inputs():
+        return {k: (pick(v) if v.dim() == 2 else v) for k, v in inp.items()}
+
+    out = {"rows_checked": wl.rows if idx is None else int(idx.numel())}
+    w = inp["weight"].cuda()
     if "rms_norm" in wl.ops:
-        y = ks.rms_norm(x, w, wl.eps)
+        y = ks.rms_norm(inp["x"].cuda(), w, wl.eps)
         torch.cuda.synchronize()
-        ref = oracle_mod.rms_norm(inp["x"], inp["weight"], wl.eps)
-        st = check_normalised(y.cpu(), ref, 0.999)
+        r = ref_inputs()
+        ref = oracle_mod.rms_norm(r["x"], r["weight"], wl.eps)
+        st = check_normalised(pick(y.cpu()), ref, 0.999)
         out["rms_norm"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
+        del y
     if "fused_add_rms_norm" in wl.ops:
         xf, rf = inp["x"].cuda(), inp["residual"].cuda()
         ks.fused_add_rms_norm(xf, rf, w, wl.eps)
         torch.cuda.synchronize()
-        rx, rr = oracle_mod.fused_add_rms_norm(inp["x"], inp["residual"], inp["weight"], wl.eps)
-        check_bitexact(rf.cpu(), rr)
-        st = check_normalised(xf.cpu(), rx, 0.999)
+        r = ref_inputs()
+        rx, rr = oracle_mod.fused_add_rms_norm(r["x"], r["residual"], r["weight"], wl.eps)
+        check_bitexact(pick(rf.cpu()), rr)
+        st = check_normalised(pick(xf.cpu()), rx, 0.999)
         out["fused_add_rms_norm"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6),
                                      "residual": "bit-exact"}
+        del xf, rf
     return out
 
 
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+class Rig:
+    """Rotating HBM-resident copies of a workload's batch and graph-timed launches."""
+
+    def __init__(self, wl, inp, ks, rotate_mib: int):
+        self.wl, self.ks = wl, ks
+        esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
+        self.tensor_bytes = wl.rows * wl.hidden * esize
+        per_set = 2 * self.tensor_bytes * len(wl.ops)
+        # enough copies to pass through more than the last-level cache between
+        # two uses of one copy; capped for tiny (launch-bound) batches
+        self.nsets = min(MAX_SETS, max(2, -(-rotate_mib * (1 << 20) // per_set)))
+        x0 = inp["x"].cuda()
+        r0 = inp["residual"].cuda() if "residual" in inp else None
+        self.w = inp["weight"].cuda()
+        self.sets = []
+        for _ in range(self.nsets):
+            s = {}
+            if "rms_norm" in wl.ops:
+                s["x"] = x0.clone()
+                s["out"] = torch.empty_like(x0)
+            if "fused_add_rms_norm" in wl.ops:
+                s["fx"] = x0.clone()
+                s["fr"] = r0.clone()
+            self.sets.append(s)
+        del x0, r0
+        self.rotation_mib = self.nsets * per_set / 2**20
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+
+    def launch(self, op: str, i: int) -> None:
+        s = self.sets[i % self.nsets]
+        if op == "rms_norm":
+            self.ks.rms_norm(s["x"], self.w, self.wl.eps, out=s["out"])
+        else:
+            self.ks.fused_add_rms_norm(s["fx"], s["fr"], self.w, self.wl.eps)
+
+    def timed_graph(self, body, per_rotation: int, reps: int) -> float:
+        """Capture body(i) for i in range(per_rotation) into a HIP graph and replay
+        it `reps` times between two events on the launch stream; milliseconds."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(graph, stream=self.stream):
+                for i in range(per_rotation):
+                    body(i)
+            graph.replay()                                   # untimed
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(self.stream)
+            for _ in range(reps):
+                graph.replay()
+            ev1.record(self.stream)
+            torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1)
+
+    def warmup(self, n: int) -> None:
+        with torch.cuda.stream(self.stream):
+            for i in range(n):
+                for op in self.wl.ops:
+                    self.launch(op, i)
+        torch.cuda.synchronize()
+
+    def copy_reference(self, reps: int) -> dict:
+        """The runtime's device-to-device copy of one batch-sized tensor per launch."""
+        n = self.nsets
+        srcs = [s.get("x", s.get("fx")) for s in self.sets]
+        dsts = [s.get("out", s.get("fr")) for s in self.sets]
+        ms = self.timed_graph(lambda i: dsts[i % n].copy_(srcs[i % n]), n, reps)
+        us = ms * 1e3 / (n * reps)
+        gbps = 2 * self.tensor_bytes / (us * 1e-6) / 1e9
+        return {"bytes": 2 * self.tensor_bytes, "us_per_copy": round(us, 3), "gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def measure(wl, inp, ks, args) -> dict:
+    """Whole-step and per-op throughput of one workload."""
+    esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
+    op_bytes = {op: algorithmic_bytes(op, wl.rows, wl.hidden, esize) for op in wl.ops}
+    rig = Rig(wl, inp, ks, args.rotate_mib)
+    log(f"{wl.name}: {rig.nsets} rotating copies, {rig.rotation_mib:.0f} MiB")
+    reps = max(1, -(-args.steps // rig.nsets))
+    steps = reps * rig.nsets
+    rig.warmup(args.warmup)
+    total_ms = rig.timed_graph(lambda i: [rig.launch(op, i) for op in wl.ops], rig.nsets, reps)
+    per_op = {}
+    for op in wl.ops:
+        ms = rig.timed_graph(lambda i, op=op: rig.launch(op, i), rig.nsets, reps)
+        us = ms * 1e3 / steps
+        gbps = op_bytes[op] / (us * 1e-6) / 1e9
+        per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
+                      "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                      "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden, wl.rows).as_dict()}
+    copy = rig.copy_reference(reps)
+    ms_per_step = total_ms / steps
+    result = {"steps": steps, "reps": reps, "nsets": rig.nsets, "rotation_mib": rig.rotation_mib,
+              "ms_per_step": ms_per_step, "step_bytes": sum(op_bytes.values()),
+              "value": sum(op_bytes.values()) / (ms_per_step * 1e-3) / 1e9, "per_op": per_op,
+              "copy_reference": copy}
+    del rig
+    torch.cuda.empty_cache()
+    return result
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline
+# ---------------------------------------------------------------------------
 def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
     """The oracle as it stands, single-threaded on a host core, on whole steps of the workload."""
     t0 = time.perf_counter()
@@ -148,6 +293,9 @@ def _cpu_model() -> str:
     return platform.processor()
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic from counters
+# ---------------------------------------------------------------------------
 def load_traffic(workload: str) -> dict | None:
     """Counter-derived HBM bytes per launch, if taken on the current kernel sources."""
     try:
@@ -158,9 +306,6 @@ def load_traffic(workload: str) -> dict | None:
     if data.get("kernel_source_hash") != kernel_source_hash():
         return None
     return data.get("workloads", {}).get(workload)
-
-
-COPY_REPS = 5
 
 
 def copy_calibration(mib: int) -> None:
@@ -193,10 +338,14 @@ def _counter_rows(directory: str) -> list[dict]:
 def _per_kernel_kib(directory: str, counter: str) -> dict[str, list[float]]:
     out: dict[str, list[float]] = {}
     for r in _counter_rows(directory):
-        if r.get("Counter_Name") != counter:
-            continue
-        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        if r.get("Counter_Name") == counter:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     return out
+
+
+def _median(vals: list[float]) -> float:
+    vals = sorted(vals)
+    return vals[len(vals) // 2]
 
 
 def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> None:
@@ -208,15 +357,13 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
     cw = _per_kernel_kib(copy_write_dir, "WRITE_SIZE")
 
     def copy_kib(d: dict) -> float:
-        vals = [v for k, vs in d.items() if "copy" in k.lower() for v in vs]
-        vals.sort()
-        return vals[len(vals) // 2]          # median over the calibration copies
+        return _median([v for k, vs in d.items() if "copy" in k.lower() for v in vs])
 
-    calib_bytes = None
-    for line in open(os.path.join(copy_fetch_dir, "calibration.json")) if os.path.exists(
-            os.path.join(copy_fetch_dir, "calibration.json")) else []:
-        calib_bytes = json.loads(line)["copy_calibration_bytes"]
-    calib_bytes = calib_bytes or (256 << 20)
+    calib_path = os.path.join(copy_fetch_dir, "calibration.json")
+    calib_bytes = 256 << 20
+    if os.path.exists(calib_path):
+        with open(calib_path) as f:
+            calib_bytes = json.loads(f.readline())["copy_calibration_bytes"]
     fetch_scale = calib_bytes / (copy_kib(cf) * 1024)
     write_scale = calib_bytes / (copy_kib(cw) * 1024)
     wl = workloads.WORKLOADS["C3b"]
@@ -226,8 +373,8 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
         if "ks::" not in name or "rms_norm" not in name:
             continue
         op = "fused_add_rms_norm" if "fused_add_rms_norm" in name else "rms_norm"
-        f = sorted(fetch[name])[len(fetch[name]) // 2] * 1024 * fetch_scale
-        w = sorted(write.get(name, [0.0]))[len(write.get(name, [0.0])) // 2] * 1024 * write_scale
+        f = _median(fetch[name]) * 1024 * fetch_scale
+        w = _median(write.get(name, [0.0])) * 1024 * write_scale
         alg = algorithmic_bytes(op, wl.rows, wl.hidden, esize)
         kernels[name] = {"op": op, "dispatches": len(fetch[name]), "fetch_bytes": round(f),
                          "write_bytes": round(w), "traffic_bytes": round(f + w), "algorithmic_bytes": alg,
@@ -238,6 +385,37 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps(data, indent=1))
+
+
+# ---------------------------------------------------------------------------
+# modes
+# ---------------------------------------------------------------------------
+def sweep_workloads(args, ks, oracle_mod) -> None:
+    """Every workload of the pages' benchmark set: parity, then per-op timing."""
+    lines = ["| Workload | Op | dtype | rows x hidden | us/call | GB/s | % of 8 TB/s | copy ref GB/s | rotation MiB "
+             "| plan (team x pieces, hints) | max ulp | exact |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, wl in workloads.WORKLOADS.items():
+        log("generating", name, wl.describe())
+        inp = workloads.make_inputs(wl)
+        parity = parity_gate(wl, inp, ks, oracle_mod)
+        res = measure(wl, inp, ks, args)
+        for op in wl.ops:
+            p = res["per_op"][op]
+            pl = p["plan"]
+            plan = (f"{pl['threads_per_row']}x{pl['vectors_per_thread']} "
+                    f"nt{pl['load_nt']}{pl['store_nt']} lds{pl['weight_lds']}")
+            lines.append(f"| {name} | {op} | {DTYPE_TAG[wl.dtype]} | {wl.rows}x{wl.hidden} | {p['us_per_call']:.3f} | "
+                         f"{p['gbps']:.0f} | {100 * p['frac_of_peak']:.1f} | {res['copy_reference']['gbps']:.0f} | "
+                         f"{res['rotation_mib']:.0f} | {plan} | {parity[op]['max_ulp']} | "
+                         f"{parity[op]['exact_match']:.6f} |")
+            log(lines[-1])
+        del inp
+    table = "\n".join(lines)
+    print(table, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(table + "\n")
 
 
 def main() -> None:
@@ -258,13 +436,13 @@ def main() -> None:
     import oracle
     import rmsnorm_row_normalisation_amd as ks
 
-    wl = workloads.WORKLOADS[args.workload]
-    esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
-    op_bytes = {op: algorithmic_bytes(op, wl.rows, wl.hidden, esize) for op in wl.ops}
-    step_bytes = sum(op_bytes.values())
     dev = torch.cuda.get_device_properties(0)
     log("device", dev.name, getattr(dev, "gcnArchName", "?"), "CUs", dev.multi_processor_count)
+    if args.sweep_workloads:
+        sweep_workloads(args, ks, oracle)
+        return
 
+    wl = workloads.WORKLOADS[args.workload]
     log("generating inputs", wl.describe())
     inp = workloads.make_inputs(wl)
     try:
@@ -272,84 +450,9 @@ def main() -> None:
     except AssertionError as exc:
         fail(f"parity gate failed, nothing timed: {exc}")
     log("parity", parity)
-
-    # rotating copies of the batch, resident in HBM
-    per_set = 0
-    if "rms_norm" in wl.ops:
-        per_set += 2 * wl.rows * wl.hidden * esize
-    if "fused_add_rms_norm" in wl.ops:
-        per_set += 2 * wl.rows * wl.hidden * esize
-    nsets = max(1, -(-args.rotate_mib * (1 << 20) // per_set))
-    x0, r0 = inp["x"].cuda(), inp.get("residual")
-    r0 = r0.cuda() if r0 is not None else None
-    w = inp["weight"].cuda()
-    sets = []
-    for _ in range(nsets):
-        s = {}
-        if "rms_norm" in wl.ops:
-            s["x"] = x0.clone()
-            s["out"] = torch.empty_like(x0)
-        if "fused_add_rms_norm" in wl.ops:
-            s["fx"] = x0.clone()
-            s["fr"] = r0.clone()
-        sets.append(s)
-    torch.cuda.synchronize()
-    log(f"{nsets} rotating sets, {nsets * per_set / 2**20:.0f} MiB")
-
-    stream = torch.cuda.Stream()
-
-    def launch(op: str, i: int):
-        s = sets[i % nsets]
-        if op == "rms_norm":
-            ks.rms_norm(s["x"], w, wl.eps, out=s["out"])
-        else:
-            ks.fused_add_rms_norm(s["fx"], s["fr"], w, wl.eps)
-
-    def timed_graph(ops: tuple[str, ...], reps: int) -> float:
-        """Capture one rotation (nsets steps of `ops`) into a HIP graph, replay it
-        `reps` times between two events on the launch stream; returns milliseconds."""
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(nsets):
-                for op in ops:
-                    launch(op, i)
-        graph.replay()                                   # untimed
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(reps):
-            graph.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1)
-
-    reps = max(1, -(-args.steps // nsets))
-    steps = reps * nsets                                   # whole rotations over the copies
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            for op in wl.ops:
-                launch(op, i)
-        torch.cuda.synchronize()
-        # whole job: every step runs all ops of the path
-        t0 = time.perf_counter()
-        total_ms = timed_graph(wl.ops, reps)
-        wall = time.perf_counter() - t0
-        log(f"whole-step graph: {steps} steps in {total_ms:.3f} ms")
-        # per kernel: back-to-back launches of one op
-        per_op = {}
-        for op in wl.ops:
-            ms = timed_graph((op,), reps)
-            us = ms * 1e3 / steps
-            gbps = op_bytes[op] / (us * 1e-6) / 1e9
-            per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
-                          "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                          "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden, wl.rows).as_dict()}
-        log("per op", per_op)
-
-    ms_per_step = total_ms / steps
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    timing_mode = (f"HIP graph replay, {reps} replays of {nsets} steps; per op: graphs of back-to-back "
-                   "launches of that op")
+    res = measure(wl, inp, ks, args)
+    per_op = res["per_op"]
+    log("per op", per_op)
 
     dominant = max(wl.ops, key=lambda op: per_op[op]["us_per_call"])
     traffic = load_traffic(args.workload)
@@ -357,24 +460,26 @@ def main() -> None:
                 "achieved": per_op[dominant]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(per_op[dominant]["gbps"] / HBM_PEAK_GBPS, 4),
                 "traffic": (traffic or {}).get(dominant)}
-
+    timing_mode = (f"HIP graph replay, {res['reps']} replays of {res['nsets']} steps; per op: graphs of "
+                   "back-to-back launches of that op")
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "metric": METRIC, "value": round(res["value"], 1), "unit": "GB/s", "n_gpus": 1, "steps": res["steps"],
+        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_TAG[wl.dtype], "data": "synthetic",
         "config": {"workload": wl.describe(), "ops": list(wl.ops), "rows": wl.rows, "hidden": wl.hidden,
                    "eps": wl.eps, "timing": timing_mode,
-                   "cache": f"cold: {nsets} rotating copies ({nsets * per_set / 2**20:.0f} MiB)"},
-        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+                   "cache": f"cold: {res['nsets']} rotating copies ({res['rotation_mib']:.0f} MiB)"},
+        "frac_of_peak": round(res["value"] / HBM_PEAK_GBPS, 4),
         "per_op": per_op,
         "roofline": roofline,
+        "copy_reference": res["copy_reference"],
         "parity": parity,
         "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", "?"), "cus": dev.multi_processor_count},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for about {args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(wl, inp, oracle, args.cpu_seconds, step_bytes)
+        line["cpu_baseline"] = cpu_baseline(wl, inp, oracle, args.cpu_seconds, res["step_bytes"])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -24,7 +24,8 @@
  *            the same buffers race, as with any asynchronous kernel.
  * Arithmetic Per row: widen to fp32; sum of squares in fp32; mean = sum / H
  *            (IEEE division); scale = rsqrt(mean + eps) (eps rounded to fp32;
- *            the rsqrt is correctly rounded); y = (v * scale) * fp32(weight);
+ *            rsqrt evaluated in double and rounded once to fp32);
+ *            y = (v * scale) * fp32(weight);
  *            output rounded to the dtype with round-to-nearest-even.  The
  *            summation order depends only on hidden, dtype and alignment, so
  *            a row's result does not depend on how many rows are in the

@@ -21,8 +21,10 @@
  *     in index order in double and the sum is rounded once to fp32; the mean
  *     is one IEEE fp32 division by H.
  *   - eps is rounded to fp32 and added in fp32.
- *   - rsqrt is the correctly rounded value: double sqrt and double divide
- *     (both IEEE), rounded once to fp32.
+ *   - rsqrt is evaluated in double precision (IEEE sqrt, then IEEE divide)
+ *     and rounded once to fp32: the correctly rounded fp32 value except when
+ *     the exact result lies within about 2^-52 (relative) of an fp32
+ *     rounding boundary.
  *   - The multiplications run left to right as written: (x * scale) * w.
  *   - "cast_to_input_dtype" is IEEE round-to-nearest, ties-to-even, with
  *     subnormals kept, overflow to infinity and NaN kept as a quiet NaN.

@@ -244,8 +244,10 @@ template <int kTpr, int kBlock> __device__ __forceinline__ float team_sum(float 
     return team_fold<kTpr, kBlock>(v);
 }
 
-// rsqrt(sum / H + eps) with fp32 mean and add, and a correctly rounded
-// reciprocal square root (IEEE double sqrt and divide, one rounding to fp32).
+// rsqrt(sum / H + eps) with fp32 mean and add, and the reciprocal square root
+// evaluated in double (IEEE sqrt, IEEE divide) and rounded once to fp32: the
+// correctly rounded value except within about 2^-52 of an fp32 rounding
+// boundary, and the same operations the CPU oracle performs.
 __device__ __forceinline__ float row_scale(float sum_sq, int32_t hidden, float eps)
 {
     const float mean = sum_sq / (float)hidden;
