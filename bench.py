@@ -94,6 +94,11 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--sweep-workloads", action="store_true",
                     help="measure every workload (per op) and print a markdown table instead of the bench line")
     ap.add_argument("--out", default=None, help="with --sweep-workloads: also write the table to this file")
+    ap.add_argument("--json-out", default=None, help="also write the per-case results (JSON) to this file")
+    ap.add_argument("--baseline", default=None,
+                    help="a previous --json-out file: exit with status 2 if any matching case got slower "
+                         "by more than --max-regression-percent")
+    ap.add_argument("--max-regression-percent", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run device-to-device copies of MIB MiB (the counter calibration run) and exit")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -388,10 +393,56 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
 
 
 # ---------------------------------------------------------------------------
+# regression gate: cases matched by (op, dtype, rows, hidden)
+# ---------------------------------------------------------------------------
+def case_key(case: dict) -> tuple:
+    return (case["op"], case["dtype"], int(case["rows"]), int(case["hidden"]))
+
+
+def cases_from(wl, per_op: dict) -> list[dict]:
+    return [{"op": op, "dtype": wl.dtype, "rows": wl.rows, "hidden": wl.hidden,
+             "us_per_call": v["us_per_call"], "gbps": v["gbps"]} for op, v in per_op.items()]
+
+
+def regressions(current: list[dict], baseline: list[dict], max_percent: float) -> list[dict]:
+    """Cases present in both lists whose time per call grew by more than max_percent."""
+    base = {case_key(c): c for c in baseline}
+    out = []
+    for c in current:
+        b = base.get(case_key(c))
+        if b is None or b["us_per_call"] <= 0:
+            continue
+        pct = 100.0 * (c["us_per_call"] - b["us_per_call"]) / b["us_per_call"]
+        if pct > max_percent:
+            out.append({"case": list(case_key(c)), "baseline_us": b["us_per_call"], "us": c["us_per_call"],
+                        "regression_percent": round(pct, 2)})
+    return out
+
+
+def finish_cases(args, cases: list[dict]) -> None:
+    """Write the per-case JSON and apply the regression gate (exit status 2)."""
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            json.dump({"cases": cases, "kernel_source_hash": kernel_source_hash()}, f, indent=1)
+    if args.baseline:
+        with open(args.baseline) as f:
+            base = json.load(f)["cases"]
+        bad = regressions(cases, base, args.max_regression_percent)
+        matched = sum(1 for c in cases if case_key(c) in {case_key(b) for b in base})
+        log(f"regression gate: {matched} matching cases, {len(bad)} slower by more than "
+            f"{args.max_regression_percent:g}%")
+        for r in bad:
+            log("  regression", r)
+        if bad:
+            sys.exit(2)
+
+
+# ---------------------------------------------------------------------------
 # modes
 # ---------------------------------------------------------------------------
 def sweep_workloads(args, ks, oracle_mod) -> None:
     """Every workload of the pages' benchmark set: parity, then per-op timing."""
+    cases = []
     lines = ["| Workload | Op | dtype | rows x hidden | us/call | GB/s | % of 8 TB/s | copy ref GB/s | rotation MiB "
              "| plan (team x pieces, hints) | max ulp | exact |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -400,6 +451,7 @@ def sweep_workloads(args, ks, oracle_mod) -> None:
         inp = workloads.make_inputs(wl)
         parity = parity_gate(wl, inp, ks, oracle_mod)
         res = measure(wl, inp, ks, args)
+        cases.extend(cases_from(wl, res["per_op"]))
         for op in wl.ops:
             p = res["per_op"][op]
             pl = p["plan"]
@@ -416,6 +468,7 @@ def sweep_workloads(args, ks, oracle_mod) -> None:
     if args.out:
         with open(args.out, "w") as f:
             f.write(table + "\n")
+    finish_cases(args, cases)
 
 
 def main() -> None:
@@ -483,6 +536,7 @@ def main() -> None:
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+    finish_cases(args, cases_from(wl, per_op))
 
 
 if __name__ == "__main__":
