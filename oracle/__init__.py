@@ -1,13 +1,13 @@
-"""CPU oracle for RMSNorm and fused residual-add RMSNorm.
+"""CPU oracle for RMSNorm, fused residual-add RMSNorm and SwiGLU.
 
 TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package; the GPU product path
 never does, and the two share no code.
 
 ``ks_oracle.c`` holds all arithmetic (kernscope README, "Numerical contract":
-"RMSNorm" and "Fused residual-add RMSNorm").  This module only builds and
-loads that library and marshals torch CPU tensors (used as plain byte
-containers) to it.  ``brute64`` is a second, independent fp64 / exact-rational
+"RMSNorm", "Fused residual-add RMSNorm" and "SwiGLU activation").  This module
+only builds and loads that library and marshals torch CPU tensors (used as
+plain byte containers) to it.  ``brute64`` is a second, independent fp64 / exact-rational
 check for tiny inputs.
 """
 from __future__ import annotations
@@ -46,6 +46,8 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_round_f32_array.restype = c_int
     lib.oracle_widen_array.argtypes = [c_int, vp, vp, i64]
     lib.oracle_widen_array.restype = c_int
+    lib.oracle_silu_and_mul.argtypes = [c_int, vp, vp, i64, i64]
+    lib.oracle_silu_and_mul.restype = c_int
     return lib
 
 
@@ -101,6 +103,22 @@ def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor,
     if st != 0:
         raise ValueError(f"oracle_fused_add_rms_norm failed with status {st}")
     return xo, ro
+
+
+def silu_and_mul(x: torch.Tensor, lib: ctypes.CDLL | None = None) -> torch.Tensor:
+    """SwiGLU of x with shape (..., 2D): returns a new (..., D) tensor."""
+    lib = lib or load()
+    if x.device.type != "cpu" or x.dtype not in _DTYPE_CODE or not x.is_contiguous():
+        raise ValueError("oracle needs a contiguous CPU tensor of a supported dtype")
+    if x.dim() == 0 or x.shape[-1] == 0 or x.shape[-1] % 2:
+        raise ValueError("the last dimension must be nonempty and even")
+    d = x.shape[-1] // 2
+    rows = x.numel() // x.shape[-1]
+    out = torch.empty(*x.shape[:-1], d, dtype=x.dtype)
+    st = lib.oracle_silu_and_mul(_DTYPE_CODE[x.dtype], x.data_ptr(), out.data_ptr(), rows, d)
+    if st != 0:
+        raise ValueError(f"oracle_silu_and_mul failed with status {st}")
+    return out
 
 
 def round_f32(values: torch.Tensor, dtype: torch.dtype, lib: ctypes.CDLL | None = None) -> torch.Tensor:

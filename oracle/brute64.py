@@ -1,14 +1,16 @@
 """Exact-arithmetic brute force for tiny inputs.  TEST INFRASTRUCTURE ONLY.
 
-A second statement of the kernscope "Numerical contract" (sections "RMSNorm"
-and "Fused residual-add RMSNorm") that shares nothing with ``ks_oracle.c``:
+A second statement of the kernscope "Numerical contract" (sections "RMSNorm",
+"Fused residual-add RMSNorm" and "SwiGLU activation") that shares nothing with
+``ks_oracle.c``:
 the sum of squares, the mean and eps are exact rationals, the square root is
 taken to 80 significant digits, and the result is rounded ONCE to the output
 format (round to nearest, ties to even) by integer arithmetic on the rational.
 Only the fused form's fp32 residual sum is rounded to fp32 first, because the
 contract defines s as an fp32 value.
 
-It is meant for a few hundred elements at most (pure Python).
+It is meant for a few hundred elements at most (pure Python).  The SwiGLU
+statement at the end follows the same approach.
 """
 from __future__ import annotations
 
@@ -71,3 +73,22 @@ def fused_add_rms_norm(x: list[list[float]], r: list[list[float]], w: list[float
     s = [[round_to(Fraction(a) + Fraction(b), "float32") for a, b in zip(xr, rr)] for xr, rr in zip(x, r)]
     residual = [[round_to(Fraction(v), fmt) for v in row] for row in s]
     return rms_norm(s, w, eps32, fmt), residual
+
+
+def _sigmoid(g: Fraction) -> Fraction:
+    with localcontext() as ctx:
+        ctx.prec = 80
+        e = (-Decimal(g.numerator) / Decimal(g.denominator)).exp()
+        return Fraction(1 / (1 + e))
+
+
+def silu_and_mul(x: list[list[float]], fmt: str) -> list[list[float]]:
+    """SwiGLU of rows of 2D values (kernscope "Numerical contract" > "SwiGLU
+    activation"): gate * sigmoid(gate) * up with an 80-digit exponential and one
+    rounding to the output format."""
+    out = []
+    for row in x:
+        d = len(row) // 2
+        out.append([round_to(Fraction(g) * _sigmoid(Fraction(g)) * Fraction(u), fmt)
+                    for g, u in zip(row[:d], row[d:])])
+    return out

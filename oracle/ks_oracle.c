@@ -1,6 +1,6 @@
 /*
- * CPU oracle for RMSNorm row normalisation and the fused residual-add
- * variant.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU oracle for RMSNorm row normalisation, the fused residual-add variant
+ * and the SwiGLU activation.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this file's library; the GPU library never
  * does, and the two share no code, headers or constants.
  *
@@ -250,5 +250,37 @@ int oracle_widen_array(int dtype, const uint16_t *in, float *out, int64_t n)
     const format_t *f = format_of(dtype);
     for (int64_t i = 0; i < n; ++i)
         out[i] = (float)decode_format(in[i], f);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* SwiGLU activation (kernscope README, "Numerical contract" > "SwiGLU        */
+/* activation"; shapes from its "Inputs" section): x holds rows of 2D        */
+/* values, gate = the first D, up = the last D;                              */
+/*   out[r, j] = cast(fp32(gate) * sigmoid(fp32(gate)) * fp32(up))           */
+/* with fp32 intermediates, multiplied left to right.                        */
+/* Reading where the page is silent: sigmoid(g) is the fp32 value nearest   */
+/* 1 / (1 + e^-g), evaluated in double with the C library's exp and rounded  */
+/* once to fp32.                                                             */
+/* ------------------------------------------------------------------------ */
+static float sigmoid32(float g)
+{
+    return (float)(1.0 / (1.0 + exp(-(double)g)));
+}
+
+int oracle_silu_and_mul(int dtype, const void *x, void *out, int64_t rows, int64_t d)
+{
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+        return ORACLE_BAD_ARG;
+    if (rows < 0 || d <= 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t j = 0; j < d; ++j) {
+            float g = load_elem(dtype, x, r * 2 * d + j);
+            float u = load_elem(dtype, x, r * 2 * d + d + j);
+            float t = g * sigmoid32(g);
+            store_elem(dtype, out, r * d + j, t * u);
+        }
+    }
     return ORACLE_OK;
 }

@@ -306,9 +306,79 @@ def pin_zeros_and_empty(lib) -> None:
         assert ex.shape == er.shape == (0, 64)
 
 
+# --------------------------------------------------------------------------
+# SwiGLU (kernscope "Numerical contract" > "SwiGLU activation")
+# --------------------------------------------------------------------------
+SWIGLU_SHAPES = [(2,), (3, 10), (2, 3, 14), (2, 64), (3, 402)]
+
+
+def _swiglu_case(shape, dtype, seed):
+    x = workloads.random_case(shape, dtype, seed, x=workloads.normal(0, 2))["x"]
+    flat = x.reshape(-1)
+    # extreme gate values: the sigmoid saturates at both ends
+    extremes = torch.tensor([0.0, -0.0, 20.0, -20.0, 100.0, -100.0, 1e-3, -1e-3]).to(x.dtype)
+    k = min(len(extremes), flat.numel() // 2)
+    flat[:k] = extremes[:k]
+    return x
+
+
+def pin_swiglu_brute_force(lib) -> None:
+    for dtype in ("bfloat16", "float16", "float32"):
+        for i, shape in enumerate(SWIGLU_SHAPES):
+            x = _swiglu_case(shape, dtype, 300 + i)
+            want = brute64.silu_and_mul(_values(x), dtype)
+            got = oracle.silu_and_mul(x, lib=lib)
+            want_t = _from_values(want, x.dtype, got.shape)
+            # 16-bit outputs: at most 1 ulp.  fp32 outputs: the page's fp32 tolerance
+            # (the contract's fp32 sigmoid is subnormal for very negative gates, so a
+            # count of ulps there says nothing)
+            check_normalised(got, want_t)
+
+
+def torch_swiglu(x: torch.Tensor) -> torch.Tensor:
+    d = x.shape[-1] // 2
+    g, u = x[..., :d].float(), x[..., d:].float()
+    return (torch.nn.functional.silu(g) * u).to(x.dtype)
+
+
+def pin_swiglu_library(lib) -> None:
+    for dtype in ("bfloat16", "float16"):
+        x = workloads.random_case((256, 2 * 1024), dtype, 310, x=workloads.normal(0, 2))["x"]
+        check_normalised(oracle.silu_and_mul(x, lib=lib), torch_swiglu(x), min_exact_rate=0.999)
+    x = workloads.random_case((64, 2 * 512), "float32", 311)["x"]
+    check_normalised(oracle.silu_and_mul(x, lib=lib), torch_swiglu(x))
+
+
+def pin_swiglu_closed_forms(lib) -> None:
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
+        d = 300
+        g = torch.full((4, d), 0.0)
+        g[0] = torch.linspace(18.0, 60.0, d)      # fp32 sigmoid rounds to exactly 1 from g >= 18
+        g[1] = 0.0                                 # silu(0) = 0
+        g[2] = -torch.linspace(18.0, 60.0, d)
+        g[3] = torch.linspace(-3, 3, d)
+        u = torch.linspace(-2.0, 2.0, d).expand(4, d)
+        x = torch.cat([g, u], dim=1).to(dtype).contiguous()
+        y = oracle.silu_and_mul(x, lib=lib)
+        gq, uq = x[:, :d].float(), x[:, d:].float()
+        check_bitexact(y[0], (gq[0] * uq[0]).to(dtype))
+        assert bool((y[1].float() == 0).all())
+        # very negative gates: |out| <= |g| e^g |u| (sigmoid(g) < e^g), up to the output's rounding
+        # (1%, or half a quantum where the output is subnormal)
+        quantum = torch.finfo(dtype).tiny * torch.finfo(dtype).eps
+        bound = (gq[2].abs() * torch.exp(gq[2]) * uq[2].abs()) * 1.01 + quantum / 2
+        assert bool((y[2].float().abs() <= bound).all())
+        # odd in up: negating the up half negates the output exactly
+        xn = torch.cat([x[:, :d], -x[:, d:]], dim=1).contiguous()
+        assert int(ulp_distance(oracle.silu_and_mul(xn, lib=lib), -y).max()) == 0
+    e = torch.zeros(0, 8, dtype=torch.bfloat16)
+    assert oracle.silu_and_mul(e, lib=lib).shape == (0, 4)
+
+
 ALL_PINS = [
     pin_constant_rows, pin_unit_weight_rms, pin_brute_force, pin_scaling_and_sign, pin_fused_residual,
     pin_batch_invariance, pin_casts, pin_library_formula, pin_unrounded_sum, pin_zeros_and_empty,
+    pin_swiglu_brute_force, pin_swiglu_library, pin_swiglu_closed_forms,
 ]
 
 

@@ -41,6 +41,13 @@ MUTANTS = [
      "int bias = -f->emin;\n    uint32_t exp_all_ones"),
     ("scale_in_fp32_sqrt_of_mean_only", "float d = mean + eps;               /* fp32 add */",
      "float d = mean + eps * 0.5f;"),
+    ("swiglu_sigmoid_sign", "return (float)(1.0 / (1.0 + exp(-(double)g)));",
+     "return (float)(1.0 / (1.0 + exp((double)g)));"),
+    ("swiglu_halves_swapped", "float g = load_elem(dtype, x, r * 2 * d + j);\n            float u = load_elem(dtype, x, r * 2 * d + d + j);",
+     "float u = load_elem(dtype, x, r * 2 * d + j);\n            float g = load_elem(dtype, x, r * 2 * d + d + j);"),
+    ("swiglu_no_gate_factor", "float t = g * sigmoid32(g);", "float t = sigmoid32(g);"),
+    ("swiglu_up_off_by_one", "float u = load_elem(dtype, x, r * 2 * d + d + j);",
+     "float u = load_elem(dtype, x, r * 2 * d + d + (j + 1) % d);"),
 ]
 
 
