@@ -66,6 +66,11 @@ MAX_SETS = 1024
 
 
 def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
+    """Bytes the contract must move.  rms_norm: read x, write out, read the weight
+    once; fused: read x and residual, write both, read the weight; silu_and_mul
+    (hidden = input width 2D): read x, write the D-wide output."""
+    if op == "silu_and_mul":
+        return (rows * hidden + rows * (hidden // 2)) * esize
     per_row = 2 if op == "rms_norm" else 4
     return (per_row * rows * hidden + hidden) * esize
 
@@ -136,6 +141,13 @@ def parity_gate(wl, inp, ks, oracle_mod) -> dict:
         return {k: (pick(v) if v.dim() == 2 else v) for k, v in inp.items()}
 
     out = {"rows_checked": wl.rows if idx is None else int(idx.numel())}
+    if "silu_and_mul" in wl.ops:
+        y = ks.silu_and_mul(inp["x"].cuda())
+        torch.cuda.synchronize()
+        ref = oracle_mod.silu_and_mul(pick(inp["x"]))
+        st = check_normalised(pick(y.cpu()), ref, 0.999)
+        out["silu_and_mul"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
+        return out
     w = inp["weight"].cuda()
     if "rms_norm" in wl.ops:
         y = ks.rms_norm(inp["x"].cuda(), w, wl.eps)
@@ -169,16 +181,20 @@ class Rig:
         self.wl, self.ks = wl, ks
         esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
         self.tensor_bytes = wl.rows * wl.hidden * esize
-        per_set = 2 * self.tensor_bytes * len(wl.ops)
+        footprint = {"rms_norm": 2.0, "fused_add_rms_norm": 2.0, "silu_and_mul": 1.5}   # tensors per copy
+        per_set = int(sum(footprint[op] for op in wl.ops) * self.tensor_bytes)
         # enough copies to pass through more than the last-level cache between
         # two uses of one copy; capped for tiny (launch-bound) batches
         self.nsets = min(MAX_SETS, max(2, -(-rotate_mib * (1 << 20) // per_set)))
         x0 = inp["x"].cuda()
         r0 = inp["residual"].cuda() if "residual" in inp else None
-        self.w = inp["weight"].cuda()
+        self.w = inp["weight"].cuda() if "weight" in inp else None
         self.sets = []
         for _ in range(self.nsets):
             s = {}
+            if "silu_and_mul" in wl.ops:
+                s["sx"] = x0.clone()
+                s["sout"] = torch.empty(wl.rows, wl.hidden // 2, dtype=x0.dtype, device=x0.device)
             if "rms_norm" in wl.ops:
                 s["x"] = x0.clone()
                 s["out"] = torch.empty_like(x0)
@@ -195,8 +211,10 @@ class Rig:
         s = self.sets[i % self.nsets]
         if op == "rms_norm":
             self.ks.rms_norm(s["x"], self.w, self.wl.eps, out=s["out"])
-        else:
+        elif op == "fused_add_rms_norm":
             self.ks.fused_add_rms_norm(s["fx"], s["fr"], self.w, self.wl.eps)
+        else:
+            self.ks.silu_and_mul(s["sx"], out=s["sout"])
 
     def timed_graph(self, body, per_rotation: int, reps: int) -> float:
         """Capture body(i) for i in range(per_rotation) into a HIP graph and replay
@@ -226,9 +244,10 @@ class Rig:
     def copy_reference(self, reps: int) -> dict:
         """The runtime's device-to-device copy of one batch-sized tensor per launch."""
         n = self.nsets
-        srcs = [s.get("x", s.get("fx")) for s in self.sets]
-        dsts = [s.get("out", s.get("fr")) for s in self.sets]
+        srcs = [s.get("x", s.get("fx", s.get("sx"))) for s in self.sets]
+        dsts = [torch.empty_like(t) for t in srcs]
         ms = self.timed_graph(lambda i: dsts[i % n].copy_(srcs[i % n]), n, reps)
+        del dsts
         us = ms * 1e3 / (n * reps)
         gbps = 2 * self.tensor_bytes / (us * 1e-6) / 1e9
         return {"bytes": 2 * self.tensor_bytes, "us_per_copy": round(us, 3), "gbps": round(gbps, 1),
@@ -252,7 +271,8 @@ def measure(wl, inp, ks, args) -> dict:
         gbps = op_bytes[op] / (us * 1e-6) / 1e9
         per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                      "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden, wl.rows).as_dict()}
+                      "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden // 2 if op == "silu_and_mul" else wl.hidden,
+                                          wl.rows).as_dict()}
     copy = rig.copy_reference(reps)
     ms_per_step = total_ms / steps
     result = {"steps": steps, "reps": reps, "nsets": rig.nsets, "rotation_mib": rig.rotation_mib,

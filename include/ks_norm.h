@@ -1,6 +1,6 @@
 /*
- * ks_norm: RMSNorm row normalisation and fused residual-add RMSNorm for
- * AMD Instinct MI355X (gfx950).  C ABI.
+ * ks_norm: RMSNorm row normalisation, fused residual-add RMSNorm and the
+ * SwiGLU activation for AMD Instinct MI355X (gfx950).  C ABI.
  *
  * The operations are the ones defined in the kernscope README, section
  * "Numerical contract" (subsections "RMSNorm" and "Fused residual-add
@@ -68,7 +68,8 @@ typedef enum {
 
 typedef enum {
     KS_OP_RMS_NORM = 0,
-    KS_OP_FUSED_ADD_RMS_NORM = 1
+    KS_OP_FUSED_ADD_RMS_NORM = 1,
+    KS_OP_SILU_AND_MUL = 2
 } ks_op_t;
 
 /* How a launch maps rows onto threads.
@@ -155,6 +156,30 @@ ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight,
 ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight,
                                      int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
                                      const ks_plan_t *plan, hipStream_t stream);
+
+/*
+ * SwiGLU activation (kernscope README, "Numerical contract" > "SwiGLU
+ * activation"; shapes as in its "Inputs" section):
+ *   out[r, j] = cast( fp32(g) * sigmoid(fp32(g)) * fp32(u) ),
+ *   g = x[r, j], u = x[r, d + j], 0 <= j < d,
+ * with fp32 intermediates multiplied left to right; sigmoid(g) = 1 / (1 +
+ * exp(-g)) with the device exp (within a few fp32 ulps of the exact value).
+ * x    [rows, 2 d] input, gate half first; read only.
+ * out  [rows, d] output; must not overlap x (KS_ERROR_OVERLAP).
+ * d    output width, 1 <= d <= 2^24 (any parity).  rows may be 0.
+ * Errors and stream rules as above.  The vector path needs 16-byte aligned
+ * x and out and d * element size a multiple of 16; any other case runs a
+ * narrower path with the same result.  Elementwise, so every plan gives the
+ * same bits.
+ */
+ks_status_t ks_silu_and_mul(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
+                            hipStream_t stream);
+
+/* SwiGLU with an explicit plan (op KS_OP_SILU_AND_MUL, hidden = d); plans
+ * with weight_lds set are rejected, and the generic plan is the single
+ * grid-stride one (threads_per_row = block_threads = 256, rows_per_block = 1). */
+ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
+                               const ks_plan_t *plan, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *ks_status_string(ks_status_t status);

@@ -1,4 +1,4 @@
-"""RMSNorm row normalisation and fused residual-add RMSNorm for MI355X (gfx950).
+"""RMSNorm, fused residual-add RMSNorm and SwiGLU for MI355X (gfx950).
 
 The computation lives in ``libks_norm.so`` (hand-written HIP kernels behind a
 C ABI, ``include/ks_norm.h``); this package is its thin Python binding.
@@ -16,10 +16,13 @@ from .binding import (  # noqa: F401
     ks_get_plan,
     ks_rms_norm,
     ks_rms_norm_ex,
+    ks_silu_and_mul,
+    ks_silu_and_mul_ex,
     ks_version,
     lib,
     library_path,
     rms_norm,
+    silu_and_mul,
 )
 
 __version__ = "0.1.0"

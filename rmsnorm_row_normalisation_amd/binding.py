@@ -1,9 +1,9 @@
 """ctypes binding of libks_norm.so: argument marshalling only.
 
 The ``ks_*`` functions mirror the C ABI in ``include/ks_norm.h`` one to one
-(raw device pointers as ints).  ``rms_norm`` and ``fused_add_rms_norm`` are
-the tensor-level calls with the kernscope API shape (README, "API contract"
-and "Inputs"): they check devices, dtypes, shapes, contiguity and
+(raw device pointers as ints).  ``rms_norm``, ``fused_add_rms_norm`` and
+``silu_and_mul`` are the tensor-level calls with the kernscope API shape
+(README, "API contract" and "Inputs"): they check devices, dtypes, shapes, contiguity and
 ``requires_grad`` (the accelerator kernels are inference-only), then pass the
 tensors' device pointers and torch's current HIP stream to the library.
 Every step of the computation runs in the library's kernels; there is no
@@ -20,7 +20,7 @@ DEFAULT_LIB = os.path.join(_PKG, "libks_norm.so")
 
 KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP = range(5)
 KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM = 0, 1
+KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL = 0, 1, 2
 KS_PATH_VECTOR, KS_PATH_GENERIC = 0, 1
 
 
@@ -86,12 +86,14 @@ def lib() -> ctypes.CDLL:
         h.ks_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_fused_add_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_get_plan.argtypes = [i32, i32, i64, i64, i32, ctypes.POINTER(Plan)]
+        h.ks_silu_and_mul.argtypes = [vp, vp, i64, i64, i32, vp]
+        h.ks_silu_and_mul_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
         h.ks_last_hip_error.argtypes = []
         h.ks_version.restype = ctypes.c_char_p
         for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
-                     "ks_get_plan", "ks_last_hip_error"):
+                     "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -132,6 +134,14 @@ def ks_fused_add_rms_norm_ex(x: int, residual: int, weight: int, rows: int, hidd
                              plan: Plan | None, stream: int) -> int:
     return lib().ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype,
                                           ctypes.byref(plan) if plan is not None else None, stream)
+
+
+def ks_silu_and_mul(out: int, x: int, rows: int, d: int, dtype: int, stream: int) -> int:
+    return lib().ks_silu_and_mul(out, x, rows, d, dtype, stream)
+
+
+def ks_silu_and_mul_ex(out: int, x: int, rows: int, d: int, dtype: int, plan: Plan | None, stream: int) -> int:
+    return lib().ks_silu_and_mul_ex(out, x, rows, d, dtype, ctypes.byref(plan) if plan is not None else None, stream)
 
 
 def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True) -> Plan:
@@ -203,7 +213,34 @@ def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Te
     _check(st, "ks_fused_add_rms_norm")
 
 
+def silu_and_mul(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
+    """SwiGLU of x with shape (..., 2D): a new (..., D) tensor (kernscope "SwiGLU activation")."""
+    if x.dtype not in KS_DTYPE:
+        raise TypeError(f"silu_and_mul: unsupported dtype {x.dtype}")
+    if x.device.type != "cuda":
+        raise ValueError(f"silu_and_mul: tensors must be on a HIP device, got {x.device}")
+    if not x.is_contiguous():
+        raise ValueError("silu_and_mul: x must be contiguous")
+    if x.requires_grad:
+        raise ValueError("silu_and_mul: inference-only kernel; got a tensor that requires grad")
+    if x.dim() == 0 or x.shape[-1] == 0 or x.shape[-1] % 2:
+        raise ValueError("silu_and_mul: the last dimension must be nonempty and even")
+    d = x.shape[-1] // 2
+    rows = x.numel() // x.shape[-1]
+    shape = (*x.shape[:-1], d)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif out.shape != shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError(f"silu_and_mul: out must be a contiguous {x.dtype} tensor of shape {shape}")
+    with torch.cuda.device(x.device):
+        st = ks_silu_and_mul_ex(out.data_ptr(), x.data_ptr(), rows, d, KS_DTYPE[x.dtype], plan, _stream(x))
+    _check(st, "ks_silu_and_mul")
+    return out
+
+
 def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: bool = True) -> Plan:
-    """The plan the library picks for this op, dtype, row size and batch (ks_get_plan)."""
-    code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM}[op]
+    """The plan the library picks for this op, dtype, row size and batch (ks_get_plan).
+    For silu_and_mul, ``hidden`` is the output width D."""
+    code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM,
+            "silu_and_mul": KS_OP_SILU_AND_MUL}[op]
     return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned)

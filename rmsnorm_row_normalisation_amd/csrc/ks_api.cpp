@@ -1,5 +1,6 @@
 // C ABI of ks_norm: argument validation, overlap checks, the launch policy
-// and the calls into the per-dtype kernel units.  Validation and the policy
+// and the calls into the per-dtype kernel units (RMSNorm, fused residual-add
+// RMSNorm, SwiGLU).  Validation and the policy
 // make no HIP call, so they run (and are tested) on machines without a GPU.
 #include <math.h>
 #include <stdint.h>
@@ -103,10 +104,14 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.load_nt = 1;
         plan.store_nt = 1;
         plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;
+        // (SwiGLU has no weight and no reduction; the same spread suits it)
         return plan;
     }
     plan.path = KS_PATH_GENERIC;
-    if (aligned && row_bytes % 16 == 0) {
+    if (op == KS_OP_SILU_AND_MUL) {            // elementwise grid-stride loop
+        plan.threads_per_row = ks::kSwigluGenericBlock;
+        plan.elems_per_access = 1;
+    } else if (aligned && row_bytes % 16 == 0) {
         plan.threads_per_row = 1024;
         plan.elems_per_access = vec_elems;
     } else {
@@ -129,8 +134,16 @@ bool hints_compiled(const ks_plan_t &p)
 
 // Whether an explicit plan names a compiled kernel that covers this row and
 // suits the buffers' alignment.
-bool plan_fits(const ks_plan_t &p, ks_dtype_t dtype, int64_t hidden, bool aligned)
+bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned)
 {
+    if (op == KS_OP_SILU_AND_MUL) {
+        if (p.weight_lds != 0)
+            return false;
+        if (p.path == KS_PATH_GENERIC)
+            return p.threads_per_row == ks::kSwigluGenericBlock && p.vectors_per_thread == 0 &&
+                   p.elems_per_access == 1 && p.rows_per_block == 1 && p.block_threads == ks::kSwigluGenericBlock &&
+                   p.load_nt == 0 && p.store_nt == 0;
+    }
     const int64_t esize = elem_size(dtype);
     const int64_t row_bytes = hidden * esize;
     const int vec_elems = (int)(16 / esize);
@@ -189,7 +202,7 @@ ks_status_t select_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype
         *out = policy(op, dtype, rows, hidden, aligned);
         return KS_SUCCESS;
     }
-    if (!plan_fits(*requested, dtype, hidden, aligned))
+    if (!plan_fits(*requested, op, dtype, hidden, aligned))
         return KS_ERROR_INVALID_VALUE;
     *out = *requested;
     return KS_SUCCESS;
@@ -254,12 +267,47 @@ ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight, i
     return ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype, nullptr, stream);
 }
 
+ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
+                               const ks_plan_t *plan, hipStream_t stream)
+{
+    if (!valid_dtype(dtype))
+        return KS_ERROR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || rows > kMaxRows || d <= 0 || d > kMaxHidden)
+        return KS_ERROR_INVALID_VALUE;
+    if (rows > 0 && (out == nullptr || x == nullptr))
+        return KS_ERROR_INVALID_VALUE;
+    const bool aligned = aligned16(out) && aligned16(x);
+    ks::SwigluLaunch l{out, x, rows, (int32_t)d, {}, stream};
+    ks_status_t st = select_plan(plan, KS_OP_SILU_AND_MUL, dtype, rows, d, aligned, &l.plan);
+    if (st != KS_SUCCESS || rows == 0)
+        return st;
+    const int64_t es = elem_size(dtype);
+    if (overlaps(out, rows * d * es, x, rows * 2 * d * es))
+        return KS_ERROR_OVERLAP;
+    hipError_t err;
+    switch (dtype) {
+    case KS_DTYPE_FLOAT32: err = ks::launch_swiglu_f32(l); break;
+    case KS_DTYPE_FLOAT16: err = ks::launch_swiglu_f16(l); break;
+    default: err = ks::launch_swiglu_bf16(l); break;
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return KS_ERROR_HIP;
+    }
+    return KS_SUCCESS;
+}
+
+ks_status_t ks_silu_and_mul(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype, hipStream_t stream)
+{
+    return ks_silu_and_mul_ex(out, x, rows, d, dtype, nullptr, stream);
+}
+
 ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned, ks_plan_t *plan)
 {
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
-        (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM))
+        (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL))
         return KS_ERROR_INVALID_VALUE;
     *plan = policy(op, dtype, rows, hidden, aligned != 0);
     return KS_SUCCESS;

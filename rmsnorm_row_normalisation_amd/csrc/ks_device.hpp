@@ -107,6 +107,17 @@ template <> struct Pack<bf16> {
     }
 };
 
+// The compiler may fuse "fp32 multiply, then convert to fp16" into one
+// v_fma_mixlo_f16, which rounds the exact product straight to fp16 (measured:
+// it differs from rounding to fp32 first on about 6e-5 of products).  The
+// contract rounds to fp32 first, so every value converted to fp16 passes
+// through this empty asm, which keeps it an fp32 value (no instruction).
+__device__ __forceinline__ float as_fp32(float v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
 template <> struct Pack<f16> {
     static constexpr int kBytes = 2;
     static constexpr int kElems = 8;
@@ -119,8 +130,8 @@ template <> struct Pack<f16> {
     // round to nearest even (v_cvt_f16_f32 under the default rounding mode)
     __device__ static __forceinline__ unsigned two(float a, float b)
     {
-        unsigned lo = __builtin_bit_cast(unsigned short, (_Float16)a);
-        unsigned hi = __builtin_bit_cast(unsigned short, (_Float16)b);
+        unsigned lo = __builtin_bit_cast(unsigned short, (_Float16)as_fp32(a));
+        unsigned hi = __builtin_bit_cast(unsigned short, (_Float16)as_fp32(b));
         return lo | (hi << 16);
     }
     __device__ static __forceinline__ u32x4 put(const float *f)
@@ -149,7 +160,10 @@ template <> struct Scalar<bf16> {
 };
 template <> struct Scalar<f16> {
     __device__ static __forceinline__ float get(const void *p, int64_t i) { return (float)((const _Float16 *)p)[i]; }
-    __device__ static __forceinline__ void put(void *p, int64_t i, float v) { ((_Float16 *)p)[i] = (_Float16)v; }
+    __device__ static __forceinline__ void put(void *p, int64_t i, float v)
+    {
+        ((_Float16 *)p)[i] = (_Float16)as_fp32(v);
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -467,6 +481,114 @@ __device__ __forceinline__ void generic_body(const Params &p)
 }
 
 // ---------------------------------------------------------------------------
+// SwiGLU activation: out[r, j] = (g * sigmoid(g)) * u with g = x[r, j] and
+// u = x[r, d + j] widened to fp32, rounded once to the storage dtype.
+// Elementwise: every launch shape gives the same result.
+// ---------------------------------------------------------------------------
+struct SwigluParams {
+    void *out;        // [rows, d]
+    const void *x;    // [rows, 2 d]: gate half, then up half
+    int64_t rows;
+    int32_t d;
+};
+
+// sigmoid(g) for outputs rounded to 16 bits.  e^-g comes from the hardware
+// base-2 exponential, with -g * log2(e) carried as hi + lo (log2(e) split into
+// an fp32 head and tail, the head product's error recovered by an FMA) and
+// 2^lo applied to first order; 1 / (1 + e) is the hardware reciprocal with one
+// Newton step.  Within a few fp32 ulps of the exact value, far below half an
+// ulp of bf16 or fp16.  -g is clamped to [-20, 88]: from g >= 20 the result is
+// exactly 1, as the exact value rounds to 1 in fp32; below g = -88 (exact
+// value under 2^-126) it is 0.  NaN stays NaN in the product with g.
+__device__ __forceinline__ float sigmoid_fast(float g)
+{
+    constexpr float kLog2e = 1.44269502f;       // fp32 nearest to log2(e)
+    constexpr float kLog2eTail = 1.925963e-8f;  // log2(e) - kLog2e
+    constexpr float kLn2 = 0.693147182f;
+    const float x = fminf(fmaxf(-g, -20.0f), 88.0f);
+    const float hi = x * kLog2e;
+    const float lo = __builtin_fmaf(x, kLog2eTail, __builtin_fmaf(x, kLog2e, -hi));
+    const float e2 = __builtin_amdgcn_exp2f(hi);
+    const float e = __builtin_fmaf(e2, lo * kLn2, e2);
+    const float d = 1.0f + e;
+    float r = __builtin_amdgcn_rcpf(d);
+    r = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+    return -g > 88.0f ? 0.0f : r;
+}
+
+// fp32 outputs (tolerance 1e-6 relative) use the device library's exp and an
+// IEEE division; 16-bit outputs use sigmoid_fast.
+template <typename T> __device__ __forceinline__ float swiglu_one(float g, float u)
+{
+    float s;
+    if constexpr (Pack<T>::kBytes == 4)
+        s = 1.0f / (1.0f + expf(-g));
+    else
+        s = sigmoid_fast(g);
+    const float t = g * s;
+    return t * u;
+}
+
+// A team of kTpr lanes owns a row; lane l handles output pieces l + k * kTpr
+// (16 bytes each) and the matching gate and up pieces.
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>
+__device__ __forceinline__ void swiglu_vec_body(const SwigluParams &p)
+{
+    constexpr int kE = Pack<T>::kElems;
+    constexpr int kRpb = kBlock / kTpr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;
+    const int team = tid / kTpr;
+    const int64_t row0 = (int64_t)blockIdx.x * kRpb;
+    const int64_t left = p.rows - row0;
+    const uint32_t nrows = left < kRpb ? (uint32_t)left : (uint32_t)kRpb;
+    const uint32_t out_row = (uint32_t)p.d * (uint32_t)Pack<T>::kBytes;   // bytes of one output row
+    const uint32_t in_row = 2u * out_row;
+    const auto rx = make_rsrc((const char *)p.x + (size_t)row0 * in_row, nrows * in_row);
+    const auto ro = make_rsrc((char *)p.out + (size_t)row0 * out_row, nrows * out_row);
+
+    uint32_t goff[kVpt], ooff[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        const uint32_t c = (uint32_t)(k * kTpr + lane) * 16u;
+        const bool in = c < out_row;
+        goff[k] = in ? (uint32_t)team * in_row + c : kOutOfRange;
+        ooff[k] = in ? (uint32_t)team * out_row + c : kOutOfRange;
+    }
+    u32x4 gv[kVpt], uv[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        gv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, goff[k], 0, kLoadCpol);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)   // the up piece sits one output row further on
+        uv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, goff[k] == kOutOfRange ? kOutOfRange : goff[k] + out_row,
+                                                      0, kLoadCpol);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float o[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            o[e] = swiglu_one<T>(Pack<T>::get(gv[k], e), Pack<T>::get(uv[k], e));
+        __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ro, ooff[k], 0, kStoreCpol);
+    }
+}
+
+// Any alignment and width: one element per thread per step, grid-stride.
+template <typename T>
+__device__ __forceinline__ void swiglu_generic_body(const SwigluParams &p)
+{
+    const int64_t total = p.rows * (int64_t)p.d;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / p.d;
+        const int64_t j = i - r * p.d;
+        const float g = Scalar<T>::get(p.x, r * 2 * (int64_t)p.d + j);
+        const float u = Scalar<T>::get(p.x, r * 2 * (int64_t)p.d + p.d + j);
+        Scalar<T>::put(p.out, i, swiglu_one<T>(g, u));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel entry points, one name per operation and path.
 // ---------------------------------------------------------------------------
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
@@ -491,6 +613,18 @@ template <typename T, int kTpr, int kEpa, int kBlock>
 __global__ __launch_bounds__(kBlock) void fused_add_rms_norm_generic(Params p)
 {
     generic_body<T, true, kTpr, kEpa, kBlock>(p);
+}
+
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>
+__global__ __launch_bounds__(kBlock) void silu_and_mul_vec(SwigluParams p)
+{
+    swiglu_vec_body<T, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol>(p);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void silu_and_mul_generic(SwigluParams p)
+{
+    swiglu_generic_body<T>(p);
 }
 
 }  // namespace ks

@@ -24,6 +24,16 @@ struct Launch {
     hipStream_t stream;
 };
 
+// One SwiGLU launch (out [rows, d], x [rows, 2 d]).
+struct SwigluLaunch {
+    void *out;
+    const void *x;
+    int64_t rows;
+    int32_t d;
+    ks_plan_t plan;
+    hipStream_t stream;
+};
+
 // Cache-policy bits of a buffer instruction that marks it non-temporal.
 constexpr int kNonTemporal = 2;
 
@@ -39,6 +49,12 @@ KS_DECLARE_LAUNCH(f32)
 KS_DECLARE_LAUNCH(f16)
 KS_DECLARE_LAUNCH(bf16)
 #undef KS_DECLARE_LAUNCH
+hipError_t launch_swiglu_f32(const SwigluLaunch &l);
+hipError_t launch_swiglu_f16(const SwigluLaunch &l);
+hipError_t launch_swiglu_bf16(const SwigluLaunch &l);
+
+// The one generic SwiGLU plan: a grid-stride loop over elements.
+constexpr int kSwigluGenericBlock = 256;
 
 // Vector path limits: threads per row 8..1024 (powers of two), vectors per
 // thread 1..8 (1..4 when a row spans 1024 threads, to stay within the VGPR

@@ -117,4 +117,77 @@ hipError_t launch_generic_typed(const Launch &l)
     return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// SwiGLU
+// ---------------------------------------------------------------------------
+template <typename Kernel>
+hipError_t run_swiglu(Kernel kernel, const SwigluLaunch &l, int block)
+{
+    SwigluParams p{l.out, l.x, l.rows, l.d};
+    const int64_t rpb = block / l.plan.threads_per_row;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)((l.rows + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int TPR, int V>
+hipError_t swiglu_one(const SwigluLaunch &l)
+{
+    constexpr int B = TPR < 256 ? 256 : TPR;
+    constexpr int NT = kNonTemporal;
+    const ks_plan_t &p = l.plan;
+    if (!p.load_nt && !p.store_nt)
+        return run_swiglu(silu_and_mul_vec<T, TPR, V, B, 0, 0>, l, B);
+    if (p.load_nt && p.store_nt)
+        return run_swiglu(silu_and_mul_vec<T, TPR, V, B, NT, NT>, l, B);
+    if (!p.load_nt && p.store_nt)
+        return run_swiglu(silu_and_mul_vec<T, TPR, V, B, 0, NT>, l, B);
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int TPR>
+hipError_t swiglu_by_vpt(const SwigluLaunch &l)
+{
+    switch (l.plan.vectors_per_thread) {
+    case 1: return swiglu_one<T, TPR, 1>(l);
+    case 2: return swiglu_one<T, TPR, 2>(l);
+    case 3: return swiglu_one<T, TPR, 3>(l);
+    case 4: return swiglu_one<T, TPR, 4>(l);
+    default: break;
+    }
+    if constexpr (TPR < kMaxTpr) {
+        switch (l.plan.vectors_per_thread) {
+        case 5: return swiglu_one<T, TPR, 5>(l);
+        case 6: return swiglu_one<T, TPR, 6>(l);
+        case 7: return swiglu_one<T, TPR, 7>(l);
+        case 8: return swiglu_one<T, TPR, 8>(l);
+        default: break;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_swiglu_typed(const SwigluLaunch &l)
+{
+    if (l.plan.path == KS_PATH_GENERIC) {
+        SwigluParams p{l.out, l.x, l.rows, l.d};
+        const int64_t total = l.rows * (int64_t)l.d;
+        int64_t blocks = (total + kSwigluGenericBlock - 1) / kSwigluGenericBlock;
+        blocks = blocks > 8192 ? 8192 : blocks;   // grid-stride beyond 2M threads
+        hipLaunchKernelGGL(silu_and_mul_generic<T>, dim3((unsigned)blocks), dim3(kSwigluGenericBlock), 0, l.stream, p);
+        return hipGetLastError();
+    }
+    switch (l.plan.threads_per_row) {
+    case 8: return swiglu_by_vpt<T, 8>(l);
+    case 16: return swiglu_by_vpt<T, 16>(l);
+    case 32: return swiglu_by_vpt<T, 32>(l);
+    case 64: return swiglu_by_vpt<T, 64>(l);
+    case 128: return swiglu_by_vpt<T, 128>(l);
+    case 256: return swiglu_by_vpt<T, 256>(l);
+    case 512: return swiglu_by_vpt<T, 512>(l);
+    case 1024: return swiglu_by_vpt<T, 1024>(l);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace ks

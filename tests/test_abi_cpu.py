@@ -274,3 +274,47 @@ def test_ctypes_signatures_match_header():
     for name in ("ks_rms_norm_ex", "ks_fused_add_rms_norm_ex"):
         assert len(getattr(h, name).argtypes) == 9
     assert ctypes.sizeof(b.Plan) == 36
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU entry points (kernscope "Inputs": nonempty even last dimension, any D,
+# empty batches allowed, x read-only and the output a separate tensor)
+# ---------------------------------------------------------------------------
+def silu(out, x, rows, d, dtype=BF16, plan=None):
+    return b.ks_silu_and_mul_ex(out, x, rows, d, dtype, plan, 0)
+
+
+def test_silu_statuses():
+    x, out = A, A + 256 * MB
+    assert silu(out, x, 4, 4096, dtype=9) == DTYPE
+    assert silu(out, x, -1, 4096) == INVALID
+    assert silu(out, x, 4, 0) == INVALID
+    assert silu(out, x, 4, 2**24 + 1) == INVALID
+    assert silu(None, x, 4, 4096) == INVALID
+    assert silu(out, None, 4, 4096) == INVALID
+    assert silu(None, None, 0, 4096) == OK                 # empty batch: no HIP call
+    assert silu(x + 4096 * 2, x, 4, 4096) == OVERLAP       # output inside the input
+    assert silu(x - 100, x, 4, 4096) == OVERLAP
+    assert b.ks_silu_and_mul(None, None, 0, 7, BF16, 0) == OK
+
+
+def test_silu_plans():
+    x, out = A, A + 256 * MB
+    p = ks.get_plan("silu_and_mul", torch.bfloat16, 4096, 512).as_dict()
+    assert p["path"] == 0 and p["weight_lds"] == 0 and p["load_nt"] == 1 and p["store_nt"] == 1
+    assert silu(out, x, 0, 4096, plan=b.Plan.from_dict(p)) == OK
+    assert silu(out, x, 0, 4096, plan=b.Plan.from_dict({**p, "weight_lds": 1})) == INVALID
+    g = ks.get_plan("silu_and_mul", torch.bfloat16, 4095, 512).as_dict()      # odd row bytes: generic
+    assert (g["path"], g["threads_per_row"], g["rows_per_block"], g["block_threads"]) == (1, 256, 1, 256)
+    assert silu(out, x, 0, 4095, plan=b.Plan.from_dict(g)) == OK
+    assert silu(out, x, 0, 4095, plan=b.Plan.from_dict({**g, "threads_per_row": 64})) == INVALID
+    # unaligned buffers cannot take a vector plan
+    assert silu(out + 2, x, 4, 4096, plan=b.Plan.from_dict(p)) == INVALID
+
+
+def test_silu_tensor_api_checks():
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ks.silu_and_mul(x)                                      # not on a HIP device
+    with pytest.raises(TypeError):
+        ks.silu_and_mul(x.to(torch.int32))

@@ -265,3 +265,38 @@ def test_graph_replays_match_eager():
         say("graph replay", rep)
         for got, want in zip((out, xf, rf), eager):
             check_bitexact(got.cpu(), want.cpu())
+
+
+def test_fp16_outputs_round_through_fp32():
+    """The contract rounds (v * scale) * w to fp32 and then to the dtype.  Constant
+    rows with exact sums make scale identical on both sides, so every output is
+    RN16(RN32(t * w)) and must match the oracle bit for bit; with every fp16
+    weight in [1, 2) and several eps values, dozens of positions differ from a
+    single rounding RN16(t * w), which a fused multiply-convert would produce."""
+    import numpy as np
+
+    h = 1024
+    w = torch.arange(0x3C00, 0x4000, dtype=torch.int32).to(torch.int16).view(torch.float16)   # all of [1, 2)
+    cs = [m * 2.0 ** k for m in range(64, 128) for k in range(-8, 4)]   # <= 7 significant bits: exact sums
+    cs = cs + [-c for c in cs[::7]]
+    x = torch.tensor(cs, dtype=torch.float32)[:, None].expand(len(cs), h).to(torch.float16).contiguous()
+    half = (x.float() / 2).to(torch.float16)
+    c32 = np.array(cs, dtype=np.float32)
+    wn = w.float().numpy()
+    discriminating = 0
+    for eps in (1e-3, 3e-3, 1e-2, 0.1, 0.37, 1.0):
+        # host model of the pipeline: mean of h equal squares is exact, then fp32 steps
+        d = (c32 * c32 + np.float32(eps)).astype(np.float32)
+        scale = (1.0 / np.sqrt(d.astype(np.float64))).astype(np.float32)
+        t = (c32 * scale).astype(np.float32)
+        double = (t[:, None] * wn[None, :]).astype(np.float32).astype(np.float16)
+        single = (t[:, None].astype(np.float64) * wn[None, :].astype(np.float64)).astype(np.float16)
+        discriminating += int((double.view(np.uint16) != single.view(np.uint16)).sum())
+        y, _ = gpu_run("rms_norm", {"x": x, "weight": w}, eps)
+        check_bitexact(y, torch.from_numpy(double))
+        check_bitexact(y, oracle.rms_norm(x, w, eps))
+        fx, fr = gpu_run("fused_add_rms_norm", {"x": half, "residual": half.clone(), "weight": w}, eps)
+        check_bitexact(fr, x)
+        check_bitexact(fx, torch.from_numpy(double))
+    say("fp16 double rounding: positions where a single rounding differs:", discriminating)
+    assert discriminating > 20

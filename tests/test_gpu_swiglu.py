@@ -1,0 +1,142 @@
+"""SwiGLU (silu_and_mul) on the GPU against the CPU oracle, element by element.
+
+Bar: within 1 ulp of bf16/fp16 (|difference| <= 1e-6 near zero) and at least
+99.9% bit-identical on large cases; fp32 within rtol = atol = 1e-6.  Cases:
+the kernscope SwiGLU baseline shape (512x8192 -> 4096, bf16), a 7B-model FFN
+(2048x22016 -> 11008, bf16), fp16 2048x8192, the kernscope checklist (all
+dtypes, odd D, empty batches, contiguous offset views, extreme gate values),
+widths past the vector path, every compiled plan, and graph replays.
+"""
+import pytest
+import torch
+
+import oracle
+import rmsnorm_row_normalisation_amd as ks
+import workloads
+from compare import check_bitexact, check_normalised
+from gpu_cases import HINTS, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+DTYPES = ["bfloat16", "float16", "float32"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def gpu_swiglu(x: torch.Tensor, plan=None, offset: int = 0) -> torch.Tensor:
+    if offset:
+        buf = torch.empty(x.numel() + offset, dtype=x.dtype, device="cuda")
+        xd = buf[offset:].view(x.shape)
+        xd.copy_(x.cuda())
+        obuf = torch.empty(x.numel() // 2 + offset, dtype=x.dtype, device="cuda")
+        out = obuf[offset:].view(*x.shape[:-1], x.shape[-1] // 2)
+        ks.silu_and_mul(xd, out=out, plan=plan)
+    else:
+        out = ks.silu_and_mul(x.cuda(), plan=plan)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def check(name, x, plan=None, offset=0, exact=None):
+    say("swiglu", name, tuple(x.shape), x.dtype, plan.as_dict() if plan is not None else "policy", offset)
+    got = gpu_swiglu(x, plan, offset)
+    ref = oracle.silu_and_mul(x)
+    if exact is None:
+        exact = got.numel() >= 20000
+    return check_normalised(got, ref, 0.999 if exact else None)
+
+
+@pytest.mark.parametrize("name", ["S1", "S2", "S3"])
+def test_workloads(name):
+    wl = workloads.WORKLOADS[name]
+    x = workloads.make_inputs(wl)["x"]
+    say(name, check(name, x))
+
+
+SHAPES = [(2,), (3, 10), (2, 3, 14), (1, 2), (5, 126), (7, 2000), (3, 8194), (130, 3072), (2, 2 * 32768),
+          (2, 2 * 40000)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(shape, dtype):
+    x = workloads.random_case(shape, dtype, seed=sum(shape), x=workloads.normal(0, 2))["x"]
+    check("shape", x)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_offset_views_and_empty(dtype):
+    x = workloads.random_case((37, 2 * 1024), dtype, seed=5)["x"]
+    check("offset", x, offset=1)
+    e = torch.empty(0, 16, dtype=workloads.DTYPES[dtype], device="cuda")
+    assert ks.silu_and_mul(e).shape == (0, 8)
+    e3 = torch.empty(3, 0, 16, dtype=workloads.DTYPES[dtype], device="cuda")
+    assert ks.silu_and_mul(e3).shape == (3, 0, 8)
+
+
+def test_extreme_gates():
+    for dtype in (torch.bfloat16, torch.float16, torch.float32):
+        d = 512
+        g = torch.linspace(-120, 120, d)
+        g[:6] = torch.tensor([float("inf"), float("-inf"), float("nan"), 0.0, -0.0, 88.0])
+        u = torch.linspace(-3, 3, d)
+        x = torch.stack([torch.cat([g, u]), torch.cat([-g, u])]).to(dtype).contiguous()
+        got = gpu_swiglu(x)
+        ref = oracle.silu_and_mul(x)
+        assert bool((torch.isnan(got) == torch.isnan(ref)).all())
+        check_normalised(got, ref)
+        # gates >= 18: the sigmoid is exactly 1 in fp32, so out = RNE(fl32(g * u))
+        big = x[0, :d].float() >= 18
+        want = (x[0, :d].float() * x[0, d:].float()).to(dtype)
+        check_bitexact(got[0][big], want[big])
+
+
+@pytest.mark.parametrize("dtype,d", [("bfloat16", 4096), ("float16", 1536), ("float32", 1000)])
+def test_every_plan(dtype, d):
+    """All compiled plans give the same bits (elementwise) and meet the oracle bar."""
+    x = workloads.random_case((70, 2 * d), dtype, seed=d)["x"]
+    ref = oracle.silu_and_mul(x)
+    es = x.element_size()
+    first = None
+    tpr = 8
+    plans = []
+    while tpr <= 1024:
+        maxv = 4 if tpr == 1024 else 8
+        for vpt in range(1, maxv + 1):
+            if tpr * vpt * 16 >= d * es and (d * es) % 16 == 0:
+                block = max(256, tpr)
+                for lnt, snt, wl in HINTS:
+                    if wl:
+                        continue
+                    plans.append(ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt, elems_per_access=16 // es,
+                                         rows_per_block=block // tpr, block_threads=block, load_nt=lnt, store_nt=snt))
+        tpr *= 2
+    plans.append(ks.Plan(path=1, threads_per_row=256, vectors_per_thread=0, elems_per_access=1, rows_per_block=1,
+                         block_threads=256))
+    assert len(plans) > 10
+    for plan in plans:
+        got = gpu_swiglu(x, plan)
+        check_normalised(got, ref, 0.999)
+        if first is None:
+            first = got
+        else:
+            check_bitexact(got, first)
+
+
+def test_graph_replays_match_eager():
+    x = workloads.make_inputs(workloads.WORKLOADS["S1"])["x"].cuda()
+    out = ks.silu_and_mul(x)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ks.silu_and_mul(x, out=out)
+    for rep in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_bitexact(out.cpu(), eager.cpu())

@@ -1,5 +1,9 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
+RMSNorm workloads (C*) and SwiGLU workloads (S*: 512x8192 -> 512x4096 bf16 as in
+the kernscope SwiGLU baseline, and the 7B-model FFN width 11008 at sequence
+2048 from the Triton Kernels benchmark table).
+
 This module draws random numbers and nothing else: it holds none of the
 normalisation's arithmetic, so both the CPU oracle and the GPU path can take
 their inputs from it without sharing any of the method.
@@ -58,10 +62,10 @@ class Workload:
     rows: int
     hidden: int
     x: Dist
-    weight: Dist
+    weight: Dist | None
     eps: float
     seed_x: int
-    seed_w: int
+    seed_w: int | None
     residual: Dist | None = None
     seed_r: int | None = None
     outlier_frac: float = 0.0
@@ -80,12 +84,13 @@ class Workload:
             parts[-1] += f" with {self.outlier_frac:.0%} of elements x{self.outlier_scale:g}"
         if self.residual is not None and "fused_add_rms_norm" in self.ops:
             parts.append(f"residual ~{self.residual}")
-        parts.append(f"weight ~{self.weight}")
-        parts.append(f"eps={self.eps:g}")
+        if self.weight is not None:
+            parts.append(f"weight ~{self.weight}")
+            parts.append(f"eps={self.eps:g}")
         return ", ".join(parts)
 
 
-RMS, FUSED = "rms_norm", "fused_add_rms_norm"
+RMS, FUSED, SWIGLU = "rms_norm", "fused_add_rms_norm", "silu_and_mul"
 
 WORKLOADS: dict[str, Workload] = {
     # small case the oracle finishes in milliseconds
@@ -108,6 +113,10 @@ WORKLOADS: dict[str, Workload] = {
     "C5f": Workload("C5f", (FUSED,), "bfloat16", 32768, 8192, normal(0, 2), normal(1, 0.1), 1e-6, 5001, 5003,
                     residual=normal(0, 2), seed_r=5002),
     "C5r": Workload("C5r", (RMS,), "bfloat16", 8192, 16384, normal(0, 2), normal(1, 0.1), 1e-6, 5101, 5103),
+    # SwiGLU: `hidden` is the input width 2D (gate half, then up half)
+    "S1": Workload("S1", (SWIGLU,), "bfloat16", 512, 2 * 4096, normal(0, 1), None, 0.0, 6001, None),
+    "S2": Workload("S2", (SWIGLU,), "bfloat16", 2048, 2 * 11008, normal(0, 1), None, 0.0, 6101, None),
+    "S3": Workload("S3", (SWIGLU,), "float16", 2048, 2 * 4096, normal(0, 1), None, 0.0, 6201, None),
 }
 
 
@@ -129,11 +138,10 @@ def make_inputs(wl: Workload, rows: int | None = None) -> dict[str, torch.Tensor
         k = int(round(wl.outlier_frac * n))
         idx = np.random.default_rng(wl.seed_outlier).choice(n, size=k, replace=False)
         x[idx] *= np.float32(wl.outlier_scale)
-    out = {
-        "x": _to_dtype(x, wl.torch_dtype, (rows, wl.hidden)),
-        "weight": _to_dtype(wl.weight.draw(np.random.default_rng(wl.seed_w), wl.hidden), wl.torch_dtype,
-                            (wl.hidden,)),
-    }
+    out = {"x": _to_dtype(x, wl.torch_dtype, (rows, wl.hidden))}
+    if wl.weight is not None:
+        out["weight"] = _to_dtype(wl.weight.draw(np.random.default_rng(wl.seed_w), wl.hidden), wl.torch_dtype,
+                                  (wl.hidden,))
     if wl.residual is not None:
         r = wl.residual.draw(np.random.default_rng(wl.seed_r), n)
         out["residual"] = _to_dtype(r, wl.torch_dtype, (rows, wl.hidden))
