@@ -373,9 +373,20 @@ def _median(vals: list[float]) -> float:
     return vals[len(vals) // 2]
 
 
-def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> None:
-    """Counter-derived HBM bytes per launch of each kernel, scaled so that the
-    calibration copy reads and writes exactly its own size."""
+def kernel_op(name: str) -> str | None:
+    """The operation a demangled kernel name belongs to (None for other kernels)."""
+    if "ks::" not in name:
+        return None
+    for op in ("fused_add_rms_norm", "rms_norm", "silu_and_mul"):
+        if op in name:
+            return op
+    return None
+
+
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> None:
+    """Counter-derived HBM bytes per launch of each kernel of one workload,
+    scaled so that the calibration copy reads and writes exactly its own size.
+    Entries of other workloads taken on the same kernel sources are kept."""
     fetch = _per_kernel_kib(fetch_dir, "FETCH_SIZE")
     write = _per_kernel_kib(write_dir, "WRITE_SIZE")
     cf = _per_kernel_kib(copy_fetch_dir, "FETCH_SIZE")
@@ -391,25 +402,36 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_wr
             calib_bytes = json.loads(f.readline())["copy_calibration_bytes"]
     fetch_scale = calib_bytes / (copy_kib(cf) * 1024)
     write_scale = calib_bytes / (copy_kib(cw) * 1024)
-    wl = workloads.WORKLOADS["C3b"]
-    esize = 2
+    wl = workloads.WORKLOADS[workload]
+    esize = wl.torch_dtype.itemsize
     kernels = {}
     for name in fetch:
-        if "ks::" not in name or "rms_norm" not in name:
+        op = kernel_op(name)
+        if op is None or op not in wl.ops:
             continue
-        op = "fused_add_rms_norm" if "fused_add_rms_norm" in name else "rms_norm"
         f = _median(fetch[name]) * 1024 * fetch_scale
         w = _median(write.get(name, [0.0])) * 1024 * write_scale
         alg = algorithmic_bytes(op, wl.rows, wl.hidden, esize)
         kernels[name] = {"op": op, "dispatches": len(fetch[name]), "fetch_bytes": round(f),
                          "write_bytes": round(w), "traffic_bytes": round(f + w), "algorithmic_bytes": alg,
                          "traffic_over_algorithmic": round((f + w) / alg, 4)}
-    data = {"kernel_source_hash": kernel_source_hash(), "fetch_scale": round(fetch_scale, 5),
-            "write_scale": round(write_scale, 5), "calibration_copy_bytes": calib_bytes, "kernels": kernels,
-            "workloads": {"C3b": {k["op"]: k["traffic_bytes"] for k in kernels.values()}}}
+    data = {}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        pass
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        data = {"kernel_source_hash": kernel_source_hash(), "workloads": {}, "kernels": {}}
+    data.setdefault("calibration", {})[workload] = {"fetch_scale": round(fetch_scale, 5),
+                                                    "write_scale": round(write_scale, 5),
+                                                    "copy_bytes": calib_bytes}
+    data.setdefault("kernels", {})[workload] = kernels
+    data.setdefault("workloads", {})[workload] = {k["op"]: k["traffic_bytes"] for k in kernels.values()}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
-    print(json.dumps(data, indent=1))
+    print(json.dumps({"workload": workload, "calibration": data["calibration"][workload], "kernels": kernels},
+                     indent=1))
 
 
 # ---------------------------------------------------------------------------
@@ -494,7 +516,7 @@ def sweep_workloads(args, ks, oracle_mod) -> None:
 def main() -> None:
     args = parse()
     if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
+        traffic_summary(args.workload, *args.traffic_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

@@ -67,10 +67,18 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // These rules were fitted to timings of every compiled shape and hint
 // combination for hidden 1024..16384 and 1..32768 rows (bf16).
 // Rows wider than 64 KiB, or unaligned buffers, take the generic path.
+//
+// SwiGLU (pieces are 16-byte pieces of the output row, each reading two input
+// pieces) has no reduction and about three times the arithmetic per byte, so
+// it wants more, shorter lanes: at most 2 pieces per lane, and a 1024-lane
+// team where that covers the row with no more idle piece slots than a
+// 512-lane team does.  Fitted to timings for output widths 1024..14336 and
+// 1..8192 rows (bf16, fp16).
 constexpr int64_t kTargetLanes = 131072;
 constexpr int64_t kLargeBatchPieces = int64_t(1) << 22;
 constexpr int64_t kWeightLdsPieces = int64_t(1) << 18;
 constexpr int kPolicyMaxTpr = 512;
+constexpr int64_t kSwigluMaxVpt = 2;
 
 int64_t pow2_ceil(int64_t v)
 {
@@ -90,11 +98,18 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     const int64_t nvec = row_bytes / 16;
     if (aligned && row_bytes % 16 == 0 && nvec <= (int64_t)kPolicyMaxTpr * ks::kMaxVpt) {
         const int64_t pieces = rows * nvec;
-        const int64_t max_vpt = pieces >= kLargeBatchPieces ? 4 : ks::kMaxVpt;
+        const bool swiglu = op == KS_OP_SILU_AND_MUL;
+        const int64_t max_vpt = swiglu ? kSwigluMaxVpt : pieces >= kLargeBatchPieces ? 4 : ks::kMaxVpt;
         int64_t vpt = pow2_ceil((pieces + kTargetLanes - 1) / kTargetLanes);
         vpt = vpt < 1 ? 1 : vpt > max_vpt ? max_vpt : vpt;
         int64_t tpr = pow2_ceil((nvec + vpt - 1) / vpt);
-        tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > kPolicyMaxTpr ? kPolicyMaxTpr : tpr;
+        if (swiglu && tpr > kPolicyMaxTpr) {
+            const int64_t slots512 = (nvec + kPolicyMaxTpr - 1) / kPolicyMaxTpr * kPolicyMaxTpr;
+            const int64_t slots1024 = (nvec + ks::kMaxTpr - 1) / ks::kMaxTpr * ks::kMaxTpr;
+            tpr = slots1024 <= slots512 ? ks::kMaxTpr : kPolicyMaxTpr;
+        }
+        const int64_t max_tpr = swiglu ? ks::kMaxTpr : kPolicyMaxTpr;
+        tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > max_tpr ? max_tpr : tpr;
         plan.path = KS_PATH_VECTOR;
         plan.threads_per_row = (int32_t)tpr;
         plan.vectors_per_thread = (int32_t)((nvec + tpr - 1) / tpr);
@@ -104,7 +119,6 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.load_nt = 1;
         plan.store_nt = 1;
         plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;
-        // (SwiGLU has no weight and no reduction; the same spread suits it)
         return plan;
     }
     plan.path = KS_PATH_GENERIC;

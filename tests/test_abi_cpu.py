@@ -312,6 +312,41 @@ def test_silu_plans():
     assert silu(out + 2, x, 4, 4096, plan=b.Plan.from_dict(p)) == INVALID
 
 
+# (output width D, rows) -> (threads per row, pieces per lane): the fastest
+# plan of a sweep over every compiled shape on one MI355X (bf16), or one
+# within 1% of it.
+SILU_EXPECTED = {
+    (1024, 2048): (64, 2), (1024, 8192): (64, 2),
+    (4096, 512): (256, 2), (4096, 2048): (256, 2), (4096, 8192): (256, 2),
+    (11008, 512): (512, 3), (11008, 2048): (512, 3), (11008, 8192): (512, 3),
+    (14336, 128): (1024, 2), (14336, 512): (1024, 2), (14336, 2048): (1024, 2), (14336, 8192): (1024, 2),
+}
+
+
+@pytest.mark.parametrize("key", sorted(SILU_EXPECTED))
+def test_silu_policy_table(key):
+    d, rows = key
+    p = ks.get_plan("silu_and_mul", torch.bfloat16, d, rows).as_dict()
+    assert (p["threads_per_row"], p["vectors_per_thread"]) == SILU_EXPECTED[key]
+
+
+def test_silu_policy_rule():
+    """At most 2 pieces per lane; a 1024-lane team only where it wastes no
+    more piece slots than a 512-lane one; every plan is accepted."""
+    for d in (8, 64, 1000, 1024, 4096, 5120, 8192, 11008, 14336, 16384, 24576, 32768):
+        nvec = d * 2 // 16
+        for rows in (0, 1, 64, 512, 2048, 8192, 2**20):
+            p = ks.get_plan("silu_and_mul", torch.bfloat16, d, rows).as_dict()
+            assert p["path"] == 0
+            tpr, vpt = p["threads_per_row"], p["vectors_per_thread"]
+            assert tpr * vpt >= nvec and vpt <= (8 if tpr == 512 else 4 if tpr == 1024 else 2)
+            if tpr == 1024:
+                assert -(-nvec // 1024) * 1024 <= -(-nvec // 512) * 512
+            elif vpt > 2:
+                assert tpr == 512
+            assert silu(A + 256 * MB, A, 0, d, plan=b.Plan.from_dict(p)) == OK
+
+
 def test_silu_tensor_api_checks():
     x = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):

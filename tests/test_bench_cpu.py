@@ -49,12 +49,23 @@ def test_traffic_summary(tmp_path, monkeypatch):
     _counter_csv(tmp_path / "cf", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 131072.0)])
     _counter_csv(tmp_path / "cw", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 262144.0)])
     (tmp_path / "cf" / "calibration.json").write_text(json.dumps({"copy_calibration_bytes": 256 << 20}))
-    bench.traffic_summary(*(str(tmp_path / d) for d in ("f", "w", "cf", "cw")))
+    bench.traffic_summary("C3b", *(str(tmp_path / d) for d in ("f", "w", "cf", "cw")))
     data = json.load(open(tmp_path / "t.json"))
-    entry = data["kernels"][k]
-    assert data["fetch_scale"] == pytest.approx(2.0) and data["write_scale"] == pytest.approx(1.0)
+    entry = data["kernels"]["C3b"][k]
+    cal = data["calibration"]["C3b"]
+    assert cal["fetch_scale"] == pytest.approx(2.0) and cal["write_scale"] == pytest.approx(1.0)
     assert entry["fetch_bytes"] == 32 << 20 and entry["write_bytes"] == 32 << 20
     assert data["workloads"]["C3b"]["fused_add_rms_norm"] == 64 << 20
+    assert bench.load_traffic("C3b") == {"fused_add_rms_norm": 64 << 20}
+    # a second workload on the same sources is merged; SwiGLU kernels are recognised
+    s = "void ks::silu_and_mul_vec<ks::bf16, 512, 3, 512, 2, 2>(ks::SwigluParams)"
+    _counter_csv(tmp_path / "f2", [(s, "FETCH_SIZE", 1024.0), (k, "FETCH_SIZE", 1.0)])
+    _counter_csv(tmp_path / "w2", [(s, "WRITE_SIZE", 512.0)])
+    bench.traffic_summary("S2", *(str(tmp_path / d) for d in ("f2", "w2", "cf", "cw")))
+    data = json.load(open(tmp_path / "t.json"))
+    assert set(data["workloads"]) == {"C3b", "S2"}
+    assert data["workloads"]["S2"] == {"silu_and_mul": (2 << 20) + (512 << 10)}
+    assert bench.kernel_op(k) == "fused_add_rms_norm" and bench.kernel_op("__amd_rocclr_copyBuffer") is None
 
 
 def test_regressions():
