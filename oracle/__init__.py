@@ -1,11 +1,11 @@
-"""CPU oracle for RMSNorm, fused residual-add RMSNorm and SwiGLU.
+"""CPU oracle for RMSNorm, fused residual-add RMSNorm, SwiGLU and softmax.
 
 TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package; the GPU product path
 never does, and the two share no code.
 
 ``ks_oracle.c`` holds all arithmetic (kernscope README, "Numerical contract":
-"RMSNorm", "Fused residual-add RMSNorm" and "SwiGLU activation").  This module
+"RMSNorm", "Fused residual-add RMSNorm", "SwiGLU activation" and "Softmax").  This module
 only builds and loads that library and marshals torch CPU tensors (used as
 plain byte containers) to it.  ``brute64`` is a second, independent fp64 / exact-rational
 check for tiny inputs.
@@ -48,6 +48,8 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_widen_array.restype = c_int
     lib.oracle_silu_and_mul.argtypes = [c_int, vp, vp, i64, i64]
     lib.oracle_silu_and_mul.restype = c_int
+    lib.oracle_softmax.argtypes = [c_int, vp, vp, i64, i64]
+    lib.oracle_softmax.restype = c_int
     return lib
 
 
@@ -118,6 +120,21 @@ def silu_and_mul(x: torch.Tensor, lib: ctypes.CDLL | None = None) -> torch.Tenso
     st = lib.oracle_silu_and_mul(_DTYPE_CODE[x.dtype], x.data_ptr(), out.data_ptr(), rows, d)
     if st != 0:
         raise ValueError(f"oracle_silu_and_mul failed with status {st}")
+    return out
+
+
+def softmax(x: torch.Tensor, lib: ctypes.CDLL | None = None) -> torch.Tensor:
+    """Softmax of x with shape (..., H) over the last dimension: a new tensor."""
+    lib = lib or load()
+    if x.device.type != "cpu" or x.dtype not in _DTYPE_CODE or not x.is_contiguous():
+        raise ValueError("oracle needs a contiguous CPU tensor of a supported dtype")
+    if x.dim() == 0 or x.shape[-1] == 0:
+        raise ValueError("the last dimension must be nonempty")
+    hidden = x.shape[-1]
+    out = torch.empty_like(x)
+    st = lib.oracle_softmax(_DTYPE_CODE[x.dtype], x.data_ptr(), out.data_ptr(), x.numel() // hidden, hidden)
+    if st != 0:
+        raise ValueError(f"oracle_softmax failed with status {st}")
     return out
 
 

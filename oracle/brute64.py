@@ -1,7 +1,7 @@
 """Exact-arithmetic brute force for tiny inputs.  TEST INFRASTRUCTURE ONLY.
 
 A second statement of the kernscope "Numerical contract" (sections "RMSNorm",
-"Fused residual-add RMSNorm" and "SwiGLU activation") that shares nothing with
+"Fused residual-add RMSNorm", "SwiGLU activation" and "Softmax") that shares nothing with
 ``ks_oracle.c``:
 the sum of squares, the mean and eps are exact rationals, the square root is
 taken to 80 significant digits, and the result is rounded ONCE to the output
@@ -10,7 +10,7 @@ Only the fused form's fp32 residual sum is rounded to fp32 first, because the
 contract defines s as an fp32 value.
 
 It is meant for a few hundred elements at most (pure Python).  The SwiGLU
-statement at the end follows the same approach.
+and softmax statements at the end follow the same approach.
 """
 from __future__ import annotations
 
@@ -91,4 +91,24 @@ def silu_and_mul(x: list[list[float]], fmt: str) -> list[list[float]]:
         d = len(row) // 2
         out.append([round_to(Fraction(g) * _sigmoid(Fraction(g)) * Fraction(u), fmt)
                     for g, u in zip(row[:d], row[d:])])
+    return out
+
+
+def _exp(q: Fraction) -> Fraction:
+    with localcontext() as ctx:
+        ctx.prec = 80
+        return Fraction((Decimal(q.numerator) / Decimal(q.denominator)).exp())
+
+
+def softmax(x: list[list[float]], fmt: str) -> list[list[float]]:
+    """Softmax of rows of finite values (kernscope "Numerical contract" >
+    "Softmax"): the row maximum, z = the fp32 rounding of each element minus it
+    (the contract forms z in fp32), 80-digit exponentials, an exact sum and
+    quotient, rounded to fp32 and then to the output format."""
+    out = []
+    for row in x:
+        m = max(Fraction(v) for v in row)
+        es = [_exp(Fraction(round_to(Fraction(v) - m, "float32"))) for v in row]
+        s = sum(es)
+        out.append([round_to(Fraction(round_to(e / s, "float32")), fmt) for e in es])
     return out

@@ -1,6 +1,6 @@
 /*
- * CPU oracle for RMSNorm row normalisation, the fused residual-add variant
- * and the SwiGLU activation.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU oracle for RMSNorm row normalisation, the fused residual-add variant,
+ * the SwiGLU activation and softmax over the last dimension.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this file's library; the GPU library never
  * does, and the two share no code, headers or constants.
  *
@@ -282,5 +282,58 @@ int oracle_silu_and_mul(int dtype, const void *x, void *out, int64_t rows, int64
             store_elem(dtype, out, r * d + j, t * u);
         }
     }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Softmax over the last dimension (kernscope README, "Numerical contract" > */
+/* "Softmax"; shapes from its "Inputs" section):                             */
+/*   z   = fp32(x) - max(fp32(x)) over the row,                              */
+/*   out = cast(exp(z) / sum(exp(z)) over the row)                           */
+/* with the maximum, exponential, sum and division in fp32.  The page's      */
+/* rules for non-finite rows (NaN or +inf anywhere, or a row of only -inf:   */
+/* NaN everywhere; -inf entries of other rows: 0) are what IEEE arithmetic   */
+/* gives once the maximum propagates NaN, so no case is special-cased here.  */
+/* Readings where the page is silent:                                        */
+/*   - the maximum of a row holding a NaN is NaN (as PyTorch's max is);      */
+/*   - z is one IEEE fp32 subtraction of the widened element and the max;    */
+/*   - the fp32 quotient is the fp32 value nearest exp(z) / sum(exp(z)) for  */
+/*     those fp32 z: the exponentials are evaluated in double by the C       */
+/*     library, summed in index order and divided in double, and the         */
+/*     quotient is rounded once to fp32, then cast to the input dtype.       */
+/* ------------------------------------------------------------------------ */
+int oracle_softmax(int dtype, const void *x, void *out, int64_t rows, int64_t hidden)
+{
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+        return ORACLE_BAD_ARG;
+    if (rows < 0 || hidden <= 0)
+        return ORACLE_BAD_ARG;
+    double *e = (double *)malloc((size_t)hidden * sizeof(double));
+    if (e == NULL)
+        return ORACLE_NO_MEMORY;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t base = r * hidden;
+        float m = -INFINITY;
+        int has_nan = 0;
+        for (int64_t j = 0; j < hidden; ++j) {
+            float v = load_elem(dtype, x, base + j);
+            if (isnan(v))
+                has_nan = 1;
+            else if (v > m)
+                m = v;
+        }
+        if (has_nan)
+            m = NAN;
+        double sum = 0.0;
+        for (int64_t j = 0; j < hidden; ++j) {
+            float z = load_elem(dtype, x, base + j) - m;   /* fp32 subtraction */
+            e[j] = exp((double)z);
+            sum += e[j];
+        }
+        /* every element was read above, so out may alias x */
+        for (int64_t j = 0; j < hidden; ++j)
+            store_elem(dtype, out, base + j, (float)(e[j] / sum));
+    }
+    free(e);
     return ORACLE_OK;
 }

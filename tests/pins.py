@@ -375,10 +375,123 @@ def pin_swiglu_closed_forms(lib) -> None:
     assert oracle.silu_and_mul(e, lib=lib).shape == (0, 4)
 
 
+# --------------------------------------------------------------------------
+# Softmax (kernscope "Numerical contract" > "Softmax"; nonfinite rules there)
+# --------------------------------------------------------------------------
+SOFTMAX_SHAPES = [(1,), (2, 5), (3, 17), (2, 64), (2, 3, 40)]
+INF, NAN = float("inf"), float("nan")
+
+
+def _softmax_case(shape, dtype, seed):
+    x = workloads.random_case(shape, dtype, seed, x=workloads.normal(0, 3))["x"]
+    flat = x.reshape(-1)
+    if flat.numel() >= 8:
+        # mixed magnitudes: z = x - max is inexact in fp32 here, so forming z in
+        # a wider format would show; and logits far beyond exp's fp32 range
+        flat[:4] = torch.tensor([100.0, 1e-3, -37.25, 99.5]).to(x.dtype)
+        flat[4:8] = torch.tensor([-120.0, 3.0e-2, -0.0, 0.0]).to(x.dtype)
+    return x
+
+
+def pin_softmax_brute_force(lib) -> None:
+    """Bit-exact agreement with exact rationals and an 80-digit exponential (the
+    oracle's double evaluation is off by about 1e-15 relative, so the two can
+    round differently only within about 2^-50 of a rounding boundary)."""
+    for dtype in ("bfloat16", "float16", "float32"):
+        for i, shape in enumerate(SOFTMAX_SHAPES):
+            x = _softmax_case(shape, dtype, 400 + i)
+            got = oracle.softmax(x, lib=lib)
+            want = _from_values(brute64.softmax(_values(x), dtype), x.dtype, got.shape)
+            check_bitexact(got, want)
+
+
+def _sigmoid64(t: torch.Tensor) -> torch.Tensor:
+    return 1.0 / (1.0 + torch.exp(-t))
+
+
+def pin_softmax_closed_forms(lib) -> None:
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
+        # a constant row gives 1/H everywhere (z = 0, exp = 1, sum = H)
+        for h in (1, 3, 7, 100, 1000, 4096):
+            for c in (0.0, -2.5, 7.0, 1024.0, -60000.0):
+                x = torch.full((2, h), c).to(dt)
+                want = torch.full((2, h), 1.0 / h, dtype=torch.float64).to(torch.float32).to(dt)
+                check_bitexact(oracle.softmax(x, lib=lib), want)
+        # two entries: the logistic function of their difference
+        a = torch.linspace(-6, 6, 49).to(dt).float()
+        b = torch.linspace(3, -3, 49).to(dt).float()
+        x = torch.stack([a, b], dim=1).to(dt).contiguous()
+        y = oracle.softmax(x, lib=lib)
+        d = (a - b).double()       # exact here: both are multiples of 1/8 within +-9
+        want = torch.stack([_sigmoid64(d), _sigmoid64(-d)], dim=1).to(torch.float32).to(dt)
+        assert int(ulp_distance(y, want).max()) <= 1
+        # logits far beyond exp's range: only differences matter, so the result
+        # equals that of the shifted row exactly (the shifts are exact here)
+        big = torch.tensor([[1024.0, 1016.0, 1008.0, 0.0], [0.0, -1024.0, -2048.0, -4096.0]]).to(dt)
+        small = torch.tensor([[0.0, -8.0, -16.0, -1024.0], [0.0, -1024.0, -2048.0, -4096.0]]).to(dt)
+        yb = oracle.softmax(big, lib=lib)
+        check_bitexact(yb, oracle.softmax(small, lib=lib))
+        assert bool(torch.isfinite(yb.float()).all()) and float(yb[1, 0]) == 1.0 and bool((yb[1, 1:] == 0).all())
+        # shift invariance, bit for bit: values on a 1/2 grid below 64 in magnitude
+        # (7 significant bits, so exact in every dtype, and so is every z)
+        g = (torch.randint(-16, 16, (8, 33), generator=torch.Generator().manual_seed(5)).double() / 2)
+        check_bitexact(oracle.softmax((g + 32).to(dt), lib=lib), oracle.softmax(g.to(dt), lib=lib))
+
+
+def pin_softmax_invariants(lib) -> None:
+    for dt, tol in ((torch.float32, 2.0**-23), (torch.float16, 2.0**-10), (torch.bfloat16, 2.0**-7)):
+        x = workloads.random_case((64, 300), {torch.float32: "float32", torch.float16: "float16",
+                                              torch.bfloat16: "bfloat16"}[dt], 410,
+                                  x=workloads.normal(0, 4))["x"]
+        y = oracle.softmax(x, lib=lib)
+        yd = y.double()
+        # each output is within half an ulp of an exact quotient: the row sums to 1
+        # within about half an ulp of 1 in total
+        assert float((yd.sum(-1) - 1).abs().max()) <= tol, float((yd.sum(-1) - 1).abs().max())
+        # order preserving: larger logits never get smaller probabilities
+        xs, order = x.float().sort(dim=-1)
+        ys = torch.gather(yd, 1, order)
+        assert bool((ys[:, 1:] >= ys[:, :-1]).all())
+        # reversing a row reverses its output
+        yr = oracle.softmax(x.flip(-1).contiguous(), lib=lib)
+        assert int(ulp_distance(yr.flip(-1), y).max()) <= 1
+        assert float((ulp_distance(yr.flip(-1), y) == 0).double().mean()) >= 0.99
+
+
+def pin_softmax_nonfinite(lib) -> None:
+    """The page's rules: NaN or +inf anywhere, or only -inf: NaN everywhere in
+    the row; -inf entries of a row with finite values: 0, the rest as if they
+    were absent.  A single element: 1 when finite."""
+    for dt in (torch.bfloat16, torch.float16, torch.float32):
+        rows = torch.tensor([[1.0, NAN, 2.0, -INF], [INF, 1.0, 2.0, 3.0], [-INF] * 4, [INF, INF, 0.0, -INF],
+                             [NAN] * 4, [-INF, 0.5, -INF, 2.0]]).to(dt)
+        y = oracle.softmax(rows, lib=lib).float()
+        assert bool(torch.isnan(y[:5]).all())
+        assert float(y[5, 0]) == 0.0 and float(y[5, 2]) == 0.0
+        masked = oracle.softmax(torch.tensor([[0.5, 2.0]]).to(dt), lib=lib)
+        check_bitexact(oracle.softmax(rows[5:6].contiguous(), lib=lib)[:, [1, 3]].contiguous(), masked)
+        one = oracle.softmax(torch.tensor([[3.0], [-1e4], [INF], [-INF], [NAN]]).to(dt), lib=lib).float()
+        assert one[0, 0] == 1.0 and one[1, 0] == 1.0 and bool(torch.isnan(one[2:]).all())
+        assert oracle.softmax(torch.zeros(0, 7, dtype=dt), lib=lib).shape == (0, 7)
+
+
+def pin_softmax_library(lib) -> None:
+    """torch.softmax on the widened input (the page's own reference) lands within
+    the output tolerance."""
+    for dtype in ("bfloat16", "float16"):
+        x = workloads.random_case((256, 1024), dtype, 420, x=workloads.normal(0, 2))["x"]
+        ref = torch.softmax(x.float(), dim=-1).to(x.dtype)
+        check_normalised(oracle.softmax(x, lib=lib), ref, min_exact_rate=0.999)
+    x = workloads.random_case((64, 1000), "float32", 421, x=workloads.normal(0, 2))["x"]
+    check_normalised(oracle.softmax(x, lib=lib), torch.softmax(x, dim=-1))
+
+
 ALL_PINS = [
     pin_constant_rows, pin_unit_weight_rms, pin_brute_force, pin_scaling_and_sign, pin_fused_residual,
     pin_batch_invariance, pin_casts, pin_library_formula, pin_unrounded_sum, pin_zeros_and_empty,
     pin_swiglu_brute_force, pin_swiglu_library, pin_swiglu_closed_forms,
+    pin_softmax_brute_force, pin_softmax_closed_forms, pin_softmax_invariants, pin_softmax_nonfinite,
+    pin_softmax_library,
 ]
 
 

@@ -48,6 +48,18 @@ MUTANTS = [
     ("swiglu_no_gate_factor", "float t = g * sigmoid32(g);", "float t = sigmoid32(g);"),
     ("swiglu_up_off_by_one", "float u = load_elem(dtype, x, r * 2 * d + d + j);",
      "float u = load_elem(dtype, x, r * 2 * d + d + (j + 1) % d);"),
+    ("softmax_no_max_shift", "float z = load_elem(dtype, x, base + j) - m;",
+     "float z = load_elem(dtype, x, base + j);"),
+    ("softmax_max_never_updated", "else if (v > m)\n                m = v;", "else if (v < m)\n                m = v;"),
+    ("softmax_z_in_double", "float z = load_elem(dtype, x, base + j) - m;",
+     "double z = (double)load_elem(dtype, x, base + j) - (double)m;"),
+    ("softmax_exp_sign", "e[j] = exp((double)z);", "e[j] = exp(-(double)z);"),
+    ("softmax_divides_by_h", "(float)(e[j] / sum)", "(float)(e[j] / (double)hidden)"),
+    ("softmax_sum_skips_last", "sum += e[j];", "if (j + 1 < hidden)\n                sum += e[j];"),
+    ("softmax_output_shifted", "store_elem(dtype, out, base + j, (float)(e[j] / sum));",
+     "store_elem(dtype, out, base + (j + 1) % hidden, (float)(e[j] / sum));"),
+    ("softmax_quotient_unrounded_to_fp32", "store_elem(dtype, out, base + j, (float)(e[j] / sum));",
+     "store_elem(dtype, out, base + j, (float)(e[j] / sum * (1.0 + 0x1p-30)));"),
 ]
 
 

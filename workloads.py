@@ -1,8 +1,12 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
-RMSNorm workloads (C*) and SwiGLU workloads (S*: 512x8192 -> 512x4096 bf16 as in
+RMSNorm workloads (C*), SwiGLU workloads (S*: 512x8192 -> 512x4096 bf16 as in
 the kernscope SwiGLU baseline, and the 7B-model FFN width 11008 at sequence
-2048 from the Triton Kernels benchmark table).
+2048 from the Triton Kernels benchmark table) and softmax workloads (X*: the
+kernscope softmax measurements at 512 rows of 1024, 128 and 8192 bf16, its
+65536-column fp16 accumulation case, and the RMSNorm headline shape 2048x4096
+as an HBM-bound softmax batch).  The softmax pages state no input
+distribution; N(0, 1) logits are used, as in their usage example.
 
 This module draws random numbers and nothing else: it holds none of the
 normalisation's arithmetic, so both the CPU oracle and the GPU path can take
@@ -90,7 +94,7 @@ class Workload:
         return ", ".join(parts)
 
 
-RMS, FUSED, SWIGLU = "rms_norm", "fused_add_rms_norm", "silu_and_mul"
+RMS, FUSED, SWIGLU, SOFTMAX = "rms_norm", "fused_add_rms_norm", "silu_and_mul", "softmax"
 
 WORKLOADS: dict[str, Workload] = {
     # small case the oracle finishes in milliseconds
@@ -117,6 +121,12 @@ WORKLOADS: dict[str, Workload] = {
     "S1": Workload("S1", (SWIGLU,), "bfloat16", 512, 2 * 4096, normal(0, 1), None, 0.0, 6001, None),
     "S2": Workload("S2", (SWIGLU,), "bfloat16", 2048, 2 * 11008, normal(0, 1), None, 0.0, 6101, None),
     "S3": Workload("S3", (SWIGLU,), "float16", 2048, 2 * 4096, normal(0, 1), None, 0.0, 6201, None),
+    # softmax over the last dimension
+    "X1": Workload("X1", (SOFTMAX,), "bfloat16", 512, 1024, normal(0, 1), None, 0.0, 7001, None),
+    "X2": Workload("X2", (SOFTMAX,), "bfloat16", 512, 128, normal(0, 1), None, 0.0, 7101, None),
+    "X3": Workload("X3", (SOFTMAX,), "bfloat16", 512, 8192, normal(0, 1), None, 0.0, 7201, None),
+    "X4": Workload("X4", (SOFTMAX,), "float16", 8, 65536, normal(0, 1), None, 0.0, 7301, None),
+    "X5": Workload("X5", (SOFTMAX,), "bfloat16", 2048, 4096, normal(0, 1), None, 0.0, 7401, None),
 }
 
 
