@@ -1,4 +1,5 @@
-"""Benchmark: RMSNorm and fused residual-add RMSNorm on one MI355X.
+"""Benchmark: RMSNorm and fused residual-add RMSNorm on one MI355X (the
+default workload), and the SwiGLU (S*) and softmax (X*) workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b]
     python bench.py --sweep-workloads [--out FILE]      # every workload, one table
@@ -28,7 +29,8 @@ Timing:
     that size achieves on this GPU.
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
-writes both, (4 R H + H) elements.
+writes both, (4 R H + H) elements; silu_and_mul reads [R, 2D] and writes
+[R, D]; softmax reads and writes [R, H].
 
 Before any timing the outputs are checked against the CPU oracle (all rows, or
 sampled rows for batches over 2^24 elements); on a mismatch nothing is timed
@@ -68,9 +70,12 @@ MAX_SETS = 1024
 def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
     """Bytes the contract must move.  rms_norm: read x, write out, read the weight
     once; fused: read x and residual, write both, read the weight; silu_and_mul
-    (hidden = input width 2D): read x, write the D-wide output."""
+    (hidden = input width 2D): read x, write the D-wide output; softmax: read x,
+    write out."""
     if op == "silu_and_mul":
         return (rows * hidden + rows * (hidden // 2)) * esize
+    if op == "softmax":
+        return 2 * rows * hidden * esize
     per_row = 2 if op == "rms_norm" else 4
     return (per_row * rows * hidden + hidden) * esize
 
@@ -148,6 +153,13 @@ def parity_gate(wl, inp, ks, oracle_mod) -> dict:
         st = check_normalised(pick(y.cpu()), ref, 0.999)
         out["silu_and_mul"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
         return out
+    if "softmax" in wl.ops:
+        y = ks.softmax(inp["x"].cuda())
+        torch.cuda.synchronize()
+        ref = oracle_mod.softmax(pick(inp["x"]))
+        st = check_normalised(pick(y.cpu()), ref, 0.999)
+        out["softmax"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
+        return out
     w = inp["weight"].cuda()
     if "rms_norm" in wl.ops:
         y = ks.rms_norm(inp["x"].cuda(), w, wl.eps)
@@ -181,7 +193,7 @@ class Rig:
         self.wl, self.ks = wl, ks
         esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
         self.tensor_bytes = wl.rows * wl.hidden * esize
-        footprint = {"rms_norm": 2.0, "fused_add_rms_norm": 2.0, "silu_and_mul": 1.5}   # tensors per copy
+        footprint = {"rms_norm": 2.0, "fused_add_rms_norm": 2.0, "silu_and_mul": 1.5, "softmax": 2.0}
         per_set = int(sum(footprint[op] for op in wl.ops) * self.tensor_bytes)
         # enough copies to pass through more than the last-level cache between
         # two uses of one copy; capped for tiny (launch-bound) batches
@@ -195,6 +207,9 @@ class Rig:
             if "silu_and_mul" in wl.ops:
                 s["sx"] = x0.clone()
                 s["sout"] = torch.empty(wl.rows, wl.hidden // 2, dtype=x0.dtype, device=x0.device)
+            if "softmax" in wl.ops:
+                s["mx"] = x0.clone()
+                s["mout"] = torch.empty_like(x0)
             if "rms_norm" in wl.ops:
                 s["x"] = x0.clone()
                 s["out"] = torch.empty_like(x0)
@@ -213,6 +228,8 @@ class Rig:
             self.ks.rms_norm(s["x"], self.w, self.wl.eps, out=s["out"])
         elif op == "fused_add_rms_norm":
             self.ks.fused_add_rms_norm(s["fx"], s["fr"], self.w, self.wl.eps)
+        elif op == "softmax":
+            self.ks.softmax(s["mx"], out=s["mout"])
         else:
             self.ks.silu_and_mul(s["sx"], out=s["sout"])
 
@@ -244,7 +261,7 @@ class Rig:
     def copy_reference(self, reps: int) -> dict:
         """The runtime's device-to-device copy of one batch-sized tensor per launch."""
         n = self.nsets
-        srcs = [s.get("x", s.get("fx", s.get("sx"))) for s in self.sets]
+        srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx")))) for s in self.sets]
         dsts = [torch.empty_like(t) for t in srcs]
         ms = self.timed_graph(lambda i: dsts[i % n].copy_(srcs[i % n]), n, reps)
         del dsts
@@ -296,6 +313,10 @@ def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
             oracle_mod.rms_norm(inp["x"], inp["weight"], wl.eps)
         if "fused_add_rms_norm" in wl.ops:
             oracle_mod.fused_add_rms_norm(inp["x"], inp["residual"], inp["weight"], wl.eps)
+        if "silu_and_mul" in wl.ops:
+            oracle_mod.silu_and_mul(inp["x"])
+        if "softmax" in wl.ops:
+            oracle_mod.softmax(inp["x"])
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -377,7 +398,7 @@ def kernel_op(name: str) -> str | None:
     """The operation a demangled kernel name belongs to (None for other kernels)."""
     if "ks::" not in name:
         return None
-    for op in ("fused_add_rms_norm", "rms_norm", "silu_and_mul"):
+    for op in ("fused_add_rms_norm", "rms_norm", "silu_and_mul", "softmax"):
         if op in name:
             return op
     return None

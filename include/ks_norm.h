@@ -1,10 +1,11 @@
 /*
- * ks_norm: RMSNorm row normalisation, fused residual-add RMSNorm and the
- * SwiGLU activation for AMD Instinct MI355X (gfx950).  C ABI.
+ * ks_norm: RMSNorm row normalisation, fused residual-add RMSNorm, the SwiGLU
+ * activation and softmax for AMD Instinct MI355X (gfx950).  C ABI.
  *
  * The operations are the ones defined in the kernscope README, section
- * "Numerical contract" (subsections "RMSNorm" and "Fused residual-add
- * RMSNorm"), with the input rules of its "Inputs" section.  The C-ABI
+ * "Numerical contract" (subsections "RMSNorm", "Fused residual-add RMSNorm",
+ * "SwiGLU activation" and "Softmax"), with the input rules of its "Inputs"
+ * section.  The C-ABI
  * convention (a status code from every entry point, device pointers, an
  * explicit stream) follows the kernel-set README ("What it is", last line of
  * the operator table).
@@ -69,7 +70,8 @@ typedef enum {
 typedef enum {
     KS_OP_RMS_NORM = 0,
     KS_OP_FUSED_ADD_RMS_NORM = 1,
-    KS_OP_SILU_AND_MUL = 2
+    KS_OP_SILU_AND_MUL = 2,
+    KS_OP_SOFTMAX = 3
 } ks_op_t;
 
 /* How a launch maps rows onto threads.
@@ -78,7 +80,8 @@ typedef enum {
  *                    row; the row is read once and written once.
  *   KS_PATH_GENERIC  `threads_per_row` threads stride over the row with
  *                    `elems_per_access`-element accesses, in two passes (sum,
- *                    then normalise and store); used for unaligned buffers,
+ *                    then normalise and store; softmax: three, maximum, sum,
+ *                    store); used for unaligned buffers,
  *                    row sizes that are not a multiple of 16 bytes, and rows
  *                    wider than the vector path holds. */
 typedef enum {
@@ -130,8 +133,8 @@ ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight,
                                   ks_dtype_t dtype, hipStream_t stream);
 
 /*
- * The launch plan the two calls above use for this op, dtype, batch and row
- * size.  All vector-path plans sum a row in one canonical order, so the plan
+ * The launch plan the calls of this header use for this op, dtype, batch and
+ * row size.  All vector-path plans sum a row in one canonical order, so the plan
  * may change with `rows` while every row's result stays the same; the path
  * (vector or generic) depends only on dtype, hidden and alignment.
  * `aligned` != 0 means all buffers are 16-byte aligned.  No HIP call.
@@ -180,6 +183,35 @@ ks_status_t ks_silu_and_mul(void *out, const void *x, int64_t rows, int64_t d, k
  * grid-stride one (threads_per_row = block_threads = 256, rows_per_block = 1). */
 ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
                                const ks_plan_t *plan, hipStream_t stream);
+
+/*
+ * Softmax over the last dimension (kernscope README, "Numerical contract" >
+ * "Softmax"; shapes as in its "Inputs" section):
+ *   z = fp32(x[r, :]) - max(fp32(x[r, :])),
+ *   out[r, :] = cast( exp(z) / sum(exp(z)) ),
+ * with fp32 maximum, exponential, sum and quotient.  A row holding a NaN or
+ * +inf, or only -inf, comes out all NaN; -inf entries of any other row come
+ * out 0 (the page's rules, which are what the IEEE arithmetic above gives).
+ * x       [rows, hidden] input, read only (unless out == x).
+ * out     [rows, hidden] output.  It may be exactly x (in place); any other
+ *         overlap is KS_ERROR_OVERLAP.
+ * hidden  1 <= hidden <= 2^24; rows may be 0.  There is no eps.
+ * Arithmetic: exp is the device library's expf for fp32 and the hardware
+ * base-2 exponential for 16-bit dtypes (with a first-order correction of the
+ * argument's rounding for fp16); the row sum follows the canonical fold of
+ * the RMSNorm sum of squares (vector path: the same bits for every plan);
+ * the quotient is exp * (1 / sum) with the reciprocal an IEEE division, plus
+ * one remainder correction for fp32.  Within 1 ulp of the exactly evaluated
+ * contract for 16-bit dtypes and well within rtol = atol = 1e-6 for fp32.
+ * Errors and stream rules as above.
+ */
+ks_status_t ks_softmax(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                       hipStream_t stream);
+
+/* Softmax with an explicit plan (op KS_OP_SOFTMAX); plans with weight_lds
+ * set are rejected. */
+ks_status_t ks_softmax_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                          const ks_plan_t *plan, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *ks_status_string(ks_status_t status);

@@ -1,4 +1,4 @@
-"""RMSNorm, fused residual-add RMSNorm and SwiGLU for MI355X (gfx950).
+"""RMSNorm, fused residual-add RMSNorm, SwiGLU and softmax for MI355X (gfx950).
 
 The computation lives in ``libks_norm.so`` (hand-written HIP kernels behind a
 C ABI, ``include/ks_norm.h``); this package is its thin Python binding.
@@ -23,6 +23,9 @@ from .binding import (  # noqa: F401
     library_path,
     rms_norm,
     silu_and_mul,
+    softmax,
+    ks_softmax,
+    ks_softmax_ex,
 )
 
 __version__ = "0.1.0"

@@ -1,8 +1,8 @@
 """ctypes binding of libks_norm.so: argument marshalling only.
 
 The ``ks_*`` functions mirror the C ABI in ``include/ks_norm.h`` one to one
-(raw device pointers as ints).  ``rms_norm``, ``fused_add_rms_norm`` and
-``silu_and_mul`` are the tensor-level calls with the kernscope API shape
+(raw device pointers as ints).  ``rms_norm``, ``fused_add_rms_norm``,
+``silu_and_mul`` and ``softmax`` are the tensor-level calls with the kernscope API shape
 (README, "API contract" and "Inputs"): they check devices, dtypes, shapes, contiguity and
 ``requires_grad`` (the accelerator kernels are inference-only), then pass the
 tensors' device pointers and torch's current HIP stream to the library.
@@ -20,7 +20,7 @@ DEFAULT_LIB = os.path.join(_PKG, "libks_norm.so")
 
 KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP = range(5)
 KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL = 0, 1, 2
+KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX = 0, 1, 2, 3
 KS_PATH_VECTOR, KS_PATH_GENERIC = 0, 1
 
 
@@ -88,12 +88,15 @@ def lib() -> ctypes.CDLL:
         h.ks_get_plan.argtypes = [i32, i32, i64, i64, i32, ctypes.POINTER(Plan)]
         h.ks_silu_and_mul.argtypes = [vp, vp, i64, i64, i32, vp]
         h.ks_silu_and_mul_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
+        h.ks_softmax.argtypes = [vp, vp, i64, i64, i32, vp]
+        h.ks_softmax_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
         h.ks_last_hip_error.argtypes = []
         h.ks_version.restype = ctypes.c_char_p
         for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
-                     "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex"):
+                     "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
+                     "ks_softmax_ex"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -142,6 +145,14 @@ def ks_silu_and_mul(out: int, x: int, rows: int, d: int, dtype: int, stream: int
 
 def ks_silu_and_mul_ex(out: int, x: int, rows: int, d: int, dtype: int, plan: Plan | None, stream: int) -> int:
     return lib().ks_silu_and_mul_ex(out, x, rows, d, dtype, ctypes.byref(plan) if plan is not None else None, stream)
+
+
+def ks_softmax(out: int, x: int, rows: int, hidden: int, dtype: int, stream: int) -> int:
+    return lib().ks_softmax(out, x, rows, hidden, dtype, stream)
+
+
+def ks_softmax_ex(out: int, x: int, rows: int, hidden: int, dtype: int, plan: Plan | None, stream: int) -> int:
+    return lib().ks_softmax_ex(out, x, rows, hidden, dtype, ctypes.byref(plan) if plan is not None else None, stream)
 
 
 def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True) -> Plan:
@@ -238,9 +249,34 @@ def silu_and_mul(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan
     return out
 
 
+def softmax(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
+    """Softmax over the last dimension (kernscope "Softmax"): returns ``out`` (a new
+    tensor unless given; may be ``x``)."""
+    if x.dtype not in KS_DTYPE:
+        raise TypeError(f"softmax: unsupported dtype {x.dtype}")
+    if x.device.type != "cuda":
+        raise ValueError(f"softmax: tensors must be on a HIP device, got {x.device}")
+    if not x.is_contiguous():
+        raise ValueError("softmax: x must be contiguous")
+    if x.requires_grad:
+        raise ValueError("softmax: inference-only kernel; got a tensor that requires grad")
+    if x.dim() == 0 or x.shape[-1] == 0:
+        raise ValueError("softmax: the last dimension must be nonempty")
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError(f"softmax: out must be a contiguous {x.dtype} tensor of shape {tuple(x.shape)}")
+    with torch.cuda.device(x.device):
+        st = ks_softmax_ex(out.data_ptr(), x.data_ptr(), rows, hidden, KS_DTYPE[x.dtype], plan, _stream(x))
+    _check(st, "ks_softmax")
+    return out
+
+
 def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: bool = True) -> Plan:
     """The plan the library picks for this op, dtype, row size and batch (ks_get_plan).
     For silu_and_mul, ``hidden`` is the output width D."""
     code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM,
-            "silu_and_mul": KS_OP_SILU_AND_MUL}[op]
+            "silu_and_mul": KS_OP_SILU_AND_MUL, "softmax": KS_OP_SOFTMAX}[op]
     return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned)

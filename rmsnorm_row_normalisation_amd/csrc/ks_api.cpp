@@ -1,6 +1,6 @@
 // C ABI of ks_norm: argument validation, overlap checks, the launch policy
 // and the calls into the per-dtype kernel units (RMSNorm, fused residual-add
-// RMSNorm, SwiGLU).  Validation and the policy
+// RMSNorm, SwiGLU, softmax).  Validation and the policy
 // make no HIP call, so they run (and are tested) on machines without a GPU.
 #include <math.h>
 #include <stdint.h>
@@ -118,7 +118,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.rows_per_block = plan.block_threads / (int32_t)tpr;
         plan.load_nt = 1;
         plan.store_nt = 1;
-        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;
+        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;   // softmax: no weight
         return plan;
     }
     plan.path = KS_PATH_GENERIC;
@@ -150,6 +150,8 @@ bool hints_compiled(const ks_plan_t &p)
 // suits the buffers' alignment.
 bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned)
 {
+    if (op == KS_OP_SOFTMAX && p.weight_lds != 0)
+        return false;
     if (op == KS_OP_SILU_AND_MUL) {
         if (p.weight_lds != 0)
             return false;
@@ -191,15 +193,25 @@ ks_status_t launch(ks::Launch &l, ks_dtype_t dtype)
 {
     hipError_t err;
     const bool vec = l.plan.path == KS_PATH_VECTOR;
+    const bool fused = l.op == KS_OP_FUSED_ADD_RMS_NORM;
     switch (dtype) {
     case KS_DTYPE_FLOAT32:
-        err = !vec ? ks::launch_generic_f32(l) : l.fused ? ks::launch_vec_f32_fused(l) : ks::launch_vec_f32_rms(l);
+        err = l.op == KS_OP_SOFTMAX ? ks::launch_softmax_f32(l)
+              : !vec                ? ks::launch_generic_f32(l)
+              : fused               ? ks::launch_vec_f32_fused(l)
+                                    : ks::launch_vec_f32_rms(l);
         break;
     case KS_DTYPE_FLOAT16:
-        err = !vec ? ks::launch_generic_f16(l) : l.fused ? ks::launch_vec_f16_fused(l) : ks::launch_vec_f16_rms(l);
+        err = l.op == KS_OP_SOFTMAX ? ks::launch_softmax_f16(l)
+              : !vec                ? ks::launch_generic_f16(l)
+              : fused               ? ks::launch_vec_f16_fused(l)
+                                    : ks::launch_vec_f16_rms(l);
         break;
     default:
-        err = !vec ? ks::launch_generic_bf16(l) : l.fused ? ks::launch_vec_bf16_fused(l) : ks::launch_vec_bf16_rms(l);
+        err = l.op == KS_OP_SOFTMAX ? ks::launch_softmax_bf16(l)
+              : !vec                ? ks::launch_generic_bf16(l)
+              : fused               ? ks::launch_vec_bf16_fused(l)
+                                    : ks::launch_vec_bf16_rms(l);
         break;
     }
     if (err != hipSuccess) {
@@ -235,7 +247,7 @@ ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t
     if (rows > 0 && (out == nullptr || x == nullptr || weight == nullptr))
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(out) && aligned16(x) && aligned16(weight);
-    ks::Launch l{out, x, nullptr, weight, rows, (int32_t)hidden, eps, false, {}, stream};
+    ks::Launch l{out, x, nullptr, weight, rows, (int32_t)hidden, eps, KS_OP_RMS_NORM, {}, stream};
     st = select_plan(plan, KS_OP_RMS_NORM, dtype, rows, hidden, aligned, &l.plan);
     if (st != KS_SUCCESS || rows == 0)
         return st;
@@ -263,7 +275,7 @@ ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight
     if (rows > 0 && (x == nullptr || residual == nullptr || weight == nullptr))
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(x) && aligned16(residual) && aligned16(weight);
-    ks::Launch l{x, x, residual, weight, rows, (int32_t)hidden, eps, true, {}, stream};
+    ks::Launch l{x, x, residual, weight, rows, (int32_t)hidden, eps, KS_OP_FUSED_ADD_RMS_NORM, {}, stream};
     st = select_plan(plan, KS_OP_FUSED_ADD_RMS_NORM, dtype, rows, hidden, aligned, &l.plan);
     if (st != KS_SUCCESS || rows == 0)
         return st;
@@ -316,12 +328,38 @@ ks_status_t ks_silu_and_mul(void *out, const void *x, int64_t rows, int64_t d, k
     return ks_silu_and_mul_ex(out, x, rows, d, dtype, nullptr, stream);
 }
 
+ks_status_t ks_softmax_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                          const ks_plan_t *plan, hipStream_t stream)
+{
+    if (!valid_dtype(dtype))
+        return KS_ERROR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
+        return KS_ERROR_INVALID_VALUE;
+    if (rows > 0 && (out == nullptr || x == nullptr))
+        return KS_ERROR_INVALID_VALUE;
+    const bool aligned = aligned16(out) && aligned16(x);
+    ks::Launch l{out, x, nullptr, nullptr, rows, (int32_t)hidden, 0.0f, KS_OP_SOFTMAX, {}, stream};
+    ks_status_t st = select_plan(plan, KS_OP_SOFTMAX, dtype, rows, hidden, aligned, &l.plan);
+    if (st != KS_SUCCESS || rows == 0)
+        return st;
+    const int64_t nbytes = rows * hidden * elem_size(dtype);
+    if (out != x && overlaps(out, nbytes, x, nbytes))
+        return KS_ERROR_OVERLAP;
+    return launch(l, dtype);
+}
+
+ks_status_t ks_softmax(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype, hipStream_t stream)
+{
+    return ks_softmax_ex(out, x, rows, hidden, dtype, nullptr, stream);
+}
+
 ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned, ks_plan_t *plan)
 {
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
-        (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL))
+        (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL &&
+         op != KS_OP_SOFTMAX))
         return KS_ERROR_INVALID_VALUE;
     *plan = policy(op, dtype, rows, hidden, aligned != 0);
     return KS_SUCCESS;

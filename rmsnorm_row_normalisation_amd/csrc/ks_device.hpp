@@ -1,10 +1,13 @@
-// Device code for RMSNorm and fused residual-add RMSNorm on gfx950 (CDNA4).
+// Device code for RMSNorm, fused residual-add RMSNorm, the SwiGLU activation
+// and softmax on gfx950 (CDNA4).
 //
 // Operation (kernscope README, "Numerical contract"): per row, widen to fp32,
 // sum of squares in fp32, scale = rsqrt(sum / H + eps), y = (v * scale) *
 // fp32(w), round to the storage dtype.  The fused form first forms the fp32
 // sum s = x + residual, stores cast(s) to residual, and normalises the
-// unrounded s into x.
+// unrounded s into x.  SwiGLU and softmax are described in their own
+// sections below; softmax uses the same two kernel families, with a row
+// maximum before the sum and three passes on the generic path.
 //
 // Two kernel families:
 //   *_vec           a team of kTpr lanes owns a row; each lane keeps kVpt
@@ -55,6 +58,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
 }
 
+// Two-lane vectors for paired conversions.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 // Storage dtype tags (kernel names carry them, e.g. rms_norm_vec<ks::bf16, ...>).
 struct f32 {};
 struct f16 {};
@@ -89,12 +97,13 @@ template <> struct Pack<bf16> {
         unsigned w = v[e >> 1];
         return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     }
-    // round to nearest even (v_cvt_pk_bf16_f32 under the default rounding mode)
+    // round to nearest even; a two-lane conversion becomes one
+    // v_cvt_pk_bf16_f32 (two scalar conversions would need a third
+    // instruction to merge the halves)
     __device__ static __forceinline__ unsigned two(float a, float b)
     {
-        unsigned lo = __builtin_bit_cast(unsigned short, (__bf16)a);
-        unsigned hi = __builtin_bit_cast(unsigned short, (__bf16)b);
-        return lo | (hi << 16);
+        const f32x2 v = {a, b};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
     }
     __device__ static __forceinline__ u32x4 put(const float *f)
     {
@@ -127,12 +136,11 @@ template <> struct Pack<f16> {
         unsigned short h = (unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu));
         return (float)__builtin_bit_cast(_Float16, h);   // exact widening
     }
-    // round to nearest even (v_cvt_f16_f32 under the default rounding mode)
+    // round to nearest even; one v_cvt_pk_f16_f32 for the pair
     __device__ static __forceinline__ unsigned two(float a, float b)
     {
-        unsigned lo = __builtin_bit_cast(unsigned short, (_Float16)as_fp32(a));
-        unsigned hi = __builtin_bit_cast(unsigned short, (_Float16)as_fp32(b));
-        return lo | (hi << 16);
+        const f32x2 v = {as_fp32(a), as_fp32(b)};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
     }
     __device__ static __forceinline__ u32x4 put(const float *f)
     {
@@ -182,30 +190,34 @@ template <> struct Scalar<f16> {
 // between batch sizes without changing any result.  Each step adds two
 // values; fp32 addition is commutative, so partner lanes agree bitwise.
 // ---------------------------------------------------------------------------
-template <int kCtrl> __device__ __forceinline__ float dpp_add(float v)
+// The value of lane ^ kMask, kMask a power of two below 64.
+template <int kMask> __device__ __forceinline__ float xor_partner(float v)
 {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+    if constexpr (kMask == 1)                        // quad_perm [1,0,3,2]
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    else if constexpr (kMask == 2)                   // quad_perm [2,3,0,1]
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    else if constexpr (kMask <= 16)                  // ds_swizzle bit mode: lane ^ kMask within 32 lanes
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (kMask << 10)));
+    else
+        return __shfl_xor(v, kMask, 64);
 }
 
-// v + (v of lane ^ kMask), kMask a power of two below 64.
-template <int kMask> __device__ __forceinline__ float xor_add(float v)
-{
-    if constexpr (kMask == 1)
-        return dpp_add<0xB1>(v);                     // quad_perm [1,0,3,2]
-    else if constexpr (kMask == 2)
-        return dpp_add<0x4E>(v);                     // quad_perm [2,3,0,1]
-    else if constexpr (kMask <= 16)                  // ds_swizzle bit mode: lane ^ kMask within 32 lanes
-        return v + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (kMask << 10)));
-    else
-        return v + __shfl_xor(v, kMask, 64);
-}
+// Reduction operators.  Max is exact, so its order never matters; the sum's
+// order is the canonical fold described above.
+struct SumOp {
+    __device__ static __forceinline__ float apply(float a, float b) { return a + b; }
+};
+struct MaxOp {
+    __device__ static __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
+};
 
 // Butterfly over aligned groups of kWidth lanes, masks kWidth/2 down to 1.
-template <int kWidth> __device__ __forceinline__ float butterfly(float v)
+template <int kWidth, typename Op = SumOp> __device__ __forceinline__ float butterfly(float v)
 {
     if constexpr (kWidth >= 2) {
-        v = xor_add<kWidth / 2>(v);
-        v = butterfly<kWidth / 2>(v);
+        v = Op::apply(v, xor_partner<kWidth / 2>(v));
+        v = butterfly<kWidth / 2, Op>(v);
     }
     return v;
 }
@@ -227,10 +239,12 @@ template <int kSlots> __device__ __forceinline__ float local_fold(float *part)
 
 // Finish the canonical fold across a team of kTpr lanes (kTpr a power of two)
 // in a block of kBlock threads.  Every thread of the block must call this.
-template <int kTpr, int kBlock> __device__ __forceinline__ float team_fold(float v)
+// Each operator has its own LDS slots, so a kernel may reduce once per
+// operator without a barrier in between.
+template <int kTpr, int kBlock, typename Op = SumOp> __device__ __forceinline__ float team_fold(float v)
 {
     if constexpr (kTpr <= 64) {
-        return butterfly<kTpr>(v);
+        return butterfly<kTpr, Op>(v);
     } else {
         constexpr int kWaves = kTpr / 64;            // waves per row
         __shared__ float lanes[kBlock];
@@ -246,8 +260,8 @@ template <int kTpr, int kBlock> __device__ __forceinline__ float team_fold(float
         for (int n = kWaves; n > 1; n /= 2)
 #pragma unroll
             for (int j = 0; j < n / 2; ++j)
-                a[j] = a[j] + a[j + n / 2];
-        return butterfly<64>(a[0]);
+                a[j] = Op::apply(a[j], a[j + n / 2]);
+        return butterfly<64, Op>(a[0]);
     }
 }
 
@@ -589,6 +603,185 @@ __device__ __forceinline__ void swiglu_generic_body(const SwigluParams &p)
 }
 
 // ---------------------------------------------------------------------------
+// Softmax over the last dimension: z = x - max(x) over the row (fp32), out =
+// exp(z) / sum(exp(z)), rounded once to the storage dtype.  The maximum is
+// exact in any order; the sum follows the same canonical fold as the sum of
+// squares above, so every vector plan gives the same bits.  A NaN or +inf
+// anywhere in a row, or a row of only -inf, makes some z NaN and with it the
+// sum and every output of that row; -inf entries of other rows give exp = 0.
+// ---------------------------------------------------------------------------
+
+// exp(z) for z <= 0, -inf or NaN.
+//   fp32 outputs: the device library's expf (about 1 ulp).
+//   fp16 outputs: the hardware base-2 exponential of z * log2(e) with the
+//     product's rounding error carried to first order (as in sigmoid_fast):
+//     within about 2 fp32 ulps.  z is clamped at -150, where the result is
+//     0 anyway, so that -inf does not turn the correction into NaN.
+//   bf16 outputs: the hardware exponential of the rounded product.  Its
+//     relative error |z| * 2^-24 stays far below half a bf16 ulp (2^-9) for
+//     every z whose result is not negligible next to the row's maximum (1).
+template <typename T> __device__ __forceinline__ float softmax_exp(float z)
+{
+    constexpr float kLog2e = 1.44269502f;       // fp32 nearest to log2(e)
+    constexpr float kLog2eTail = 1.925963e-8f;  // log2(e) - kLog2e
+    constexpr float kLn2 = 0.693147182f;
+    if constexpr (Pack<T>::kBytes == 4) {
+        return expf(z);
+    } else if constexpr (__is_same(T, bf16)) {
+        return __builtin_amdgcn_exp2f(z * kLog2e);
+    } else {
+        const float x = z < -150.0f ? -150.0f : z;   // NaN passes through
+        const float hi = x * kLog2e;
+        const float lo = __builtin_fmaf(x, kLog2eTail, __builtin_fmaf(x, kLog2e, -hi));
+        const float e2 = __builtin_amdgcn_exp2f(hi);
+        return __builtin_fmaf(e2, lo * kLn2, e2);
+    }
+}
+
+// e / sum with r = 1 / sum (IEEE division, once per row).  fp32 outputs add
+// one remainder correction (q + (e - q sum) r), which brings the product
+// e * r to within about half an ulp of the quotient; for 16-bit outputs the
+// product alone is far inside the output's rounding.
+template <typename T> __device__ __forceinline__ float softmax_div(float e, float sum, float r)
+{
+    const float q = e * r;
+    if constexpr (Pack<T>::kBytes == 4)
+        return __builtin_fmaf(__builtin_fmaf(-q, sum, e), r, q);
+    else
+        return q;
+}
+
+// Vector kernel: a team of kTpr lanes owns a row held in VGPRs (pieces
+// lane + k * kTpr), read once from HBM and written once.
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>
+__device__ __forceinline__ void softmax_vec_body(const Params &p)
+{
+    constexpr int kE = Pack<T>::kElems;
+    constexpr int kRpb = kBlock / kTpr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;
+    const int team = tid / kTpr;
+    const int64_t row0 = (int64_t)blockIdx.x * kRpb;
+    const int64_t left = p.rows - row0;
+    const uint32_t nrows = left < kRpb ? (uint32_t)left : (uint32_t)kRpb;
+    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)Pack<T>::kBytes;
+    const uint32_t blk_bytes = nrows * row_bytes;
+    const size_t base = (size_t)row0 * row_bytes;
+    const auto rx = make_rsrc((const char *)p.x + base, blk_bytes);
+    const auto ry = make_rsrc((char *)p.y + base, blk_bytes);
+
+    uint32_t off[kVpt];
+    bool in_row[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        const uint32_t c = (uint32_t)(k * kTpr + lane) * 16u;
+        in_row[k] = c < row_bytes;
+        off[k] = in_row[k] ? (uint32_t)team * row_bytes + c : kOutOfRange;
+    }
+    u32x4 xv[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kLoadCpol);
+
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float pm = Pack<T>::get(xv[k], 0);
+#pragma unroll
+        for (int e = 1; e < kE; ++e)
+            pm = fmaxf(pm, Pack<T>::get(xv[k], e));
+        mx = in_row[k] ? fmaxf(mx, pm) : mx;   // pieces past the row read as zeros
+    }
+    const float m = team_fold<kTpr, kBlock, MaxOp>(mx);
+
+    float ev[kVpt][kE];
+    float part[kVpt];   // per-piece sums, elements in index order
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            ev[k][e] = softmax_exp<T>(Pack<T>::get(xv[k], e) - m);
+            a = a + ev[k][e];
+        }
+        part[k] = in_row[k] ? a : 0.0f;
+    }
+    const float sum = team_fold<kTpr, kBlock>(local_fold<kVpt>(part));
+    const float r = 1.0f / sum;
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float o[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            o[e] = softmax_div<T>(ev[k][e], sum, r);
+        __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kStoreCpol);
+    }
+}
+
+// Generic kernel: three passes over the row (maximum, sum, store), kEpa
+// elements per access as in generic_body.  Each lane reads and writes the
+// same elements in the last pass, after the whole team has finished the
+// first two, so out may be x.
+template <typename T, int kTpr, int kEpa, int kBlock>
+__device__ __forceinline__ void softmax_generic_body(const Params &p)
+{
+    constexpr int kRpb = kBlock / kTpr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;
+    const int team = tid / kTpr;
+    const int64_t row = (int64_t)blockIdx.x * kRpb + team;
+    const bool active = row < p.rows;   // no early return before the reductions
+    const int64_t H = p.hidden;
+    const int64_t base = active ? row * H : 0;
+    constexpr int64_t kStride = (int64_t)kTpr * kEpa;
+
+    float mx = -__builtin_inff();
+    if (active) {
+        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+            if constexpr (kEpa == 1) {
+                mx = fmaxf(mx, Scalar<T>::get(p.x, base + j));
+            } else {
+                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e)
+                    mx = fmaxf(mx, Pack<T>::get(xv, e));
+            }
+        }
+    }
+    const float m = team_fold<kTpr, kBlock, MaxOp>(mx);
+    float s = 0.0f;
+    if (active) {
+        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+            if constexpr (kEpa == 1) {
+                s = s + softmax_exp<T>(Scalar<T>::get(p.x, base + j) - m);
+            } else {
+                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e)
+                    s = s + softmax_exp<T>(Pack<T>::get(xv, e) - m);
+            }
+        }
+    }
+    const float sum = team_sum<kTpr, kBlock>(s);
+    if (!active)
+        return;
+    const float r = 1.0f / sum;
+    for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+        if constexpr (kEpa == 1) {
+            const float e = softmax_exp<T>(Scalar<T>::get(p.x, base + j) - m);
+            Scalar<T>::put(p.y, base + j, softmax_div<T>(e, sum, r));
+        } else {
+            const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+            float o[kEpa];
+#pragma unroll
+            for (int e = 0; e < kEpa; ++e)
+                o[e] = softmax_div<T>(softmax_exp<T>(Pack<T>::get(xv, e) - m), sum, r);
+            *(u32x4 *)((char *)p.y + (base + j) * Pack<T>::kBytes) = Pack<T>::put(o);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel entry points, one name per operation and path.
 // ---------------------------------------------------------------------------
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
@@ -625,6 +818,18 @@ template <typename T>
 __global__ __launch_bounds__(256) void silu_and_mul_generic(SwigluParams p)
 {
     swiglu_generic_body<T>(p);
+}
+
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>
+__global__ __launch_bounds__(kBlock) void softmax_vec(Params p)
+{
+    softmax_vec_body<T, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol>(p);
+}
+
+template <typename T, int kTpr, int kEpa, int kBlock>
+__global__ __launch_bounds__(kBlock) void softmax_generic(Params p)
+{
+    softmax_generic_body<T, kTpr, kEpa, kBlock>(p);
 }
 
 }  // namespace ks

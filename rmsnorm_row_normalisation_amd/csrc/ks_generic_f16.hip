@@ -5,7 +5,8 @@ namespace ks {
 
 hipError_t launch_generic_f16(const Launch &l)
 {
-    return l.fused ? launch_generic_typed<f16, true>(l) : launch_generic_typed<f16, false>(l);
+    return l.op == KS_OP_FUSED_ADD_RMS_NORM ? launch_generic_typed<f16, KS_OP_FUSED_ADD_RMS_NORM>(l)
+                                           : launch_generic_typed<f16, KS_OP_RMS_NORM>(l);
 }
 
 }  // namespace ks

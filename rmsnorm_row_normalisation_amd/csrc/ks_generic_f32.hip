@@ -5,7 +5,8 @@ namespace ks {
 
 hipError_t launch_generic_f32(const Launch &l)
 {
-    return l.fused ? launch_generic_typed<f32, true>(l) : launch_generic_typed<f32, false>(l);
+    return l.op == KS_OP_FUSED_ADD_RMS_NORM ? launch_generic_typed<f32, KS_OP_FUSED_ADD_RMS_NORM>(l)
+                                           : launch_generic_typed<f32, KS_OP_RMS_NORM>(l);
 }
 
 }  // namespace ks

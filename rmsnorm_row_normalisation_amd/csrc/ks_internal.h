@@ -9,7 +9,8 @@
 
 namespace ks {
 
-// Everything one launch needs.  `plan` has been validated against the
+// Everything one launch of a row operation needs (softmax uses y = out and
+// x only).  `plan` has been validated against the
 // buffers (see plan_fits in ks_api.cpp) before a launch function sees it.
 struct Launch {
     void *y;
@@ -19,7 +20,7 @@ struct Launch {
     int64_t rows;
     int32_t hidden;
     float eps;
-    bool fused;
+    ks_op_t op;         // KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM or KS_OP_SOFTMAX
     ks_plan_t plan;
     hipStream_t stream;
 };
@@ -52,6 +53,9 @@ KS_DECLARE_LAUNCH(bf16)
 hipError_t launch_swiglu_f32(const SwigluLaunch &l);
 hipError_t launch_swiglu_f16(const SwigluLaunch &l);
 hipError_t launch_swiglu_bf16(const SwigluLaunch &l);
+hipError_t launch_softmax_f32(const Launch &l);
+hipError_t launch_softmax_f16(const Launch &l);
+hipError_t launch_softmax_bf16(const Launch &l);
 
 // The one generic SwiGLU plan: a grid-stride loop over elements.
 constexpr int kSwigluGenericBlock = 256;

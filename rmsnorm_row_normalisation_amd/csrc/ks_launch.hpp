@@ -19,101 +19,108 @@ hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
     return hipGetLastError();
 }
 
-// The kernel entry point of one op.
-template <bool F, typename T, int TPR, int V, int B, int LC, int SC, bool WL>
+// The kernel entry point of one op (OP is a ks_op_t: RMSNorm, fused or softmax).
+template <int OP, typename T, int TPR, int V, int B, int LC, int SC, bool WL>
 constexpr auto vec_entry()
 {
-    if constexpr (F)
+    if constexpr (OP == KS_OP_FUSED_ADD_RMS_NORM)
         return fused_add_rms_norm_vec<T, TPR, V, B, LC, SC, WL>;
+    else if constexpr (OP == KS_OP_SOFTMAX)
+        return softmax_vec<T, TPR, V, B, LC, SC>;
     else
         return rms_norm_vec<T, TPR, V, B, LC, SC, WL>;
 }
 
-template <bool F, typename T, int TPR, int EPA, int B>
+template <int OP, typename T, int TPR, int EPA, int B>
 constexpr auto generic_entry()
 {
-    if constexpr (F)
+    if constexpr (OP == KS_OP_FUSED_ADD_RMS_NORM)
         return fused_add_rms_norm_generic<T, TPR, EPA, B>;
+    else if constexpr (OP == KS_OP_SOFTMAX)
+        return softmax_generic<T, TPR, EPA, B>;
     else
         return rms_norm_generic<T, TPR, EPA, B>;
 }
 
-// The compiled memory-hint variants of one launch shape.
-template <typename T, bool F, int TPR, int V>
+// The compiled memory-hint variants of one launch shape (softmax has no
+// weight, so no LDS-staged variant).
+template <typename T, int OP, int TPR, int V>
 hipError_t vec_one(const Launch &l)
 {
     constexpr int B = TPR < 256 ? 256 : TPR;
     constexpr int NT = kNonTemporal;
     const ks_plan_t &p = l.plan;
     if (!p.load_nt && !p.store_nt && !p.weight_lds)
-        return run(vec_entry<F, T, TPR, V, B, 0, 0, false>(), l, B);
+        return run(vec_entry<OP, T, TPR, V, B, 0, 0, false>(), l, B);
     if (p.load_nt && p.store_nt && !p.weight_lds)
-        return run(vec_entry<F, T, TPR, V, B, NT, NT, false>(), l, B);
+        return run(vec_entry<OP, T, TPR, V, B, NT, NT, false>(), l, B);
     if (!p.load_nt && p.store_nt && !p.weight_lds)
-        return run(vec_entry<F, T, TPR, V, B, 0, NT, false>(), l, B);
-    if (p.load_nt && p.store_nt && p.weight_lds)
-        return run(vec_entry<F, T, TPR, V, B, NT, NT, true>(), l, B, (size_t)V * TPR * 16);
+        return run(vec_entry<OP, T, TPR, V, B, 0, NT, false>(), l, B);
+    if constexpr (OP != KS_OP_SOFTMAX) {
+        if (p.load_nt && p.store_nt && p.weight_lds)
+            return run(vec_entry<OP, T, TPR, V, B, NT, NT, true>(), l, B, (size_t)V * TPR * 16);
+    }
     return hipErrorInvalidValue;
 }
 
-template <typename T, bool F, int TPR>
+template <typename T, int OP, int TPR>
 hipError_t vec_by_vpt(const Launch &l)
 {
     switch (l.plan.vectors_per_thread) {
-    case 1: return vec_one<T, F, TPR, 1>(l);
-    case 2: return vec_one<T, F, TPR, 2>(l);
-    case 3: return vec_one<T, F, TPR, 3>(l);
-    case 4: return vec_one<T, F, TPR, 4>(l);
+    case 1: return vec_one<T, OP, TPR, 1>(l);
+    case 2: return vec_one<T, OP, TPR, 2>(l);
+    case 3: return vec_one<T, OP, TPR, 3>(l);
+    case 4: return vec_one<T, OP, TPR, 4>(l);
     default: break;
     }
     if constexpr (TPR < kMaxTpr) {
         switch (l.plan.vectors_per_thread) {
-        case 5: return vec_one<T, F, TPR, 5>(l);
-        case 6: return vec_one<T, F, TPR, 6>(l);
-        case 7: return vec_one<T, F, TPR, 7>(l);
-        case 8: return vec_one<T, F, TPR, 8>(l);
+        case 5: return vec_one<T, OP, TPR, 5>(l);
+        case 6: return vec_one<T, OP, TPR, 6>(l);
+        case 7: return vec_one<T, OP, TPR, 7>(l);
+        case 8: return vec_one<T, OP, TPR, 8>(l);
         default: break;
         }
     }
     return hipErrorInvalidValue;
 }
 
-template <typename T, bool F>
+template <typename T, int OP>
 hipError_t vec_by_tpr(const Launch &l)
 {
     switch (l.plan.threads_per_row) {
-    case 8: return vec_by_vpt<T, F, 8>(l);
-    case 16: return vec_by_vpt<T, F, 16>(l);
-    case 32: return vec_by_vpt<T, F, 32>(l);
-    case 64: return vec_by_vpt<T, F, 64>(l);
-    case 128: return vec_by_vpt<T, F, 128>(l);
-    case 256: return vec_by_vpt<T, F, 256>(l);
-    case 512: return vec_by_vpt<T, F, 512>(l);
-    case 1024: return vec_by_vpt<T, F, 1024>(l);
+    case 8: return vec_by_vpt<T, OP, 8>(l);
+    case 16: return vec_by_vpt<T, OP, 16>(l);
+    case 32: return vec_by_vpt<T, OP, 32>(l);
+    case 64: return vec_by_vpt<T, OP, 64>(l);
+    case 128: return vec_by_vpt<T, OP, 128>(l);
+    case 256: return vec_by_vpt<T, OP, 256>(l);
+    case 512: return vec_by_vpt<T, OP, 512>(l);
+    case 1024: return vec_by_vpt<T, OP, 1024>(l);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, bool F, int EPA>
+template <typename T, int OP, int EPA>
 hipError_t generic_by_tpr(const Launch &l)
 {
     switch (l.plan.threads_per_row) {
-    case 8: return run(generic_entry<F, T, 8, EPA, 256>(), l, 256);
-    case 64: return run(generic_entry<F, T, 64, EPA, 256>(), l, 256);
-    case 256: return run(generic_entry<F, T, 256, EPA, 256>(), l, 256);
-    case 1024: return run(generic_entry<F, T, 1024, EPA, 1024>(), l, 1024);
+    case 8: return run(generic_entry<OP, T, 8, EPA, 256>(), l, 256);
+    case 64: return run(generic_entry<OP, T, 64, EPA, 256>(), l, 256);
+    case 256: return run(generic_entry<OP, T, 256, EPA, 256>(), l, 256);
+    case 1024: return run(generic_entry<OP, T, 1024, EPA, 1024>(), l, 1024);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, bool F>
+template <typename T, int OP>
 hipError_t launch_generic_typed(const Launch &l)
 {
     constexpr int kVecElems = Pack<T>::kElems;
     if (l.plan.elems_per_access == 1)
-        return generic_by_tpr<T, F, 1>(l);
+        return generic_by_tpr<T, OP, 1>(l);
     if (l.plan.elems_per_access == kVecElems)
-        return generic_by_tpr<T, F, kVecElems>(l);
+        return generic_by_tpr<T, OP, kVecElems>(l);
     return hipErrorInvalidValue;
 }
 

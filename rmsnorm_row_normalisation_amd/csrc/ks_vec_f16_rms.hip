@@ -3,6 +3,6 @@
 
 namespace ks {
 
-hipError_t launch_vec_f16_rms(const Launch &l) { return vec_by_tpr<f16, false>(l); }
+hipError_t launch_vec_f16_rms(const Launch &l) { return vec_by_tpr<f16, KS_OP_RMS_NORM>(l); }
 
 }  // namespace ks

@@ -3,6 +3,6 @@
 
 namespace ks {
 
-hipError_t launch_vec_f32_rms(const Launch &l) { return vec_by_tpr<f32, false>(l); }
+hipError_t launch_vec_f32_rms(const Launch &l) { return vec_by_tpr<f32, KS_OP_RMS_NORM>(l); }
 
 }  // namespace ks

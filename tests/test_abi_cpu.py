@@ -353,3 +353,56 @@ def test_silu_tensor_api_checks():
         ks.silu_and_mul(x)                                      # not on a HIP device
     with pytest.raises(TypeError):
         ks.silu_and_mul(x.to(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# Softmax entry points (kernscope "Inputs": nonempty last dimension, empty
+# batches allowed, a new output; the C ABI also allows out == x exactly)
+# ---------------------------------------------------------------------------
+def smax(out, x, rows, hidden, dtype=BF16, plan=None):
+    return b.ks_softmax_ex(out, x, rows, hidden, dtype, plan, 0)
+
+
+def test_softmax_statuses():
+    x, out = A, A + 256 * MB
+    assert smax(out, x, 4, 1024, dtype=9) == DTYPE
+    assert smax(out, x, -1, 1024) == INVALID
+    assert smax(out, x, 4, 0) == INVALID
+    assert smax(out, x, 4, 2**24 + 1) == INVALID
+    assert smax(None, x, 4, 1024) == INVALID
+    assert smax(out, None, 4, 1024) == INVALID
+    assert smax(None, None, 0, 1024) == OK                 # empty batch: no HIP call
+    assert smax(x + 2, x, 4, 1024) == OVERLAP              # partial overlap
+    assert smax(x - 2048, x, 4, 1024) == OVERLAP
+    assert b.ks_softmax(None, None, 0, 1, BF16, 0) == OK
+
+
+def test_softmax_plans_and_policy():
+    x, out = A, A + 256 * MB
+    for dtype, code, es in ((torch.float32, F32, 4), (torch.float16, F16, 2), (torch.bfloat16, BF16, 2)):
+        for hidden in (1, 5, 8, 128, 1000, 1023, 1024, 4096, 8192, 16384, 32768, 65536, 2**24):
+            for rows in (1, 512, 8192):
+                for aligned in (True, False):
+                    p = ks.get_plan("softmax", dtype, hidden, rows, aligned).as_dict()
+                    assert p["weight_lds"] == 0
+                    if p["path"] == 0:
+                        assert aligned and (hidden * es) % 16 == 0 and hidden * es <= 65536
+                        assert (p["load_nt"], p["store_nt"]) == (1, 1)
+                    base = A if aligned else A + 2
+                    assert smax(base + 256 * MB, base, 0, hidden, dtype=code, plan=b.Plan.from_dict(p)) == OK
+    p = ks.get_plan("softmax", torch.bfloat16, 1024, 512).as_dict()
+    assert smax(out, x, 0, 1024, plan=b.Plan.from_dict({**p, "weight_lds": 1})) == INVALID
+    assert smax(out + 2, x, 4, 1024, plan=b.Plan.from_dict(p)) == INVALID     # unaligned: no vector plan
+    # the vector plan is the normalisation's: same team and pieces per lane
+    for hidden, rows in ((1024, 512), (128, 512), (8192, 512), (4096, 2048)):
+        q = ks.get_plan("rms_norm", torch.bfloat16, hidden, rows).as_dict()
+        p = ks.get_plan("softmax", torch.bfloat16, hidden, rows).as_dict()
+        assert (p["threads_per_row"], p["vectors_per_thread"]) == (q["threads_per_row"], q["vectors_per_thread"])
+
+
+def test_softmax_tensor_api_checks():
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ks.softmax(x)                                           # not on a HIP device
+    with pytest.raises(TypeError):
+        ks.softmax(x.to(torch.int32))
