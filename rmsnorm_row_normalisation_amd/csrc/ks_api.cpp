@@ -68,6 +68,11 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // combination for hidden 1024..16384 and 1..32768 rows (bf16).
 // Rows wider than 64 KiB, or unaligned buffers, take the generic path.
 //
+// Softmax keeps every element of its piece in registers as an fp32
+// exponential between the two reductions, so it takes at most 4 pieces per
+// lane, and 2 from 4M pieces (fitted to timings for hidden 128..16384 and
+// 1..8192 rows, bf16).
+//
 // SwiGLU (pieces are 16-byte pieces of the output row, each reading two input
 // pieces) has no reduction and about three times the arithmetic per byte, so
 // it wants more, shorter lanes: at most 2 pieces per lane, and a 1024-lane
@@ -99,7 +104,11 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     if (aligned && row_bytes % 16 == 0 && nvec <= (int64_t)kPolicyMaxTpr * ks::kMaxVpt) {
         const int64_t pieces = rows * nvec;
         const bool swiglu = op == KS_OP_SILU_AND_MUL;
-        const int64_t max_vpt = swiglu ? kSwigluMaxVpt : pieces >= kLargeBatchPieces ? 4 : ks::kMaxVpt;
+        const bool large = pieces >= kLargeBatchPieces;
+        const int64_t max_vpt = swiglu                  ? kSwigluMaxVpt
+                                : op == KS_OP_SOFTMAX ? (large ? 2 : 4)
+                                : large                 ? 4
+                                                        : ks::kMaxVpt;
         int64_t vpt = pow2_ceil((pieces + kTargetLanes - 1) / kTargetLanes);
         vpt = vpt < 1 ? 1 : vpt > max_vpt ? max_vpt : vpt;
         int64_t tpr = pow2_ceil((nvec + vpt - 1) / vpt);
