@@ -1,11 +1,13 @@
-"""CPU oracle for RMSNorm, fused residual-add RMSNorm, SwiGLU and softmax.
+"""CPU oracle for RMSNorm, fused residual-add RMSNorm (in place and out of
+place), SwiGLU and softmax.
 
 TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package; the GPU product path
 never does, and the two share no code.
 
 ``ks_oracle.c`` holds all arithmetic (kernscope README, "Numerical contract":
-"RMSNorm", "Fused residual-add RMSNorm", "SwiGLU activation" and "Softmax").  This module
+"RMSNorm", "Fused residual-add RMSNorm", "SwiGLU activation" and "Softmax";
+Triton Kernels README, "Kernels": the out-of-place residual-fused RMSNorm).  This module
 only builds and loads that library and marshals torch CPU tensors (used as
 plain byte containers) to it.  ``brute64`` is a second, independent fp64 / exact-rational
 check for tiny inputs.
@@ -49,6 +51,8 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_silu_and_mul.argtypes = [c_int, vp, vp, i64, i64]
     lib.oracle_silu_and_mul.restype = c_int
     lib.oracle_softmax.argtypes = [c_int, vp, vp, i64, i64]
+    lib.oracle_rms_norm_residual.argtypes = [c_int, vp, vp, vp, vp, i64, i64, c_float]
+    lib.oracle_rms_norm_residual.restype = c_int
     lib.oracle_softmax.restype = c_int
     return lib
 
@@ -105,6 +109,21 @@ def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor,
     if st != 0:
         raise ValueError(f"oracle_fused_add_rms_norm failed with status {st}")
     return xo, ro
+
+
+def rms_norm_residual(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                      lib: ctypes.CDLL | None = None) -> torch.Tensor:
+    """Out of place: a new tensor RMSNorm(x + residual) * w; the inputs are unchanged."""
+    lib = lib or load()
+    rows, hidden = _check_rows(x, w)
+    if residual.shape != x.shape or residual.dtype != x.dtype or not residual.is_contiguous():
+        raise ValueError("residual must match x")
+    out = torch.empty_like(x)
+    st = lib.oracle_rms_norm_residual(_DTYPE_CODE[x.dtype], x.data_ptr(), residual.data_ptr(), w.data_ptr(),
+                                      out.data_ptr(), rows, hidden, eps)
+    if st != 0:
+        raise ValueError(f"oracle_rms_norm_residual failed with status {st}")
+    return out
 
 
 def silu_and_mul(x: torch.Tensor, lib: ctypes.CDLL | None = None) -> torch.Tensor:

@@ -75,6 +75,14 @@ def fused_add_rms_norm(x: list[list[float]], r: list[list[float]], w: list[float
     return rms_norm(s, w, eps32, fmt), residual
 
 
+def rms_norm_residual(x: list[list[float]], r: list[list[float]], w: list[float], eps32: float,
+                      fmt: str) -> list[list[float]]:
+    """Out of place: the normalisation of the fp32 sum s = x + r (rounded to fp32,
+    as the fused contract defines s), nothing else written."""
+    s = [[round_to(Fraction(a) + Fraction(b), "float32") for a, b in zip(xr, rr)] for xr, rr in zip(x, r)]
+    return rms_norm(s, w, eps32, fmt)
+
+
 def _sigmoid(g: Fraction) -> Fraction:
     with localcontext() as ctx:
         ctx.prec = 80

@@ -1,6 +1,7 @@
 /*
- * CPU oracle for RMSNorm row normalisation, the fused residual-add variant,
- * the SwiGLU activation and softmax over the last dimension.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU oracle for RMSNorm row normalisation, the fused residual-add variant
+ * (in place, and out of place), the SwiGLU activation and softmax over the
+ * last dimension.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this file's library; the GPU library never
  * does, and the two share no code, headers or constants.
  *
@@ -225,6 +226,39 @@ int oracle_fused_add_rms_norm(int dtype, void *x, void *residual, const void *w,
             float t = s[j] * scale;
             float u = t * load_elem(dtype, w, j);
             store_elem(dtype, x, base + j, u);
+        }
+    }
+    free(s);
+    return ORACLE_OK;
+}
+
+/* Out of place (Triton Kernels README, "Kernels": the residual-fused
+   RMSNorm, RMSNorm(x + residual) * w, with FP32 accumulation as in its
+   RMSNorm row): out <- cast(s * scale(s) * fp32(w)) with s = fp32(x) +
+   fp32(residual); x and residual are only read.  Reading where the page is
+   silent: s is the unrounded fp32 sum, as in the kernscope fused contract,
+   and the normalisation is the kernscope one.  out may equal x or residual:
+   a row's inputs are all read before its first output is written. */
+int oracle_rms_norm_residual(int dtype, const void *x, const void *residual, const void *w,
+                             void *out, int64_t rows, int64_t hidden, float eps)
+{
+    int st = check_args(dtype, rows, hidden, eps);
+    if (st != ORACLE_OK)
+        return st;
+    float *s = (float *)malloc((size_t)hidden * sizeof(float));
+    if (!s)
+        return ORACLE_NO_MEMORY;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t base = r * hidden;
+        double sum_sq = 0.0;
+        for (int64_t j = 0; j < hidden; ++j) {
+            s[j] = load_elem(dtype, x, base + j) + load_elem(dtype, residual, base + j);
+            sum_sq += (double)s[j] * (double)s[j];
+        }
+        float scale = row_scale(sum_sq, hidden, eps);
+        for (int64_t j = 0; j < hidden; ++j) {
+            float t = s[j] * scale;
+            store_elem(dtype, out, base + j, t * load_elem(dtype, w, j));
         }
     }
     free(s);

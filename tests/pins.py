@@ -307,6 +307,40 @@ def pin_zeros_and_empty(lib) -> None:
 
 
 # --------------------------------------------------------------------------
+# Out-of-place residual RMSNorm (Triton Kernels README, "Kernels")
+# --------------------------------------------------------------------------
+def pin_residual_out_of_place(lib) -> None:
+    """Brute force on tiny shapes; x + x is RMSNorm of x with eps / 4 bit for bit
+    (every step scales by a power of two); a zero residual is rms_norm; the
+    inputs are left unchanged; the sum is not rounded before normalising."""
+    for dtype in ("bfloat16", "float16", "float32"):
+        for i, shape in enumerate(BRUTE_SHAPES):
+            inp = workloads.random_case(shape, dtype, 500 + i, residual=workloads.normal(0, 0.7))
+            x, r, w = inp["x"], inp["residual"], inp["weight"]
+            eps32 = float(np.float32(1e-6))
+            want = brute64.rms_norm_residual(_values(x), _values(r), [float(v) for v in w.float()], eps32, dtype)
+            got = oracle.rms_norm_residual(x, r, w, 1e-6, lib=lib)
+            _check_brute(got, _from_values(want, x.dtype, shape), dtype, shape)
+        inp = workloads.random_case((16, 1000), dtype, 510)
+        x, r, w = inp["x"], inp["residual"], inp["weight"]
+        # keep x away from the fp16 subnormal range, where doubling is still exact
+        # but the eps / 4 identity needs every scaled value normal
+        x = (torch.sign(x.float()) * x.float().abs().clamp_min(2.0 ** -6)).to(x.dtype)
+        x0, r0 = x.clone(), r.clone()
+        eps32 = float(np.float32(1e-5))
+        check_bitexact(oracle.rms_norm_residual(x, x, w, eps32, lib=lib), oracle.rms_norm(x, w, eps32 / 4, lib=lib))
+        check_bitexact(oracle.rms_norm_residual(x, torch.zeros_like(x), w, 1e-6, lib=lib),
+                       oracle.rms_norm(x, w, 1e-6, lib=lib))
+        y = oracle.rms_norm_residual(x, r, w, 1e-6, lib=lib)
+        check_bitexact(x, x0)
+        check_bitexact(r, r0)
+        if dtype != "float32":
+            # normalising the rounded sum is a different (<= 1 ulp away) result
+            rounded = oracle.rms_norm((x.float() + r.float()).to(x.dtype), w, 1e-6, lib=lib)
+            assert float((ulp_distance(y, rounded) == 0).double().mean()) < 0.999
+
+
+# --------------------------------------------------------------------------
 # SwiGLU (kernscope "Numerical contract" > "SwiGLU activation")
 # --------------------------------------------------------------------------
 SWIGLU_SHAPES = [(2,), (3, 10), (2, 3, 14), (2, 64), (3, 402)]
@@ -491,7 +525,7 @@ ALL_PINS = [
     pin_batch_invariance, pin_casts, pin_library_formula, pin_unrounded_sum, pin_zeros_and_empty,
     pin_swiglu_brute_force, pin_swiglu_library, pin_swiglu_closed_forms,
     pin_softmax_brute_force, pin_softmax_closed_forms, pin_softmax_invariants, pin_softmax_nonfinite,
-    pin_softmax_library,
+    pin_softmax_library, pin_residual_out_of_place,
 ]
 
 

@@ -48,6 +48,13 @@ MUTANTS = [
     ("swiglu_no_gate_factor", "float t = g * sigmoid32(g);", "float t = sigmoid32(g);"),
     ("swiglu_up_off_by_one", "float u = load_elem(dtype, x, r * 2 * d + d + j);",
      "float u = load_elem(dtype, x, r * 2 * d + d + (j + 1) % d);"),
+    ("residual_oop_subtracts", "s[j] = load_elem(dtype, x, base + j) + load_elem(dtype, residual, base + j);\n            sum_sq += (double)s[j] * (double)s[j];",
+     "s[j] = load_elem(dtype, x, base + j) - load_elem(dtype, residual, base + j);\n            sum_sq += (double)s[j] * (double)s[j];"),
+    ("residual_oop_rounds_sum", "sum_sq += (double)s[j] * (double)s[j];",
+     "store_elem(dtype, out, base + j, s[j]);   /* rounds s to the dtype */\n"
+     "            s[j] = load_elem(dtype, out, base + j);\n            sum_sq += (double)s[j] * (double)s[j];"),
+    ("residual_oop_no_weight", "store_elem(dtype, out, base + j, t * load_elem(dtype, w, j));",
+     "store_elem(dtype, out, base + j, t);"),
     ("softmax_no_max_shift", "float z = load_elem(dtype, x, base + j) - m;",
      "float z = load_elem(dtype, x, base + j);"),
     ("softmax_max_never_updated", "else if (v > m)\n                m = v;", "else if (v < m)\n                m = v;"),
