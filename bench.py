@@ -29,8 +29,9 @@ Timing:
     that size achieves on this GPU.
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
-writes both, (4 R H + H) elements; silu_and_mul reads [R, 2D] and writes
-[R, D]; softmax reads and writes [R, H].
+writes both, (4 R H + H) elements; rms_norm_residual reads x and residual
+and writes out, (3 R H + H); silu_and_mul reads [R, 2D] and writes [R, D];
+softmax reads and writes [R, H].
 
 Before any timing the outputs are checked against the CPU oracle (all rows, or
 sampled rows for batches over 2^24 elements); on a mismatch nothing is timed
@@ -71,12 +72,13 @@ def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
     """Bytes the contract must move.  rms_norm: read x, write out, read the weight
     once; fused: read x and residual, write both, read the weight; silu_and_mul
     (hidden = input width 2D): read x, write the D-wide output; softmax: read x,
-    write out."""
+    write out; rms_norm_residual: read x and residual, write out, read the
+    weight."""
     if op == "silu_and_mul":
         return (rows * hidden + rows * (hidden // 2)) * esize
     if op == "softmax":
         return 2 * rows * hidden * esize
-    per_row = 2 if op == "rms_norm" else 4
+    per_row = {"rms_norm": 2, "rms_norm_residual": 3}.get(op, 4)
     return (per_row * rows * hidden + hidden) * esize
 
 
@@ -169,6 +171,14 @@ def parity_gate(wl, inp, ks, oracle_mod) -> dict:
         st = check_normalised(pick(y.cpu()), ref, 0.999)
         out["rms_norm"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
         del y
+    if "rms_norm_residual" in wl.ops:
+        y = ks.rms_norm_residual(inp["x"].cuda(), inp["residual"].cuda(), w, wl.eps)
+        torch.cuda.synchronize()
+        r = ref_inputs()
+        ref = oracle_mod.rms_norm_residual(r["x"], r["residual"], r["weight"], wl.eps)
+        st = check_normalised(pick(y.cpu()), ref, 0.999)
+        out["rms_norm_residual"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
+        del y
     if "fused_add_rms_norm" in wl.ops:
         xf, rf = inp["x"].cuda(), inp["residual"].cuda()
         ks.fused_add_rms_norm(xf, rf, w, wl.eps)
@@ -193,7 +203,8 @@ class Rig:
         self.wl, self.ks = wl, ks
         esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
         self.tensor_bytes = wl.rows * wl.hidden * esize
-        footprint = {"rms_norm": 2.0, "fused_add_rms_norm": 2.0, "silu_and_mul": 1.5, "softmax": 2.0}
+        footprint = {"rms_norm": 2.0, "fused_add_rms_norm": 2.0, "silu_and_mul": 1.5, "softmax": 2.0,
+                     "rms_norm_residual": 3.0}
         per_set = int(sum(footprint[op] for op in wl.ops) * self.tensor_bytes)
         # enough copies to pass through more than the last-level cache between
         # two uses of one copy; capped for tiny (launch-bound) batches
@@ -207,6 +218,10 @@ class Rig:
             if "silu_and_mul" in wl.ops:
                 s["sx"] = x0.clone()
                 s["sout"] = torch.empty(wl.rows, wl.hidden // 2, dtype=x0.dtype, device=x0.device)
+            if "rms_norm_residual" in wl.ops:
+                s["ox"] = x0.clone()
+                s["or"] = r0.clone()
+                s["oout"] = torch.empty_like(x0)
             if "softmax" in wl.ops:
                 s["mx"] = x0.clone()
                 s["mout"] = torch.empty_like(x0)
@@ -230,6 +245,8 @@ class Rig:
             self.ks.fused_add_rms_norm(s["fx"], s["fr"], self.w, self.wl.eps)
         elif op == "softmax":
             self.ks.softmax(s["mx"], out=s["mout"])
+        elif op == "rms_norm_residual":
+            self.ks.rms_norm_residual(s["ox"], s["or"], self.w, self.wl.eps, out=s["oout"])
         else:
             self.ks.silu_and_mul(s["sx"], out=s["sout"])
 
@@ -261,7 +278,7 @@ class Rig:
     def copy_reference(self, reps: int) -> dict:
         """The runtime's device-to-device copy of one batch-sized tensor per launch."""
         n = self.nsets
-        srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx")))) for s in self.sets]
+        srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx", s.get("ox"))))) for s in self.sets]
         dsts = [torch.empty_like(t) for t in srcs]
         ms = self.timed_graph(lambda i: dsts[i % n].copy_(srcs[i % n]), n, reps)
         del dsts
@@ -317,6 +334,8 @@ def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
             oracle_mod.silu_and_mul(inp["x"])
         if "softmax" in wl.ops:
             oracle_mod.softmax(inp["x"])
+        if "rms_norm_residual" in wl.ops:
+            oracle_mod.rms_norm_residual(inp["x"], inp["residual"], inp["weight"], wl.eps)
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -398,7 +417,7 @@ def kernel_op(name: str) -> str | None:
     """The operation a demangled kernel name belongs to (None for other kernels)."""
     if "ks::" not in name:
         return None
-    for op in ("fused_add_rms_norm", "rms_norm", "silu_and_mul", "softmax"):
+    for op in ("fused_add_rms_norm", "rms_norm_residual", "rms_norm", "silu_and_mul", "softmax"):
         if op in name:
             return op
     return None

@@ -5,7 +5,8 @@
  * The operations are the ones defined in the kernscope README, section
  * "Numerical contract" (subsections "RMSNorm", "Fused residual-add RMSNorm",
  * "SwiGLU activation" and "Softmax"), with the input rules of its "Inputs"
- * section.  The C-ABI
+ * section, and the out-of-place residual RMSNorm of the Triton Kernels README
+ * ("Kernels").  The C-ABI
  * convention (a status code from every entry point, device pointers, an
  * explicit stream) follows the kernel-set README ("What it is", last line of
  * the operator table).
@@ -71,7 +72,8 @@ typedef enum {
     KS_OP_RMS_NORM = 0,
     KS_OP_FUSED_ADD_RMS_NORM = 1,
     KS_OP_SILU_AND_MUL = 2,
-    KS_OP_SOFTMAX = 3
+    KS_OP_SOFTMAX = 3,
+    KS_OP_RMS_NORM_RESIDUAL = 4
 } ks_op_t;
 
 /* How a launch maps rows onto threads.
@@ -131,6 +133,28 @@ ks_status_t ks_rms_norm(void *out, const void *x, const void *weight,
 ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight,
                                   int64_t rows, int64_t hidden, float eps,
                                   ks_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Out-of-place residual RMSNorm (Triton Kernels README, "Kernels": the
+ * residual-fused RMSNorm, RMSNorm(x + residual) * w), with the kernscope
+ * fused contract's arithmetic:
+ *   s   = fp32(x) + fp32(residual)      (unrounded)
+ *   out = cast( s * rsqrt(mean(s^2) + eps) * fp32(weight) )
+ * Nothing but out is written: a row moves three times its size (read x and
+ * residual, write out) instead of the in-place form's four.
+ * out       [rows, hidden] output.  It may be exactly x or exactly residual;
+ *           any other overlap with x, residual or weight is KS_ERROR_OVERLAP.
+ * x, residual [rows, hidden], read only (they may overlap each other).
+ * weight    [hidden], read only.
+ * Errors, streams and plans as for ks_rms_norm (op KS_OP_RMS_NORM_RESIDUAL).
+ */
+ks_status_t ks_rms_norm_residual(void *out, const void *x, const void *residual, const void *weight,
+                                 int64_t rows, int64_t hidden, float eps,
+                                 ks_dtype_t dtype, hipStream_t stream);
+
+ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residual, const void *weight,
+                                    int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
+                                    const ks_plan_t *plan, hipStream_t stream);
 
 /*
  * The launch plan the calls of this header use for this op, dtype, batch and

@@ -257,8 +257,8 @@ int oracle_rms_norm_residual(int dtype, const void *x, const void *residual, con
         }
         float scale = row_scale(sum_sq, hidden, eps);
         for (int64_t j = 0; j < hidden; ++j) {
-            float t = s[j] * scale;
-            store_elem(dtype, out, base + j, t * load_elem(dtype, w, j));
+            float scaled = s[j] * scale;
+            store_elem(dtype, out, base + j, scaled * load_elem(dtype, w, j));
         }
     }
     free(s);

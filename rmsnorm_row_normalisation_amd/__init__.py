@@ -1,4 +1,5 @@
-"""RMSNorm, fused residual-add RMSNorm, SwiGLU and softmax for MI355X (gfx950).
+"""RMSNorm, fused residual-add RMSNorm (in place and out of place), SwiGLU and
+softmax for MI355X (gfx950).
 
 The computation lives in ``libks_norm.so`` (hand-written HIP kernels behind a
 C ABI, ``include/ks_norm.h``); this package is its thin Python binding.
@@ -26,6 +27,9 @@ from .binding import (  # noqa: F401
     softmax,
     ks_softmax,
     ks_softmax_ex,
+    rms_norm_residual,
+    ks_rms_norm_residual,
+    ks_rms_norm_residual_ex,
 )
 
 __version__ = "0.1.0"

@@ -2,7 +2,7 @@
 
 The ``ks_*`` functions mirror the C ABI in ``include/ks_norm.h`` one to one
 (raw device pointers as ints).  ``rms_norm``, ``fused_add_rms_norm``,
-``silu_and_mul`` and ``softmax`` are the tensor-level calls with the kernscope API shape
+``rms_norm_residual``, ``silu_and_mul`` and ``softmax`` are the tensor-level calls with the kernscope API shape
 (README, "API contract" and "Inputs"): they check devices, dtypes, shapes, contiguity and
 ``requires_grad`` (the accelerator kernels are inference-only), then pass the
 tensors' device pointers and torch's current HIP stream to the library.
@@ -20,7 +20,7 @@ DEFAULT_LIB = os.path.join(_PKG, "libks_norm.so")
 
 KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP = range(5)
 KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX = 0, 1, 2, 3
+KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX, KS_OP_RMS_NORM_RESIDUAL = 0, 1, 2, 3, 4
 KS_PATH_VECTOR, KS_PATH_GENERIC = 0, 1
 
 
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         h.ks_silu_and_mul.argtypes = [vp, vp, i64, i64, i32, vp]
         h.ks_silu_and_mul_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_softmax.argtypes = [vp, vp, i64, i64, i32, vp]
+        h.ks_rms_norm_residual.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
+        h.ks_rms_norm_residual_ex.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_softmax_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
@@ -96,7 +98,7 @@ def lib() -> ctypes.CDLL:
         h.ks_version.restype = ctypes.c_char_p
         for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
                      "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
-                     "ks_softmax_ex"):
+                     "ks_softmax_ex", "ks_rms_norm_residual", "ks_rms_norm_residual_ex"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -137,6 +139,17 @@ def ks_fused_add_rms_norm_ex(x: int, residual: int, weight: int, rows: int, hidd
                              plan: Plan | None, stream: int) -> int:
     return lib().ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype,
                                           ctypes.byref(plan) if plan is not None else None, stream)
+
+
+def ks_rms_norm_residual(out: int, x: int, residual: int, weight: int, rows: int, hidden: int, eps: float,
+                         dtype: int, stream: int) -> int:
+    return lib().ks_rms_norm_residual(out, x, residual, weight, rows, hidden, eps, dtype, stream)
+
+
+def ks_rms_norm_residual_ex(out: int, x: int, residual: int, weight: int, rows: int, hidden: int, eps: float,
+                            dtype: int, plan: Plan | None, stream: int) -> int:
+    return lib().ks_rms_norm_residual_ex(out, x, residual, weight, rows, hidden, eps, dtype,
+                                         ctypes.byref(plan) if plan is not None else None, stream)
 
 
 def ks_silu_and_mul(out: int, x: int, rows: int, d: int, dtype: int, stream: int) -> int:
@@ -224,6 +237,26 @@ def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: torch.Te
     _check(st, "ks_fused_add_rms_norm")
 
 
+def rms_norm_residual(x: torch.Tensor, residual: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
+                      out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
+    """Out of place: RMSNorm(x + residual) * weight with the fp32 sum (Triton Kernels
+    README, "Kernels"); returns ``out`` (a new tensor unless given; may be x or residual)."""
+    rows, hidden = _check_tensors("rms_norm_residual", x, weight, residual)
+    if residual.shape != x.shape:
+        raise ValueError("rms_norm_residual: residual must have the shape of x")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_tensors("rms_norm_residual", out, weight)
+        if out.shape != x.shape:
+            raise ValueError("rms_norm_residual: out must have the shape of x")
+    with torch.cuda.device(x.device):
+        st = ks_rms_norm_residual_ex(out.data_ptr(), x.data_ptr(), residual.data_ptr(), weight.data_ptr(), rows,
+                                     hidden, float(eps), KS_DTYPE[x.dtype], plan, _stream(x))
+    _check(st, "ks_rms_norm_residual")
+    return out
+
+
 def silu_and_mul(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
     """SwiGLU of x with shape (..., 2D): a new (..., D) tensor (kernscope "SwiGLU activation")."""
     if x.dtype not in KS_DTYPE:
@@ -278,5 +311,6 @@ def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: b
     """The plan the library picks for this op, dtype, row size and batch (ks_get_plan).
     For silu_and_mul, ``hidden`` is the output width D."""
     code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM,
-            "silu_and_mul": KS_OP_SILU_AND_MUL, "softmax": KS_OP_SOFTMAX}[op]
+            "silu_and_mul": KS_OP_SILU_AND_MUL, "softmax": KS_OP_SOFTMAX,
+            "rms_norm_residual": KS_OP_RMS_NORM_RESIDUAL}[op]
     return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned)

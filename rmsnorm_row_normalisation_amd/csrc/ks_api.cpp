@@ -1,6 +1,6 @@
 // C ABI of ks_norm: argument validation, overlap checks, the launch policy
 // and the calls into the per-dtype kernel units (RMSNorm, fused residual-add
-// RMSNorm, SwiGLU, softmax).  Validation and the policy
+// RMSNorm in place and out of place, SwiGLU, softmax).  Validation and the policy
 // make no HIP call, so they run (and are tested) on machines without a GPU.
 #include <math.h>
 #include <stdint.h>
@@ -64,6 +64,10 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 //   * the fused kernel stages the weight in LDS from 2^18 pieces up, where
 //     several rows per compute unit share it; below that the staging barrier
 //     costs more than the L2 re-reads it saves.
+// The two forms that add a residual (in place and out of place) read two
+// streams per row: from 4M pieces they take at most 2 pieces per lane and
+// teams of up to 1024 lanes.  The out-of-place form never stages the weight
+// in LDS (measured slower at every batch size).
 // These rules were fitted to timings of every compiled shape and hint
 // combination for hidden 1024..16384 and 1..32768 rows (bf16).
 // Rows wider than 64 KiB, or unaligned buffers, take the generic path.
@@ -104,9 +108,11 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     if (aligned && row_bytes % 16 == 0 && nvec <= (int64_t)kPolicyMaxTpr * ks::kMaxVpt) {
         const int64_t pieces = rows * nvec;
         const bool swiglu = op == KS_OP_SILU_AND_MUL;
+        const bool adds_residual = op == KS_OP_FUSED_ADD_RMS_NORM || op == KS_OP_RMS_NORM_RESIDUAL;
         const bool large = pieces >= kLargeBatchPieces;
         const int64_t max_vpt = swiglu                  ? kSwigluMaxVpt
                                 : op == KS_OP_SOFTMAX ? (large ? 2 : 4)
+                                : adds_residual && large ? 2
                                 : large                 ? 4
                                                         : ks::kMaxVpt;
         int64_t vpt = pow2_ceil((pieces + kTargetLanes - 1) / kTargetLanes);
@@ -117,7 +123,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
             const int64_t slots1024 = (nvec + ks::kMaxTpr - 1) / ks::kMaxTpr * ks::kMaxTpr;
             tpr = slots1024 <= slots512 ? ks::kMaxTpr : kPolicyMaxTpr;
         }
-        const int64_t max_tpr = swiglu ? ks::kMaxTpr : kPolicyMaxTpr;
+        const int64_t max_tpr = (swiglu || (adds_residual && large)) ? ks::kMaxTpr : kPolicyMaxTpr;
         tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > max_tpr ? max_tpr : tpr;
         plan.path = KS_PATH_VECTOR;
         plan.threads_per_row = (int32_t)tpr;
@@ -127,7 +133,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.rows_per_block = plan.block_threads / (int32_t)tpr;
         plan.load_nt = 1;
         plan.store_nt = 1;
-        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;   // softmax: no weight
+        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;
         return plan;
     }
     plan.path = KS_PATH_GENERIC;
@@ -202,25 +208,28 @@ ks_status_t launch(ks::Launch &l, ks_dtype_t dtype)
 {
     hipError_t err;
     const bool vec = l.plan.path == KS_PATH_VECTOR;
-    const bool fused = l.op == KS_OP_FUSED_ADD_RMS_NORM;
+    const ks_op_t op = l.op;
     switch (dtype) {
     case KS_DTYPE_FLOAT32:
-        err = l.op == KS_OP_SOFTMAX ? ks::launch_softmax_f32(l)
-              : !vec                ? ks::launch_generic_f32(l)
-              : fused               ? ks::launch_vec_f32_fused(l)
-                                    : ks::launch_vec_f32_rms(l);
+        err = op == KS_OP_SOFTMAX                 ? ks::launch_softmax_f32(l)
+              : !vec                              ? ks::launch_generic_f32(l)
+              : op == KS_OP_FUSED_ADD_RMS_NORM    ? ks::launch_vec_f32_fused(l)
+              : op == KS_OP_RMS_NORM_RESIDUAL     ? ks::launch_vec_f32_residual(l)
+                                                  : ks::launch_vec_f32_rms(l);
         break;
     case KS_DTYPE_FLOAT16:
-        err = l.op == KS_OP_SOFTMAX ? ks::launch_softmax_f16(l)
-              : !vec                ? ks::launch_generic_f16(l)
-              : fused               ? ks::launch_vec_f16_fused(l)
-                                    : ks::launch_vec_f16_rms(l);
+        err = op == KS_OP_SOFTMAX                 ? ks::launch_softmax_f16(l)
+              : !vec                              ? ks::launch_generic_f16(l)
+              : op == KS_OP_FUSED_ADD_RMS_NORM    ? ks::launch_vec_f16_fused(l)
+              : op == KS_OP_RMS_NORM_RESIDUAL     ? ks::launch_vec_f16_residual(l)
+                                                  : ks::launch_vec_f16_rms(l);
         break;
     default:
-        err = l.op == KS_OP_SOFTMAX ? ks::launch_softmax_bf16(l)
-              : !vec                ? ks::launch_generic_bf16(l)
-              : fused               ? ks::launch_vec_bf16_fused(l)
-                                    : ks::launch_vec_bf16_rms(l);
+        err = op == KS_OP_SOFTMAX                 ? ks::launch_softmax_bf16(l)
+              : !vec                              ? ks::launch_generic_bf16(l)
+              : op == KS_OP_FUSED_ADD_RMS_NORM    ? ks::launch_vec_bf16_fused(l)
+              : op == KS_OP_RMS_NORM_RESIDUAL     ? ks::launch_vec_bf16_residual(l)
+                                                  : ks::launch_vec_bf16_rms(l);
         break;
     }
     if (err != hipSuccess) {
@@ -302,6 +311,37 @@ ks_status_t ks_fused_add_rms_norm(void *x, void *residual, const void *weight, i
     return ks_fused_add_rms_norm_ex(x, residual, weight, rows, hidden, eps, dtype, nullptr, stream);
 }
 
+ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residual, const void *weight,
+                                   int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
+                                   const ks_plan_t *plan, hipStream_t stream)
+{
+    ks_status_t st = check_sizes(dtype, rows, hidden, eps);
+    if (st != KS_SUCCESS)
+        return st;
+    if (rows > 0 && (out == nullptr || x == nullptr || residual == nullptr || weight == nullptr))
+        return KS_ERROR_INVALID_VALUE;
+    const bool aligned = aligned16(out) && aligned16(x) && aligned16(residual) && aligned16(weight);
+    ks::Launch l{out, x, const_cast<void *>(residual), weight, rows, (int32_t)hidden, eps,
+                 KS_OP_RMS_NORM_RESIDUAL, {}, stream};
+    st = select_plan(plan, KS_OP_RMS_NORM_RESIDUAL, dtype, rows, hidden, aligned, &l.plan);
+    if (st != KS_SUCCESS || rows == 0)
+        return st;
+    const int64_t es = elem_size(dtype);
+    const int64_t nbytes = rows * hidden * es;
+    // x and residual are only read (they may overlap each other); out may be
+    // exactly either of them, and must not touch the weight
+    if ((out != x && overlaps(out, nbytes, x, nbytes)) || (out != residual && overlaps(out, nbytes, residual, nbytes)) ||
+        overlaps(out, nbytes, weight, hidden * es))
+        return KS_ERROR_OVERLAP;
+    return launch(l, dtype);
+}
+
+ks_status_t ks_rms_norm_residual(void *out, const void *x, const void *residual, const void *weight, int64_t rows,
+                                 int64_t hidden, float eps, ks_dtype_t dtype, hipStream_t stream)
+{
+    return ks_rms_norm_residual_ex(out, x, residual, weight, rows, hidden, eps, dtype, nullptr, stream);
+}
+
 ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
                                const ks_plan_t *plan, hipStream_t stream)
 {
@@ -368,7 +408,7 @@ ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidd
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
         (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL &&
-         op != KS_OP_SOFTMAX))
+         op != KS_OP_SOFTMAX && op != KS_OP_RMS_NORM_RESIDUAL))
         return KS_ERROR_INVALID_VALUE;
     *plan = policy(op, dtype, rows, hidden, aligned != 0);
     return KS_SUCCESS;

@@ -1,5 +1,6 @@
-// Device code for RMSNorm, fused residual-add RMSNorm, the SwiGLU activation
-// and softmax on gfx950 (CDNA4).
+// Device code for RMSNorm, fused residual-add RMSNorm (in place, and the
+// out-of-place RMSNorm(x + residual) * w), the SwiGLU activation and softmax
+// on gfx950 (CDNA4).
 //
 // Operation (kernscope README, "Numerical contract"): per row, widen to fp32,
 // sum of squares in fp32, scale = rsqrt(sum / H + eps), y = (v * scale) *
@@ -286,12 +287,15 @@ __device__ __forceinline__ float row_scale(float sum_sq, int32_t hidden, float e
 // ---------------------------------------------------------------------------
 // Vector kernel: row held in VGPRs.
 //
+// kFused: the row is s = x + residual (fp32), else x.  kStoreSum: the
+// rounded s is written back to residual (the in-place fused form; without it
+// the out-of-place residual form writes only y).
 // kLoadCpol / kStoreCpol: cache-policy bits of the streamed x / residual /
 // out accesses (0 = default, 2 = non-temporal).  kWeightLds: the workgroup
 // first stages the weight row in LDS (one HBM/L2 read per workgroup instead
 // of one per row); needs row_bytes of dynamic LDS.
 // ---------------------------------------------------------------------------
-template <typename T, bool kFused, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol,
+template <typename T, bool kFused, bool kStoreSum, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol,
           bool kWeightLds>
 __device__ __forceinline__ void vec_body(const Params &p)
 {
@@ -398,7 +402,8 @@ __device__ __forceinline__ void vec_body(const Params &p)
             part[k] = a;
             // this lane has read every element it will write: store the
             // rounded residual now, so the writes start before the reduction
-            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(s[k]), rr, off[k], 0, kStoreCpol);
+            if constexpr (kStoreSum)
+                __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(s[k]), rr, off[k], 0, kStoreCpol);
         }
         const float scale = row_scale(team_fold<kTpr, kBlock>(local_fold<kVpt>(part)), p.hidden, p.eps);
 #pragma unroll
@@ -419,7 +424,7 @@ __device__ __forceinline__ void vec_body(const Params &p)
 // kEpa == 1: scalar accesses (any alignment); kEpa == 16 / sizeof(T): 16-byte
 // accesses (aligned buffers, row bytes a multiple of 16).
 // ---------------------------------------------------------------------------
-template <typename T, bool kFused, int kTpr, int kEpa, int kBlock>
+template <typename T, bool kFused, bool kStoreSum, int kTpr, int kEpa, int kBlock>
 __device__ __forceinline__ void generic_body(const Params &p)
 {
     constexpr int kRpb = kBlock / kTpr;
@@ -465,7 +470,8 @@ __device__ __forceinline__ void generic_body(const Params &p)
             float v = Scalar<T>::get(p.x, base + j);
             if constexpr (kFused) {
                 v = v + Scalar<T>::get(p.res, base + j);
-                Scalar<T>::put(p.res, base + j, v);
+                if constexpr (kStoreSum)
+                    Scalar<T>::put(p.res, base + j, v);
             }
             const float t = v * scale;
             Scalar<T>::put(p.y, base + j, t * Scalar<T>::get(p.w, j));
@@ -478,7 +484,8 @@ __device__ __forceinline__ void generic_body(const Params &p)
 #pragma unroll
                 for (int e = 0; e < kEpa; ++e)
                     v[e] = Pack<T>::get(xv, e) + Pack<T>::get(rv, e);
-                *(u32x4 *)((char *)p.res + (base + j) * Pack<T>::kBytes) = Pack<T>::put(v);
+                if constexpr (kStoreSum)
+                    *(u32x4 *)((char *)p.res + (base + j) * Pack<T>::kBytes) = Pack<T>::put(v);
             } else {
 #pragma unroll
                 for (int e = 0; e < kEpa; ++e)
@@ -787,25 +794,37 @@ __device__ __forceinline__ void softmax_generic_body(const Params &p)
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
 __global__ __launch_bounds__(kBlock) void rms_norm_vec(Params p)
 {
-    vec_body<T, false, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
+    vec_body<T, false, false, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
 __global__ __launch_bounds__(kBlock) void fused_add_rms_norm_vec(Params p)
 {
-    vec_body<T, true, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
+    vec_body<T, true, true, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
+}
+
+template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
+__global__ __launch_bounds__(kBlock) void rms_norm_residual_vec(Params p)
+{
+    vec_body<T, true, false, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
 __global__ __launch_bounds__(kBlock) void rms_norm_generic(Params p)
 {
-    generic_body<T, false, kTpr, kEpa, kBlock>(p);
+    generic_body<T, false, false, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
 __global__ __launch_bounds__(kBlock) void fused_add_rms_norm_generic(Params p)
 {
-    generic_body<T, true, kTpr, kEpa, kBlock>(p);
+    generic_body<T, true, true, kTpr, kEpa, kBlock>(p);
+}
+
+template <typename T, int kTpr, int kEpa, int kBlock>
+__global__ __launch_bounds__(kBlock) void rms_norm_residual_generic(Params p)
+{
+    generic_body<T, true, false, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>

@@ -1,12 +1,15 @@
-// Generic-path kernels for float32, both operations.
+// Generic-path kernels for float32, the three normalisation operations.
 #include "ks_launch.hpp"
 
 namespace ks {
 
 hipError_t launch_generic_f32(const Launch &l)
 {
-    return l.op == KS_OP_FUSED_ADD_RMS_NORM ? launch_generic_typed<f32, KS_OP_FUSED_ADD_RMS_NORM>(l)
-                                           : launch_generic_typed<f32, KS_OP_RMS_NORM>(l);
+    switch (l.op) {
+    case KS_OP_FUSED_ADD_RMS_NORM: return launch_generic_typed<f32, KS_OP_FUSED_ADD_RMS_NORM>(l);
+    case KS_OP_RMS_NORM_RESIDUAL: return launch_generic_typed<f32, KS_OP_RMS_NORM_RESIDUAL>(l);
+    default: return launch_generic_typed<f32, KS_OP_RMS_NORM>(l);
+    }
 }
 
 }  // namespace ks

@@ -20,7 +20,7 @@ struct Launch {
     int64_t rows;
     int32_t hidden;
     float eps;
-    ks_op_t op;         // KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM or KS_OP_SOFTMAX
+    ks_op_t op;         // KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_RMS_NORM_RESIDUAL or KS_OP_SOFTMAX
     ks_plan_t plan;
     hipStream_t stream;
 };
@@ -42,9 +42,10 @@ constexpr int kNonTemporal = 2;
 // in its own translation unit so they compile in parallel).  Return
 // hipErrorInvalidValue when no kernel was compiled for the plan (plan_fits
 // rules that out before a launch).
-#define KS_DECLARE_LAUNCH(dt)                          \
-    hipError_t launch_vec_##dt##_rms(const Launch &l);   \
-    hipError_t launch_vec_##dt##_fused(const Launch &l); \
+#define KS_DECLARE_LAUNCH(dt)                             \
+    hipError_t launch_vec_##dt##_rms(const Launch &l);      \
+    hipError_t launch_vec_##dt##_fused(const Launch &l);    \
+    hipError_t launch_vec_##dt##_residual(const Launch &l); \
     hipError_t launch_generic_##dt(const Launch &l);
 KS_DECLARE_LAUNCH(f32)
 KS_DECLARE_LAUNCH(f16)

@@ -19,12 +19,15 @@ hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
     return hipGetLastError();
 }
 
-// The kernel entry point of one op (OP is a ks_op_t: RMSNorm, fused or softmax).
+// The kernel entry point of one op (OP is a ks_op_t: RMSNorm, fused in place,
+// out-of-place residual, or softmax).
 template <int OP, typename T, int TPR, int V, int B, int LC, int SC, bool WL>
 constexpr auto vec_entry()
 {
     if constexpr (OP == KS_OP_FUSED_ADD_RMS_NORM)
         return fused_add_rms_norm_vec<T, TPR, V, B, LC, SC, WL>;
+    else if constexpr (OP == KS_OP_RMS_NORM_RESIDUAL)
+        return rms_norm_residual_vec<T, TPR, V, B, LC, SC, WL>;
     else if constexpr (OP == KS_OP_SOFTMAX)
         return softmax_vec<T, TPR, V, B, LC, SC>;
     else
@@ -36,6 +39,8 @@ constexpr auto generic_entry()
 {
     if constexpr (OP == KS_OP_FUSED_ADD_RMS_NORM)
         return fused_add_rms_norm_generic<T, TPR, EPA, B>;
+    else if constexpr (OP == KS_OP_RMS_NORM_RESIDUAL)
+        return rms_norm_residual_generic<T, TPR, EPA, B>;
     else if constexpr (OP == KS_OP_SOFTMAX)
         return softmax_generic<T, TPR, EPA, B>;
     else

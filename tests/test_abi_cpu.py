@@ -162,7 +162,11 @@ EXPECTED = {
     ("rms_norm", torch.float16, 4096, 2048): (0, 64, 8, 4, 0),
     ("fused_add_rms_norm", torch.bfloat16, 1536, 4): (0, 256, 1, 1, 0),  # decode 4x1536
     ("fused_add_rms_norm", torch.bfloat16, 8192, 1): (0, 512, 2, 1, 0),  # decode 1x8192
-    ("fused_add_rms_norm", torch.bfloat16, 8192, 32768): (0, 256, 4, 1, 1),   # prefill 32768x8192
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 32768): (0, 512, 2, 1, 1),   # prefill 32768x8192
+    ("fused_add_rms_norm", torch.bfloat16, 16384, 8192): (0, 1024, 2, 1, 1),  # 4M+ pieces: up to 1024 lanes
+    ("fused_add_rms_norm", torch.bfloat16, 4096, 8192): (0, 256, 2, 1, 1),
+    ("rms_norm_residual", torch.bfloat16, 4096, 2048): (0, 64, 8, 4, 0),      # never stages the weight
+    ("rms_norm_residual", torch.bfloat16, 16384, 8192): (0, 1024, 2, 1, 0),
     ("rms_norm", torch.bfloat16, 16384, 8192): (0, 512, 4, 1, 0),        # prefill 8192x16384
     ("rms_norm", torch.float32, 4096, 2048): (0, 128, 8, 2, 0),
     ("rms_norm", torch.bfloat16, 5, 3): (1, 8, 0, 32, 0),                # odd sizes: generic scalar path
@@ -432,3 +436,43 @@ def test_softmax_tensor_api_checks():
         ks.softmax(x)                                           # not on a HIP device
     with pytest.raises(TypeError):
         ks.softmax(x.to(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# Out-of-place residual RMSNorm (Triton Kernels README, "Kernels"): x and
+# residual read only, out may be exactly either of them
+# ---------------------------------------------------------------------------
+def resid(out, x, r, w, rows, hidden, eps=1e-6, dtype=BF16, plan=None):
+    return b.ks_rms_norm_residual_ex(out, x, r, w, rows, hidden, eps, dtype, plan, 0)
+
+
+def test_residual_statuses_and_overlaps():
+    x, r, w, out = A, A + 256 * MB, A + 512 * MB, A + 768 * MB
+    assert resid(out, x, r, w, 4, 4096, dtype=9) == DTYPE
+    assert resid(out, x, r, w, -1, 4096) == INVALID
+    assert resid(out, x, r, w, 4, 0) == INVALID
+    assert resid(out, x, r, w, 4, 4096, eps=0.0) == INVALID
+    assert resid(out, x, r, w, 4, 4096, eps=float("nan")) == INVALID
+    for args in ((None, x, r, w), (out, None, r, w), (out, x, None, w), (out, x, r, None)):
+        assert resid(*args, 4, 4096) == INVALID
+    assert resid(None, None, None, None, 0, 4096) == OK
+    assert resid(x, x, r, w, 4, 4096) != OVERLAP             # out == x: allowed
+    assert resid(r, x, r, w, 4, 4096) != OVERLAP             # out == residual: allowed
+    assert resid(x + 2, x, r, w, 4, 4096) == OVERLAP
+    assert resid(r - 2, x, r, w, 4, 4096) == OVERLAP
+    assert resid(out, x, r, out + 100, 4, 4096) == OVERLAP   # weight inside out
+    assert resid(out, x, x + 64, w, 0, 4096) == OK           # x and residual may overlap (read only)
+    assert b.ks_rms_norm_residual(None, None, None, None, 0, 8, 1e-6, BF16, 0) == OK
+
+
+def test_residual_plans_follow_the_fused_rule():
+    """Same shapes as the in-place form, without LDS weight staging."""
+    for hidden in (8, 1000, 1024, 4096, 8192, 16384, 32768, 32769, 70000):
+        for rows in (1, 64, 2048, 65536):
+            for aligned in (True, False):
+                p = ks.get_plan("rms_norm_residual", torch.bfloat16, hidden, rows, aligned).as_dict()
+                q = ks.get_plan("fused_add_rms_norm", torch.bfloat16, hidden, rows, aligned).as_dict()
+                assert p == {**q, "weight_lds": 0}
+                base = A if aligned else A + 2
+                assert resid(base + 768 * MB, base, base + 256 * MB, base + 512 * MB, 0, hidden,
+                             plan=b.Plan.from_dict(p)) == OK

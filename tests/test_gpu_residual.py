@@ -1,0 +1,138 @@
+"""Out-of-place RMSNorm(x + residual) * w on the GPU against the CPU oracle.
+
+Bar: the normalisation bar (within 1 ulp of bf16/fp16 with |difference| <=
+1e-6 near zero, >= 99.9% bit-identical on large cases; fp32 within rtol =
+atol = 1e-6).  Cases: the Triton Kernels README example shape (fp16
+[2048, 4096], unit weight) and the headline shape in bf16, edge and ragged
+shapes in all dtypes, unaligned buffers, out == x and out == residual, inputs
+left unchanged, every compiled plan (vector plans bit-identical), and
+graph replays.
+"""
+import pytest
+import torch
+
+import oracle
+import rmsnorm_row_normalisation_amd as ks
+import workloads
+from compare import check_bitexact, check_normalised
+from gpu_cases import HINTS, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+DTYPES = ["bfloat16", "float16", "float32"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _dev(t: torch.Tensor, offset: int) -> torch.Tensor:
+    if offset == 0:
+        return t.cuda()
+    buf = torch.empty(t.numel() + offset, dtype=t.dtype, device="cuda")
+    view = buf[offset:].view(t.shape)
+    view.copy_(t.cuda())
+    return view
+
+
+def run(inp, eps, plan=None, offset=0, alias=None):
+    x, r, w = _dev(inp["x"], offset), _dev(inp["residual"], offset), _dev(inp["weight"], offset)
+    out = {"x": x, "residual": r}.get(alias) if alias else None
+    if out is None and offset:
+        out = _dev(torch.empty_like(inp["x"]), offset)
+    y = ks.rms_norm_residual(x, r, w, eps, out=out, plan=plan)
+    torch.cuda.synchronize()
+    return y.cpu(), x.cpu(), r.cpu()
+
+
+def check(name, inp, eps, plan=None, offset=0, alias=None, exact=None):
+    say("residual", name, tuple(inp["x"].shape), inp["x"].dtype, "plan" if plan is not None else "policy",
+        f"offset={offset}", f"alias={alias}")
+    y, xo, ro = run(inp, eps, plan, offset, alias)
+    ref = oracle.rms_norm_residual(inp["x"], inp["residual"], inp["weight"], eps)
+    if exact is None:
+        exact = y.numel() >= 20000
+    st = check_normalised(y, ref, 0.999 if exact else None)
+    if alias != "x":
+        check_bitexact(xo, inp["x"])
+    if alias != "residual":
+        check_bitexact(ro, inp["residual"])
+    return st
+
+
+@pytest.mark.parametrize("name", ["R1", "R2"])
+def test_workloads(name):
+    wl = workloads.WORKLOADS[name]
+    say(name, check(name, workloads.make_inputs(wl), wl.eps))
+
+
+SHAPES = [(5,), (2, 3, 5), (3, 1000), (512, 1024), (7, 1023), (4, 4096), (2, 8200), (2, 16384), (2, 32768),
+          (2, 40000)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(shape, dtype):
+    inp = workloads.random_case(shape, dtype, seed=sum(shape) + 3, residual=workloads.normal(0, 0.7))
+    check("shape", inp, 1e-6)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_unaligned_and_aliases(dtype):
+    inp = workloads.random_case((37, 4096), dtype, seed=77)
+    check("offset", inp, 1e-5, offset=1)
+    check("out=x", inp, 1e-5, alias="x")
+    check("out=residual", inp, 1e-5, alias="residual")
+
+
+@pytest.mark.parametrize("dtype,hidden", [("bfloat16", 4096), ("float16", 1536), ("float32", 1000)])
+def test_every_plan(dtype, hidden):
+    inp = workloads.random_case((70, hidden), dtype, seed=hidden + 1)
+    ref = oracle.rms_norm_residual(inp["x"], inp["residual"], inp["weight"], 1e-6)
+    es = inp["x"].element_size()
+    first = None
+    tpr = 8
+    n = 0
+    while tpr <= 1024:
+        maxv = 4 if tpr == 1024 else 8
+        for vpt in range(1, maxv + 1):
+            if tpr * vpt * 16 >= hidden * es:
+                block = max(256, tpr)
+                for lnt, snt, wl in HINTS:
+                    plan = ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt, elems_per_access=16 // es,
+                                   rows_per_block=block // tpr, block_threads=block, load_nt=lnt, store_nt=snt,
+                                   weight_lds=wl)
+                    y, _, _ = run(inp, 1e-6, plan)
+                    check_normalised(y, ref, 0.999)
+                    if first is None:
+                        first = y
+                    else:
+                        check_bitexact(y, first)
+                    n += 1
+        tpr *= 2
+    assert n > 10
+    for t in (8, 64, 256, 1024):
+        for epa in (1, 16 // es):
+            block = 1024 if t == 1024 else 256
+            plan = ks.Plan(path=1, threads_per_row=t, vectors_per_thread=0, elems_per_access=epa,
+                           rows_per_block=block // t, block_threads=block)
+            check_normalised(run(inp, 1e-6, plan)[0], ref, 0.999)
+
+
+def test_graph_replays_match_eager():
+    wl = workloads.WORKLOADS["R2"]
+    inp = workloads.make_inputs(wl)
+    x, r, w = inp["x"].cuda(), inp["residual"].cuda(), inp["weight"].cuda()
+    out = ks.rms_norm_residual(x, r, w, wl.eps)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ks.rms_norm_residual(x, r, w, wl.eps, out=out)
+    for _ in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_bitexact(out.cpu(), eager.cpu())

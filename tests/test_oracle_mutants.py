@@ -23,8 +23,8 @@ MUTANTS = [
      "float u = t;\n            store_elem(dtype, out"),
     ("weight_reversed", "float u = t * load_elem(dtype, w, j);\n            store_elem(dtype, out",
      "float u = t * load_elem(dtype, w, hidden - 1 - j);\n            store_elem(dtype, out"),
-    ("fused_sub", "s[j] = load_elem(dtype, x, base + j) + load_elem(dtype, residual, base + j);",
-     "s[j] = load_elem(dtype, x, base + j) - load_elem(dtype, residual, base + j);"),
+    ("fused_sub", "s[j] = load_elem(dtype, x, base + j) + load_elem(dtype, residual, base + j);\n            double v",
+     "s[j] = load_elem(dtype, x, base + j) - load_elem(dtype, residual, base + j);\n            double v"),
     ("fused_residual_is_x", "store_elem(dtype, residual, base + j, s[j]);",
      "store_elem(dtype, residual, base + j, load_elem(dtype, x, base + j));"),
     ("fused_normalises_rounded_sum", "float t = s[j] * scale;",
@@ -53,8 +53,8 @@ MUTANTS = [
     ("residual_oop_rounds_sum", "sum_sq += (double)s[j] * (double)s[j];",
      "store_elem(dtype, out, base + j, s[j]);   /* rounds s to the dtype */\n"
      "            s[j] = load_elem(dtype, out, base + j);\n            sum_sq += (double)s[j] * (double)s[j];"),
-    ("residual_oop_no_weight", "store_elem(dtype, out, base + j, t * load_elem(dtype, w, j));",
-     "store_elem(dtype, out, base + j, t);"),
+    ("residual_oop_no_weight", "store_elem(dtype, out, base + j, scaled * load_elem(dtype, w, j));",
+     "store_elem(dtype, out, base + j, scaled);"),
     ("softmax_no_max_shift", "float z = load_elem(dtype, x, base + j) - m;",
      "float z = load_elem(dtype, x, base + j);"),
     ("softmax_max_never_updated", "else if (v > m)\n                m = v;", "else if (v < m)\n                m = v;"),

@@ -5,7 +5,9 @@ the kernscope SwiGLU baseline, and the 7B-model FFN width 11008 at sequence
 2048 from the Triton Kernels benchmark table) and softmax workloads (X*: the
 kernscope softmax measurements at 512 rows of 1024, 128 and 8192 bf16, its
 65536-column fp16 accumulation case, and the RMSNorm headline shape 2048x4096
-as an HBM-bound softmax batch).  The softmax pages state no input
+as an HBM-bound softmax batch) and out-of-place residual RMSNorm workloads
+(R*: the Triton Kernels README usage example, fp16 [2048, 4096] with unit
+weight, and the headline shape in bf16).  The softmax pages state no input
 distribution; N(0, 1) logits are used, as in their usage example.
 
 This module draws random numbers and nothing else: it holds none of the
@@ -86,7 +88,7 @@ class Workload:
         parts = [f"{ops} {self.dtype} [{self.rows},{self.hidden}]", f"x ~{self.x}"]
         if self.outlier_frac:
             parts[-1] += f" with {self.outlier_frac:.0%} of elements x{self.outlier_scale:g}"
-        if self.residual is not None and "fused_add_rms_norm" in self.ops:
+        if self.residual is not None and ("fused_add_rms_norm" in self.ops or "rms_norm_residual" in self.ops):
             parts.append(f"residual ~{self.residual}")
         if self.weight is not None:
             parts.append(f"weight ~{self.weight}")
@@ -95,6 +97,7 @@ class Workload:
 
 
 RMS, FUSED, SWIGLU, SOFTMAX = "rms_norm", "fused_add_rms_norm", "silu_and_mul", "softmax"
+RESIDUAL = "rms_norm_residual"
 
 WORKLOADS: dict[str, Workload] = {
     # small case the oracle finishes in milliseconds
@@ -121,6 +124,14 @@ WORKLOADS: dict[str, Workload] = {
     "S1": Workload("S1", (SWIGLU,), "bfloat16", 512, 2 * 4096, normal(0, 1), None, 0.0, 6001, None),
     "S2": Workload("S2", (SWIGLU,), "bfloat16", 2048, 2 * 11008, normal(0, 1), None, 0.0, 6101, None),
     "S3": Workload("S3", (SWIGLU,), "float16", 2048, 2 * 4096, normal(0, 1), None, 0.0, 6201, None),
+    # out-of-place RMSNorm(x + residual) * w: the Triton Kernels README example
+    # (fp16 [2048, 4096], randn x and residual, unit weight) and the headline
+    # shape with the C3b distributions
+    "R1": Workload("R1", (RESIDUAL,), "float16", 2048, 4096, normal(0, 1), normal(1, 0), 1e-6, 8001, 8003,
+                   residual=normal(0, 1), seed_r=8002),
+    "R2": Workload("R2", (RESIDUAL,), "bfloat16", 2048, 4096, normal(0, 1), uniform(0.5, 1.5), 1e-5, 8101, 8103,
+                   residual=normal(0, 0.5), seed_r=8102, outlier_frac=0.01, outlier_scale=100.0,
+                   seed_outlier=8104),
     # softmax over the last dimension
     "X1": Workload("X1", (SOFTMAX,), "bfloat16", 512, 1024, normal(0, 1), None, 0.0, 7001, None),
     "X2": Workload("X2", (SOFTMAX,), "bfloat16", 512, 128, normal(0, 1), None, 0.0, 7101, None),
