@@ -1,5 +1,5 @@
-"""CPU oracle for RMSNorm, fused residual-add RMSNorm (in place and out of
-place), SwiGLU and softmax.
+"""CPU oracle for RMSNorm (forward and backward), fused residual-add RMSNorm
+(in place and out of place), SwiGLU and softmax.
 
 TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package; the GPU product path
@@ -53,6 +53,8 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_softmax.argtypes = [c_int, vp, vp, i64, i64]
     lib.oracle_rms_norm_residual.argtypes = [c_int, vp, vp, vp, vp, i64, i64, c_float]
     lib.oracle_rms_norm_residual.restype = c_int
+    lib.oracle_rms_norm_backward.argtypes = [c_int, vp, vp, vp, vp, vp, i64, i64, c_float]
+    lib.oracle_rms_norm_backward.restype = c_int
     lib.oracle_softmax.restype = c_int
     return lib
 
@@ -124,6 +126,22 @@ def rms_norm_residual(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor, 
     if st != 0:
         raise ValueError(f"oracle_rms_norm_residual failed with status {st}")
     return out
+
+
+def rms_norm_backward(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                      lib: ctypes.CDLL | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Gradients (dx, dw) of rms_norm(x, w, eps) for the incoming gradient dy."""
+    lib = lib or load()
+    rows, hidden = _check_rows(x, w)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous() or dy.device.type != "cpu":
+        raise ValueError("dy must match x")
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    st = lib.oracle_rms_norm_backward(_DTYPE_CODE[x.dtype], dy.data_ptr(), x.data_ptr(), w.data_ptr(),
+                                      dx.data_ptr(), dw.data_ptr(), rows, hidden, eps)
+    if st != 0:
+        raise ValueError(f"oracle_rms_norm_backward failed with status {st}")
+    return dx, dw
 
 
 def silu_and_mul(x: torch.Tensor, lib: ctypes.CDLL | None = None) -> torch.Tensor:

@@ -83,6 +83,23 @@ def rms_norm_residual(x: list[list[float]], r: list[list[float]], w: list[float]
     return rms_norm(s, w, eps32, fmt)
 
 
+def rms_norm_backward(dy: list[list[float]], x: list[list[float]], w: list[float], eps32: float,
+                      fmt: str) -> tuple[list[list[float]], list[float]]:
+    """Gradients of y_j = x_j rho w_j, rho = (sum x^2 / H + eps)^(-1/2), for the
+    incoming dy: exact rationals with an 80-digit rho, each rounded once."""
+    hidden = len(w)
+    dx, dw = [], [Fraction(0)] * hidden
+    for grow, row in zip(dy, x):
+        m = sum(Fraction(v) ** 2 for v in row) / hidden + Fraction(eps32)
+        rho = _inv_sqrt(m)
+        dot = sum(Fraction(g) * Fraction(wj) * Fraction(v) for g, wj, v in zip(grow, w, row))
+        coef = rho ** 3 * dot / hidden
+        dx.append([round_to(rho * Fraction(g) * Fraction(wj) - coef * Fraction(v), fmt)
+                   for g, wj, v in zip(grow, w, row)])
+        dw = [acc + Fraction(g) * Fraction(v) * rho for acc, g, v in zip(dw, grow, row)]
+    return dx, [round_to(v, fmt) for v in dw]
+
+
 def _sigmoid(g: Fraction) -> Fraction:
     with localcontext() as ctx:
         ctx.prec = 80

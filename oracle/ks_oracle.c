@@ -1,7 +1,7 @@
 /*
- * CPU oracle for RMSNorm row normalisation, the fused residual-add variant
- * (in place, and out of place), the SwiGLU activation and softmax over the
- * last dimension.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU oracle for RMSNorm row normalisation (forward and backward), the
+ * fused residual-add variant (in place, and out of place), the SwiGLU
+ * activation and softmax over the last dimension.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
  * benchmark's CPU-baseline leg load this file's library; the GPU library never
  * does, and the two share no code, headers or constants.
  *
@@ -262,6 +262,62 @@ int oracle_rms_norm_residual(int dtype, const void *x, const void *residual, con
         }
     }
     free(s);
+    return ORACLE_OK;
+}
+
+/* round a double v once to the dtype (ties to even) and store it as element i */
+static void store_elem_exact(int dtype, void *p, int64_t i, double v)
+{
+    if (dtype == ORACLE_F32) {
+        ((float *)p)[i] = (float)v;
+        return;
+    }
+    const format_t *f = format_of(dtype);
+    ((uint16_t *)p)[i] = encode_format(round_to_format(v, f), f);
+}
+
+/* RMSNorm backward.  No page states a backward contract; the kernscope
+   README says the PyTorch reference of rms_norm supports autograd, so the
+   gradients are those of the forward contract
+       y_j = x_j * rho * w_j,   rho = (sum_k x_k^2 / H + eps)^(-1/2),
+   for an incoming gradient dy (the final cast passes gradients through):
+       dx_j = rho * dy_j * w_j - (rho^3 / H) * x_j * sum_k dy_k * w_k * x_k
+       dw_j = sum over rows of dy_j * x_j * rho.
+   Readings: the gradients are evaluated exactly (in double, from the widened
+   inputs and eps rounded to fp32) and rounded once to the dtype; dw may be
+   NULL (not wanted); for rows == 0, dw is zero. */
+int oracle_rms_norm_backward(int dtype, const void *dy, const void *x, const void *w, void *dx, void *dw,
+                             int64_t rows, int64_t hidden, float eps)
+{
+    int st = check_args(dtype, rows, hidden, eps);
+    if (st != ORACLE_OK)
+        return st;
+    double *dw_sum = (double *)calloc((size_t)hidden, sizeof(double));
+    if (!dw_sum)
+        return ORACLE_NO_MEMORY;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t base = r * hidden;
+        double sum_sq = 0.0, dot = 0.0;
+        for (int64_t j = 0; j < hidden; ++j) {
+            double xv = (double)load_elem(dtype, x, base + j);
+            double gv = (double)load_elem(dtype, dy, base + j) * (double)load_elem(dtype, w, j);
+            sum_sq += xv * xv;
+            dot += gv * xv;
+        }
+        double rho = 1.0 / sqrt(sum_sq / (double)hidden + (double)eps);
+        double coef = rho * rho * rho * dot / (double)hidden;
+        for (int64_t j = 0; j < hidden; ++j) {
+            double xv = (double)load_elem(dtype, x, base + j);
+            double dyv = (double)load_elem(dtype, dy, base + j);
+            double grad = rho * dyv * (double)load_elem(dtype, w, j) - coef * xv;
+            store_elem_exact(dtype, dx, base + j, grad);
+            dw_sum[j] += dyv * xv * rho;
+        }
+    }
+    if (dw != NULL)
+        for (int64_t j = 0; j < hidden; ++j)
+            store_elem_exact(dtype, dw, j, dw_sum[j]);
+    free(dw_sum);
     return ORACLE_OK;
 }
 

@@ -341,6 +341,99 @@ def pin_residual_out_of_place(lib) -> None:
 
 
 # --------------------------------------------------------------------------
+# RMSNorm backward: the gradients of the forward contract (no page states a
+# backward contract; the kernscope reference supports autograd)
+# --------------------------------------------------------------------------
+def _autograd64(dy, x, w, eps32):
+    """torch autograd, in float64, of the forward formula on the widened inputs."""
+    xd = x.double().requires_grad_()
+    wd = w.double().requires_grad_()
+    y = xd * torch.rsqrt(xd.pow(2).mean(-1, keepdim=True) + eps32) * wd
+    y.backward(dy.double())
+    return xd.grad, wd.grad
+
+
+def _round_like(v: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    return v.to(torch.float32).to(dtype)
+
+
+def pin_backward_autograd(lib) -> None:
+    """fp64 autograd (a different route to the same derivative) within 1 ulp."""
+    for dtype in ("bfloat16", "float16", "float32"):
+        for i, shape in enumerate([(3, 7), (4, 64), (2, 3, 100), (16, 1000)]):
+            inp = workloads.random_case(shape, dtype, 600 + i)
+            x, w = inp["x"], inp["weight"]
+            dy = workloads.random_case(shape, dtype, 650 + i)["residual"]
+            eps32 = float(np.float32(1e-5))
+            gx, gw = oracle.rms_norm_backward(dy, x, w, 1e-5, lib=lib)
+            ax, aw = _autograd64(dy.reshape(-1, shape[-1]), x.reshape(-1, shape[-1]), w, eps32)
+            ax = _round_like(ax.reshape(shape), x.dtype)
+            aw = _round_like(aw, x.dtype)
+            assert int(ulp_distance(gx, ax).max()) <= 1, (dtype, shape)
+            assert int(ulp_distance(gw, aw).max()) <= 1, (dtype, shape)
+            assert float((ulp_distance(gx, ax) == 0).double().mean()) >= 0.99
+
+
+def pin_backward_brute_force(lib) -> None:
+    for dtype in ("bfloat16", "float16", "float32"):
+        for i, shape in enumerate([(5,), (2, 3, 5), (3, 17), (2, 64)]):
+            inp = workloads.random_case(shape, dtype, 700 + i)
+            x, w = inp["x"], inp["weight"]
+            dy = workloads.random_case(shape, dtype, 750 + i)["residual"]
+            eps32 = float(np.float32(1e-6))
+            bx, bw = brute64.rms_norm_backward(_values(dy), _values(x), [float(v) for v in w.float()], eps32, dtype)
+            gx, gw = oracle.rms_norm_backward(dy, x, w, 1e-6, lib=lib)
+            assert int(ulp_distance(gx, _from_values(bx, x.dtype, shape)).max()) <= 1
+            assert int(ulp_distance(gw, _from_values([bw], x.dtype, (1, shape[-1])).reshape(-1)).max()) <= 1
+
+
+def pin_backward_identities(lib) -> None:
+    """Scale invariance up to eps: sum_j dx_j x_j = eps rho^3 sum_j dy_j w_j x_j;
+    a single row with dy = 1 has dw = x rho, the forward output with unit
+    weight; finite differences of the (pinned) forward oracle; zero dy gives
+    zero gradients; dy scales the gradients exactly; no rows: dw = 0."""
+    inp = workloads.random_case((6, 300), "float32", 801)
+    x, w = inp["x"], inp["weight"]
+    dy = workloads.random_case((6, 300), "float32", 802)["residual"]
+    eps = 1e-2                       # large enough that the identity's right side is not tiny
+    eps32 = float(np.float32(eps))
+    gx, gw = oracle.rms_norm_backward(dy, x, w, eps, lib=lib)
+    xd, wd, dyd = x.double(), w.double(), dy.double()
+    rho = 1.0 / torch.sqrt(xd.pow(2).mean(-1) + eps32)
+    lhs = (gx.double() * xd).sum(-1)
+    rhs = eps32 * rho ** 3 * (dyd * wd * xd).sum(-1)
+    bound = (gx.double() * xd).abs().sum(-1) * 2.0 ** -23 + rhs.abs() * 1e-12
+    assert bool(((lhs - rhs).abs() <= bound).all()), (lhs - rhs, bound)
+    one = torch.ones(1, 300, dtype=torch.float32)
+    _, g1 = oracle.rms_norm_backward(one, x[:1].contiguous(), w, eps, lib=lib)
+    fwd = oracle.rms_norm(x[:1].contiguous(), torch.ones(300, dtype=torch.float32), eps, lib=lib).reshape(-1)
+    assert int(ulp_distance(g1, fwd).max()) <= 1
+    # central differences of L(x) = sum(dy * y(x)) with the forward oracle in fp32
+    h = 2.0 ** -7
+    for j in (0, 17, 299):
+        xp, xm = x[2:3].clone(), x[2:3].clone()
+        xp[0, j] += h
+        xm[0, j] -= h
+        lp = (dyd[2:3] * oracle.rms_norm(xp, w, eps, lib=lib).double()).sum()
+        lm = (dyd[2:3] * oracle.rms_norm(xm, w, eps, lib=lib).double()).sum()
+        fd = float((lp - lm) / (2 * h))
+        assert abs(fd - float(gx[2, j])) <= 2e-3 * (abs(float(gx[2, j])) + 0.05), (j, fd, float(gx[2, j]))
+    zx, zw = oracle.rms_norm_backward(torch.zeros_like(dy), x, w, eps, lib=lib)
+    assert bool((zx == 0).all()) and bool((zw == 0).all())
+    for dtype in (torch.bfloat16, torch.float16):
+        xb, wb, db = x.to(dtype), w.to(dtype), (dy * 0.25).to(dtype)
+        ax, aw = oracle.rms_norm_backward(db, xb, wb, eps, lib=lib)
+        bx, bw = oracle.rms_norm_backward((db.float() * 4).to(dtype), xb, wb, eps, lib=lib)
+        # exact where the smaller gradient is a normal number (subnormals have a
+        # fixed quantum, so scaling them is not exact)
+        normal = ax.float().abs() >= torch.finfo(dtype).tiny
+        check_bitexact(bx[normal], (ax.float() * 4).to(dtype)[normal])
+        check_bitexact(bw, (aw.float() * 4).to(dtype))
+    ex, ew = oracle.rms_norm_backward(torch.zeros(0, 300), torch.zeros(0, 300), w, eps, lib=lib)
+    assert ex.shape == (0, 300) and bool((ew == 0).all())
+
+
+# --------------------------------------------------------------------------
 # SwiGLU (kernscope "Numerical contract" > "SwiGLU activation")
 # --------------------------------------------------------------------------
 SWIGLU_SHAPES = [(2,), (3, 10), (2, 3, 14), (2, 64), (3, 402)]
@@ -525,7 +618,8 @@ ALL_PINS = [
     pin_batch_invariance, pin_casts, pin_library_formula, pin_unrounded_sum, pin_zeros_and_empty,
     pin_swiglu_brute_force, pin_swiglu_library, pin_swiglu_closed_forms,
     pin_softmax_brute_force, pin_softmax_closed_forms, pin_softmax_invariants, pin_softmax_nonfinite,
-    pin_softmax_library, pin_residual_out_of_place,
+    pin_softmax_library, pin_residual_out_of_place, pin_backward_autograd, pin_backward_brute_force,
+    pin_backward_identities,
 ]
 
 

@@ -55,6 +55,20 @@ MUTANTS = [
      "            s[j] = load_elem(dtype, out, base + j);\n            sum_sq += (double)s[j] * (double)s[j];"),
     ("residual_oop_no_weight", "store_elem(dtype, out, base + j, scaled * load_elem(dtype, w, j));",
      "store_elem(dtype, out, base + j, scaled);"),
+    ("backward_sign", "double grad = rho * dyv * (double)load_elem(dtype, w, j) - coef * xv;",
+     "double grad = rho * dyv * (double)load_elem(dtype, w, j) + coef * xv;"),
+    ("backward_rho_squared", "double coef = rho * rho * rho * dot / (double)hidden;",
+     "double coef = rho * rho * dot / (double)hidden;"),
+    ("backward_dot_without_weight",
+     "double gv = (double)load_elem(dtype, dy, base + j) * (double)load_elem(dtype, w, j);",
+     "double gv = (double)load_elem(dtype, dy, base + j);"),
+    ("backward_dw_without_rho", "dw_sum[j] += dyv * xv * rho;", "dw_sum[j] += dyv * xv;"),
+    ("backward_dw_times_weight", "dw_sum[j] += dyv * xv * rho;",
+     "dw_sum[j] += dyv * xv * rho * (double)load_elem(dtype, w, j);"),
+    ("backward_eps_dropped", "double rho = 1.0 / sqrt(sum_sq / (double)hidden + (double)eps);",
+     "double rho = 1.0 / sqrt(sum_sq / (double)hidden);"),
+    ("backward_grad_without_weight", "double grad = rho * dyv * (double)load_elem(dtype, w, j) - coef * xv;",
+     "double grad = rho * dyv - coef * xv;"),
     ("softmax_no_max_shift", "float z = load_elem(dtype, x, base + j) - m;",
      "float z = load_elem(dtype, x, base + j);"),
     ("softmax_max_never_updated", "else if (v > m)\n                m = v;", "else if (v < m)\n                m = v;"),
