@@ -73,11 +73,14 @@ def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
     once; fused: read x and residual, write both, read the weight; silu_and_mul
     (hidden = input width 2D): read x, write the D-wide output; softmax: read x,
     write out; rms_norm_residual: read x and residual, write out, read the
-    weight."""
+    weight; rms_norm_backward: read x and dy, write dx, read the weight and
+    write its gradient (the fp32 workspace of partial sums is extra)."""
     if op == "silu_and_mul":
         return (rows * hidden + rows * (hidden // 2)) * esize
     if op == "softmax":
         return 2 * rows * hidden * esize
+    if op == "rms_norm_backward":
+        return (3 * rows * hidden + 2 * hidden) * esize
     per_row = {"rms_norm": 2, "rms_norm_residual": 3}.get(op, 4)
     return (per_row * rows * hidden + hidden) * esize
 
@@ -133,7 +136,7 @@ def log(*a):
 def parity_gate(wl, inp, ks, oracle_mod) -> dict:
     """GPU vs oracle on the full batch (or on sampled rows of a large one) before any timing."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from compare import check_bitexact, check_normalised
+    from compare import backward_magnitudes, check_bitexact, check_gradient, check_normalised
 
     if wl.rows * wl.hidden <= FULL_PARITY_ELEMS:
         idx = None
@@ -154,6 +157,16 @@ def parity_gate(wl, inp, ks, oracle_mod) -> dict:
         ref = oracle_mod.silu_and_mul(pick(inp["x"]))
         st = check_normalised(pick(y.cpu()), ref, 0.999)
         out["silu_and_mul"] = {"max_ulp": st.max_ulp, "exact_match": round(st.exact_rate, 6)}
+        return out
+    if "rms_norm_backward" in wl.ops:
+        gx, gw = ks.rms_norm_backward(inp["residual"].cuda(), inp["x"].cuda(), inp["weight"].cuda(), wl.eps)
+        torch.cuda.synchronize()
+        rx, rw = oracle_mod.rms_norm_backward(inp["residual"], inp["x"], inp["weight"], wl.eps)
+        mdx, mdw = backward_magnitudes(inp["residual"], inp["x"], inp["weight"], wl.eps)
+        st = check_gradient(gx.cpu(), rx, mdx, 0.99)
+        sw = check_gradient(gw.cpu(), rw, mdw)
+        out["rms_norm_backward"] = {"dx_max_ulp": st.max_ulp, "dx_exact_match": round(st.exact_rate, 6),
+                                    "dw_max_ulp": sw.max_ulp, "dw_exact_match": round(sw.exact_rate, 6)}
         return out
     if "softmax" in wl.ops:
         y = ks.softmax(inp["x"].cuda())
@@ -204,7 +217,7 @@ class Rig:
         esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
         self.tensor_bytes = wl.rows * wl.hidden * esize
         footprint = {"rms_norm": 2.0, "fused_add_rms_norm": 2.0, "silu_and_mul": 1.5, "softmax": 2.0,
-                     "rms_norm_residual": 3.0}
+                     "rms_norm_residual": 3.0, "rms_norm_backward": 3.0}
         per_set = int(sum(footprint[op] for op in wl.ops) * self.tensor_bytes)
         # enough copies to pass through more than the last-level cache between
         # two uses of one copy; capped for tiny (launch-bound) batches
@@ -218,6 +231,11 @@ class Rig:
             if "silu_and_mul" in wl.ops:
                 s["sx"] = x0.clone()
                 s["sout"] = torch.empty(wl.rows, wl.hidden // 2, dtype=x0.dtype, device=x0.device)
+            if "rms_norm_backward" in wl.ops:
+                s["bx"] = x0.clone()
+                s["bdy"] = r0.clone()
+                s["bdx"] = torch.empty_like(x0)
+                s["bdw"] = torch.empty_like(self.w)
             if "rms_norm_residual" in wl.ops:
                 s["ox"] = x0.clone()
                 s["or"] = r0.clone()
@@ -233,6 +251,9 @@ class Rig:
                 s["fr"] = r0.clone()
             self.sets.append(s)
         del x0, r0
+        if "rms_norm_backward" in wl.ops:
+            self.workspace = torch.empty(ks.ks_rms_norm_backward_workspace_size(wl.rows, wl.hidden),
+                                         dtype=torch.uint8, device="cuda")
         self.rotation_mib = self.nsets * per_set / 2**20
         self.stream = torch.cuda.Stream()
         torch.cuda.synchronize()
@@ -247,6 +268,9 @@ class Rig:
             self.ks.softmax(s["mx"], out=s["mout"])
         elif op == "rms_norm_residual":
             self.ks.rms_norm_residual(s["ox"], s["or"], self.w, self.wl.eps, out=s["oout"])
+        elif op == "rms_norm_backward":
+            self.ks.rms_norm_backward(s["bdy"], s["bx"], self.w, self.wl.eps, workspace=self.workspace,
+                                      dx=s["bdx"], dweight=s["bdw"])
         else:
             self.ks.silu_and_mul(s["sx"], out=s["sout"])
 
@@ -278,7 +302,7 @@ class Rig:
     def copy_reference(self, reps: int) -> dict:
         """The runtime's device-to-device copy of one batch-sized tensor per launch."""
         n = self.nsets
-        srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx", s.get("ox"))))) for s in self.sets]
+        srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx", s.get("ox", s.get("bx")))))) for s in self.sets]
         dsts = [torch.empty_like(t) for t in srcs]
         ms = self.timed_graph(lambda i: dsts[i % n].copy_(srcs[i % n]), n, reps)
         del dsts
@@ -336,6 +360,8 @@ def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
             oracle_mod.softmax(inp["x"])
         if "rms_norm_residual" in wl.ops:
             oracle_mod.rms_norm_residual(inp["x"], inp["residual"], inp["weight"], wl.eps)
+        if "rms_norm_backward" in wl.ops:
+            oracle_mod.rms_norm_backward(inp["residual"], inp["x"], inp["weight"], wl.eps)
         steps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -417,7 +443,7 @@ def kernel_op(name: str) -> str | None:
     """The operation a demangled kernel name belongs to (None for other kernels)."""
     if "ks::" not in name:
         return None
-    for op in ("fused_add_rms_norm", "rms_norm_residual", "rms_norm", "silu_and_mul", "softmax"):
+    for op in ("fused_add_rms_norm", "rms_norm_residual", "rms_norm_backward", "rms_norm", "silu_and_mul", "softmax"):
         if op in name:
             return op
     return None
@@ -467,7 +493,10 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
                                                     "write_scale": round(write_scale, 5),
                                                     "copy_bytes": calib_bytes}
     data.setdefault("kernels", {})[workload] = kernels
-    data.setdefault("workloads", {})[workload] = {k["op"]: k["traffic_bytes"] for k in kernels.values()}
+    per_op: dict[str, int] = {}
+    for k in kernels.values():           # an op of several kernels moves their sum
+        per_op[k["op"]] = per_op.get(k["op"], 0) + k["traffic_bytes"]
+    data.setdefault("workloads", {})[workload] = per_op
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(data, f, indent=1)
     print(json.dumps({"workload": workload, "calibration": data["calibration"][workload], "kernels": kernels},

@@ -1,6 +1,7 @@
 /*
- * ks_norm: RMSNorm row normalisation, fused residual-add RMSNorm, the SwiGLU
- * activation and softmax for AMD Instinct MI355X (gfx950).  C ABI.
+ * ks_norm: RMSNorm row normalisation (forward and backward), fused
+ * residual-add RMSNorm, the SwiGLU activation and softmax for AMD Instinct
+ * MI355X (gfx950).  C ABI.
  *
  * The operations are the ones defined in the kernscope README, section
  * "Numerical contract" (subsections "RMSNorm", "Fused residual-add RMSNorm",
@@ -17,8 +18,9 @@
  *            (row stride = hidden elements); weight is a dense [hidden] array.
  *            All buffers hold the same dtype.  There are no stride arguments.
  * Memory     Every pointer is a device pointer owned by the caller.  The
- *            library never allocates, frees, copies or synchronises.  weight
- *            is only read.  Any alignment is accepted; 16-byte aligned
+ *            library never allocates, frees, copies or synchronises (scratch
+ *            memory, where a call needs it, is a caller-owned workspace).
+ *            weight is only read.  Any alignment is accepted; 16-byte aligned
  *            buffers with hidden * sizeof(element) a multiple of 16 take the
  *            vector path, others a narrower path with identical results.
  * Streams    Work is enqueued on `stream` (0 = the default stream) and the
@@ -73,7 +75,8 @@ typedef enum {
     KS_OP_FUSED_ADD_RMS_NORM = 1,
     KS_OP_SILU_AND_MUL = 2,
     KS_OP_SOFTMAX = 3,
-    KS_OP_RMS_NORM_RESIDUAL = 4
+    KS_OP_RMS_NORM_RESIDUAL = 4,
+    KS_OP_RMS_NORM_BACKWARD = 5
 } ks_op_t;
 
 /* How a launch maps rows onto threads.
@@ -155,6 +158,43 @@ ks_status_t ks_rms_norm_residual(void *out, const void *x, const void *residual,
 ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residual, const void *weight,
                                     int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
                                     const ks_plan_t *plan, hipStream_t stream);
+
+/*
+ * RMSNorm backward: the gradients of ks_rms_norm's contract.  No page states
+ * a backward contract; the kernscope README's PyTorch reference of rms_norm
+ * supports autograd, so these are the derivatives of
+ *   y_j = x_j * rho * w_j,   rho = rsqrt(mean(x^2) + eps)
+ * (the final cast passes gradients through), for an incoming gradient dy:
+ *   dx_j = rho * (g_j - c * x_j),  g_j = dy_j * w_j,  c = rho^2 * sum_k(g_k * x_k) / H
+ *   dw_j = sum over rows of dy_j * (x_j * rho)
+ * in fp32 (rho is bit-identical to the forward's scale), rounded to the dtype.
+ * dx         [rows, hidden] output.
+ * dweight    [hidden] output, or NULL when the weight gradient is not wanted.
+ *            With rows == 0 it is set to zero (one launch).
+ * dy, x      [rows, hidden], read only.    weight  [hidden], read only.
+ * workspace  fp32 scratch owned by the caller, at least
+ *            ks_rms_norm_backward_workspace_size(rows, hidden) bytes, 4-byte
+ *            aligned; needed only when dweight is not NULL (else may be NULL).
+ *            Its contents on entry do not matter and are left undefined.
+ * Overlaps: dx, dweight and workspace must not overlap each other or any
+ * input (KS_ERROR_OVERLAP); the inputs may overlap each other.
+ * dx does not depend on the plan or the batch; dw is summed in a fixed order
+ * (deterministic for a given plan and batch size).  A workspace that is
+ * missing or too small is KS_ERROR_INVALID_VALUE.  Errors, streams and plans
+ * as above (op KS_OP_RMS_NORM_BACKWARD: vector plans use 1024-thread
+ * workgroups, at most 4 pieces per lane for fp32 and 2 for 16-bit dtypes,
+ * non-temporal hints on).
+ */
+ks_status_t ks_rms_norm_backward_workspace_size(int64_t rows, int64_t hidden, size_t *bytes);
+
+ks_status_t ks_rms_norm_backward(void *dx, void *dweight, const void *dy, const void *x, const void *weight,
+                                 int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, const void *x, const void *weight,
+                                    int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
+                                    void *workspace, size_t workspace_bytes, const ks_plan_t *plan,
+                                    hipStream_t stream);
 
 /*
  * The launch plan the calls of this header use for this op, dtype, batch and

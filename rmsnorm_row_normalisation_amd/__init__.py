@@ -1,5 +1,5 @@
-"""RMSNorm, fused residual-add RMSNorm (in place and out of place), SwiGLU and
-softmax for MI355X (gfx950).
+"""RMSNorm (forward and backward), fused residual-add RMSNorm (in place and out
+of place), SwiGLU and softmax for MI355X (gfx950).
 
 The computation lives in ``libks_norm.so`` (hand-written HIP kernels behind a
 C ABI, ``include/ks_norm.h``); this package is its thin Python binding.
@@ -30,6 +30,10 @@ from .binding import (  # noqa: F401
     rms_norm_residual,
     ks_rms_norm_residual,
     ks_rms_norm_residual_ex,
+    rms_norm_backward,
+    ks_rms_norm_backward,
+    ks_rms_norm_backward_ex,
+    ks_rms_norm_backward_workspace_size,
 )
 
 __version__ = "0.1.0"

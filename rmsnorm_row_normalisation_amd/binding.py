@@ -2,7 +2,8 @@
 
 The ``ks_*`` functions mirror the C ABI in ``include/ks_norm.h`` one to one
 (raw device pointers as ints).  ``rms_norm``, ``fused_add_rms_norm``,
-``rms_norm_residual``, ``silu_and_mul`` and ``softmax`` are the tensor-level calls with the kernscope API shape
+``rms_norm_residual``, ``rms_norm_backward``, ``silu_and_mul`` and ``softmax``
+are the tensor-level calls with the kernscope API shape
 (README, "API contract" and "Inputs"): they check devices, dtypes, shapes, contiguity and
 ``requires_grad`` (the accelerator kernels are inference-only), then pass the
 tensors' device pointers and torch's current HIP stream to the library.
@@ -20,7 +21,8 @@ DEFAULT_LIB = os.path.join(_PKG, "libks_norm.so")
 
 KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP = range(5)
 KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX, KS_OP_RMS_NORM_RESIDUAL = 0, 1, 2, 3, 4
+(KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX, KS_OP_RMS_NORM_RESIDUAL,
+ KS_OP_RMS_NORM_BACKWARD) = range(6)
 KS_PATH_VECTOR, KS_PATH_GENERIC = 0, 1
 
 
@@ -90,6 +92,11 @@ def lib() -> ctypes.CDLL:
         h.ks_silu_and_mul_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_softmax.argtypes = [vp, vp, i64, i64, i32, vp]
         h.ks_rms_norm_residual.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, vp]
+        sz = ctypes.c_size_t
+        h.ks_rms_norm_backward_workspace_size.argtypes = [i64, i64, ctypes.POINTER(sz)]
+        h.ks_rms_norm_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, sz, vp]
+        h.ks_rms_norm_backward_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, f32, i32, vp, sz, ctypes.POINTER(Plan),
+                                              vp]
         h.ks_rms_norm_residual_ex.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_softmax_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_status_string.argtypes = [i32]
@@ -98,7 +105,8 @@ def lib() -> ctypes.CDLL:
         h.ks_version.restype = ctypes.c_char_p
         for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
                      "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
-                     "ks_softmax_ex", "ks_rms_norm_residual", "ks_rms_norm_residual_ex"):
+                     "ks_softmax_ex", "ks_rms_norm_residual", "ks_rms_norm_residual_ex",
+                     "ks_rms_norm_backward_workspace_size", "ks_rms_norm_backward", "ks_rms_norm_backward_ex"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -150,6 +158,25 @@ def ks_rms_norm_residual_ex(out: int, x: int, residual: int, weight: int, rows: 
                             dtype: int, plan: Plan | None, stream: int) -> int:
     return lib().ks_rms_norm_residual_ex(out, x, residual, weight, rows, hidden, eps, dtype,
                                          ctypes.byref(plan) if plan is not None else None, stream)
+
+
+def ks_rms_norm_backward_workspace_size(rows: int, hidden: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ks_rms_norm_backward_workspace_size(rows, hidden, ctypes.byref(n)),
+           "ks_rms_norm_backward_workspace_size")
+    return n.value
+
+
+def ks_rms_norm_backward(dx: int, dw: int, dy: int, x: int, weight: int, rows: int, hidden: int, eps: float,
+                         dtype: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    return lib().ks_rms_norm_backward(dx, dw, dy, x, weight, rows, hidden, eps, dtype, workspace, workspace_bytes,
+                                      stream)
+
+
+def ks_rms_norm_backward_ex(dx: int, dw: int, dy: int, x: int, weight: int, rows: int, hidden: int, eps: float,
+                            dtype: int, workspace: int, workspace_bytes: int, plan: Plan | None, stream: int) -> int:
+    return lib().ks_rms_norm_backward_ex(dx, dw, dy, x, weight, rows, hidden, eps, dtype, workspace,
+                                         workspace_bytes, ctypes.byref(plan) if plan is not None else None, stream)
 
 
 def ks_silu_and_mul(out: int, x: int, rows: int, d: int, dtype: int, stream: int) -> int:
@@ -257,6 +284,44 @@ def rms_norm_residual(x: torch.Tensor, residual: torch.Tensor, weight: torch.Ten
     return out
 
 
+def rms_norm_backward(dy: torch.Tensor, x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
+                      weight_grad: bool = True, plan: Plan | None = None, workspace: torch.Tensor | None = None,
+                      dx: torch.Tensor | None = None,
+                      dweight: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor | None]:
+    """Gradients (dx, dweight) of rms_norm(x, weight, eps) for the incoming gradient dy.
+    dweight is None when ``weight_grad`` is False.  The fp32 workspace the weight
+    gradient needs is allocated through torch unless given (a uint8 device tensor
+    of at least ks_rms_norm_backward_workspace_size bytes)."""
+    rows, hidden = _check_tensors("rms_norm_backward", x, weight, dy)
+    if dy.shape != x.shape:
+        raise ValueError("rms_norm_backward: dy must have the shape of x")
+    if dx is None:
+        dx = torch.empty_like(x)
+    else:
+        _check_tensors("rms_norm_backward", dx, weight)
+        if dx.shape != x.shape:
+            raise ValueError("rms_norm_backward: dx must have the shape of x")
+    if not weight_grad:
+        dw = None
+    elif dweight is None:
+        dw = torch.empty_like(weight)
+    else:
+        _check_tensors("rms_norm_backward", x, dweight)
+        dw = dweight
+    need = ks_rms_norm_backward_workspace_size(rows, hidden) if weight_grad else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    elif workspace.device != x.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"rms_norm_backward: workspace must be a contiguous tensor of >= {need} bytes on {x.device}")
+    with torch.cuda.device(x.device):
+        st = ks_rms_norm_backward_ex(dx.data_ptr(), dw.data_ptr() if dw is not None else None, dy.data_ptr(),
+                                     x.data_ptr(), weight.data_ptr(), rows, hidden, float(eps), KS_DTYPE[x.dtype],
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(), plan,
+                                     _stream(x))
+    _check(st, "ks_rms_norm_backward")
+    return dx, dw
+
+
 def silu_and_mul(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
     """SwiGLU of x with shape (..., 2D): a new (..., D) tensor (kernscope "SwiGLU activation")."""
     if x.dtype not in KS_DTYPE:
@@ -312,5 +377,5 @@ def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: b
     For silu_and_mul, ``hidden`` is the output width D."""
     code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM,
             "silu_and_mul": KS_OP_SILU_AND_MUL, "softmax": KS_OP_SOFTMAX,
-            "rms_norm_residual": KS_OP_RMS_NORM_RESIDUAL}[op]
+            "rms_norm_residual": KS_OP_RMS_NORM_RESIDUAL, "rms_norm_backward": KS_OP_RMS_NORM_BACKWARD}[op]
     return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned)

@@ -1,6 +1,7 @@
 // C ABI of ks_norm: argument validation, overlap checks, the launch policy
-// and the calls into the per-dtype kernel units (RMSNorm, fused residual-add
-// RMSNorm in place and out of place, SwiGLU, softmax).  Validation and the policy
+// and the calls into the per-dtype kernel units (RMSNorm forward and
+// backward, fused residual-add RMSNorm in place and out of place, SwiGLU,
+// softmax).  Validation and the policy
 // make no HIP call, so they run (and are tested) on machines without a GPU.
 #include <math.h>
 #include <stdint.h>
@@ -38,9 +39,12 @@ ks_status_t check_sizes(ks_dtype_t dtype, int64_t rows, int64_t hidden, float ep
     return KS_SUCCESS;
 }
 
-// Half-open byte ranges [a, a + n) and [b, b + m) share a byte.
+// Half-open byte ranges [a, a + n) and [b, b + m) share a byte (an empty
+// range shares none).
 bool overlaps(const void *a, int64_t n, const void *b, int64_t m)
 {
+    if (n <= 0 || m <= 0)
+        return false;
     const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
     return pa < pb + (uintptr_t)m && pb < pa + (uintptr_t)n;
 }
@@ -97,6 +101,27 @@ int64_t pow2_ceil(int64_t v)
     return p;
 }
 
+// RMSNorm backward (vector path): 1024-thread workgroups that walk row
+// groups, at most 4 (fp32) or 2 (16-bit) pieces per lane, the team the power
+// of two covering the row (8..1024 lanes); x and dy loads and dx stores
+// non-temporal.
+ks_plan_t backward_vector_plan(int64_t nvec, int vec_elems, int max_vpt)
+{
+    ks_plan_t plan;
+    memset(&plan, 0, sizeof(plan));
+    int64_t tpr = pow2_ceil((nvec + max_vpt - 1) / max_vpt);
+    tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > ks::kMaxTpr ? ks::kMaxTpr : tpr;
+    plan.path = KS_PATH_VECTOR;
+    plan.threads_per_row = (int32_t)tpr;
+    plan.vectors_per_thread = (int32_t)((nvec + tpr - 1) / tpr);
+    plan.elems_per_access = vec_elems;
+    plan.block_threads = ks::kBwdBlock;
+    plan.rows_per_block = ks::kBwdBlock / (int32_t)tpr;
+    plan.load_nt = 1;
+    plan.store_nt = 1;
+    return plan;
+}
+
 ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned)
 {
     ks_plan_t plan;
@@ -105,7 +130,10 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     const int64_t row_bytes = hidden * esize;
     const int vec_elems = (int)(16 / esize);
     const int64_t nvec = row_bytes / 16;
-    if (aligned && row_bytes % 16 == 0 && nvec <= (int64_t)kPolicyMaxTpr * ks::kMaxVpt) {
+    const int bwd_vpt = ks::bwd_max_vpt((int)esize);
+    if (op == KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * bwd_vpt)
+        return backward_vector_plan(nvec, vec_elems, bwd_vpt);
+    if (op != KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)kPolicyMaxTpr * ks::kMaxVpt) {
         const int64_t pieces = rows * nvec;
         const bool swiglu = op == KS_OP_SILU_AND_MUL;
         const bool adds_residual = op == KS_OP_FUSED_ADD_RMS_NORM || op == KS_OP_RMS_NORM_RESIDUAL;
@@ -179,6 +207,16 @@ bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t hidden,
     const int64_t row_bytes = hidden * esize;
     const int vec_elems = (int)(16 / esize);
     const bool vec_ok = aligned && row_bytes % 16 == 0;
+    if (op == KS_OP_RMS_NORM_BACKWARD && p.path == KS_PATH_VECTOR) {
+        if (!vec_ok || !is_pow2_team(p.threads_per_row) || p.vectors_per_thread < 1 ||
+            p.vectors_per_thread > ks::bwd_max_vpt((int)esize))
+            return false;
+        if ((int64_t)p.threads_per_row * p.vectors_per_thread * 16 < row_bytes)
+            return false;
+        return p.elems_per_access == vec_elems && p.block_threads == ks::kBwdBlock &&
+               p.rows_per_block == ks::kBwdBlock / p.threads_per_row && p.load_nt == 1 && p.store_nt == 1 &&
+               p.weight_lds == 0;
+    }
     if (p.path == KS_PATH_VECTOR) {
         if (!vec_ok || !is_pow2_team(p.threads_per_row) || !hints_compiled(p))
             return false;
@@ -342,6 +380,67 @@ ks_status_t ks_rms_norm_residual(void *out, const void *x, const void *residual,
     return ks_rms_norm_residual_ex(out, x, residual, weight, rows, hidden, eps, dtype, nullptr, stream);
 }
 
+ks_status_t ks_rms_norm_backward_workspace_size(int64_t rows, int64_t hidden, size_t *bytes)
+{
+    if (bytes == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
+        return KS_ERROR_INVALID_VALUE;
+    *bytes = (size_t)ks::bwd_workspace_floats(rows, hidden) * sizeof(float);
+    return KS_SUCCESS;
+}
+
+ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, const void *x, const void *weight,
+                                    int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype, void *workspace,
+                                    size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream)
+{
+    ks_status_t st = check_sizes(dtype, rows, hidden, eps);
+    if (st != KS_SUCCESS)
+        return st;
+    if (rows > 0 && (dx == nullptr || dy == nullptr || x == nullptr || weight == nullptr))
+        return KS_ERROR_INVALID_VALUE;
+    const size_t need = (size_t)ks::bwd_workspace_floats(rows, hidden) * sizeof(float);
+    if (dweight != nullptr && need > 0 &&
+        (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 3u) != 0))
+        return KS_ERROR_INVALID_VALUE;
+    const bool aligned = aligned16(dx) && aligned16(dy) && aligned16(x) && aligned16(weight);
+    ks::BwdLaunch l{dx, dweight, dy, x, weight, (float *)workspace, rows, (int32_t)hidden, eps, {}, stream};
+    st = select_plan(plan, KS_OP_RMS_NORM_BACKWARD, dtype, rows, hidden, aligned, &l.plan);
+    if (st != KS_SUCCESS || (rows == 0 && dweight == nullptr))
+        return st;
+    const int64_t es = elem_size(dtype);
+    const int64_t nbytes = rows * hidden * es;
+    const int64_t wbytes = hidden * es;
+    const int64_t kbytes = dweight != nullptr ? (int64_t)need : 0;
+    // outputs and workspace touch nothing else; the inputs may overlap each other
+    if (overlaps(dx, nbytes, dy, nbytes) || overlaps(dx, nbytes, x, nbytes) || overlaps(dx, nbytes, weight, wbytes) ||
+        overlaps(dx, nbytes, dweight, dweight ? wbytes : 0) || overlaps(dx, nbytes, workspace, kbytes))
+        return KS_ERROR_OVERLAP;
+    if (dweight != nullptr &&
+        (overlaps(dweight, wbytes, dy, nbytes) || overlaps(dweight, wbytes, x, nbytes) ||
+         overlaps(dweight, wbytes, weight, wbytes) || overlaps(dweight, wbytes, workspace, kbytes) ||
+         overlaps(workspace, kbytes, dy, nbytes) || overlaps(workspace, kbytes, x, nbytes) ||
+         overlaps(workspace, kbytes, weight, wbytes)))
+        return KS_ERROR_OVERLAP;
+    hipError_t err;
+    switch (dtype) {
+    case KS_DTYPE_FLOAT32: err = ks::launch_bwd_f32(l); break;
+    case KS_DTYPE_FLOAT16: err = ks::launch_bwd_f16(l); break;
+    default: err = ks::launch_bwd_bf16(l); break;
+    }
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return KS_ERROR_HIP;
+    }
+    return KS_SUCCESS;
+}
+
+ks_status_t ks_rms_norm_backward(void *dx, void *dweight, const void *dy, const void *x, const void *weight,
+                                 int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream)
+{
+    return ks_rms_norm_backward_ex(dx, dweight, dy, x, weight, rows, hidden, eps, dtype, workspace, workspace_bytes,
+                                   nullptr, stream);
+}
+
 ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
                                const ks_plan_t *plan, hipStream_t stream)
 {
@@ -408,7 +507,7 @@ ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidd
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
         (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL &&
-         op != KS_OP_SOFTMAX && op != KS_OP_RMS_NORM_RESIDUAL))
+         op != KS_OP_SOFTMAX && op != KS_OP_RMS_NORM_RESIDUAL && op != KS_OP_RMS_NORM_BACKWARD))
         return KS_ERROR_INVALID_VALUE;
     *plan = policy(op, dtype, rows, hidden, aligned != 0);
     return KS_SUCCESS;

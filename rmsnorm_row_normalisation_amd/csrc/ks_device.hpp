@@ -1,6 +1,6 @@
-// Device code for RMSNorm, fused residual-add RMSNorm (in place, and the
-// out-of-place RMSNorm(x + residual) * w), the SwiGLU activation and softmax
-// on gfx950 (CDNA4).
+// Device code for RMSNorm (forward and backward), fused residual-add RMSNorm
+// (in place, and the out-of-place RMSNorm(x + residual) * w), the SwiGLU
+// activation and softmax on gfx950 (CDNA4).
 //
 // Operation (kernscope README, "Numerical contract"): per row, widen to fp32,
 // sum of squares in fp32, scale = rsqrt(sum / H + eps), y = (v * scale) *
@@ -789,6 +789,318 @@ __device__ __forceinline__ void softmax_generic_body(const Params &p)
 }
 
 // ---------------------------------------------------------------------------
+// RMSNorm backward: for y_j = x_j * rho * w_j with rho = rsqrt(mean(x^2) +
+// eps), and an incoming gradient dy,
+//   dx_j = rho * (g_j - c * x_j),  g_j = dy_j * w_j,  c = rho^2 * sum(g * x) / H,
+//   dw_j = sum over rows of dy_j * (x_j * rho).
+// rho is the forward's fp32 scale (row_scale, bit-identical to the forward).
+// The two row sums (x^2 and g * x) use the canonical fold, so dx does not
+// depend on the plan.  dw is summed without atomics, in a fixed order: each
+// team accumulates its rows' terms in registers (rows in increasing order),
+// each workgroup adds its teams' sums in team order into one fp32 partial
+// row, and a second kernel adds the partial rows in a fixed order.
+// ---------------------------------------------------------------------------
+struct BwdParams {
+    void *dx;           // [rows, hidden] output
+    const void *dy;     // [rows, hidden]
+    const void *x;      // [rows, hidden]
+    const void *w;      // [hidden]
+    float *part;        // [gridDim.x or chunks, hidden] fp32 partial sums of dw (null: no dw)
+    float *rho;         // [rows] per-row scale (generic path, when dw is wanted)
+    int64_t rows;
+    int32_t hidden;
+    float eps;
+};
+
+// Two team sums in the canonical fold, safe to call repeatedly in one kernel:
+// barriers on both sides of the LDS exchange.  Every thread of the block
+// must call this.
+template <int kTpr, int kBlock> __device__ __forceinline__ void team_fold2(float &a, float &b)
+{
+    if constexpr (kTpr <= 64) {
+        a = butterfly<kTpr>(a);
+        b = butterfly<kTpr>(b);
+    } else {
+        constexpr int kWaves = kTpr / 64;
+        __shared__ float la[kBlock], lb[kBlock];
+        __syncthreads();                       // readers of the previous call are done
+        la[threadIdx.x] = a;
+        lb[threadIdx.x] = b;
+        __syncthreads();
+        const int lane = threadIdx.x & 63;
+        const int first = (threadIdx.x / kTpr) * kTpr;
+        float pa[kWaves], pb[kWaves];
+#pragma unroll
+        for (int j = 0; j < kWaves; ++j) {
+            pa[j] = la[first + j * 64 + lane];
+            pb[j] = lb[first + j * 64 + lane];
+        }
+#pragma unroll
+        for (int n = kWaves; n > 1; n /= 2)
+#pragma unroll
+            for (int j = 0; j < n / 2; ++j) {
+                pa[j] = pa[j] + pa[j + n / 2];
+                pb[j] = pb[j] + pb[j + n / 2];
+            }
+        a = butterfly<64>(pa[0]);
+        b = butterfly<64>(pb[0]);
+    }
+}
+
+// Vector kernel: the weight pieces stay in VGPRs; the block walks row groups
+// blockIdx.x, blockIdx.x + gridDim.x, ... (the same count for every thread,
+// so the barriers inside team_fold2 are uniform).  x and dy are streamed
+// once with non-temporal loads; dx is stored non-temporal.
+template <typename T, int kTpr, int kVpt, int kBlock>
+__device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
+{
+    constexpr int kE = Pack<T>::kElems;
+    constexpr int kRpb = kBlock / kTpr;
+    constexpr int kNt = 2;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;
+    const int team = tid / kTpr;
+    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)Pack<T>::kBytes;
+    const auto rw = make_rsrc(p.w, row_bytes);
+
+    bool in_row[kVpt];
+    u32x4 wv[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        const uint32_t c = (uint32_t)(k * kTpr + lane) * 16u;
+        in_row[k] = c < row_bytes;
+        wv[k] = __builtin_amdgcn_raw_buffer_load_b128(rw, in_row[k] ? c : kOutOfRange, 0, 0);
+    }
+    float acc[kVpt][kE];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            acc[k][e] = 0.0f;
+
+    for (int64_t g = blockIdx.x; g * kRpb < p.rows; g += gridDim.x) {
+        const int64_t row0 = g * kRpb;
+        const int64_t left = p.rows - row0;
+        const uint32_t nrows = left < kRpb ? (uint32_t)left : (uint32_t)kRpb;
+        const uint32_t blk_bytes = nrows * row_bytes;     // rows past the batch are out of range
+        const size_t base = (size_t)row0 * row_bytes;
+        const auto rx = make_rsrc((const char *)p.x + base, blk_bytes);
+        const auto rdy = make_rsrc((const char *)p.dy + base, blk_bytes);
+        const auto rdx = make_rsrc((char *)p.dx + base, blk_bytes);
+        uint32_t off[kVpt];
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            off[k] = in_row[k] ? (uint32_t)team * row_bytes + (uint32_t)(k * kTpr + lane) * 16u : kOutOfRange;
+        u32x4 xv[kVpt], dv[kVpt];
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kNt);
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            dv[k] = __builtin_amdgcn_raw_buffer_load_b128(rdy, off[k], 0, kNt);
+
+        float ps[kVpt], pc[kVpt];   // per-piece sums of x^2 and of g * x, elements in index order
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            float a = 0.0f, b = 0.0f;
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const float xe = Pack<T>::get(xv[k], e);
+                const float ge = Pack<T>::get(dv[k], e) * Pack<T>::get(wv[k], e);
+                a = __builtin_fmaf(xe, xe, a);
+                b = __builtin_fmaf(ge, xe, b);
+            }
+            ps[k] = a;
+            pc[k] = b;
+        }
+        float ss = local_fold<kVpt>(ps);
+        float dot = local_fold<kVpt>(pc);
+        team_fold2<kTpr, kBlock>(ss, dot);
+        const float rho = row_scale(ss, p.hidden, p.eps);
+        const float c = ((dot / (float)p.hidden) * rho) * rho;
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            float o[kE];
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const float xe = Pack<T>::get(xv[k], e);
+                const float de = Pack<T>::get(dv[k], e);
+                const float ge = de * Pack<T>::get(wv[k], e);
+                o[e] = __builtin_fmaf(-c, xe, ge) * rho;
+                acc[k][e] = __builtin_fmaf(de, xe * rho, acc[k][e]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), rdx, off[k], 0, kNt);
+        }
+    }
+    if (p.part == nullptr)
+        return;
+    // this workgroup's partial row: the teams' sums added in team order
+    float *prow = p.part + (size_t)blockIdx.x * (size_t)p.hidden;
+    if constexpr (kRpb == 1) {
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k)
+            if (in_row[k])
+#pragma unroll
+                for (int e = 0; e < kE; ++e)
+                    prow[(k * kTpr + lane) * kE + e] = acc[k][e];
+    } else {
+        __shared__ float red[kBlock * kE];
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+                red[(team * kTpr + lane) * kE + e] = acc[k][e];
+            __syncthreads();
+            for (int q = tid; q < kTpr * kE; q += kBlock) {    // q = lane' * kE + e'
+                float sum = red[q];
+                for (int t = 1; t < kRpb; ++t)
+                    sum = sum + red[t * kTpr * kE + q];
+                const int piece = k * kTpr + q / kE;
+                if ((uint32_t)piece * 16u < row_bytes)
+                    prow[piece * kE + q % kE] = sum;
+            }
+        }
+    }
+}
+
+// Generic kernel: one team per row, two passes (the two sums, then dx), kEpa
+// elements per access; stores each row's rho when dw is wanted.
+template <typename T, int kTpr, int kEpa, int kBlock>
+__device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
+{
+    constexpr int kRpb = kBlock / kTpr;
+    const int tid = threadIdx.x;
+    const int lane = tid % kTpr;
+    const int team = tid / kTpr;
+    const int64_t row = (int64_t)blockIdx.x * kRpb + team;
+    const bool active = row < p.rows;
+    const int64_t H = p.hidden;
+    const int64_t base = active ? row * H : 0;
+    constexpr int64_t kStride = (int64_t)kTpr * kEpa;
+
+    float ss = 0.0f, dot = 0.0f;
+    if (active) {
+        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+            if constexpr (kEpa == 1) {
+                const float xe = Scalar<T>::get(p.x, base + j);
+                const float ge = Scalar<T>::get(p.dy, base + j) * Scalar<T>::get(p.w, j);
+                ss = __builtin_fmaf(xe, xe, ss);
+                dot = __builtin_fmaf(ge, xe, dot);
+            } else {
+                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+                const u32x4 dv = *(const u32x4 *)((const char *)p.dy + (base + j) * Pack<T>::kBytes);
+                const u32x4 wv = *(const u32x4 *)((const char *)p.w + j * Pack<T>::kBytes);
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e) {
+                    const float xe = Pack<T>::get(xv, e);
+                    const float ge = Pack<T>::get(dv, e) * Pack<T>::get(wv, e);
+                    ss = __builtin_fmaf(xe, xe, ss);
+                    dot = __builtin_fmaf(ge, xe, dot);
+                }
+            }
+        }
+    }
+    team_fold2<kTpr, kBlock>(ss, dot);
+    if (!active)
+        return;
+    const float rho = row_scale(ss, p.hidden, p.eps);
+    const float c = ((dot / (float)p.hidden) * rho) * rho;
+    if (p.rho != nullptr && lane == 0)
+        p.rho[row] = rho;
+    for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
+        if constexpr (kEpa == 1) {
+            const float xe = Scalar<T>::get(p.x, base + j);
+            const float ge = Scalar<T>::get(p.dy, base + j) * Scalar<T>::get(p.w, j);
+            Scalar<T>::put(p.dx, base + j, __builtin_fmaf(-c, xe, ge) * rho);
+        } else {
+            const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+            const u32x4 dv = *(const u32x4 *)((const char *)p.dy + (base + j) * Pack<T>::kBytes);
+            const u32x4 wv = *(const u32x4 *)((const char *)p.w + j * Pack<T>::kBytes);
+            float o[kEpa];
+#pragma unroll
+            for (int e = 0; e < kEpa; ++e) {
+                const float xe = Pack<T>::get(xv, e);
+                const float ge = Pack<T>::get(dv, e) * Pack<T>::get(wv, e);
+                o[e] = __builtin_fmaf(-c, xe, ge) * rho;
+            }
+            *(u32x4 *)((char *)p.dx + (base + j) * Pack<T>::kBytes) = Pack<T>::put(o);
+        }
+    }
+}
+
+// Generic path, dw partials: block (blockIdx.x, blockIdx.y) sums the columns
+// blockIdx.x * 256 + threadIdx.x over the rows of chunk blockIdx.y (chunks of
+// ceil(rows / gridDim.y) consecutive rows), in row order.
+template <typename T>
+__device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per = (p.rows + gridDim.y - 1) / gridDim.y;
+    const int64_t r0 = (int64_t)blockIdx.y * per;
+    const int64_t r1 = r0 + per < p.rows ? r0 + per : p.rows;
+    if (j >= p.hidden)
+        return;
+    float acc = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) {
+        const int64_t i = r * p.hidden + j;
+        acc = __builtin_fmaf(Scalar<T>::get(p.dy, i), Scalar<T>::get(p.x, i) * p.rho[r], acc);
+    }
+    p.part[(size_t)blockIdx.y * (size_t)p.hidden + j] = acc;
+}
+
+// dw[j] = the nparts partial rows added in a fixed order: wave v of the
+// 1024-thread block adds rows v, v + 16, v + 32, ... in turn (four
+// independent loads in flight per step), then the 16 wave sums are folded
+// in half (v with v + 8, then v + 4, ...) and rounded to the dtype.
+constexpr int kDwBlock = 1024;
+constexpr int kDwWaves = kDwBlock / 64;
+
+struct DwParams {
+    void *dw;
+    const float *part;
+    int32_t nparts;
+    int32_t hidden;
+};
+
+template <typename T>
+__device__ __forceinline__ void bwd_dw_body(const DwParams &p)
+{
+    __shared__ float red[kDwWaves][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + lane;
+    float s = 0.0f;
+    if (j < p.hidden) {
+        const float *col = p.part + j;
+        const size_t step = (size_t)kDwWaves * (size_t)p.hidden;
+        int q = wave;
+        for (; q + 3 * kDwWaves < p.nparts; q += 4 * kDwWaves) {
+            const float a = col[(size_t)q * p.hidden];
+            const float b = col[(size_t)q * p.hidden + step];
+            const float c = col[(size_t)q * p.hidden + 2 * step];
+            const float d = col[(size_t)q * p.hidden + 3 * step];
+            s = s + a;
+            s = s + b;
+            s = s + c;
+            s = s + d;
+        }
+        for (; q < p.nparts; q += kDwWaves)
+            s = s + col[(size_t)q * p.hidden];
+    }
+    red[wave][lane] = s;
+    __syncthreads();
+#pragma unroll
+    for (int n = kDwWaves / 2; n >= 1; n /= 2) {
+        if (wave < n)
+            red[wave][lane] = red[wave][lane] + red[wave + n][lane];
+        __syncthreads();
+    }
+    if (wave == 0 && j < p.hidden)
+        Scalar<T>::put(p.dw, j, red[0][lane]);
+}
+
+// ---------------------------------------------------------------------------
 // Kernel entry points, one name per operation and path.
 // ---------------------------------------------------------------------------
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
@@ -837,6 +1149,30 @@ template <typename T>
 __global__ __launch_bounds__(256) void silu_and_mul_generic(SwigluParams p)
 {
     swiglu_generic_body<T>(p);
+}
+
+template <typename T, int kTpr, int kVpt, int kBlock>
+__global__ __launch_bounds__(kBlock) void rms_norm_backward_vec(BwdParams p)
+{
+    bwd_vec_body<T, kTpr, kVpt, kBlock>(p);
+}
+
+template <typename T, int kTpr, int kEpa, int kBlock>
+__global__ __launch_bounds__(kBlock) void rms_norm_backward_generic(BwdParams p)
+{
+    bwd_generic_body<T, kTpr, kEpa, kBlock>(p);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rms_norm_backward_colsum(BwdParams p)
+{
+    bwd_colsum_body<T>(p);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kDwBlock) void rms_norm_backward_dw(DwParams p)
+{
+    bwd_dw_body<T>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>

@@ -35,6 +35,41 @@ struct SwigluLaunch {
     hipStream_t stream;
 };
 
+// One RMSNorm backward call (dx, and dw unless dw is null).  `work` is the
+// caller's fp32 workspace (see bwd_workspace_floats).
+struct BwdLaunch {
+    void *dx;
+    void *dw;
+    const void *dy;
+    const void *x;
+    const void *w;
+    float *work;
+    int64_t rows;
+    int32_t hidden;
+    float eps;
+    ks_plan_t plan;
+    hipStream_t stream;
+};
+
+// Backward: at most this many fp32 partial rows of dw (vector path: one per
+// workgroup; generic path: one per chunk of rows); 1024-thread workgroups
+// (128 VGPRs per lane) on the vector path, where x, dy, the weight and the dw
+// sums of a lane's pieces stay in VGPRs: at most 4 pieces per lane for fp32
+// and 2 for 16-bit dtypes (whose pieces hold 8 sums each; 3 or more spill).
+constexpr int kBwdMaxParts = 256;
+constexpr int kBwdBlock = 1024;
+constexpr int kBwdMaxVpt32 = 4;
+constexpr int kBwdMaxVpt16 = 2;
+inline int bwd_max_vpt(int elem_bytes) { return elem_bytes == 4 ? kBwdMaxVpt32 : kBwdMaxVpt16; }
+
+// fp32 elements of workspace a backward call needs: the partial rows and, on
+// the generic path, one rho per row.
+inline int64_t bwd_workspace_floats(int64_t rows, int64_t hidden)
+{
+    const int64_t parts = rows < kBwdMaxParts ? rows : kBwdMaxParts;
+    return parts * hidden + rows;
+}
+
 // Cache-policy bits of a buffer instruction that marks it non-temporal.
 constexpr int kNonTemporal = 2;
 
@@ -54,6 +89,9 @@ KS_DECLARE_LAUNCH(bf16)
 hipError_t launch_swiglu_f32(const SwigluLaunch &l);
 hipError_t launch_swiglu_f16(const SwigluLaunch &l);
 hipError_t launch_swiglu_bf16(const SwigluLaunch &l);
+hipError_t launch_bwd_f32(const BwdLaunch &l);
+hipError_t launch_bwd_f16(const BwdLaunch &l);
+hipError_t launch_bwd_bf16(const BwdLaunch &l);
 hipError_t launch_softmax_f32(const Launch &l);
 hipError_t launch_softmax_f16(const Launch &l);
 hipError_t launch_softmax_bf16(const Launch &l);

@@ -202,4 +202,103 @@ hipError_t launch_swiglu_typed(const SwigluLaunch &l)
     }
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm backward
+// ---------------------------------------------------------------------------
+template <typename T, int TPR, int V>
+hipError_t bwd_vec_one(const BwdParams &p, unsigned grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((rms_norm_backward_vec<T, TPR, V, kBwdBlock>), dim3(grid), dim3(kBwdBlock), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int TPR>
+hipError_t bwd_vec_by_vpt(const BwdParams &p, int vpt, unsigned grid, hipStream_t stream)
+{
+    switch (vpt) {
+    case 1: return bwd_vec_one<T, TPR, 1>(p, grid, stream);
+    case 2: return bwd_vec_one<T, TPR, 2>(p, grid, stream);
+    default: break;
+    }
+    if constexpr (Pack<T>::kBytes == 4) {
+        switch (vpt) {
+        case 3: return bwd_vec_one<T, TPR, 3>(p, grid, stream);
+        case 4: return bwd_vec_one<T, TPR, 4>(p, grid, stream);
+        default: break;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+// Generic plans: 256-thread workgroups, 1024 for 1024-lane teams.
+template <typename T, int TPR, int EPA>
+hipError_t bwd_generic_one(const BwdParams &p, unsigned grid, hipStream_t stream)
+{
+    constexpr int B = TPR == 1024 ? 1024 : 256;
+    hipLaunchKernelGGL((rms_norm_backward_generic<T, TPR, EPA, B>), dim3(grid), dim3(B), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int EPA>
+hipError_t bwd_generic_by_tpr(const BwdParams &p, int tpr, unsigned grid, hipStream_t stream)
+{
+    switch (tpr) {
+    case 8: return bwd_generic_one<T, 8, EPA>(p, grid, stream);
+    case 64: return bwd_generic_one<T, 64, EPA>(p, grid, stream);
+    case 256: return bwd_generic_one<T, 256, EPA>(p, grid, stream);
+    case 1024: return bwd_generic_one<T, 1024, EPA>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_bwd_typed(const BwdLaunch &l)
+{
+    const ks_plan_t &pl = l.plan;
+    const int64_t rpb = pl.block_threads / pl.threads_per_row;
+    int32_t nparts = 0;
+    hipError_t err = hipSuccess;
+    if (l.rows > 0) {
+        BwdParams p{l.dx, l.dy, l.x, l.w, l.dw ? l.work : nullptr, nullptr, l.rows, l.hidden, l.eps};
+        if (pl.path == KS_PATH_VECTOR) {
+            const int64_t groups = (l.rows + rpb - 1) / rpb;
+            const unsigned grid = (unsigned)(groups < kBwdMaxParts ? groups : kBwdMaxParts);
+            nparts = (int32_t)grid;
+            switch (pl.threads_per_row) {
+            case 8: err = bwd_vec_by_vpt<T, 8>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 16: err = bwd_vec_by_vpt<T, 16>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 32: err = bwd_vec_by_vpt<T, 32>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 64: err = bwd_vec_by_vpt<T, 64>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 128: err = bwd_vec_by_vpt<T, 128>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 256: err = bwd_vec_by_vpt<T, 256>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 512: err = bwd_vec_by_vpt<T, 512>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 1024: err = bwd_vec_by_vpt<T, 1024>(p, pl.vectors_per_thread, grid, l.stream); break;
+            default: return hipErrorInvalidValue;
+            }
+        } else {
+            nparts = (int32_t)(l.rows < kBwdMaxParts ? l.rows : kBwdMaxParts);
+            if (l.dw)
+                p.rho = l.work + (size_t)nparts * (size_t)l.hidden;
+            const unsigned grid = (unsigned)((l.rows + rpb - 1) / rpb);
+            if (pl.elems_per_access == 1)
+                err = bwd_generic_by_tpr<T, 1>(p, pl.threads_per_row, grid, l.stream);
+            else if (pl.elems_per_access == Pack<T>::kElems)
+                err = bwd_generic_by_tpr<T, Pack<T>::kElems>(p, pl.threads_per_row, grid, l.stream);
+            else
+                return hipErrorInvalidValue;
+            if (err == hipSuccess && l.dw) {
+                const dim3 cgrid((unsigned)((l.hidden + 255) / 256), (unsigned)nparts);
+                hipLaunchKernelGGL((rms_norm_backward_colsum<T>), cgrid, dim3(256), 0, l.stream, p);
+                err = hipGetLastError();
+            }
+        }
+    }
+    if (err != hipSuccess || l.dw == nullptr)
+        return err;
+    DwParams d{l.dw, l.work, nparts, l.hidden};
+    hipLaunchKernelGGL((rms_norm_backward_dw<T>), dim3((unsigned)((l.hidden + 63) / 64)), dim3(kDwBlock), 0, l.stream,
+                       d);
+    return hipGetLastError();
+}
+
 }  // namespace ks

@@ -105,3 +105,43 @@ def check_bitexact(out: torch.Tensor, ref: torch.Tensor) -> None:
         idx = int(torch.nonzero(bad.reshape(-1))[0])
         raise AssertionError(f"{int(bad.sum())} of {o.numel()} elements differ; first at flat index {idx}: "
                              f"{hex(int(bits(o).reshape(-1)[idx]))} vs {hex(int(bits(r).reshape(-1)[idx]))}")
+
+
+def check_gradient(out: torch.Tensor, ref: torch.Tensor, magnitude: torch.Tensor,
+                   min_exact_rate: float | None = None, rel: float = 2.0 ** -16) -> ParityStats:
+    """Gate for a gradient, whose value may be a difference of much larger terms:
+    each element meets the normalisation bar (1 ulp of bf16/fp16 or |difference|
+    <= 1e-6; fp32 rtol = atol = 1e-6) against the exact value, or lies within
+    rel * magnitude of it, where magnitude bounds the terms an fp32 evaluation
+    rounds (2^-16 is 256 fp32 ulps: room for a sum over up to 2^16 elements)."""
+    st = stats(out, ref)
+    if st.n == 0:
+        return st
+    o, r = out.detach().cpu(), ref.detach().cpu()
+    if o.dtype == torch.float32:
+        ok = torch.isclose(o, r, rtol=1e-6, atol=1e-6, equal_nan=True)
+    else:
+        ok = (ulp_distance(o, r) <= 1) | ((o.float() - r.float()).abs() <= 1e-6)
+    ok = ok | ((o.double() - r.double()).abs() <= rel * magnitude.double().cpu())
+    assert bool(ok.all()), f"gradient outside the bar at {int((~ok).sum())} elements: {st}"
+    if min_exact_rate is not None and o.dtype != torch.float32:
+        assert st.exact_rate >= min_exact_rate, f"exact-match rate below {min_exact_rate}: {st}"
+    return st
+
+
+def backward_magnitudes(dy: torch.Tensor, x: torch.Tensor, w: torch.Tensor, eps: float):
+    """For the RMSNorm backward, the sizes of the terms behind each gradient
+    element, in float64 from the widened inputs (used for the tolerance only):
+    dx_j = rho (g_j - c x_j) with g = dy w and c = rho^2 sum(g x) / H, whose sum
+    rounds terms of size |g x|; dw_j sums dy_j x_j rho over the rows."""
+    import numpy as np
+
+    h = x.shape[-1]
+    xd, dyd, wd = x.double().reshape(-1, h), dy.double().reshape(-1, h), w.double()
+    rho = 1.0 / torch.sqrt(xd.pow(2).mean(-1, keepdim=True) + float(np.float32(eps)))
+    g = dyd * wd
+    gx = g * xd
+    c = rho ** 2 * gx.sum(-1, keepdim=True) / h
+    mdx = rho * (g.abs() + (c * xd).abs() + xd.abs() * rho ** 2 / h * gx.abs().sum(-1, keepdim=True))
+    mdw = (dyd * xd * rho).abs().sum(0)
+    return mdx.reshape(x.shape), mdw

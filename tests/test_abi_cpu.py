@@ -476,3 +476,67 @@ def test_residual_plans_follow_the_fused_rule():
                 base = A if aligned else A + 2
                 assert resid(base + 768 * MB, base, base + 256 * MB, base + 512 * MB, 0, hidden,
                              plan=b.Plan.from_dict(p)) == OK
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm backward: caller-owned fp32 workspace, outputs overlap nothing
+# ---------------------------------------------------------------------------
+def bwd(dx, dw, dy, x, w, rows, hidden, ws, ws_bytes, eps=1e-6, dtype=BF16, plan=None):
+    return b.ks_rms_norm_backward_ex(dx, dw, dy, x, w, rows, hidden, eps, dtype, ws, ws_bytes, plan, 0)
+
+
+def test_backward_workspace_size():
+    for rows, hidden in ((0, 8), (1, 8), (3, 1000), (256, 4096), (2048, 4096), (100000, 7)):
+        assert b.ks_rms_norm_backward_workspace_size(rows, hidden) == 4 * (min(rows, 256) * hidden + rows)
+    n = ctypes.c_size_t()
+    assert ks.lib().ks_rms_norm_backward_workspace_size(-1, 8, ctypes.byref(n)) == INVALID
+    assert ks.lib().ks_rms_norm_backward_workspace_size(4, 0, ctypes.byref(n)) == INVALID
+    assert ks.lib().ks_rms_norm_backward_workspace_size(4, 8, None) == INVALID
+
+
+def test_backward_statuses_and_overlaps():
+    dx, dw, dy, x, w, ws = (A + i * 256 * MB for i in range(6))
+    need = b.ks_rms_norm_backward_workspace_size(4, 4096)
+    args = (dx, dw, dy, x, w, 4, 4096, ws, need)
+    assert bwd(*args, dtype=9) == DTYPE
+    assert bwd(dx, dw, dy, x, w, -1, 4096, ws, need) == INVALID
+    assert bwd(dx, dw, dy, x, w, 4, 0, ws, need) == INVALID
+    assert bwd(*args, eps=-1.0) == INVALID
+    assert bwd(None, dw, dy, x, w, 4, 4096, ws, need) == INVALID
+    assert bwd(dx, dw, None, x, w, 4, 4096, ws, need) == INVALID
+    assert bwd(dx, dw, dy, x, w, 4, 4096, None, need) == INVALID        # dw wanted: workspace needed
+    assert bwd(dx, dw, dy, x, w, 4, 4096, ws, need - 4) == INVALID      # too small
+    assert bwd(dx, dw, dy, x, w, 4, 4096, ws + 2, need) == INVALID      # not 4-byte aligned
+    assert bwd(None, None, None, None, None, 0, 4096, None, 0) == OK   # nothing to do: no HIP call
+    for bad_dx in (dy, x + 64, w - 16, dw, ws + 8):
+        assert bwd(bad_dx, dw, dy, x, w, 4, 4096, ws, need) == OVERLAP
+    for bad_dw in (dy + 4, x, w, ws + 4):
+        assert bwd(dx, bad_dw, dy, x, w, 4, 4096, ws, need) == OVERLAP
+    assert bwd(dx, dw, dy, x, w, 4, 4096, x + 8, need) == OVERLAP       # workspace inside x
+    assert bwd(dx, None, dy, x, w, 0, 4096, None, 0) == OK
+
+
+def test_backward_plans():
+    for dtype, es in ((torch.float32, 4), (torch.float16, 2), (torch.bfloat16, 2)):
+        maxv = 4 if es == 4 else 2
+        for hidden in (8, 1000, 1001, 4096, 8192, 16384, 32768, 40000):
+            for aligned in (True, False):
+                p = ks.get_plan("rms_norm_backward", dtype, hidden, 2048, aligned).as_dict()
+                nvec = hidden * es // 16
+                if aligned and (hidden * es) % 16 == 0 and nvec <= 1024 * maxv:
+                    assert p["path"] == 0 and p["block_threads"] == 1024
+                    assert p["vectors_per_thread"] <= maxv and p["threads_per_row"] * p["vectors_per_thread"] >= nvec
+                    assert p["rows_per_block"] * p["threads_per_row"] == 1024
+                else:
+                    assert p["path"] == 1
+                base = A if aligned else A + 2
+                code = {4: F32, 2: F16 if dtype == torch.float16 else BF16}[es]
+                assert bwd(base, None, base + 256 * MB, base + 512 * MB, base + 768 * MB, 0, hidden, None, 0,
+                           dtype=code, plan=b.Plan.from_dict(p)) == OK
+    p = ks.get_plan("rms_norm_backward", torch.bfloat16, 4096, 2048).as_dict()
+    assert (p["threads_per_row"], p["vectors_per_thread"]) == (256, 2)
+    bad = [{**p, "vectors_per_thread": 3, "threads_per_row": 256}, {**p, "block_threads": 256, "rows_per_block": 1},
+           {**p, "weight_lds": 1}, {**p, "load_nt": 0}]
+    for q in bad:
+        assert bwd(A, None, A + 256 * MB, A + 512 * MB, A + 768 * MB, 0, 4096, None, 0,
+                   plan=b.Plan.from_dict(q)) == INVALID

@@ -1,0 +1,167 @@
+"""RMSNorm backward on the GPU against the CPU oracle (the exact gradients).
+
+Bar (tests/compare.py, check_gradient): each gradient element within 1 ulp of
+bf16/fp16 (|difference| <= 1e-6 near zero; fp32 rtol = atol = 1e-6) of the
+exact value, or within 2^-16 of the magnitude of the terms its fp32
+evaluation rounds (cancellation in dx = rho (g - c x), the sums behind c and
+dw); dx at least 99% bit-identical on large 16-bit cases.  Cases: the
+headline shape, edge and ragged shapes in all dtypes (vector and generic
+paths), unaligned buffers, dw off, a single row, every compiled plan (dx
+bit-identical across vector plans), batch invariance of dx, graph replays.
+"""
+import pytest
+import torch
+
+import oracle
+import rmsnorm_row_normalisation_amd as ks
+import workloads
+from compare import backward_magnitudes as magnitudes
+from compare import check_bitexact, check_gradient
+from gpu_cases import require_gpu, say
+
+pytestmark = pytest.mark.gpu
+DTYPES = ["bfloat16", "float16", "float32"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _dev(t, offset):
+    if offset == 0:
+        return t.cuda()
+    buf = torch.empty(t.numel() + offset, dtype=t.dtype, device="cuda")
+    v = buf[offset:].view(t.shape)
+    v.copy_(t.cuda())
+    return v
+
+
+def run(dy, x, w, eps, plan=None, offset=0, weight_grad=True):
+    dxo = _dev(torch.empty_like(x), offset) if offset else None
+    gx, gw = ks.rms_norm_backward(_dev(dy, offset), _dev(x, offset), _dev(w, offset), eps, plan=plan,
+                                  weight_grad=weight_grad, dx=dxo)
+    torch.cuda.synchronize()
+    return gx.cpu(), (gw.cpu() if gw is not None else None)
+
+
+def check(name, dy, x, w, eps, plan=None, offset=0, weight_grad=True):
+    say("backward", name, tuple(x.shape), x.dtype, plan.as_dict() if plan is not None else "policy", offset)
+    gx, gw = run(dy, x, w, eps, plan, offset, weight_grad)
+    rx, rw = oracle.rms_norm_backward(dy, x, w, eps)
+    mdx, mdw = magnitudes(dy, x, w, eps)
+    st = check_gradient(gx, rx, mdx, 0.99 if gx.numel() >= 20000 else None)
+    if weight_grad:
+        check_gradient(gw, rw, mdw)
+    return st, gx, gw
+
+
+def test_workload():
+    wl = workloads.WORKLOADS["B1"]
+    inp = workloads.make_inputs(wl)
+    st, _, _ = check("B1", inp["residual"], inp["x"], inp["weight"], wl.eps)
+    say("B1", st)
+
+
+SHAPES = [(5,), (2, 3, 5), (3, 1000), (512, 1024), (7, 1023), (300, 4096), (2, 8200), (3, 16384), (2, 32768),
+          (2, 40000), (1000, 64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(shape, dtype):
+    inp = workloads.random_case(shape, dtype, seed=sum(shape) + 11, residual=workloads.normal(0, 1))
+    check("shape", inp["residual"], inp["x"], inp["weight"], 1e-6)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_unaligned_no_dw_and_empty(dtype):
+    inp = workloads.random_case((37, 4096), dtype, seed=91)
+    check("offset", inp["residual"], inp["x"], inp["weight"], 1e-5, offset=1)
+    gx, gw = run(inp["residual"], inp["x"], inp["weight"], 1e-5, weight_grad=False)
+    assert gw is None
+    rx, _ = oracle.rms_norm_backward(inp["residual"], inp["x"], inp["weight"], 1e-5)
+    check_gradient(gx, rx, magnitudes(inp["residual"], inp["x"], inp["weight"], 1e-5)[0])
+    e = torch.empty(0, 64, dtype=workloads.DTYPES[dtype], device="cuda")
+    w = torch.ones(64, dtype=e.dtype, device="cuda")
+    ex, ew = ks.rms_norm_backward(e, e, w)
+    torch.cuda.synchronize()
+    assert ex.shape == (0, 64) and bool((ew.cpu() == 0).all())
+
+
+def _vector_plans(hidden, es):
+    maxv = 4 if es == 4 else 2
+    nvec = hidden * es // 16
+    out, tpr = [], 8
+    while tpr <= 1024:
+        for vpt in range(1, maxv + 1):
+            if tpr * vpt >= nvec:
+                out.append(ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt, elems_per_access=16 // es,
+                                   rows_per_block=1024 // tpr, block_threads=1024, load_nt=1, store_nt=1))
+        tpr *= 2
+    return out
+
+
+@pytest.mark.parametrize("dtype,hidden", [("bfloat16", 4096), ("float16", 1536), ("float32", 1000)])
+def test_every_plan(dtype, hidden):
+    """dx is the same bits for every vector plan; dw meets the bar for every plan."""
+    inp = workloads.random_case((600, hidden), dtype, seed=hidden + 5)
+    dy, x, w = inp["residual"], inp["x"], inp["weight"]
+    rx, rw = oracle.rms_norm_backward(dy, x, w, 1e-6)
+    mdx, mdw = magnitudes(dy, x, w, 1e-6)
+    first = None
+    plans = _vector_plans(hidden, x.element_size())
+    assert len(plans) >= 4
+    for plan in plans:
+        gx, gw = run(dy, x, w, 1e-6, plan)
+        check_gradient(gx, rx, mdx, 0.99)
+        check_gradient(gw, rw, mdw)
+        if first is None:
+            first = gx
+        else:
+            check_bitexact(gx, first)
+    es = x.element_size()
+    for t in (8, 64, 256, 1024):
+        for epa in (1, 16 // es):
+            block = 1024 if t == 1024 else 256
+            plan = ks.Plan(path=1, threads_per_row=t, vectors_per_thread=0, elems_per_access=epa,
+                           rows_per_block=block // t, block_threads=block)
+            gx, gw = run(dy, x, w, 1e-6, plan)
+            check_gradient(gx, rx, mdx, 0.99)
+            check_gradient(gw, rw, mdw)
+
+
+def test_dx_batch_invariance_and_dw_determinism():
+    wl = workloads.WORKLOADS["B1"]
+    inp = workloads.make_inputs(wl, rows=700)
+    dy, x, w = inp["residual"], inp["x"], inp["weight"]
+    gx, gw = run(dy, x, w, wl.eps)
+    for rows in (1, 3, 64):
+        sx, _ = run(dy[:rows].contiguous(), x[:rows].contiguous(), w, wl.eps)
+        check_bitexact(sx, gx[:rows])
+    gx2, gw2 = run(dy, x, w, wl.eps)
+    check_bitexact(gx2, gx)
+    check_bitexact(gw2, gw)
+
+
+def test_graph_replays_match_eager():
+    wl = workloads.WORKLOADS["B1"]
+    inp = workloads.make_inputs(wl)
+    dy, x, w = inp["residual"].cuda(), inp["x"].cuda(), inp["weight"].cuda()
+    ws = torch.empty(ks.ks_rms_norm_backward_workspace_size(wl.rows, wl.hidden), dtype=torch.uint8, device="cuda")
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    ks.rms_norm_backward(dy, x, w, wl.eps, workspace=ws, dx=dx, dweight=dw)
+    torch.cuda.synchronize()
+    ex, ew = dx.clone(), dw.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ks.rms_norm_backward(dy, x, w, wl.eps, workspace=ws, dx=dx, dweight=dw)
+    for _ in range(4):
+        dx.zero_()
+        dw.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_bitexact(dx.cpu(), ex.cpu())
+        check_bitexact(dw.cpu(), ew.cpu())

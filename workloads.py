@@ -7,7 +7,8 @@ kernscope softmax measurements at 512 rows of 1024, 128 and 8192 bf16, its
 65536-column fp16 accumulation case, and the RMSNorm headline shape 2048x4096
 as an HBM-bound softmax batch) and out-of-place residual RMSNorm workloads
 (R*: the Triton Kernels README usage example, fp16 [2048, 4096] with unit
-weight, and the headline shape in bf16).  The softmax pages state no input
+weight, and the headline shape in bf16) and the RMSNorm backward at the
+headline shape (B1; its incoming gradient dy ~ N(0, 1), drawn as "residual").  The softmax pages state no input
 distribution; N(0, 1) logits are used, as in their usage example.
 
 This module draws random numbers and nothing else: it holds none of the
@@ -90,6 +91,8 @@ class Workload:
             parts[-1] += f" with {self.outlier_frac:.0%} of elements x{self.outlier_scale:g}"
         if self.residual is not None and ("fused_add_rms_norm" in self.ops or "rms_norm_residual" in self.ops):
             parts.append(f"residual ~{self.residual}")
+        if self.residual is not None and "rms_norm_backward" in self.ops:
+            parts.append(f"dy ~{self.residual}")
         if self.weight is not None:
             parts.append(f"weight ~{self.weight}")
             parts.append(f"eps={self.eps:g}")
@@ -97,7 +100,7 @@ class Workload:
 
 
 RMS, FUSED, SWIGLU, SOFTMAX = "rms_norm", "fused_add_rms_norm", "silu_and_mul", "softmax"
-RESIDUAL = "rms_norm_residual"
+RESIDUAL, BACKWARD = "rms_norm_residual", "rms_norm_backward"
 
 WORKLOADS: dict[str, Workload] = {
     # small case the oracle finishes in milliseconds
@@ -132,6 +135,10 @@ WORKLOADS: dict[str, Workload] = {
     "R2": Workload("R2", (RESIDUAL,), "bfloat16", 2048, 4096, normal(0, 1), uniform(0.5, 1.5), 1e-5, 8101, 8103,
                    residual=normal(0, 0.5), seed_r=8102, outlier_frac=0.01, outlier_scale=100.0,
                    seed_outlier=8104),
+    # RMSNorm backward at the headline shape; the incoming gradient dy is drawn
+    # through the residual fields
+    "B1": Workload("B1", (BACKWARD,), "bfloat16", 2048, 4096, normal(0, 1), uniform(0.5, 1.5), 1e-5, 9001, 9003,
+                   residual=normal(0, 1), seed_r=9002),
     # softmax over the last dimension
     "X1": Workload("X1", (SOFTMAX,), "bfloat16", 512, 1024, normal(0, 1), None, 0.0, 7001, None),
     "X2": Workload("X2", (SOFTMAX,), "bfloat16", 512, 128, normal(0, 1), None, 0.0, 7101, None),
