@@ -102,7 +102,7 @@ int64_t pow2_ceil(int64_t v)
 }
 
 // RMSNorm backward (vector path): 1024-thread workgroups that walk row
-// groups, at most 4 (fp32) or 2 (16-bit) pieces per lane, the team the power
+// groups, at most 3 (fp32) or 2 (16-bit) pieces per lane, the team the power
 // of two covering the row (8..1024 lanes); x and dy loads and dx stores
 // non-temporal.
 ks_plan_t backward_vector_plan(int64_t nvec, int vec_elems, int max_vpt)

@@ -849,8 +849,9 @@ template <int kTpr, int kBlock> __device__ __forceinline__ void team_fold2(float
 
 // Vector kernel: the weight pieces stay in VGPRs; the block walks row groups
 // blockIdx.x, blockIdx.x + gridDim.x, ... (the same count for every thread,
-// so the barriers inside team_fold2 are uniform).  x and dy are streamed
-// once with non-temporal loads; dx is stored non-temporal.
+// so the barriers inside team_fold2 are uniform), loading the next group
+// while it finishes the current one.  x and dy are streamed once with
+// non-temporal loads; dx is stored non-temporal.
 template <typename T, int kTpr, int kVpt, int kBlock>
 __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
 {
@@ -878,26 +879,40 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
         for (int e = 0; e < kE; ++e)
             acc[k][e] = 0.0f;
 
-    for (int64_t g = blockIdx.x; g * kRpb < p.rows; g += gridDim.x) {
-        const int64_t row0 = g * kRpb;
-        const int64_t left = p.rows - row0;
-        const uint32_t nrows = left < kRpb ? (uint32_t)left : (uint32_t)kRpb;
-        const uint32_t blk_bytes = nrows * row_bytes;     // rows past the batch are out of range
-        const size_t base = (size_t)row0 * row_bytes;
-        const auto rx = make_rsrc((const char *)p.x + base, blk_bytes);
-        const auto rdy = make_rsrc((const char *)p.dy + base, blk_bytes);
-        const auto rdx = make_rsrc((char *)p.dx + base, blk_bytes);
-        uint32_t off[kVpt];
+    // Row group g covers rows [g * kRpb, g * kRpb + kRpb); rows past the batch
+    // fall outside the group's descriptors (zero reads, dropped stores).
+    const int64_t ngroups = (p.rows + kRpb - 1) / kRpb;
+    auto group_bytes = [&](int64_t grp) {
+        const int64_t left = p.rows - grp * kRpb;
+        return (left < kRpb ? (uint32_t)left : (uint32_t)kRpb) * row_bytes;
+    };
+    uint32_t off[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        off[k] = in_row[k] ? (uint32_t)team * row_bytes + (uint32_t)(k * kTpr + lane) * 16u : kOutOfRange;
+    auto load_group = [&](int64_t grp, u32x4 *xo, u32x4 *dyo) {
+        const size_t base = (size_t)grp * kRpb * row_bytes;
+        const auto rx = make_rsrc((const char *)p.x + base, group_bytes(grp));
+        const auto rdy = make_rsrc((const char *)p.dy + base, group_bytes(grp));
 #pragma unroll
         for (int k = 0; k < kVpt; ++k)
-            off[k] = in_row[k] ? (uint32_t)team * row_bytes + (uint32_t)(k * kTpr + lane) * 16u : kOutOfRange;
-        u32x4 xv[kVpt], dv[kVpt];
+            xo[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kNt);
 #pragma unroll
         for (int k = 0; k < kVpt; ++k)
-            xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kNt);
-#pragma unroll
-        for (int k = 0; k < kVpt; ++k)
-            dv[k] = __builtin_amdgcn_raw_buffer_load_b128(rdy, off[k], 0, kNt);
+            dyo[k] = __builtin_amdgcn_raw_buffer_load_b128(rdy, off[k], 0, kNt);
+    };
+
+    // Software pipeline: the next group's loads are in flight while this
+    // group is reduced and written.
+    u32x4 xv[kVpt], dv[kVpt];
+    int64_t g = blockIdx.x;
+    if (g < ngroups)
+        load_group(g, xv, dv);
+    while (g < ngroups) {
+        const int64_t gn = g + gridDim.x;
+        u32x4 xn[kVpt], dn[kVpt];
+        if (gn < ngroups)
+            load_group(gn, xn, dn);
 
         float ps[kVpt], pc[kVpt];   // per-piece sums of x^2 and of g * x, elements in index order
 #pragma unroll
@@ -918,6 +933,7 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
         team_fold2<kTpr, kBlock>(ss, dot);
         const float rho = row_scale(ss, p.hidden, p.eps);
         const float c = ((dot / (float)p.hidden) * rho) * rho;
+        const auto rdx = make_rsrc((char *)p.dx + (size_t)g * kRpb * row_bytes, group_bytes(g));
 #pragma unroll
         for (int k = 0; k < kVpt; ++k) {
             float o[kE];
@@ -931,6 +947,12 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
             }
             __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), rdx, off[k], 0, kNt);
         }
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            xv[k] = xn[k];
+            dv[k] = dn[k];
+        }
+        g = gn;
     }
     if (p.part == nullptr)
         return;
@@ -1050,9 +1072,9 @@ __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
 }
 
 // dw[j] = the nparts partial rows added in a fixed order: wave v of the
-// 1024-thread block adds rows v, v + 16, v + 32, ... in turn (four
-// independent loads in flight per step), then the 16 wave sums are folded
-// in half (v with v + 8, then v + 4, ...) and rounded to the dtype.
+// 1024-thread block adds rows v, v + 16, v + 32, ... in turn (loads issued
+// sixteen at a time, so their latencies overlap), then the 16 wave sums are
+// folded in half (v with v + 8, then v + 4, ...) and rounded to the dtype.
 constexpr int kDwBlock = 1024;
 constexpr int kDwWaves = kDwBlock / 64;
 
@@ -1075,15 +1097,14 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
         const float *col = p.part + j;
         const size_t step = (size_t)kDwWaves * (size_t)p.hidden;
         int q = wave;
-        for (; q + 3 * kDwWaves < p.nparts; q += 4 * kDwWaves) {
-            const float a = col[(size_t)q * p.hidden];
-            const float b = col[(size_t)q * p.hidden + step];
-            const float c = col[(size_t)q * p.hidden + 2 * step];
-            const float d = col[(size_t)q * p.hidden + 3 * step];
-            s = s + a;
-            s = s + b;
-            s = s + c;
-            s = s + d;
+        for (; q + 15 * kDwWaves < p.nparts; q += 16 * kDwWaves) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = col[(size_t)q * p.hidden + u * step];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                s = s + v[u];
         }
         for (; q < p.nparts; q += kDwWaves)
             s = s + col[(size_t)q * p.hidden];

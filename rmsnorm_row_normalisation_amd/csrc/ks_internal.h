@@ -53,12 +53,13 @@ struct BwdLaunch {
 
 // Backward: at most this many fp32 partial rows of dw (vector path: one per
 // workgroup; generic path: one per chunk of rows); 1024-thread workgroups
-// (128 VGPRs per lane) on the vector path, where x, dy, the weight and the dw
-// sums of a lane's pieces stay in VGPRs: at most 4 pieces per lane for fp32
-// and 2 for 16-bit dtypes (whose pieces hold 8 sums each; 3 or more spill).
+// (128 VGPRs per lane) on the vector path, where x, dy, the next group's x
+// and dy, the weight and the dw sums of a lane's pieces stay in VGPRs: at
+// most 3 pieces per lane for fp32 and 2 for 16-bit dtypes (whose pieces hold
+// 8 sums each); one more spills.
 constexpr int kBwdMaxParts = 256;
 constexpr int kBwdBlock = 1024;
-constexpr int kBwdMaxVpt32 = 4;
+constexpr int kBwdMaxVpt32 = 3;
 constexpr int kBwdMaxVpt16 = 2;
 inline int bwd_max_vpt(int elem_bytes) { return elem_bytes == 4 ? kBwdMaxVpt32 : kBwdMaxVpt16; }
 

@@ -221,11 +221,8 @@ hipError_t bwd_vec_by_vpt(const BwdParams &p, int vpt, unsigned grid, hipStream_
     default: break;
     }
     if constexpr (Pack<T>::kBytes == 4) {
-        switch (vpt) {
-        case 3: return bwd_vec_one<T, TPR, 3>(p, grid, stream);
-        case 4: return bwd_vec_one<T, TPR, 4>(p, grid, stream);
-        default: break;
-        }
+        if (vpt == 3)
+            return bwd_vec_one<T, TPR, 3>(p, grid, stream);
     }
     return hipErrorInvalidValue;
 }

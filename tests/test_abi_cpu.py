@@ -518,7 +518,7 @@ def test_backward_statuses_and_overlaps():
 
 def test_backward_plans():
     for dtype, es in ((torch.float32, 4), (torch.float16, 2), (torch.bfloat16, 2)):
-        maxv = 4 if es == 4 else 2
+        maxv = 3 if es == 4 else 2
         for hidden in (8, 1000, 1001, 4096, 8192, 16384, 32768, 40000):
             for aligned in (True, False):
                 p = ks.get_plan("rms_norm_backward", dtype, hidden, 2048, aligned).as_dict()

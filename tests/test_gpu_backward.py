@@ -90,7 +90,7 @@ def test_unaligned_no_dw_and_empty(dtype):
 
 
 def _vector_plans(hidden, es):
-    maxv = 4 if es == 4 else 2
+    maxv = 3 if es == 4 else 2
     nvec = hidden * es // 16
     out, tpr = [], 8
     while tpr <= 1024:
