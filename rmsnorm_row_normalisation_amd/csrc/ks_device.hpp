@@ -420,6 +420,35 @@ __device__ __forceinline__ void vec_body(const Params &p)
 }
 
 // ---------------------------------------------------------------------------
+// Element groups of the generic kernels: kEpa == 1 is one scalar element (any
+// alignment), kEpa == Pack<T>::kElems one 16-byte piece.  The generic loops
+// visit a lane's accesses kGenericBatch at a time, issuing all their loads
+// before using any, so the loads' latencies overlap (one access per
+// iteration left these kernels latency-bound); the element order of every
+// sum is unchanged.
+// ---------------------------------------------------------------------------
+constexpr int kGenericBatch = 4;
+
+template <typename T, int kEpa> struct Access {
+    using V = u32x4;
+    __device__ static __forceinline__ V load(const void *p, int64_t i)
+    {
+        return *(const u32x4 *)((const char *)p + i * Pack<T>::kBytes);
+    }
+    __device__ static __forceinline__ float get(const V &v, int e) { return Pack<T>::get(v, e); }
+    __device__ static __forceinline__ void store(void *p, int64_t i, const float *f)
+    {
+        *(u32x4 *)((char *)p + i * Pack<T>::kBytes) = Pack<T>::put(f);
+    }
+};
+template <typename T> struct Access<T, 1> {
+    using V = float;
+    __device__ static __forceinline__ V load(const void *p, int64_t i) { return Scalar<T>::get(p, i); }
+    __device__ static __forceinline__ float get(const V &v, int) { return v; }
+    __device__ static __forceinline__ void store(void *p, int64_t i, const float *f) { Scalar<T>::put(p, i, f[0]); }
+};
+
+// ---------------------------------------------------------------------------
 // Generic kernel: two passes over the row, kEpa elements per access.
 // kEpa == 1: scalar accesses (any alignment); kEpa == 16 / sizeof(T): 16-byte
 // accesses (aligned buffers, row bytes a multiple of 16).
@@ -427,6 +456,9 @@ __device__ __forceinline__ void vec_body(const Params &p)
 template <typename T, bool kFused, bool kStoreSum, int kTpr, int kEpa, int kBlock>
 __device__ __forceinline__ void generic_body(const Params &p)
 {
+    using A = Access<T, kEpa>;
+    using V = typename A::V;
+    constexpr int kU = kGenericBatch;
     constexpr int kRpb = kBlock / kTpr;
     const int tid = threadIdx.x;
     const int lane = tid % kTpr;
@@ -439,23 +471,27 @@ __device__ __forceinline__ void generic_body(const Params &p)
 
     float sum_sq = 0.0f;
     if (active) {
-        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-            if constexpr (kEpa == 1) {
-                float v = Scalar<T>::get(p.x, base + j);
-                if constexpr (kFused)
-                    v = v + Scalar<T>::get(p.res, base + j);
-                sum_sq = __builtin_fmaf(v, v, sum_sq);
-            } else {
-                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
-                u32x4 rv;
-                if constexpr (kFused)
-                    rv = *(const u32x4 *)((const char *)p.res + (base + j) * Pack<T>::kBytes);
+        for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+            V xv[kU], rv[kU];
 #pragma unroll
-                for (int e = 0; e < kEpa; ++e) {
-                    float v = Pack<T>::get(xv, e);
+            for (int u = 0; u < kU; ++u) {
+                const int64_t j = j0 + u * kStride;
+                if (j < H) {
+                    xv[u] = A::load(p.x, base + j);
                     if constexpr (kFused)
-                        v = v + Pack<T>::get(rv, e);
-                    sum_sq = __builtin_fmaf(v, v, sum_sq);
+                        rv[u] = A::load(p.res, base + j);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (j0 + u * kStride < H) {
+#pragma unroll
+                    for (int e = 0; e < kEpa; ++e) {
+                        float v = A::get(xv[u], e);
+                        if constexpr (kFused)
+                            v = v + A::get(rv[u], e);
+                        sum_sq = __builtin_fmaf(v, v, sum_sq);
+                    }
                 }
             }
         }
@@ -464,39 +500,40 @@ __device__ __forceinline__ void generic_body(const Params &p)
     if (!active)
         return;
     // Second pass: each element is read again and written by the same lane that
-    // read it in the first pass, so in-place updates are safe.
-    for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-        if constexpr (kEpa == 1) {
-            float v = Scalar<T>::get(p.x, base + j);
-            if constexpr (kFused) {
-                v = v + Scalar<T>::get(p.res, base + j);
-                if constexpr (kStoreSum)
-                    Scalar<T>::put(p.res, base + j, v);
-            }
-            const float t = v * scale;
-            Scalar<T>::put(p.y, base + j, t * Scalar<T>::get(p.w, j));
-        } else {
-            const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
-            const u32x4 wv = *(const u32x4 *)((const char *)p.w + j * Pack<T>::kBytes);
-            float v[kEpa], o[kEpa];
-            if constexpr (kFused) {
-                const u32x4 rv = *(const u32x4 *)((const char *)p.res + (base + j) * Pack<T>::kBytes);
+    // read it in the first pass (a batch's loads all precede its stores), so
+    // in-place updates are safe.
+    for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+        V xv[kU], rv[kU], wv[kU];
 #pragma unroll
-                for (int e = 0; e < kEpa; ++e)
-                    v[e] = Pack<T>::get(xv, e) + Pack<T>::get(rv, e);
-                if constexpr (kStoreSum)
-                    *(u32x4 *)((char *)p.res + (base + j) * Pack<T>::kBytes) = Pack<T>::put(v);
-            } else {
-#pragma unroll
-                for (int e = 0; e < kEpa; ++e)
-                    v[e] = Pack<T>::get(xv, e);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = j0 + u * kStride;
+            if (j < H) {
+                xv[u] = A::load(p.x, base + j);
+                wv[u] = A::load(p.w, j);
+                if constexpr (kFused)
+                    rv[u] = A::load(p.res, base + j);
             }
+        }
 #pragma unroll
-            for (int e = 0; e < kEpa; ++e) {
-                const float t = v[e] * scale;
-                o[e] = t * Pack<T>::get(wv, e);
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = j0 + u * kStride;
+            if (j < H) {
+                float v[kEpa], o[kEpa];
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e) {
+                    v[e] = A::get(xv[u], e);
+                    if constexpr (kFused)
+                        v[e] = v[e] + A::get(rv[u], e);
+                }
+                if constexpr (kFused && kStoreSum)
+                    A::store(p.res, base + j, v);
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e) {
+                    const float t = v[e] * scale;
+                    o[e] = t * A::get(wv[u], e);
+                }
+                A::store(p.y, base + j, o);
             }
-            *(u32x4 *)((char *)p.y + (base + j) * Pack<T>::kBytes) = Pack<T>::put(o);
         }
     }
 }
@@ -732,6 +769,9 @@ __device__ __forceinline__ void softmax_vec_body(const Params &p)
 template <typename T, int kTpr, int kEpa, int kBlock>
 __device__ __forceinline__ void softmax_generic_body(const Params &p)
 {
+    using A = Access<T, kEpa>;
+    using V = typename A::V;
+    constexpr int kU = kGenericBatch;
     constexpr int kRpb = kBlock / kTpr;
     const int tid = threadIdx.x;
     const int lane = tid % kTpr;
@@ -743,47 +783,58 @@ __device__ __forceinline__ void softmax_generic_body(const Params &p)
     constexpr int64_t kStride = (int64_t)kTpr * kEpa;
 
     float mx = -__builtin_inff();
+    float s = 0.0f;
     if (active) {
-        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-            if constexpr (kEpa == 1) {
-                mx = fmaxf(mx, Scalar<T>::get(p.x, base + j));
-            } else {
-                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+        for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+            V xv[kU];
 #pragma unroll
-                for (int e = 0; e < kEpa; ++e)
-                    mx = fmaxf(mx, Pack<T>::get(xv, e));
-            }
+            for (int u = 0; u < kU; ++u)
+                if (j0 + u * kStride < H)
+                    xv[u] = A::load(p.x, base + j0 + u * kStride);
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (j0 + u * kStride < H)
+#pragma unroll
+                    for (int e = 0; e < kEpa; ++e)
+                        mx = fmaxf(mx, A::get(xv[u], e));
         }
     }
     const float m = team_fold<kTpr, kBlock, MaxOp>(mx);
-    float s = 0.0f;
     if (active) {
-        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-            if constexpr (kEpa == 1) {
-                s = s + softmax_exp<T>(Scalar<T>::get(p.x, base + j) - m);
-            } else {
-                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
+        for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+            V xv[kU];
 #pragma unroll
-                for (int e = 0; e < kEpa; ++e)
-                    s = s + softmax_exp<T>(Pack<T>::get(xv, e) - m);
-            }
+            for (int u = 0; u < kU; ++u)
+                if (j0 + u * kStride < H)
+                    xv[u] = A::load(p.x, base + j0 + u * kStride);
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (j0 + u * kStride < H)
+#pragma unroll
+                    for (int e = 0; e < kEpa; ++e)
+                        s = s + softmax_exp<T>(A::get(xv[u], e) - m);
         }
     }
     const float sum = team_sum<kTpr, kBlock>(s);
     if (!active)
         return;
     const float r = 1.0f / sum;
-    for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-        if constexpr (kEpa == 1) {
-            const float e = softmax_exp<T>(Scalar<T>::get(p.x, base + j) - m);
-            Scalar<T>::put(p.y, base + j, softmax_div<T>(e, sum, r));
-        } else {
-            const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
-            float o[kEpa];
+    for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+        V xv[kU];
 #pragma unroll
-            for (int e = 0; e < kEpa; ++e)
-                o[e] = softmax_div<T>(softmax_exp<T>(Pack<T>::get(xv, e) - m), sum, r);
-            *(u32x4 *)((char *)p.y + (base + j) * Pack<T>::kBytes) = Pack<T>::put(o);
+        for (int u = 0; u < kU; ++u)
+            if (j0 + u * kStride < H)
+                xv[u] = A::load(p.x, base + j0 + u * kStride);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = j0 + u * kStride;
+            if (j < H) {
+                float o[kEpa];
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e)
+                    o[e] = softmax_div<T>(softmax_exp<T>(A::get(xv[u], e) - m), sum, r);
+                A::store(p.y, base + j, o);
+            }
         }
     }
 }
@@ -991,6 +1042,9 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
 template <typename T, int kTpr, int kEpa, int kBlock>
 __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
 {
+    using A = Access<T, kEpa>;
+    using V = typename A::V;
+    constexpr int kU = kGenericBatch;
     constexpr int kRpb = kBlock / kTpr;
     const int tid = threadIdx.x;
     const int lane = tid % kTpr;
@@ -1003,24 +1057,27 @@ __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
 
     float ss = 0.0f, dot = 0.0f;
     if (active) {
-        for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-            if constexpr (kEpa == 1) {
-                const float xe = Scalar<T>::get(p.x, base + j);
-                const float ge = Scalar<T>::get(p.dy, base + j) * Scalar<T>::get(p.w, j);
-                ss = __builtin_fmaf(xe, xe, ss);
-                dot = __builtin_fmaf(ge, xe, dot);
-            } else {
-                const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
-                const u32x4 dv = *(const u32x4 *)((const char *)p.dy + (base + j) * Pack<T>::kBytes);
-                const u32x4 wv = *(const u32x4 *)((const char *)p.w + j * Pack<T>::kBytes);
+        for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+            V xv[kU], dv[kU], wv[kU];
 #pragma unroll
-                for (int e = 0; e < kEpa; ++e) {
-                    const float xe = Pack<T>::get(xv, e);
-                    const float ge = Pack<T>::get(dv, e) * Pack<T>::get(wv, e);
-                    ss = __builtin_fmaf(xe, xe, ss);
-                    dot = __builtin_fmaf(ge, xe, dot);
+            for (int u = 0; u < kU; ++u) {
+                const int64_t j = j0 + u * kStride;
+                if (j < H) {
+                    xv[u] = A::load(p.x, base + j);
+                    dv[u] = A::load(p.dy, base + j);
+                    wv[u] = A::load(p.w, j);
                 }
             }
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (j0 + u * kStride < H)
+#pragma unroll
+                    for (int e = 0; e < kEpa; ++e) {
+                        const float xe = A::get(xv[u], e);
+                        const float ge = A::get(dv[u], e) * A::get(wv[u], e);
+                        ss = __builtin_fmaf(xe, xe, ss);
+                        dot = __builtin_fmaf(ge, xe, dot);
+                    }
         }
     }
     team_fold2<kTpr, kBlock>(ss, dot);
@@ -1030,23 +1087,30 @@ __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
     const float c = ((dot / (float)p.hidden) * rho) * rho;
     if (p.rho != nullptr && lane == 0)
         p.rho[row] = rho;
-    for (int64_t j = (int64_t)lane * kEpa; j < H; j += kStride) {
-        if constexpr (kEpa == 1) {
-            const float xe = Scalar<T>::get(p.x, base + j);
-            const float ge = Scalar<T>::get(p.dy, base + j) * Scalar<T>::get(p.w, j);
-            Scalar<T>::put(p.dx, base + j, __builtin_fmaf(-c, xe, ge) * rho);
-        } else {
-            const u32x4 xv = *(const u32x4 *)((const char *)p.x + (base + j) * Pack<T>::kBytes);
-            const u32x4 dv = *(const u32x4 *)((const char *)p.dy + (base + j) * Pack<T>::kBytes);
-            const u32x4 wv = *(const u32x4 *)((const char *)p.w + j * Pack<T>::kBytes);
-            float o[kEpa];
+    for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
+        V xv[kU], dv[kU], wv[kU];
 #pragma unroll
-            for (int e = 0; e < kEpa; ++e) {
-                const float xe = Pack<T>::get(xv, e);
-                const float ge = Pack<T>::get(dv, e) * Pack<T>::get(wv, e);
-                o[e] = __builtin_fmaf(-c, xe, ge) * rho;
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = j0 + u * kStride;
+            if (j < H) {
+                xv[u] = A::load(p.x, base + j);
+                dv[u] = A::load(p.dy, base + j);
+                wv[u] = A::load(p.w, j);
             }
-            *(u32x4 *)((char *)p.dx + (base + j) * Pack<T>::kBytes) = Pack<T>::put(o);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t j = j0 + u * kStride;
+            if (j < H) {
+                float o[kEpa];
+#pragma unroll
+                for (int e = 0; e < kEpa; ++e) {
+                    const float xe = A::get(xv[u], e);
+                    const float ge = A::get(dv[u], e) * A::get(wv[u], e);
+                    o[e] = __builtin_fmaf(-c, xe, ge) * rho;
+                }
+                A::store(p.dx, base + j, o);
+            }
         }
     }
 }
