@@ -31,6 +31,7 @@ from .binding import (  # noqa: F401
     ks_rms_norm_residual,
     ks_rms_norm_residual_ex,
     rms_norm_backward,
+    rms_norm_autograd,
     ks_rms_norm_backward,
     ks_rms_norm_backward_ex,
     ks_rms_norm_backward_workspace_size,

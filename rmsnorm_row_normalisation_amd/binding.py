@@ -322,6 +322,31 @@ def rms_norm_backward(dy: torch.Tensor, x: torch.Tensor, weight: torch.Tensor, e
     return dx, dw
 
 
+class _RMSNormFunction(torch.autograd.Function):
+    """rms_norm with its gradients from ks_rms_norm_backward (the kernscope
+    reference of rms_norm supports autograd; the kernels themselves see only
+    detached tensors)."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, weight: torch.Tensor, eps: float) -> torch.Tensor:
+        xd, wd = x.detach(), weight.detach()
+        ctx.save_for_backward(xd, wd)
+        ctx.eps = eps
+        return rms_norm(xd, wd, eps)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x, w = ctx.saved_tensors
+        dx, dw = rms_norm_backward(dy.detach().contiguous(), x, w, ctx.eps, weight_grad=ctx.needs_input_grad[1])
+        return (dx if ctx.needs_input_grad[0] else None), dw, None
+
+
+def rms_norm_autograd(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6) -> torch.Tensor:
+    """rms_norm that records the autograd graph: the forward is ks_rms_norm, the
+    backward ks_rms_norm_backward (first derivatives only)."""
+    return _RMSNormFunction.apply(x, weight, eps)
+
+
 def silu_and_mul(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
     """SwiGLU of x with shape (..., 2D): a new (..., D) tensor (kernscope "SwiGLU activation")."""
     if x.dtype not in KS_DTYPE:

@@ -540,3 +540,9 @@ def test_backward_plans():
     for q in bad:
         assert bwd(A, None, A + 256 * MB, A + 512 * MB, A + 768 * MB, 0, 4096, None, 0,
                    plan=b.Plan.from_dict(q)) == INVALID
+
+
+def test_autograd_wrapper_checks_devices():
+    x = torch.zeros(2, 8, requires_grad=True)
+    with pytest.raises(ValueError):
+        ks.rms_norm_autograd(x, torch.ones(8))

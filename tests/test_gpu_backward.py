@@ -165,3 +165,21 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         check_bitexact(dx.cpu(), ex.cpu())
         check_bitexact(dw.cpu(), ew.cpu())
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32"])
+def test_autograd_wrapper(dtype):
+    """rms_norm_autograd: the forward matches rms_norm and the gradients that
+    reach x and weight are the backward's, checked against the oracle."""
+    inp = workloads.random_case((64, 1024), dtype, seed=123)
+    x = inp["x"].cuda().requires_grad_()
+    w = inp["weight"].cuda().requires_grad_()
+    dy = inp["residual"]
+    y = ks.rms_norm_autograd(x, w, 1e-6)
+    check_bitexact(y.detach().cpu(), ks.rms_norm(inp["x"].cuda(), inp["weight"].cuda(), 1e-6).cpu())
+    y.backward(dy.cuda())
+    torch.cuda.synchronize()
+    rx, rw = oracle.rms_norm_backward(dy, inp["x"], inp["weight"], 1e-6)
+    mdx, mdw = magnitudes(dy, inp["x"], inp["weight"], 1e-6)
+    check_gradient(x.grad.cpu(), rx, mdx)
+    check_gradient(w.grad.cpu(), rw, mdw)
