@@ -270,13 +270,27 @@ def test_library_missing_fails_loudly(monkeypatch, tmp_path):
         b.lib()
 
 
+def header_arities() -> dict[str, int]:
+    """Parameter count of every function the headers declare."""
+    out = {}
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for name, params in re.findall(r"\b(ks_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+            params = params.strip()
+            out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
 def test_ctypes_signatures_match_header():
-    # every ABI function has its argument count fixed in the binding
+    """Every declared function has its argument list fixed in the binding,
+    with the header's parameter count."""
     h = ks.lib()
-    for name in ("ks_rms_norm", "ks_fused_add_rms_norm"):
-        assert len(getattr(h, name).argtypes) == 8
-    for name in ("ks_rms_norm_ex", "ks_fused_add_rms_norm_ex"):
-        assert len(getattr(h, name).argtypes) == 9
+    arities = header_arities()
+    assert len(arities) >= 17
+    for name, n in arities.items():
+        fn = getattr(h, name)
+        assert fn.argtypes is not None, name
+        assert len(fn.argtypes) == n, (name, len(fn.argtypes), n)
     assert ctypes.sizeof(b.Plan) == 36
 
 
