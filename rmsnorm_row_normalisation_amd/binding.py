@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
         h.ks_last_hip_error.argtypes = []
+        h.ks_version.argtypes = []
         h.ks_version.restype = ctypes.c_char_p
         for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
                      "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
