@@ -6,28 +6,33 @@
 // sum of squares in fp32, scale = rsqrt(sum / H + eps), y = (v * scale) *
 // fp32(w), round to the storage dtype.  The fused form first forms the fp32
 // sum s = x + residual, stores cast(s) to residual, and normalises the
-// unrounded s into x.  SwiGLU and softmax are described in their own
-// sections below; softmax uses the same two kernel families, with a row
-// maximum before the sum and three passes on the generic path.
+// unrounded s into x; the out-of-place form normalises s into out and writes
+// nothing else.  SwiGLU, softmax and the backward are described in their own
+// sections below.
 //
-// Two kernel families:
+// Kernel families (one entry point per operation and family, at the end):
 //   *_vec           a team of kTpr lanes owns a row; each lane keeps kVpt
-//                   16-byte pieces of it in VGPRs, so every byte of x (and
-//                   residual) is read from HBM once and written once.  Loads
-//                   and stores are raw buffer instructions on one descriptor
-//                   per workgroup; pieces past the end of the row get an
-//                   out-of-range offset, so they read as zero and their
-//                   stores are dropped by the hardware range check.
+//                   16-byte pieces of it in VGPRs, so every byte of the
+//                   inputs is read from HBM once and every output byte
+//                   written once.  Loads and stores are raw buffer
+//                   instructions on one descriptor per group of rows; pieces
+//                   past the end of the row get an out-of-range offset, so
+//                   they read as zero and their stores are dropped by the
+//                   hardware range check.  The backward's vector kernel walks
+//                   several row groups per workgroup.
 //   *_generic       a team of kTpr lanes strides over the row with kEpa
-//                   elements per access, in two passes (sum, then normalise
-//                   and store).  Serves unaligned buffers, rows whose byte
-//                   size is not a multiple of 16, and rows wider than the
-//                   vector kernel holds in registers.
+//                   elements per access, in passes (normalisation: sum, then
+//                   normalise and store; softmax: maximum, sum, store).
+//                   Serves unaligned buffers, rows whose byte size is not a
+//                   multiple of 16, and rows wider than the vector kernels
+//                   hold in registers.
+//   rms_norm_backward_colsum / _dw   the weight gradient's column sums.
 //
-// Reduction: the vector kernel sums every row in one canonical order that is
-// the same for every launch shape (see "Reductions" below), so its results do
-// not depend on the plan or on the batch a row is in.  The generic kernel's
-// order depends on its plan, which depends only on (op, dtype, hidden).
+// Reduction: the vector kernels sum every row in one canonical order that is
+// the same for every launch shape (see "Reductions" below), so their results
+// do not depend on the plan or on the batch a row is in.  The generic
+// kernels' order depends on the plan, which depends only on (op, dtype,
+// hidden).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -44,14 +49,15 @@ constexpr int kBufferWord3 = 0x00020000;
 // loads there return zero and stores there are discarded.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// Arguments of the row kernels (normalisation forms and softmax).
 struct Params {
-    void *y;          // rms_norm: out;   fused: x (written)
-    const void *x;    // rms_norm: x;     fused: x (read; same buffer as y)
-    void *res;        // fused: residual (read, then written); rms_norm: unused
-    const void *w;    // weight [hidden]
+    void *y;          // output: rms_norm, out-of-place residual and softmax: out; fused in place: x
+    const void *x;    // input x (fused in place: the same buffer as y)
+    void *res;        // residual (fused in place: read, then written; out of place: read); else unused
+    const void *w;    // weight [hidden] (softmax: unused)
     int64_t rows;
     int32_t hidden;
-    float eps;
+    float eps;        // softmax: unused
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)

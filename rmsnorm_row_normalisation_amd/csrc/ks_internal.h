@@ -9,9 +9,9 @@
 
 namespace ks {
 
-// Everything one launch of a row operation needs (softmax uses y = out and
-// x only).  `plan` has been validated against the
-// buffers (see plan_fits in ks_api.cpp) before a launch function sees it.
+// Everything one launch of a row operation needs (softmax uses y = out and x
+// only).  `plan` has been validated against the buffers (plan_fits in
+// ks_api.cpp) before a launch function sees it.
 struct Launch {
     void *y;
     const void *x;
