@@ -55,7 +55,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // (Every vector plan sums a row in the same canonical order, so choosing the
 // launch shape from the batch size never changes a result.)
 //
-// Vector path (aligned buffers, row bytes a multiple of 16, rows up to 64 KiB):
+// Vector path (aligned buffers, row bytes a multiple of 16, rows up to 128 KiB):
 //   * work units are the row's 16-byte pieces; a batch holds rows * nvec;
 //   * pieces per lane aim at spreading the batch over about 131072 lanes
 //     (8 waves on each of the 256 compute units), between 1 and 8 per lane,
@@ -74,7 +74,8 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // in LDS (measured slower at every batch size).
 // These rules were fitted to timings of every compiled shape and hint
 // combination for hidden 1024..16384 and 1..32768 rows (bf16).
-// Rows wider than 64 KiB, or unaligned buffers, take the generic path.
+// Rows of 64..128 KiB take 1024-lane teams (5..8 pieces per lane); wider
+// rows, or unaligned buffers, take the generic path.
 //
 // Softmax keeps every element of its piece in registers as an fp32
 // exponential between the two reductions, so it takes at most 4 pieces per
@@ -133,7 +134,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     const int bwd_vpt = ks::bwd_max_vpt((int)esize);
     if (op == KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * bwd_vpt)
         return backward_vector_plan(nvec, vec_elems, bwd_vpt);
-    if (op != KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)kPolicyMaxTpr * ks::kMaxVpt) {
+    if (op != KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * ks::kMaxVpt) {
         const int64_t pieces = rows * nvec;
         const bool swiglu = op == KS_OP_SILU_AND_MUL;
         const bool adds_residual = op == KS_OP_FUSED_ADD_RMS_NORM || op == KS_OP_RMS_NORM_RESIDUAL;
@@ -151,11 +152,17 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
             const int64_t slots1024 = (nvec + ks::kMaxTpr - 1) / ks::kMaxTpr * ks::kMaxTpr;
             tpr = slots1024 <= slots512 ? ks::kMaxTpr : kPolicyMaxTpr;
         }
-        const int64_t max_tpr = (swiglu || (adds_residual && large)) ? ks::kMaxTpr : kPolicyMaxTpr;
+        const bool wide = nvec > (int64_t)kPolicyMaxTpr * ks::kMaxVpt;   // rows over 64 KiB
+        const int64_t max_tpr = (swiglu || wide || (adds_residual && large)) ? ks::kMaxTpr : kPolicyMaxTpr;
         tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > max_tpr ? max_tpr : tpr;
+        if (wide)
+            tpr = ks::kMaxTpr;
+        int64_t pieces_per_lane = (nvec + tpr - 1) / tpr;
+        if (op == KS_OP_RMS_NORM_RESIDUAL && tpr == ks::kMaxTpr && pieces_per_lane == 7)
+            pieces_per_lane = 8;   // the 7-piece build of this form spills registers
         plan.path = KS_PATH_VECTOR;
         plan.threads_per_row = (int32_t)tpr;
-        plan.vectors_per_thread = (int32_t)((nvec + tpr - 1) / tpr);
+        plan.vectors_per_thread = (int32_t)pieces_per_lane;
         plan.elems_per_access = vec_elems;
         plan.block_threads = ks::block_threads_for((int)tpr);
         plan.rows_per_block = plan.block_threads / (int32_t)tpr;
@@ -220,8 +227,7 @@ bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t hidden,
     if (p.path == KS_PATH_VECTOR) {
         if (!vec_ok || !is_pow2_team(p.threads_per_row) || !hints_compiled(p))
             return false;
-        const int maxv = p.threads_per_row == ks::kMaxTpr ? ks::kMaxVptAt1024 : ks::kMaxVpt;
-        if (p.vectors_per_thread < 1 || p.vectors_per_thread > maxv)
+        if (p.vectors_per_thread < 1 || p.vectors_per_thread > ks::kMaxVpt)
             return false;
         if ((int64_t)p.threads_per_row * p.vectors_per_thread * 16 < row_bytes)
             return false;

@@ -101,12 +101,13 @@ hipError_t launch_softmax_bf16(const Launch &l);
 constexpr int kSwigluGenericBlock = 256;
 
 // Vector path limits: threads per row 8..1024 (powers of two), vectors per
-// thread 1..8 (1..4 when a row spans 1024 threads, to stay within the VGPR
-// budget of a 1024-thread workgroup).
+// thread 1..8, so rows of up to 128 KiB.  A 1024-thread workgroup leaves 128
+// VGPRs per lane; the forward kernels use at most 122 at 8 pieces (the
+// out-of-place residual form spills 8 at exactly 7 pieces and 1024 lanes, so
+// the policy gives it 8 pieces there).
 constexpr int kMinTpr = 8;
 constexpr int kMaxTpr = 1024;
 constexpr int kMaxVpt = 8;
-constexpr int kMaxVptAt1024 = 4;
 
 inline int block_threads_for(int tpr) { return tpr < 256 ? 256 : tpr; }
 

@@ -76,18 +76,12 @@ hipError_t vec_by_vpt(const Launch &l)
     case 2: return vec_one<T, OP, TPR, 2>(l);
     case 3: return vec_one<T, OP, TPR, 3>(l);
     case 4: return vec_one<T, OP, TPR, 4>(l);
-    default: break;
+    case 5: return vec_one<T, OP, TPR, 5>(l);
+    case 6: return vec_one<T, OP, TPR, 6>(l);
+    case 7: return vec_one<T, OP, TPR, 7>(l);
+    case 8: return vec_one<T, OP, TPR, 8>(l);
+    default: return hipErrorInvalidValue;
     }
-    if constexpr (TPR < kMaxTpr) {
-        switch (l.plan.vectors_per_thread) {
-        case 5: return vec_one<T, OP, TPR, 5>(l);
-        case 6: return vec_one<T, OP, TPR, 6>(l);
-        case 7: return vec_one<T, OP, TPR, 7>(l);
-        case 8: return vec_one<T, OP, TPR, 8>(l);
-        default: break;
-        }
-    }
-    return hipErrorInvalidValue;
 }
 
 template <typename T, int OP>
@@ -164,18 +158,12 @@ hipError_t swiglu_by_vpt(const SwigluLaunch &l)
     case 2: return swiglu_one<T, TPR, 2>(l);
     case 3: return swiglu_one<T, TPR, 3>(l);
     case 4: return swiglu_one<T, TPR, 4>(l);
-    default: break;
+    case 5: return swiglu_one<T, TPR, 5>(l);
+    case 6: return swiglu_one<T, TPR, 6>(l);
+    case 7: return swiglu_one<T, TPR, 7>(l);
+    case 8: return swiglu_one<T, TPR, 8>(l);
+    default: return hipErrorInvalidValue;
     }
-    if constexpr (TPR < kMaxTpr) {
-        switch (l.plan.vectors_per_thread) {
-        case 5: return swiglu_one<T, TPR, 5>(l);
-        case 6: return swiglu_one<T, TPR, 6>(l);
-        case 7: return swiglu_one<T, TPR, 7>(l);
-        case 8: return swiglu_one<T, TPR, 8>(l);
-        default: break;
-        }
-    }
-    return hipErrorInvalidValue;
 }
 
 template <typename T>

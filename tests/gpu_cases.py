@@ -92,7 +92,7 @@ def all_plans(dtype: torch.dtype, hidden: int, aligned: bool = True) -> list:
     if aligned and row_bytes % 16 == 0:
         tpr = 8
         while tpr <= 1024:
-            maxv = 4 if tpr == 1024 else 8
+            maxv = 8
             for vpt in range(1, maxv + 1):
                 if tpr * vpt * 16 >= row_bytes:
                     block = max(256, tpr)

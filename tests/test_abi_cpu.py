@@ -130,8 +130,12 @@ def test_explicit_plans_are_checked():
     assert rms(y, x, w, 4, 4096, plan=_plan(path=7)) == INVALID
     assert rms(y, x, w, 0, 4096, plan=_plan(threads_per_row=1024, vectors_per_thread=4, rows_per_block=1,
                                             block_threads=1024)) == OK
-    assert rms(y, x, w, 4, 4096, plan=_plan(threads_per_row=1024, vectors_per_thread=5, rows_per_block=1,
+    assert rms(y, x, w, 0, 4096, plan=_plan(threads_per_row=1024, vectors_per_thread=8, rows_per_block=1,
+                                            block_threads=1024)) == OK
+    assert rms(y, x, w, 4, 4096, plan=_plan(threads_per_row=1024, vectors_per_thread=9, rows_per_block=1,
                                             block_threads=1024)) == INVALID
+    assert rms(y, x, w, 4, 65544, plan=_plan(threads_per_row=1024, vectors_per_thread=8, rows_per_block=1,
+                                             block_threads=1024)) == INVALID     # 131088-byte rows do not fit
     # the vector path needs 16-byte aligned buffers
     assert rms(y + 2, x, w, 4, 4096, plan=_plan()) == INVALID
     # generic plans
@@ -173,7 +177,10 @@ EXPECTED = {
     ("rms_norm", torch.bfloat16, 1000, 3): (0, 128, 1, 2, 0),            # 2000-byte rows are 16-byte multiples
     ("rms_norm", torch.bfloat16, 1001, 3): (1, 64, 0, 4, 0),
     ("rms_norm", torch.bfloat16, 32768, 4): (0, 512, 8, 1, 0),           # 64 KiB rows: widest vector plan
-    ("rms_norm", torch.bfloat16, 32776, 4): (1, 1024, 0, 1, 0),          # wider: generic 16-byte path
+    ("rms_norm", torch.bfloat16, 32776, 4): (0, 1024, 5, 1, 0),          # 64..128 KiB rows: 1024-lane teams
+    ("softmax", torch.float16, 65536, 8): (0, 1024, 8, 1, 0),            # 128 KiB rows: the widest vector plan
+    ("rms_norm_residual", torch.bfloat16, 57344, 4): (0, 1024, 8, 1, 0),  # 7 pieces per lane would spill: 8
+    ("rms_norm", torch.bfloat16, 65544, 4): (1, 1024, 0, 1, 0),          # wider: generic 16-byte path
 }
 
 
@@ -357,7 +364,7 @@ def test_silu_policy_rule():
             p = ks.get_plan("silu_and_mul", torch.bfloat16, d, rows).as_dict()
             assert p["path"] == 0
             tpr, vpt = p["threads_per_row"], p["vectors_per_thread"]
-            assert tpr * vpt >= nvec and vpt <= (8 if tpr == 512 else 4 if tpr == 1024 else 2)
+            assert tpr * vpt >= nvec and vpt <= (8 if tpr >= 512 else 2)
             if tpr == 1024:
                 assert -(-nvec // 1024) * 1024 <= -(-nvec // 512) * 512
             elif vpt > 2:
@@ -404,7 +411,7 @@ def test_softmax_plans_and_policy():
                     p = ks.get_plan("softmax", dtype, hidden, rows, aligned).as_dict()
                     assert p["weight_lds"] == 0
                     if p["path"] == 0:
-                        assert aligned and (hidden * es) % 16 == 0 and hidden * es <= 65536
+                        assert aligned and (hidden * es) % 16 == 0 and hidden * es <= 131072
                         assert (p["load_nt"], p["store_nt"]) == (1, 1)
                     base = A if aligned else A + 2
                     assert smax(base + 256 * MB, base, 0, hidden, dtype=code, plan=b.Plan.from_dict(p)) == OK

@@ -94,7 +94,7 @@ def test_every_plan(dtype, hidden):
     tpr = 8
     n = 0
     while tpr <= 1024:
-        maxv = 4 if tpr == 1024 else 8
+        maxv = 8
         for vpt in range(1, maxv + 1):
             if tpr * vpt * 16 >= hidden * es:
                 block = max(256, tpr)

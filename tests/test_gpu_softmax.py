@@ -123,7 +123,7 @@ def _vector_plans(hidden: int, es: int) -> list:
     plans = []
     tpr = 8
     while tpr <= 1024:
-        maxv = 4 if tpr == 1024 else 8
+        maxv = 8
         for vpt in range(1, maxv + 1):
             if tpr * vpt * 16 >= hidden * es and (hidden * es) % 16 == 0:
                 block = max(256, tpr)

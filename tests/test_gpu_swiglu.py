@@ -103,7 +103,7 @@ def test_every_plan(dtype, d):
     tpr = 8
     plans = []
     while tpr <= 1024:
-        maxv = 4 if tpr == 1024 else 8
+        maxv = 8
         for vpt in range(1, maxv + 1):
             if tpr * vpt * 16 >= d * es and (d * es) % 16 == 0:
                 block = max(256, tpr)
