@@ -20,10 +20,10 @@ Timing:
     replayed until K steps have run, between a synchronize and two events on
     the launch stream;
   * per kernel (``per_op``, ``roofline``): the same, with a graph holding only
-    that op's launches, back to back; the average launch period includes the
-    short gap between consecutive kernels, so it is an upper bound on the
-    kernel's own duration (rocprofv3's kernel trace of the same run gives the
-    duration alone);
+    that op's launches, back to back (the median of three timed regions); the
+    average launch period includes the short gap between consecutive kernels,
+    so it is an upper bound on the kernel's own duration (rocprofv3's kernel
+    trace of the same run gives the duration alone);
   * ``copy_reference``: the HIP runtime's own device-to-device copy of one
     batch-sized tensor, timed the same way: what a plain read+write stream of
     that size achieves on this GPU.
@@ -275,23 +275,28 @@ class Rig:
         else:
             self.ks.silu_and_mul(s["sx"], out=s["sout"])
 
-    def timed_graph(self, body, per_rotation: int, reps: int) -> float:
+    def timed_graph(self, body, per_rotation: int, reps: int, repeats: int = 1) -> float:
         """Capture body(i) for i in range(per_rotation) into a HIP graph and replay
-        it `reps` times between two events on the launch stream; milliseconds."""
+        it `reps` times between two events on the launch stream; milliseconds.
+        With repeats > 1 the timed region runs that many times and the median
+        is returned."""
         graph = torch.cuda.CUDAGraph()
+        times = []
         with torch.cuda.stream(self.stream):
             with torch.cuda.graph(graph, stream=self.stream):
                 for i in range(per_rotation):
                     body(i)
             graph.replay()                                   # untimed
             torch.cuda.synchronize()
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ev0.record(self.stream)
-            for _ in range(reps):
-                graph.replay()
-            ev1.record(self.stream)
-            torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1)
+            for _ in range(repeats):
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record(self.stream)
+                for _ in range(reps):
+                    graph.replay()
+                ev1.record(self.stream)
+                torch.cuda.synchronize()
+                times.append(ev0.elapsed_time(ev1))
+        return float(np.median(times))
 
     def warmup(self, n: int) -> None:
         with torch.cuda.stream(self.stream):
@@ -325,7 +330,8 @@ def measure(wl, inp, ks, args) -> dict:
     total_ms = rig.timed_graph(lambda i: [rig.launch(op, i) for op in wl.ops], rig.nsets, reps)
     per_op = {}
     for op in wl.ops:
-        ms = rig.timed_graph(lambda i, op=op: rig.launch(op, i), rig.nsets, reps)
+        # per-op figures: median of three timed regions (run-to-run spread is a few %)
+        ms = rig.timed_graph(lambda i, op=op: rig.launch(op, i), rig.nsets, reps, repeats=3)
         us = ms * 1e3 / steps
         gbps = op_bytes[op] / (us * 1e-6) / 1e9
         per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
@@ -626,7 +632,7 @@ def main() -> None:
                 "frac": round(per_op[dominant]["gbps"] / HBM_PEAK_GBPS, 4),
                 "traffic": (traffic or {}).get(dominant)}
     timing_mode = (f"HIP graph replay, {res['reps']} replays of {res['nsets']} steps; per op: graphs of "
-                   "back-to-back launches of that op")
+                   "back-to-back launches of that op, median of three timed regions")
     line = {
         "metric": METRIC, "value": round(res["value"], 1), "unit": "GB/s", "n_gpus": 1, "steps": res["steps"],
         "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6), "higher_is_better": True,
