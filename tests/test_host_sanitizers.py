@@ -30,3 +30,18 @@ def test_abi_sweep_under_sanitizers(tmp_path):
                               "UBSAN_OPTIONS": "print_stacktrace=1"})
     assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
     assert "abi sweep:" in run.stdout
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_oracle_sweep_under_sanitizers(tmp_path):
+    """Every oracle function over small shapes and arbitrary bit patterns, each
+    buffer exactly the size the call needs."""
+    exe = tmp_path / "oracle_sweep"
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-ffp-contract=off", os.path.join(ROOT, "oracle", "ks_oracle.c"), os.path.join(HOST, "oracle_sweep.c"),
+           "-lm", "-o", str(exe)]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-3000:]
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert run.returncode == 0, (run.stdout[-2000:], run.stderr[-4000:])
+    assert "oracle sweep:" in run.stdout
