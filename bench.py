@@ -255,6 +255,9 @@ class Rig:
         if "rms_norm_backward" in wl.ops:
             self.workspace = torch.empty(ks.ks_rms_norm_backward_workspace_size(wl.rows, wl.hidden),
                                          dtype=torch.uint8, device="cuda")
+        if "softmax" in wl.ops:          # split plans keep per-chunk statistics here
+            need = ks.ks_softmax_workspace_size(wl.rows, wl.hidden, ks.KS_DTYPE[wl.torch_dtype])
+            self.softmax_workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         self.rotation_mib = self.nsets * per_set / 2**20
         self.stream = torch.cuda.Stream()
         torch.cuda.synchronize()
@@ -266,7 +269,7 @@ class Rig:
         elif op == "fused_add_rms_norm":
             self.ks.fused_add_rms_norm(s["fx"], s["fr"], self.w, self.wl.eps)
         elif op == "softmax":
-            self.ks.softmax(s["mx"], out=s["mout"])
+            self.ks.softmax(s["mx"], out=s["mout"], workspace=self.softmax_workspace)
         elif op == "rms_norm_residual":
             self.ks.rms_norm_residual(s["ox"], s["or"], self.w, self.wl.eps, out=s["oout"])
         elif op == "rms_norm_backward":
@@ -337,7 +340,7 @@ def measure(wl, inp, ks, args) -> dict:
         per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                       "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden // 2 if op == "silu_and_mul" else wl.hidden,
-                                          wl.rows).as_dict()}
+                                          wl.rows, workspace=op == "softmax").as_dict()}
     copy = rig.copy_reference(reps)
     ms_per_step = total_ms / steps
     result = {"steps": steps, "reps": reps, "nsets": rig.nsets, "rotation_mib": rig.rotation_mib,

@@ -88,20 +88,29 @@ typedef enum {
  *                    then normalise and store; softmax: three, maximum, sum,
  *                    store); used for unaligned buffers,
  *                    row sizes that are not a multiple of 16 bytes, and rows
- *                    wider than the vector path holds. */
+ *                    wider than the vector path holds.
+ *   KS_PATH_SPLIT    softmax with a workspace only: a row is cut into chunks
+ *                    of threads_per_row (256) * vectors_per_thread (1, 2 or
+ *                    4) 16-byte pieces, one workgroup per chunk and row, in
+ *                    two launches (each chunk's maximum and exponential sum,
+ *                    then the combination and the store); for wide rows in
+ *                    batches too small to fill the device one row per
+ *                    workgroup.  Needs aligned buffers, row bytes a multiple
+ *                    of 16 and at most 65535 rows. */
 typedef enum {
     KS_PATH_VECTOR = 0,
-    KS_PATH_GENERIC = 1
+    KS_PATH_GENERIC = 1,
+    KS_PATH_SPLIT = 2
 } ks_path_t;
 
 typedef struct {
     int32_t path;               /* ks_path_t */
     int32_t threads_per_row;    /* 8, 16, 32, 64, 128, 256, 512 or 1024 */
-    int32_t vectors_per_thread; /* vector path: 1..8; generic path: 0 */
+    int32_t vectors_per_thread; /* vector path: 1..8; split path: 1, 2 or 4; generic path: 0 */
     int32_t elems_per_access;   /* generic path: 1 or 16 / element size; vector path: 16 / element size */
     int32_t rows_per_block;     /* rows handled by one workgroup */
     int32_t block_threads;      /* workgroup size */
-    /* Vector path only (0 on the generic path).  Memory hints that change
+    /* Vector path (split path: 1, 1, 0; generic path: 0).  Memory hints that change
      * speed, never results; compiled combinations (load_nt, store_nt,
      * weight_lds): (0,0,0), (1,1,0), (0,1,0), (1,1,1). */
     int32_t load_nt;            /* x / residual loads marked non-temporal */
@@ -201,11 +210,15 @@ ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, con
  * row size.  All vector-path plans sum a row in one canonical order, so the plan
  * may change with `rows` while every row's result stays the same; the path
  * (vector or generic) depends only on dtype, hidden and alignment.
- * `aligned` != 0 means all buffers are 16-byte aligned.  No HIP call.
- * Returns KS_ERROR_INVALID_VALUE for a NULL plan, a bad row count or hidden
- * size, or an unknown op.
+ * `flags`: KS_PLAN_ALIGNED when all buffers are 16-byte aligned;
+ * KS_PLAN_WORKSPACE for the plan of a call that passes a workspace
+ * (ks_softmax_ws, whose plan may be a split plan; the other ops ignore it).
+ * No HIP call.  Returns KS_ERROR_INVALID_VALUE for a NULL plan, a bad row
+ * count or hidden size, an unknown op or unknown flag bits.
  */
-ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned,
+#define KS_PLAN_ALIGNED 1
+#define KS_PLAN_WORKSPACE 2
+ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags,
                         ks_plan_t *plan);
 
 /*
@@ -273,9 +286,44 @@ ks_status_t ks_softmax(void *out, const void *x, int64_t rows, int64_t hidden, k
                        hipStream_t stream);
 
 /* Softmax with an explicit plan (op KS_OP_SOFTMAX); plans with weight_lds
- * set are rejected. */
+ * set are rejected, and so are split plans, which need a workspace
+ * (ks_softmax_ws_ex). */
 ks_status_t ks_softmax_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
                           const ks_plan_t *plan, hipStream_t stream);
+
+/* Bytes of workspace ks_softmax_ws_ex needs for `plan`, or, with plan null,
+ * for the plan ks_softmax_ws picks for 16-byte aligned buffers (the most any
+ * alignment needs): 8 * rows * chunks for a split plan, else 0.  Returns
+ * KS_ERROR_INVALID_VALUE for bad sizes or a null `bytes`. */
+ks_status_t ks_softmax_workspace_size(int64_t rows, int64_t hidden, ks_dtype_t dtype, const ks_plan_t *plan,
+                                      size_t *bytes);
+
+/*
+ * Softmax with a caller-owned workspace: the same contract, arguments and
+ * overlap rules as ks_softmax, and the policy may also pick a split plan
+ * (KS_PATH_SPLIT) for wide rows in small batches, which spreads one row over
+ * many workgroups.  A split plan keeps each chunk's maximum m_c and sum s_c
+ * of exp(x - m_c) in the workspace and forms the row sum as the sum of
+ * s_c * exp(m_c - M), M the row maximum: the same contract, within the same
+ * bounds, but the row sum is rounded in another order than on the one-pass
+ * plans, so its results may differ from ks_softmax's in the last bit.
+ * workspace        device memory, 4-byte aligned, of at least
+ *                  ks_softmax_workspace_size bytes (it may be null when that
+ *                  is 0); owned by the caller, only written by the call, and
+ *                  in use until the call's work on `stream` has finished.
+ *                  It must not overlap x or out (KS_ERROR_OVERLAP).
+ * workspace_bytes  its size; too small (or a null workspace when the plan
+ *                  needs one) is KS_ERROR_INVALID_VALUE.
+ */
+ks_status_t ks_softmax_ws(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* ks_softmax_ws with an explicit plan (any plan ks_softmax_ex accepts, or a
+ * split plan: path KS_PATH_SPLIT, threads_per_row 256, vectors_per_thread 1,
+ * 2 or 4, elems_per_access 16 / element size, rows_per_block 1,
+ * block_threads 256, load_nt = store_nt = 1, weight_lds 0). */
+ks_status_t ks_softmax_ws_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                             void *workspace, size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *ks_status_string(ks_status_t status);

@@ -27,6 +27,11 @@ from .binding import (  # noqa: F401
     softmax,
     ks_softmax,
     ks_softmax_ex,
+    ks_softmax_workspace_size,
+    ks_softmax_ws,
+    ks_softmax_ws_ex,
+    KS_PLAN_ALIGNED,
+    KS_PLAN_WORKSPACE,
     rms_norm_residual,
     ks_rms_norm_residual,
     ks_rms_norm_residual_ex,

@@ -23,7 +23,7 @@ KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP
 KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 (KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX, KS_OP_RMS_NORM_RESIDUAL,
  KS_OP_RMS_NORM_BACKWARD) = range(6)
-KS_PATH_VECTOR, KS_PATH_GENERIC = 0, 1
+KS_PATH_VECTOR, KS_PATH_GENERIC, KS_PATH_SPLIT = 0, 1, 2
 
 
 class KsError(RuntimeError):
@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
                                               vp]
         h.ks_rms_norm_residual_ex.argtypes = [vp, vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_softmax_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
+        h.ks_softmax_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(Plan), ctypes.POINTER(sz)]
+        h.ks_softmax_ws.argtypes = [vp, vp, i64, i64, i32, vp, sz, vp]
+        h.ks_softmax_ws_ex.argtypes = [vp, vp, i64, i64, i32, vp, sz, ctypes.POINTER(Plan), vp]
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
         h.ks_last_hip_error.argtypes = []
@@ -107,7 +110,8 @@ def lib() -> ctypes.CDLL:
         for name in ("ks_rms_norm", "ks_fused_add_rms_norm", "ks_rms_norm_ex", "ks_fused_add_rms_norm_ex",
                      "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
                      "ks_softmax_ex", "ks_rms_norm_residual", "ks_rms_norm_residual_ex",
-                     "ks_rms_norm_backward_workspace_size", "ks_rms_norm_backward", "ks_rms_norm_backward_ex"):
+                     "ks_rms_norm_backward_workspace_size", "ks_rms_norm_backward", "ks_rms_norm_backward_ex",
+                     "ks_softmax_workspace_size", "ks_softmax_ws", "ks_softmax_ws_ex"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -196,9 +200,32 @@ def ks_softmax_ex(out: int, x: int, rows: int, hidden: int, dtype: int, plan: Pl
     return lib().ks_softmax_ex(out, x, rows, hidden, dtype, ctypes.byref(plan) if plan is not None else None, stream)
 
 
-def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True) -> Plan:
+def ks_softmax_workspace_size(rows: int, hidden: int, dtype: int, plan: Plan | None = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ks_softmax_workspace_size(rows, hidden, dtype, ctypes.byref(plan) if plan is not None else None,
+                                           ctypes.byref(n)), "ks_softmax_workspace_size")
+    return n.value
+
+
+def ks_softmax_ws(out: int, x: int, rows: int, hidden: int, dtype: int, workspace: int, workspace_bytes: int,
+                  stream: int) -> int:
+    return lib().ks_softmax_ws(out, x, rows, hidden, dtype, workspace, workspace_bytes, stream)
+
+
+def ks_softmax_ws_ex(out: int, x: int, rows: int, hidden: int, dtype: int, workspace: int, workspace_bytes: int,
+                     plan: Plan | None, stream: int) -> int:
+    return lib().ks_softmax_ws_ex(out, x, rows, hidden, dtype, workspace, workspace_bytes,
+                                  ctypes.byref(plan) if plan is not None else None, stream)
+
+
+KS_PLAN_ALIGNED = 1
+KS_PLAN_WORKSPACE = 2
+
+
+def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True, workspace: bool = False) -> Plan:
     plan = Plan()
-    _check(lib().ks_get_plan(op, dtype, rows, hidden, int(bool(aligned)), ctypes.byref(plan)), "ks_get_plan")
+    flags = (KS_PLAN_ALIGNED if aligned else 0) | (KS_PLAN_WORKSPACE if workspace else 0)
+    _check(lib().ks_get_plan(op, dtype, rows, hidden, flags, ctypes.byref(plan)), "ks_get_plan")
     return plan
 
 
@@ -373,9 +400,17 @@ def silu_and_mul(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan
     return out
 
 
-def softmax(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None) -> torch.Tensor:
+def softmax(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | None = None, split: bool = True,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Softmax over the last dimension (kernscope "Softmax"): returns ``out`` (a new
-    tensor unless given; may be ``x``)."""
+    tensor unless given; may be ``x``).
+
+    With ``split`` (the default) the call passes a workspace (ks_softmax_ws_ex),
+    so wide rows in small batches may be split over many workgroups; the
+    workspace is ``workspace`` (a contiguous tensor on x's device of at least
+    ks_softmax_workspace_size bytes) or, when that is None and the plan needs
+    one, a new tensor.  ``split=False`` (ks_softmax_ex) keeps to the one-pass
+    plans, whose bits for a row never depend on the batch it is in."""
     if x.dtype not in KS_DTYPE:
         raise TypeError(f"softmax: unsupported dtype {x.dtype}")
     if x.device.type != "cuda":
@@ -392,16 +427,30 @@ def softmax(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | No
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
         raise ValueError(f"softmax: out must be a contiguous {x.dtype} tensor of shape {tuple(x.shape)}")
+    dt = KS_DTYPE[x.dtype]
     with torch.cuda.device(x.device):
-        st = ks_softmax_ex(out.data_ptr(), x.data_ptr(), rows, hidden, KS_DTYPE[x.dtype], plan, _stream(x))
+        if not split:
+            st = ks_softmax_ex(out.data_ptr(), x.data_ptr(), rows, hidden, dt, plan, _stream(x))
+        else:
+            need = ks_softmax_workspace_size(rows, hidden, dt, plan)
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+            elif (workspace.device != x.device or not workspace.is_contiguous()
+                  or workspace.numel() * workspace.element_size() < need):
+                raise ValueError(f"softmax: workspace must be a contiguous tensor of >= {need} bytes on {x.device}")
+            wp = workspace.data_ptr() if workspace is not None else 0
+            wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            st = ks_softmax_ws_ex(out.data_ptr(), x.data_ptr(), rows, hidden, dt, wp, wb, plan, _stream(x))
     _check(st, "ks_softmax")
     return out
 
 
-def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: bool = True) -> Plan:
+def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: bool = True,
+             workspace: bool = False) -> Plan:
     """The plan the library picks for this op, dtype, row size and batch (ks_get_plan).
-    For silu_and_mul, ``hidden`` is the output width D."""
+    For silu_and_mul, ``hidden`` is the output width D; ``workspace`` asks for the
+    plan of a call that passes one (softmax: ``softmax(split=True)``)."""
     code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM,
             "silu_and_mul": KS_OP_SILU_AND_MUL, "softmax": KS_OP_SOFTMAX,
             "rms_norm_residual": KS_OP_RMS_NORM_RESIDUAL, "rms_norm_backward": KS_OP_RMS_NORM_BACKWARD}[op]
-    return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned)
+    return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned, workspace)

@@ -123,7 +123,40 @@ ks_plan_t backward_vector_plan(int64_t nvec, int vec_elems, int max_vpt)
     return plan;
 }
 
-ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned)
+// Split softmax (only where the caller gives a workspace): a split plan pays
+// two launches and a second read of x, and wins where one workgroup per row
+// leaves most compute units idle for long:
+//   * rows wider than the vector path (over 8192 pieces, where the one-pass
+//     plan is the three-pass generic one): any batch;
+//   * rows of 4096..8192 pieces: batches of at most 4 rows (4096..5119
+//     pieces), 16 (5120..6143) or 32 (6144..8192).
+// Pieces per lane: 1 while a one-piece split has at most 1024 workgroups,
+// 2 up to 4096, else 4 (longer chunks for large grids).
+// Fitted to timings of the one-pass policy plan against every split plan for
+// hidden 4096..131072 and 1..2048 rows (bf16, fp16, fp32).
+constexpr int64_t kSplitVectorPieces = 8192;
+
+int64_t split_max_rows(int64_t nvec)
+{
+    return nvec > kSplitVectorPieces ? ks::kSplitMaxRows : nvec >= 6144 ? 32 : nvec >= 5120 ? 16 : nvec >= 4096 ? 4 : 0;
+}
+
+bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, ks_plan_t *plan)
+{
+    if (op != KS_OP_SOFTMAX || !vec_ok || rows > split_max_rows(nvec))
+        return false;
+    const int64_t groups = rows * ks::split_chunks(nvec * 16, 1);
+    plan->path = KS_PATH_SPLIT;
+    plan->threads_per_row = ks::kSplitBlock;
+    plan->vectors_per_thread = groups <= 1024 ? 1 : groups <= 4096 ? 2 : 4;
+    plan->rows_per_block = 1;
+    plan->block_threads = ks::kSplitBlock;
+    plan->load_nt = 1;
+    plan->store_nt = 1;
+    return true;
+}
+
+ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned, bool split_ok = false)
 {
     ks_plan_t plan;
     memset(&plan, 0, sizeof(plan));
@@ -132,6 +165,10 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     const int vec_elems = (int)(16 / esize);
     const int64_t nvec = row_bytes / 16;
     const int bwd_vpt = ks::bwd_max_vpt((int)esize);
+    if (split_ok && split_policy(op, rows, nvec, aligned && row_bytes % 16 == 0, &plan)) {
+        plan.elems_per_access = vec_elems;
+        return plan;
+    }
     if (op == KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * bwd_vpt)
         return backward_vector_plan(nvec, vec_elems, bwd_vpt);
     if (op != KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * ks::kMaxVpt) {
@@ -198,10 +235,19 @@ bool hints_compiled(const ks_plan_t &p)
 
 // Whether an explicit plan names a compiled kernel that covers this row and
 // suits the buffers' alignment.
-bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t hidden, bool aligned)
+bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned,
+               bool split_ok)
 {
     if (op == KS_OP_SOFTMAX && p.weight_lds != 0)
         return false;
+    if (p.path == KS_PATH_SPLIT) {
+        const int64_t row_bytes = hidden * elem_size(dtype);
+        const int v = p.vectors_per_thread;
+        return split_ok && op == KS_OP_SOFTMAX && aligned && row_bytes % 16 == 0 && rows <= ks::kSplitMaxRows &&
+               p.threads_per_row == ks::kSplitBlock && (v == 1 || v == 2 || v == 4) &&
+               p.elems_per_access == (int)(16 / elem_size(dtype)) && p.rows_per_block == 1 &&
+               p.block_threads == ks::kSplitBlock && p.load_nt == 1 && p.store_nt == 1;
+    }
     if (op == KS_OP_SILU_AND_MUL) {
         if (p.weight_lds != 0)
             return false;
@@ -284,16 +330,55 @@ ks_status_t launch(ks::Launch &l, ks_dtype_t dtype)
 }
 
 ks_status_t select_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden,
-                        bool aligned, ks_plan_t *out)
+                        bool aligned, ks_plan_t *out, bool split_ok = false)
 {
     if (requested == nullptr) {
-        *out = policy(op, dtype, rows, hidden, aligned);
+        *out = policy(op, dtype, rows, hidden, aligned, split_ok);
         return KS_SUCCESS;
     }
-    if (!plan_fits(*requested, op, dtype, hidden, aligned))
+    if (!plan_fits(*requested, op, dtype, rows, hidden, aligned, split_ok))
         return KS_ERROR_INVALID_VALUE;
     *out = *requested;
     return KS_SUCCESS;
+}
+
+// Workspace bytes of a softmax plan: a (maximum, sum) pair per chunk on the
+// split path, none otherwise.
+size_t softmax_workspace_bytes(const ks_plan_t &p, int64_t rows, int64_t row_bytes)
+{
+    if (p.path != KS_PATH_SPLIT || p.vectors_per_thread < 1)
+        return 0;
+    return (size_t)ks::split_workspace_floats(rows, row_bytes, p.vectors_per_thread) * sizeof(float);
+}
+
+// Softmax with or without a workspace (split_ok: the caller passed one, so
+// the policy may pick a split plan and an explicit split plan is accepted).
+ks_status_t softmax_call(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype, void *workspace,
+                         size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream, bool split_ok)
+{
+    if (!valid_dtype(dtype))
+        return KS_ERROR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
+        return KS_ERROR_INVALID_VALUE;
+    if (rows > 0 && (out == nullptr || x == nullptr))
+        return KS_ERROR_INVALID_VALUE;
+    const bool aligned = aligned16(out) && aligned16(x);
+    ks::Launch l{out, x, nullptr, nullptr, rows, (int32_t)hidden, 0.0f, KS_OP_SOFTMAX, {}, stream};
+    ks_status_t st = select_plan(plan, KS_OP_SOFTMAX, dtype, rows, hidden, aligned, &l.plan, split_ok);
+    if (st != KS_SUCCESS)
+        return st;
+    const int64_t nbytes = rows * hidden * elem_size(dtype);
+    const size_t need = softmax_workspace_bytes(l.plan, rows, hidden * elem_size(dtype));
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 3u) != 0))
+        return KS_ERROR_INVALID_VALUE;
+    if (rows == 0)
+        return KS_SUCCESS;
+    if (out != x && overlaps(out, nbytes, x, nbytes))
+        return KS_ERROR_OVERLAP;
+    if (overlaps(workspace, (int64_t)need, out, nbytes) || overlaps(workspace, (int64_t)need, x, nbytes))
+        return KS_ERROR_OVERLAP;
+    l.work = (float *)workspace;
+    return launch(l, dtype);
 }
 
 }  // namespace
@@ -485,37 +570,48 @@ ks_status_t ks_silu_and_mul(void *out, const void *x, int64_t rows, int64_t d, k
 ks_status_t ks_softmax_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
                           const ks_plan_t *plan, hipStream_t stream)
 {
-    if (!valid_dtype(dtype))
-        return KS_ERROR_UNSUPPORTED_DTYPE;
-    if (rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
-        return KS_ERROR_INVALID_VALUE;
-    if (rows > 0 && (out == nullptr || x == nullptr))
-        return KS_ERROR_INVALID_VALUE;
-    const bool aligned = aligned16(out) && aligned16(x);
-    ks::Launch l{out, x, nullptr, nullptr, rows, (int32_t)hidden, 0.0f, KS_OP_SOFTMAX, {}, stream};
-    ks_status_t st = select_plan(plan, KS_OP_SOFTMAX, dtype, rows, hidden, aligned, &l.plan);
-    if (st != KS_SUCCESS || rows == 0)
-        return st;
-    const int64_t nbytes = rows * hidden * elem_size(dtype);
-    if (out != x && overlaps(out, nbytes, x, nbytes))
-        return KS_ERROR_OVERLAP;
-    return launch(l, dtype);
+    return softmax_call(out, x, rows, hidden, dtype, nullptr, 0, plan, stream, false);
 }
 
 ks_status_t ks_softmax(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype, hipStream_t stream)
 {
-    return ks_softmax_ex(out, x, rows, hidden, dtype, nullptr, stream);
+    return softmax_call(out, x, rows, hidden, dtype, nullptr, 0, nullptr, stream, false);
 }
 
-ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int aligned, ks_plan_t *plan)
+ks_status_t ks_softmax_workspace_size(int64_t rows, int64_t hidden, ks_dtype_t dtype, const ks_plan_t *plan,
+                                      size_t *bytes)
+{
+    if (!valid_dtype(dtype))
+        return KS_ERROR_UNSUPPORTED_DTYPE;
+    if (bytes == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
+        return KS_ERROR_INVALID_VALUE;
+    const ks_plan_t p = plan != nullptr ? *plan : policy(KS_OP_SOFTMAX, dtype, rows, hidden, true, true);
+    *bytes = softmax_workspace_bytes(p, rows, hidden * elem_size(dtype));
+    return KS_SUCCESS;
+}
+
+ks_status_t ks_softmax_ws_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                             void *workspace, size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream)
+{
+    return softmax_call(out, x, rows, hidden, dtype, workspace, workspace_bytes, plan, stream, true);
+}
+
+ks_status_t ks_softmax_ws(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    return softmax_call(out, x, rows, hidden, dtype, workspace, workspace_bytes, nullptr, stream, true);
+}
+
+ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags, ks_plan_t *plan)
 {
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
+        (flags & ~(KS_PLAN_ALIGNED | KS_PLAN_WORKSPACE)) != 0 ||
         (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL &&
          op != KS_OP_SOFTMAX && op != KS_OP_RMS_NORM_RESIDUAL && op != KS_OP_RMS_NORM_BACKWARD))
         return KS_ERROR_INVALID_VALUE;
-    *plan = policy(op, dtype, rows, hidden, aligned != 0);
+    *plan = policy(op, dtype, rows, hidden, (flags & KS_PLAN_ALIGNED) != 0, (flags & KS_PLAN_WORKSPACE) != 0);
     return KS_SUCCESS;
 }
 

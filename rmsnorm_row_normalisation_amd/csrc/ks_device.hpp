@@ -768,6 +768,128 @@ __device__ __forceinline__ void softmax_vec_body(const Params &p)
     }
 }
 
+// Split-row softmax, for wide rows in small batches: a row is cut into
+// chunks of kSplitLanes * kVpt consecutive 16-byte pieces, one 256-lane
+// workgroup per (chunk, row), so that a batch of a few rows still spreads
+// over the chip.  Two kernels:
+//   stats:  each chunk's maximum m_c (NaN if the chunk holds one) and
+//           s_c = sum of exp(x - m_c) over the chunk (canonical fold),
+//           written to the workspace as (m_c, s_c); a chunk of only -inf has
+//           s_c = 0;
+//   norm:   each chunk's workgroup reads its row's (m_c, s_c), forms
+//           M = max m_c and S = sum of s_c * exp(m_c - M) (lane l takes
+//           chunks l, l + 256, ... in order, then the canonical fold), and
+//           writes exp(x - M) / S for its chunk.
+// exp(x - M) is the value the one-pass kernels compute; S is formed in
+// another order, with the factors exp(m_c - M), so a result can differ from
+// theirs in the last bit.  The page's non-finite rules hold: a NaN or +inf
+// makes some s_c NaN (exp(NaN - m_c) or exp(inf - inf)), so S is NaN; a row
+// of only -inf has M = -inf and every m_c - M is NaN.  M itself is a plain
+// maximum (NaN m_c are skipped unless all are NaN); a NaN s_c still reaches
+// S through s_c * exp(m_c - M).  Chunks never overlap, and a workgroup stores only the
+// chunk it loaded, so out may be x.
+constexpr int kSplitLanes = 256;
+constexpr int kSplitCpol = 2;   // non-temporal loads and stores: streamed once
+
+// Maximum that keeps NaN (fmaxf drops it): a chunk holding a NaN gets
+// m_c = NaN, so its s_c is NaN and so is its row's sum.  Its own LDS slots
+// (a distinct operator), apart from the MaxOp fold of the same kernels.
+struct NanMaxOp {
+    __device__ static __forceinline__ float apply(float a, float b) { return (a != a || b != b) ? a + b : fmaxf(a, b); }
+};
+
+struct SplitParams {
+    void *y;          // out [rows, hidden]
+    const void *x;    // [rows, hidden]
+    float *stats;     // workspace [rows, chunks, 2]: (m_c, s_c)
+    int64_t rows;
+    int32_t hidden;
+    int32_t chunks;   // ceil(row pieces / (kSplitLanes * kVpt))
+};
+
+// The lane's pieces of chunk blockIdx.x of row blockIdx.y (non-temporal
+// loads; pieces past the row read as zero and are flagged).
+template <typename T, int kVpt>
+__device__ __forceinline__ void split_load(const SplitParams &p, u32x4 *xv, uint32_t *off, bool *in_row)
+{
+    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)Pack<T>::kBytes;
+    const auto rx = make_rsrc((const char *)p.x + (size_t)blockIdx.y * row_bytes, row_bytes);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        const uint32_t piece = (uint32_t)blockIdx.x * (kSplitLanes * kVpt) + (uint32_t)(k * kSplitLanes) + threadIdx.x;
+        in_row[k] = piece * 16u < row_bytes;
+        off[k] = in_row[k] ? piece * 16u : kOutOfRange;
+        xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kSplitCpol);
+    }
+}
+
+template <typename T, int kVpt>
+__device__ __forceinline__ void softmax_split_stats_body(const SplitParams &p)
+{
+    constexpr int kE = Pack<T>::kElems;
+    u32x4 xv[kVpt];
+    uint32_t off[kVpt];
+    bool in_row[kVpt];
+    split_load<T, kVpt>(p, xv, off, in_row);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float pm = Pack<T>::get(xv[k], 0);
+#pragma unroll
+        for (int e = 1; e < kE; ++e)
+            pm = NanMaxOp::apply(pm, Pack<T>::get(xv[k], e));
+        mx = in_row[k] ? NanMaxOp::apply(mx, pm) : mx;
+    }
+    const float m = team_fold<kSplitLanes, kSplitLanes, NanMaxOp>(mx);
+    float part[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float a = softmax_exp<T>(Pack<T>::get(xv[k], 0) - m);
+#pragma unroll
+        for (int e = 1; e < kE; ++e)
+            a = a + softmax_exp<T>(Pack<T>::get(xv[k], e) - m);
+        part[k] = in_row[k] ? a : 0.0f;
+    }
+    float sum = team_fold<kSplitLanes, kSplitLanes>(local_fold<kVpt>(part));
+    if (m == -__builtin_inff())
+        sum = 0.0f;                        // only -inf here: nothing to add
+    if (threadIdx.x == 0) {
+        float *st = p.stats + ((size_t)blockIdx.y * (size_t)p.chunks + blockIdx.x) * 2;
+        st[0] = m;
+        st[1] = sum;
+    }
+}
+
+template <typename T, int kVpt>
+__device__ __forceinline__ void softmax_split_norm_body(const SplitParams &p)
+{
+    constexpr int kE = Pack<T>::kElems;
+    u32x4 xv[kVpt];
+    uint32_t off[kVpt];
+    bool in_row[kVpt];
+    split_load<T, kVpt>(p, xv, off, in_row);      // in flight while the row's statistics combine
+    const float *st = p.stats + (size_t)blockIdx.y * (size_t)p.chunks * 2;
+    float mx = -__builtin_inff();
+    for (int c = threadIdx.x; c < p.chunks; c += kSplitLanes)
+        mx = fmaxf(mx, st[2 * c]);
+    const float M = team_fold<kSplitLanes, kSplitLanes, MaxOp>(mx);
+    float acc = 0.0f;
+    for (int c = threadIdx.x; c < p.chunks; c += kSplitLanes)
+        acc = acc + st[2 * c + 1] * softmax_exp<T>(st[2 * c] - M);
+    const float S = team_fold<kSplitLanes, kSplitLanes>(acc);
+    const float r = 1.0f / S;
+    const uint32_t row_bytes = (uint32_t)p.hidden * (uint32_t)Pack<T>::kBytes;
+    const auto ry = make_rsrc((char *)p.y + (size_t)blockIdx.y * row_bytes, row_bytes);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        float o[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            o[e] = softmax_div<T>(softmax_exp<T>(Pack<T>::get(xv[k], e) - M), S, r);
+        __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), ry, off[k], 0, kSplitCpol);
+    }
+}
+
 // Generic kernel: three passes over the row (maximum, sum, store), kEpa
 // elements per access as in generic_body.  Each lane reads and writes the
 // same elements in the last pass, after the whole team has finished the
@@ -1276,6 +1398,18 @@ template <typename T, int kTpr, int kEpa, int kBlock>
 __global__ __launch_bounds__(kBlock) void softmax_generic(Params p)
 {
     softmax_generic_body<T, kTpr, kEpa, kBlock>(p);
+}
+
+template <typename T, int kVpt>
+__global__ __launch_bounds__(kSplitLanes) void softmax_split_stats(SplitParams p)
+{
+    softmax_split_stats_body<T, kVpt>(p);
+}
+
+template <typename T, int kVpt>
+__global__ __launch_bounds__(kSplitLanes) void softmax_split_norm(SplitParams p)
+{
+    softmax_split_norm_body<T, kVpt>(p);
 }
 
 }  // namespace ks

@@ -23,6 +23,7 @@ struct Launch {
     ks_op_t op;         // KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_RMS_NORM_RESIDUAL or KS_OP_SOFTMAX
     ks_plan_t plan;
     hipStream_t stream;
+    float *work = nullptr;   // split softmax: the caller's workspace (split_workspace_floats)
 };
 
 // One SwiGLU launch (out [rows, d], x [rows, 2 d]).
@@ -96,6 +97,23 @@ hipError_t launch_bwd_bf16(const BwdLaunch &l);
 hipError_t launch_softmax_f32(const Launch &l);
 hipError_t launch_softmax_f16(const Launch &l);
 hipError_t launch_softmax_bf16(const Launch &l);
+
+// Split softmax plans: 256-lane workgroups, each over one chunk of
+// 256 * vectors_per_thread 16-byte pieces of one row (grid: chunks x rows,
+// so at most 65535 rows); the workspace holds an fp32 (maximum, sum) pair per
+// chunk.
+constexpr int kSplitBlock = 256;
+constexpr int64_t kSplitMaxRows = 65535;
+inline int64_t split_chunks(int64_t row_bytes, int vpt)
+{
+    const int64_t pieces = row_bytes / 16;
+    const int64_t per_chunk = (int64_t)kSplitBlock * vpt;
+    return (pieces + per_chunk - 1) / per_chunk;
+}
+inline int64_t split_workspace_floats(int64_t rows, int64_t row_bytes, int vpt)
+{
+    return rows * split_chunks(row_bytes, vpt) * 2;
+}
 
 // The one generic SwiGLU plan: a grid-stride loop over elements.
 constexpr int kSwigluGenericBlock = 256;

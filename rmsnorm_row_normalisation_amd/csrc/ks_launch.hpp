@@ -124,6 +124,40 @@ hipError_t launch_generic_typed(const Launch &l)
 }
 
 // ---------------------------------------------------------------------------
+// Split-row softmax: the statistics kernel, then the normalising kernel, on
+// one stream (the second reads what the first wrote).
+// ---------------------------------------------------------------------------
+template <typename T, int V>
+hipError_t softmax_split_one(const Launch &l)
+{
+    const int64_t chunks = split_chunks((int64_t)l.hidden * Pack<T>::kBytes, V);
+    SplitParams p{l.y, l.x, l.work, l.rows, l.hidden, (int32_t)chunks};
+    const dim3 grid((unsigned)chunks, (unsigned)l.rows);
+    hipLaunchKernelGGL((softmax_split_stats<T, V>), grid, dim3(kSplitBlock), 0, l.stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((softmax_split_norm<T, V>), grid, dim3(kSplitBlock), 0, l.stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_softmax_typed(const Launch &l)
+{
+    if (l.plan.path == KS_PATH_GENERIC)
+        return launch_generic_typed<T, KS_OP_SOFTMAX>(l);
+    if (l.plan.path == KS_PATH_SPLIT) {
+        switch (l.plan.vectors_per_thread) {
+        case 1: return softmax_split_one<T, 1>(l);
+        case 2: return softmax_split_one<T, 2>(l);
+        case 4: return softmax_split_one<T, 4>(l);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    return vec_by_tpr<T, KS_OP_SOFTMAX>(l);
+}
+
+// ---------------------------------------------------------------------------
 // SwiGLU
 // ---------------------------------------------------------------------------
 template <typename Kernel>

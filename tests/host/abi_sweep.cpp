@@ -5,7 +5,8 @@
 //   * every status is one of ks_status_t;
 //   * a call that succeeds with rows > 0 reaches exactly one launch (the
 //     backward: one launch call), a failing or empty call reaches none;
-//   * the plan ks_get_plan returns is accepted by the matching _ex call.
+//   * the plan ks_get_plan returns is accepted by the matching _ex call;
+//   * a split softmax launch carries a workspace (checked by the stand-in).
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -73,6 +74,13 @@ int main()
                         before = ks::g_launches;
                         expect_status(ks_silu_and_mul(o, x, rows, hidden, d, 0), before, rows);
                         size_t need = 0;
+                        if (ks_softmax_workspace_size(rows, hidden, d, nullptr, &need) == KS_SUCCESS) {
+                            before = ks::g_launches;
+                            expect_status(ks_softmax_ws(o, x, rows, hidden, d, at(24 * kGiB), need, 0), before, rows);
+                            before = ks::g_launches;
+                            expect_status(ks_softmax_ws(o, x, rows, hidden, d, need ? nullptr : at(24 * kGiB), need, 0),
+                                          before, rows);
+                        }
                         if (ks_rms_norm_backward_workspace_size(rows, hidden, &need) == KS_SUCCESS) {
                             before = ks::g_launches;
                             // dx, dw, dy, x, weight, workspace: disjoint except where the layout overlaps
@@ -91,9 +99,10 @@ int main()
         for (int dt = 0; dt < 3; ++dt)
             for (int64_t hidden = 1; hidden <= 70000; hidden = hidden < 64 ? hidden + 1 : hidden * 5 / 4 + 3)
                 for (int64_t rows : {1ll, 7ll, 512ll, 8192ll, 1ll << 20})
-                    for (int aligned = 0; aligned < 2; ++aligned) {
+                    for (int flags = 0; flags < 4; ++flags) {
+                        const int aligned = flags & KS_PLAN_ALIGNED;
                         ks_plan_t p;
-                        CHECK(ks_get_plan((ks_op_t)op, (ks_dtype_t)dt, rows, hidden, aligned, &p) == KS_SUCCESS);
+                        CHECK(ks_get_plan((ks_op_t)op, (ks_dtype_t)dt, rows, hidden, flags, &p) == KS_SUCCESS);
                         const uintptr_t a = aligned ? 0 : 2;
                         void *o = at(a), *x = at(4 * kGiB + a), *r = at(8 * kGiB + a), *w = at(12 * kGiB + a);
                         ks_status_t st = KS_ERROR_HIP;
@@ -103,7 +112,11 @@ int main()
                             st = ks_fused_add_rms_norm_ex(x, r, w, 0, hidden, 1e-6f, (ks_dtype_t)dt, &p, 0);
                             break;
                         case KS_OP_SILU_AND_MUL: st = ks_silu_and_mul_ex(o, x, 0, hidden, (ks_dtype_t)dt, &p, 0); break;
-                        case KS_OP_SOFTMAX: st = ks_softmax_ex(o, x, 0, hidden, (ks_dtype_t)dt, &p, 0); break;
+                        case KS_OP_SOFTMAX:
+                            st = (flags & KS_PLAN_WORKSPACE)
+                                     ? ks_softmax_ws_ex(o, x, 0, hidden, (ks_dtype_t)dt, nullptr, 0, &p, 0)
+                                     : ks_softmax_ex(o, x, 0, hidden, (ks_dtype_t)dt, &p, 0);
+                            break;
                         case KS_OP_RMS_NORM_RESIDUAL:
                             st = ks_rms_norm_residual_ex(o, x, r, w, 0, hidden, 1e-6f, (ks_dtype_t)dt, &p, 0);
                             break;
@@ -140,6 +153,11 @@ int main()
                                 before = ks::g_launches;
                                 expect_status(ks_silu_and_mul_ex(at(0), at(4 * kGiB), 4, hidden, KS_DTYPE_FLOAT16, &p,
                                                                  0), before, 4);
+                                size_t need = 0;
+                                CHECK(ks_softmax_workspace_size(4, hidden, KS_DTYPE_FLOAT16, &p, &need) == KS_SUCCESS);
+                                before = ks::g_launches;
+                                expect_status(ks_softmax_ws_ex(at(0), at(4 * kGiB), 4, hidden, KS_DTYPE_FLOAT16,
+                                                               at(8 * kGiB), need, &p, 0), before, 4);
                             }
                         }
     for (int op = -2; op < 8; ++op) {
@@ -148,6 +166,11 @@ int main()
         CHECK((op >= 0 && op <= 5) ? st == KS_SUCCESS : st == KS_ERROR_INVALID_VALUE);
     }
     CHECK(ks_get_plan(KS_OP_RMS_NORM, KS_DTYPE_BFLOAT16, 4, 4096, 1, nullptr) == KS_ERROR_INVALID_VALUE);
+    for (int flags = -1; flags < 9; ++flags) {
+        ks_plan_t p;
+        const ks_status_t st = ks_get_plan(KS_OP_SOFTMAX, KS_DTYPE_BFLOAT16, 4, 65536, flags, &p);
+        CHECK((flags >= 0 && flags < 4) ? st == KS_SUCCESS : st == KS_ERROR_INVALID_VALUE);
+    }
     for (int s = -1; s < 7; ++s)
         CHECK(ks_status_string((ks_status_t)s) != nullptr);
     printf("abi sweep: %ld checks, %ld launches\n", g_checks, ks::g_launches);

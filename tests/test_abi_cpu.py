@@ -460,6 +460,98 @@ def test_softmax_tensor_api_checks():
 
 
 # ---------------------------------------------------------------------------
+# Softmax with a caller-owned workspace: the same contract, and split plans
+# (a row over several workgroups) for wide rows in small batches
+# ---------------------------------------------------------------------------
+def smax_ws(out, x, rows, hidden, ws, ws_bytes, dtype=BF16, plan=None):
+    return b.ks_softmax_ws_ex(out, x, rows, hidden, dtype, ws, ws_bytes, plan, 0)
+
+
+def split_plan(vpt, es=2, **kw):
+    d = dict(path=b.KS_PATH_SPLIT, threads_per_row=256, vectors_per_thread=vpt, elems_per_access=16 // es,
+             rows_per_block=1, block_threads=256, load_nt=1, store_nt=1, weight_lds=0)
+    d.update(kw)
+    return b.Plan.from_dict(d)
+
+
+def test_softmax_workspace_size():
+    for rows, hidden, es, code in ((1, 65536, 2, F16), (8, 65536, 2, F16), (3, 128256, 4, F32), (7, 4104, 2, BF16)):
+        pieces = hidden * es // 16
+        for vpt in (1, 2, 4):
+            chunks = -(-pieces // (256 * vpt))     # a (maximum, sum) fp32 pair per chunk of 256 * vpt pieces
+            assert b.ks_softmax_workspace_size(rows, hidden, code, split_plan(vpt, es)) == 8 * rows * chunks
+    assert b.ks_softmax_workspace_size(8, 4096, BF16, ks.get_plan("softmax", torch.bfloat16, 4096, 8)) == 0
+    assert b.ks_softmax_workspace_size(4096, 65536, F16) == 0          # large batch: one-pass plan
+    assert b.ks_softmax_workspace_size(4096, 65544, F16) == 8 * 4096 * 9   # past the vector path: split, 4 pieces
+    assert b.ks_softmax_workspace_size(8, 1024, BF16) == 0             # narrow rows: one-pass plan
+    assert b.ks_softmax_workspace_size(0, 65536, F16) == 0
+    p = ks.get_plan("softmax", torch.float16, 65536, 8, workspace=True)
+    assert p.path == b.KS_PATH_SPLIT
+    assert b.ks_softmax_workspace_size(8, 65536, F16) == b.ks_softmax_workspace_size(8, 65536, F16, p) > 0
+    n = ctypes.c_size_t()
+    assert ks.lib().ks_softmax_workspace_size(-1, 8, BF16, None, ctypes.byref(n)) == INVALID
+    assert ks.lib().ks_softmax_workspace_size(4, 0, BF16, None, ctypes.byref(n)) == INVALID
+    assert ks.lib().ks_softmax_workspace_size(4, 8, BF16, None, None) == INVALID
+    assert ks.lib().ks_softmax_workspace_size(4, 8, 9, None, ctypes.byref(n)) == DTYPE
+
+
+def test_softmax_ws_statuses_and_overlaps():
+    x, out, ws = A, A + 256 * MB, A + 512 * MB
+    p = split_plan(1)
+    need = b.ks_softmax_workspace_size(8, 65536, BF16, p)
+    assert need == 8 * 8 * 32
+    assert smax(out, x, 8, 65536, plan=p) == INVALID                   # no workspace argument: no split plan
+    assert smax_ws(out, x, 8, 65536, None, 0, plan=p) == INVALID
+    assert smax_ws(out, x, 8, 65536, ws, need - 4, plan=p) == INVALID
+    assert smax_ws(out, x, 8, 65536, ws + 2, need, plan=p) == INVALID  # not 4-byte aligned
+    assert smax_ws(out, x, 8, 65536, x + 64, need, plan=p) == OVERLAP
+    assert smax_ws(out, x, 8, 65536, out + 8 * 65536 * 2 - 4, need, plan=p) == OVERLAP
+    assert smax_ws(out, x, 8, 65536, ws, need, dtype=9, plan=p) == DTYPE
+    assert smax_ws(out + 2, x, 8, 65536, ws, need, plan=p) == INVALID  # unaligned: no split plan
+    assert smax_ws(out, x, 8, 65540 - 1, ws, need, plan=p) == INVALID  # row bytes not a multiple of 16
+    big = b.ks_softmax_workspace_size(65536, 8192, BF16, p)
+    assert smax_ws(out, x, 65536, 8192, ws, big, plan=p) == INVALID    # grid rows past 65535
+    for bad in (split_plan(3), split_plan(8), split_plan(0), split_plan(1, threads_per_row=512),
+                split_plan(1, block_threads=512), split_plan(1, rows_per_block=2), split_plan(1, load_nt=0),
+                split_plan(1, store_nt=0), split_plan(1, weight_lds=1), split_plan(1, elems_per_access=4)):
+        assert smax_ws(out, x, 8, 65536, ws, 1 << 20, plan=bad) == INVALID, bad.as_dict()
+    assert smax_ws(None, None, 0, 65536, None, 0, plan=p) == OK        # empty batch: no HIP call
+    assert b.ks_softmax_ws(out, x, 8, 65536, F16, None, 0, 0) == INVALID   # the policy splits here
+    assert b.ks_softmax_ws(None, None, 0, 65536, F16, None, 0, 0) == OK
+    # explicit split plans are checked against every other op too
+    assert b.ks_rms_norm_ex(out, x, A + 768 * MB, 8, 65536, 1e-6, BF16, p, 0) == INVALID
+
+
+def test_softmax_split_policy():
+    for dtype, es, code in ((torch.float32, 4, F32), (torch.float16, 2, F16), (torch.bfloat16, 2, BF16)):
+        for hidden in (1000, 4096, 8192, 16384, 20480, 24576, 32768, 40960, 49152, 65536, 128256, 131072, 2**20):
+            for rows in (1, 2, 4, 5, 8, 16, 17, 32, 33, 64, 127, 128, 512, 4096, 65535, 65536):
+                for aligned in (True, False):
+                    p = ks.get_plan("softmax", dtype, hidden, rows, aligned, workspace=True).as_dict()
+                    nvec = hidden * es // 16
+                    # rows past the vector path: any batch; 4096..8192 pieces: small batches only
+                    max_rows = 65535 if nvec > 8192 else 32 if nvec >= 6144 else 16 if nvec >= 5120 else \
+                        4 if nvec >= 4096 else 0
+                    split = aligned and (hidden * es) % 16 == 0 and rows <= max_rows
+                    assert (p["path"] == b.KS_PATH_SPLIT) == split, (dtype, hidden, rows, aligned, p)
+                    if not split:
+                        assert p == ks.get_plan("softmax", dtype, hidden, rows, aligned).as_dict()
+                        continue
+                    groups = rows * -(-nvec // 256)      # workgroups at one piece per lane
+                    vpt = 1 if groups <= 1024 else 2 if groups <= 4096 else 4
+                    assert p == split_plan(vpt, es).as_dict()
+                    base = A if aligned else A + 2
+                    assert smax_ws(base + 256 * MB, base, 0, hidden, None, 0, dtype=code,
+                                   plan=b.Plan.from_dict(p)) == OK
+    # the other ops ignore the flag; unknown flag bits are rejected
+    for op in ("rms_norm", "fused_add_rms_norm", "silu_and_mul", "rms_norm_residual", "rms_norm_backward"):
+        assert (ks.get_plan(op, torch.bfloat16, 65536, 8, workspace=True).as_dict()
+                == ks.get_plan(op, torch.bfloat16, 65536, 8).as_dict())
+    plan = b.Plan()
+    assert ks.lib().ks_get_plan(3, BF16, 8, 65536, 4, ctypes.byref(plan)) == INVALID
+
+
+# ---------------------------------------------------------------------------
 # Out-of-place residual RMSNorm (Triton Kernels README, "Kernels"): x and
 # residual read only, out may be exactly either of them
 # ---------------------------------------------------------------------------

@@ -7,7 +7,11 @@ bf16), its 65536-column fp16 accumulation case, the 2048x4096 bf16 batch,
 widths 1..32776 in every dtype (vector and generic paths, ragged tails),
 unaligned offset views, empty batches, large logits, the page's non-finite
 row rules, every compiled plan (vector plans bit-identical), batch
-invariance, in-place calls and graph replays.
+invariance, in-place calls and graph replays; and the split plans (a
+caller workspace; wide rows in small batches, one row over many
+workgroups) on vocabulary-sized rows, ragged last chunks, single-chunk rows,
+non-finite values placed by chunk, in-place calls, a reused workspace and
+graph replays.
 """
 import pytest
 import torch
@@ -28,25 +32,26 @@ def _gpu():
     require_gpu()
 
 
-def gpu_softmax(x: torch.Tensor, plan=None, offset: int = 0, inplace: bool = False) -> torch.Tensor:
+def gpu_softmax(x: torch.Tensor, plan=None, offset: int = 0, inplace: bool = False, split: bool = True) -> torch.Tensor:
     if offset:
         buf = torch.empty(x.numel() + offset, dtype=x.dtype, device="cuda")
         xd = buf[offset:].view(x.shape)
         xd.copy_(x.cuda())
         obuf = torch.empty(x.numel() + offset, dtype=x.dtype, device="cuda")
-        out = ks.softmax(xd, out=obuf[offset:].view(x.shape), plan=plan)
+        out = ks.softmax(xd, out=obuf[offset:].view(x.shape), plan=plan, split=split)
     elif inplace:
         xd = x.cuda()
-        out = ks.softmax(xd, out=xd, plan=plan)
+        out = ks.softmax(xd, out=xd, plan=plan, split=split)
     else:
-        out = ks.softmax(x.cuda(), plan=plan)
+        out = ks.softmax(x.cuda(), plan=plan, split=split)
     torch.cuda.synchronize()
     return out.cpu()
 
 
-def check(name, x, plan=None, offset=0, exact=None, inplace=False):
-    say("softmax", name, tuple(x.shape), x.dtype, plan.as_dict() if plan is not None else "policy", offset)
-    got = gpu_softmax(x, plan, offset, inplace)
+def check(name, x, plan=None, offset=0, exact=None, inplace=False, split=True):
+    say("softmax", name, tuple(x.shape), x.dtype, plan.as_dict() if plan is not None else "policy", offset,
+        "split allowed" if split else "one-pass")
+    got = gpu_softmax(x, plan, offset, inplace, split)
     ref = oracle.softmax(x)
     if exact is None:
         exact = got.numel() >= 20000
@@ -69,6 +74,9 @@ SHAPES = [(1, 1), (3, 1), (5, 7), (4, 8), (2, 3, 40), (7, 1000), (3, 1023), (9, 
 def test_shapes(shape, dtype):
     x = workloads.random_case(shape, dtype, seed=sum(shape) + 7, x=workloads.normal(0, 2))["x"]
     check("shape", x)
+    rows = x.numel() // shape[-1]
+    if ks.get_plan("softmax", x.dtype, shape[-1], rows, workspace=True).path == 2:
+        check("shape", x, split=False)      # the one-pass plan of the same shape
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -94,11 +102,13 @@ def test_large_logits(dtype):
     check("large", x.contiguous())
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("hidden", [4, 1024, 40000])
-def test_nonfinite_rows(dtype, hidden):
+def test_nonfinite_rows(dtype, hidden, split):
     """NaN or +inf anywhere, or only -inf: NaN everywhere in the row; -inf
-    entries elsewhere: 0.  hidden 40000 in fp32/16-bit takes the generic path."""
+    entries elsewhere: 0.  hidden 40000 takes the generic path in fp32 and the
+    1024-lane vector path in 16-bit dtypes, or a split plan where allowed."""
     dt = workloads.DTYPES[dtype]
     x = workloads.random_case((8, hidden), dtype, seed=hidden)["x"].float()
     x[0, hidden // 2] = NAN
@@ -110,7 +120,8 @@ def test_nonfinite_rows(dtype, hidden):
     x[5, :] = NAN
     x[6, 1:] = -INF
     x = x.to(dt).contiguous()
-    got = gpu_softmax(x)
+    say("softmax nonfinite", tuple(x.shape), dtype, ks.get_plan("softmax", dt, hidden, 8, workspace=split).as_dict())
+    got = gpu_softmax(x, split=split)
     ref = oracle.softmax(x)
     assert bool((torch.isnan(got) == torch.isnan(ref)).all())
     assert bool(torch.isnan(got[:4]).all()) and bool(torch.isnan(got[5]).all())
@@ -179,6 +190,105 @@ def test_graph_replays_match_eager():
         ks.softmax(x, out=out)
     for rep in range(4):
         out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_bitexact(out.cpu(), eager.cpu())
+
+
+# ---------------------------------------------------------------------------
+# Split plans
+# ---------------------------------------------------------------------------
+def split_plan(vpt: int, es: int):
+    return ks.Plan(path=2, threads_per_row=256, vectors_per_thread=vpt, elems_per_access=16 // es, rows_per_block=1,
+                   block_threads=256, load_nt=1, store_nt=1)
+
+
+# (rows, hidden, dtype): vocabulary-sized rows (128256 and 131072 columns),
+# the 65536-column case with a ragged last chunk (65544), rows of one to a few
+# chunks (8, 4104, 16384 columns)
+SPLIT_SHAPES = [(1, 128256, "float32"), (3, 128256, "bfloat16"), (2, 131072, "float16"), (5, 32768, "bfloat16"),
+                (8, 65544, "float16"), (1, 16384, "float32"), (2, 4104, "bfloat16"), (1, 8, "float32")]
+
+
+@pytest.mark.parametrize("rows,hidden,dtype", SPLIT_SHAPES, ids=lambda v: str(v))
+def test_split_plans(rows, hidden, dtype):
+    x = workloads.random_case((rows, hidden), dtype, seed=hidden + rows, x=workloads.normal(0, 3))["x"]
+    es = x.element_size()
+    for vpt in (1, 2, 4):
+        check("split", x, plan=split_plan(vpt, es))
+
+
+@pytest.mark.parametrize("rows,hidden,dtype", [(1, 128256, "bfloat16"), (8, 65536, "float16"), (4, 50000, "float32"),
+                                               (32, 49152, "bfloat16"), (300, 40000, "float32")])
+def test_split_policy_cases(rows, hidden, dtype):
+    """Shapes the policy splits when given a workspace, against the oracle and
+    in place."""
+    x = workloads.random_case((rows, hidden), dtype, seed=rows * 7 + hidden, x=workloads.normal(0, 2))["x"]
+    assert ks.get_plan("softmax", x.dtype, hidden, rows, workspace=True).path == 2
+    check("split policy", x)
+    check("split policy in place", x, inplace=True)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_nonfinite_by_chunk(dtype):
+    """The page's row rules where they meet chunk boundaries: with 2048-element
+    fp16 chunks (256 lanes x 8), a chunk of only -inf, a chunk of NaN and -inf,
+    +inf in the last chunk, a single finite element."""
+    dt = workloads.DTYPES[dtype]
+    hidden = 65536
+    x = workloads.random_case((8, hidden), dtype, seed=99)["x"].float()
+    c = 256 * (16 // x.element_size())             # elements per chunk at one piece per lane
+    x[0, hidden // 2 + 3] = NAN
+    x[1, hidden - 1] = INF
+    x[2, :] = -INF
+    x[3, :c] = -INF                                # the first chunk only -inf
+    x[4, 5 * c:6 * c] = -INF
+    x[4, 5 * c + 17] = NAN                         # a chunk of NaN and -inf
+    x[5, :] = -INF
+    x[5, 3 * c + 1] = 2.0                          # one finite element
+    x[6, ::3] = -INF
+    x[7, c - 1] = INF
+    x[7, c] = -INF
+    x = x.to(dt).contiguous()
+    es = x.element_size()
+    ref = oracle.softmax(x)
+    for vpt in (1, 2, 4):
+        say("split nonfinite", dtype, vpt)
+        got = gpu_softmax(x, plan=split_plan(vpt, es))
+        assert bool((torch.isnan(got) == torch.isnan(ref)).all())
+        assert bool(torch.isnan(got[[0, 1, 2, 4, 7]]).all())
+        assert bool((got[3, :c].float() == 0).all())
+        assert float(got[5, 3 * c + 1]) == 1.0 and float(got[5].float().sum()) == 1.0
+        assert bool((got[6].float()[::3] == 0).all())
+        check_normalised(got, ref)
+
+
+def test_split_workspace_reuse_and_graph_replays():
+    """One workspace serves calls in a row (each call writes what it reads);
+    graph replays of a split call match the eager result."""
+    x1 = workloads.make_inputs(workloads.WORKLOADS["X4"])["x"].cuda()
+    x2 = workloads.random_case(tuple(x1.shape), "float16", seed=4242, x=workloads.normal(0, 5))["x"].cuda()
+    rows, hidden = x1.shape
+    need = ks.ks_softmax_workspace_size(rows, hidden, ks.KS_DTYPE[x1.dtype])
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for x in (x1, x2, x1):
+        say("split reuse", tuple(x.shape))
+        got = ks.softmax(x, workspace=ws)
+        torch.cuda.synchronize()
+        check_normalised(got.cpu(), oracle.softmax(x.cpu()), 0.999)
+    out = ks.softmax(x2, workspace=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ks.softmax(x2, out=out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        ws.zero_()
+        ks.softmax(x1, workspace=ws)              # eager work on the same workspace between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
