@@ -40,6 +40,7 @@ sampled rows for batches over 2^24 elements); on a mismatch nothing is timed
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -383,6 +384,23 @@ def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
             "host_cpu": _cpu_model()}
 
 
+def memory_interface() -> dict | None:
+    """The device's reported memory bus width and clock (hipDeviceGetAttribute)
+    and the bandwidth they imply (2 transfers per clock), as context next to
+    the 8 TB/s spec peak that the fractions use."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    bus, clk = ctypes.c_int(0), ctypes.c_int(0)
+    bus_width_attr, mem_clock_attr = 59, 60          # hipDeviceAttributeMemoryBusWidth / ...MemoryClockRate
+    if (hip.hipDeviceGetAttribute(ctypes.byref(bus), bus_width_attr, 0) != 0
+            or hip.hipDeviceGetAttribute(ctypes.byref(clk), mem_clock_attr, 0) != 0):
+        return None
+    gbps = 2.0 * clk.value * 1e3 * bus.value / 8 / 1e9
+    return {"bus_width_bits": bus.value, "memory_clock_khz": clk.value, "implied_gbps": round(gbps, 1)}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -648,7 +666,8 @@ def main() -> None:
         "roofline": roofline,
         "copy_reference": res["copy_reference"],
         "parity": parity,
-        "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", "?"), "cus": dev.multi_processor_count},
+        "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", "?"), "cus": dev.multi_processor_count,
+                   "memory": memory_interface()},
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
