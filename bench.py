@@ -386,8 +386,10 @@ def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
 
 def memory_interface() -> dict | None:
     """The device's reported memory bus width and clock (hipDeviceGetAttribute)
-    and the bandwidth they imply (2 transfers per clock), as context next to
-    the 8 TB/s spec peak that the fractions use."""
+    and their product (bytes per reported clock), as context next to the
+    8 TB/s spec peak that the fractions use.  The product is not a peak: the
+    HBM3E interface moves several transfers per reported clock (8 TB/s over
+    2048 GB/s is about 4)."""
     try:
         hip = ctypes.CDLL("libamdhip64.so")
     except OSError:
@@ -397,8 +399,9 @@ def memory_interface() -> dict | None:
     if (hip.hipDeviceGetAttribute(ctypes.byref(bus), bus_width_attr, 0) != 0
             or hip.hipDeviceGetAttribute(ctypes.byref(clk), mem_clock_attr, 0) != 0):
         return None
-    gbps = 2.0 * clk.value * 1e3 * bus.value / 8 / 1e9
-    return {"bus_width_bits": bus.value, "memory_clock_khz": clk.value, "implied_gbps": round(gbps, 1)}
+    gbps = clk.value * 1e3 * bus.value / 8 / 1e9
+    return {"bus_width_bits": bus.value, "memory_clock_khz": clk.value, "clock_x_bus_gbps": round(gbps, 1),
+            "spec_peak_gbps": HBM_PEAK_GBPS}
 
 
 def _cpu_model() -> str:
@@ -594,7 +597,8 @@ def sweep_workloads(args, ks, oracle_mod) -> None:
         for op in wl.ops:
             p = res["per_op"][op]
             pl = p["plan"]
-            plan = (f"{pl['threads_per_row']}x{pl['vectors_per_thread']} "
+            path = {0: "", 1: "generic ", 2: "split "}.get(pl["path"], "?")
+            plan = (f"{path}{pl['threads_per_row']}x{pl['vectors_per_thread']} "
                     f"nt{pl['load_nt']}{pl['store_nt']} lds{pl['weight_lds']}")
             lines.append(f"| {name} | {op} | {DTYPE_TAG[wl.dtype]} | {wl.rows}x{wl.hidden} | {p['us_per_call']:.3f} | "
                          f"{p['gbps']:.0f} | {100 * p['frac_of_peak']:.1f} | {res['copy_reference']['gbps']:.0f} | "
