@@ -454,6 +454,27 @@ template <typename T> struct Access<T, 1> {
     __device__ static __forceinline__ void store(void *p, int64_t i, const float *f) { Scalar<T>::put(p, i, f[0]); }
 };
 
+// A lane's running sum in the generic kernels, where one lane may add
+// thousands of batches of a long row: each batch is summed on its own, then
+// added with a compensation term (Neumaier's form of Kahan summation), so the
+// lane's sum keeps about one rounding however many batches it takes.  (A
+// plain running sum of positive terms drifts by up to one rounding per
+// addition: about 1e-6 relative for 2^24-element fp32 rows.)  Non-finite
+// sums pass through unchanged: the compensation is dropped once the sum is
+// infinite, so +inf stays +inf instead of turning into NaN.
+struct LaneSum {
+    float s = 0.0f;
+    float c = 0.0f;
+    __device__ __forceinline__ void add(float v)
+    {
+        const float t = s + v;
+        const float e = fabsf(s) >= fabsf(v) ? (s - t) + v : (v - t) + s;
+        c = __builtin_isfinite(t) ? c + e : c;
+        s = t;
+    }
+    __device__ __forceinline__ float value() const { return s + c; }
+};
+
 // ---------------------------------------------------------------------------
 // Generic kernel: two passes over the row, kEpa elements per access.
 // kEpa == 1: scalar accesses (any alignment); kEpa == 16 / sizeof(T): 16-byte
@@ -475,7 +496,7 @@ __device__ __forceinline__ void generic_body(const Params &p)
     const int64_t base = active ? row * H : 0;
     constexpr int64_t kStride = (int64_t)kTpr * kEpa;
 
-    float sum_sq = 0.0f;
+    LaneSum sum_sq;
     if (active) {
         for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
             V xv[kU], rv[kU];
@@ -488,6 +509,7 @@ __device__ __forceinline__ void generic_body(const Params &p)
                         rv[u] = A::load(p.res, base + j);
                 }
             }
+            float batch = 0.0f;
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if (j0 + u * kStride < H) {
@@ -496,13 +518,14 @@ __device__ __forceinline__ void generic_body(const Params &p)
                         float v = A::get(xv[u], e);
                         if constexpr (kFused)
                             v = v + A::get(rv[u], e);
-                        sum_sq = __builtin_fmaf(v, v, sum_sq);
+                        batch = __builtin_fmaf(v, v, batch);
                     }
                 }
             }
+            sum_sq.add(batch);
         }
     }
-    const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq), p.hidden, p.eps);
+    const float scale = row_scale(team_sum<kTpr, kBlock>(sum_sq.value()), p.hidden, p.eps);
     if (!active)
         return;
     // Second pass: each element is read again and written by the same lane that
@@ -911,7 +934,7 @@ __device__ __forceinline__ void softmax_generic_body(const Params &p)
     constexpr int64_t kStride = (int64_t)kTpr * kEpa;
 
     float mx = -__builtin_inff();
-    float s = 0.0f;
+    LaneSum s;
     if (active) {
         for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
             V xv[kU];
@@ -935,15 +958,17 @@ __device__ __forceinline__ void softmax_generic_body(const Params &p)
             for (int u = 0; u < kU; ++u)
                 if (j0 + u * kStride < H)
                     xv[u] = A::load(p.x, base + j0 + u * kStride);
+            float batch = 0.0f;
 #pragma unroll
             for (int u = 0; u < kU; ++u)
                 if (j0 + u * kStride < H)
 #pragma unroll
                     for (int e = 0; e < kEpa; ++e)
-                        s = s + softmax_exp<T>(A::get(xv[u], e) - m);
+                        batch = batch + softmax_exp<T>(A::get(xv[u], e) - m);
+            s.add(batch);
         }
     }
-    const float sum = team_sum<kTpr, kBlock>(s);
+    const float sum = team_sum<kTpr, kBlock>(s.value());
     if (!active)
         return;
     const float r = 1.0f / sum;
@@ -1183,7 +1208,7 @@ __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
     const int64_t base = active ? row * H : 0;
     constexpr int64_t kStride = (int64_t)kTpr * kEpa;
 
-    float ss = 0.0f, dot = 0.0f;
+    LaneSum ss_sum, dot_sum;
     if (active) {
         for (int64_t j0 = (int64_t)lane * kEpa; j0 < H; j0 += kU * kStride) {
             V xv[kU], dv[kU], wv[kU];
@@ -1196,6 +1221,7 @@ __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
                     wv[u] = A::load(p.w, j);
                 }
             }
+            float bs = 0.0f, bd = 0.0f;
 #pragma unroll
             for (int u = 0; u < kU; ++u)
                 if (j0 + u * kStride < H)
@@ -1203,11 +1229,14 @@ __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
                     for (int e = 0; e < kEpa; ++e) {
                         const float xe = A::get(xv[u], e);
                         const float ge = A::get(dv[u], e) * A::get(wv[u], e);
-                        ss = __builtin_fmaf(xe, xe, ss);
-                        dot = __builtin_fmaf(ge, xe, dot);
+                        bs = __builtin_fmaf(xe, xe, bs);
+                        bd = __builtin_fmaf(ge, xe, bd);
                     }
+            ss_sum.add(bs);
+            dot_sum.add(bd);
         }
     }
+    float ss = ss_sum.value(), dot = dot_sum.value();
     team_fold2<kTpr, kBlock>(ss, dot);
     if (!active)
         return;
@@ -1245,7 +1274,8 @@ __device__ __forceinline__ void bwd_generic_body(const BwdParams &p)
 
 // Generic path, dw partials: block (blockIdx.x, blockIdx.y) sums the columns
 // blockIdx.x * 256 + threadIdx.x over the rows of chunk blockIdx.y (chunks of
-// ceil(rows / gridDim.y) consecutive rows), in row order.
+// ceil(rows / gridDim.y) consecutive rows), in row order, compensated
+// (a chunk may hold thousands of rows).
 template <typename T>
 __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
 {
@@ -1255,12 +1285,12 @@ __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
     const int64_t r1 = r0 + per < p.rows ? r0 + per : p.rows;
     if (j >= p.hidden)
         return;
-    float acc = 0.0f;
+    LaneSum acc;
     for (int64_t r = r0; r < r1; ++r) {
         const int64_t i = r * p.hidden + j;
-        acc = __builtin_fmaf(Scalar<T>::get(p.dy, i), Scalar<T>::get(p.x, i) * p.rho[r], acc);
+        acc.add(Scalar<T>::get(p.dy, i) * (Scalar<T>::get(p.x, i) * p.rho[r]));
     }
-    p.part[(size_t)blockIdx.y * (size_t)p.hidden + j] = acc;
+    p.part[(size_t)blockIdx.y * (size_t)p.hidden + j] = acc.value();
 }
 
 // dw[j] = the nparts partial rows added in a fixed order: wave v of the
