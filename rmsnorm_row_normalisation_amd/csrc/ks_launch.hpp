@@ -315,8 +315,8 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
     if (err != hipSuccess || l.dw == nullptr)
         return err;
     DwParams d{l.dw, l.work, nparts, l.hidden};
-    hipLaunchKernelGGL((rms_norm_backward_dw<T>), dim3((unsigned)((l.hidden + 63) / 64)), dim3(kDwBlock), 0, l.stream,
-                       d);
+    const dim3 dgrid((unsigned)((l.hidden + kDwCols - 1) / kDwCols));
+    hipLaunchKernelGGL((rms_norm_backward_dw<T>), dgrid, dim3(kDwBlock), 0, l.stream, d);
     return hipGetLastError();
 }
 
