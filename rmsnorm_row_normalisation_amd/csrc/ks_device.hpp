@@ -27,12 +27,15 @@
 //                   multiple of 16, and rows wider than the vector kernels
 //                   hold in registers.
 //   rms_norm_backward_colsum / _dw   the weight gradient's column sums.
+//   softmax_split_stats / _norm      softmax with a row cut into chunks, one
+//                   workgroup per chunk (wide rows in small batches), with
+//                   per-chunk statistics in a caller workspace.
 //
 // Reduction: the vector kernels sum every row in one canonical order that is
 // the same for every launch shape (see "Reductions" below), so their results
 // do not depend on the plan or on the batch a row is in.  The generic
 // kernels' order depends on the plan, which depends only on (op, dtype,
-// hidden).
+// hidden); the split softmax sums in its own order (chunk sums, rescaled).
 #pragma once
 
 #include <hip/hip_runtime.h>
