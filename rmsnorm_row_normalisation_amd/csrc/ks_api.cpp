@@ -53,7 +53,8 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // The launch policy: a function of op, dtype, rows, hidden and alignment.
 // (Every vector plan sums a row in the same canonical order, so choosing the
-// launch shape from the batch size never changes a result.)
+// launch shape from the batch size never changes a result.  The one
+// exception is the split softmax, which only calls with a workspace get.)
 //
 // Vector path (aligned buffers, row bytes a multiple of 16, rows up to 128 KiB):
 //   * work units are the row's 16-byte pieces; a batch holds rows * nvec;
