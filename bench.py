@@ -26,7 +26,10 @@ Timing:
     trace of the same run gives the duration alone);
   * ``copy_reference``: the HIP runtime's own device-to-device copy of one
     batch-sized tensor, timed the same way: what a plain read+write stream of
-    that size achieves on this GPU.
+    that size achieves on this GPU;
+  * ``copy_ceiling``: the same copy of 1 GiB, where launch costs vanish: what
+    a read+write stream reaches on this GPU at all (context, not the
+    denominator: fractions are of the 8 TB/s spec).
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
 writes both, (4 R H + H) elements; rms_norm_residual reads x and residual
@@ -430,6 +433,34 @@ def load_traffic(workload: str) -> dict | None:
     return data.get("workloads", {}).get(workload)
 
 
+def copy_ceiling(mib: int = 1024, reps: int = 8) -> dict:
+    """The runtime's device-to-device copy of MIB MiB (read MIB, write MIB) on
+    the same stream and clock as the kernels: what a plain read+write stream
+    reaches on this device at a size where launch costs vanish.  Context for
+    the fractions of the 8 TB/s spec, never their denominator."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    ms = float(np.median(times))
+    del src, dst
+    torch.cuda.empty_cache()
+    gbps = 2 * n / (ms * 1e-3) / 1e9
+    return {"bytes": 2 * n, "ms_per_copy": round(ms, 4), "gbps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def copy_calibration(mib: int) -> None:
     """Plain device-to-device copies of a known size: the reference the HBM
     counters are scaled by (bytes read = bytes written = MIB MiB per copy)."""
@@ -669,6 +700,7 @@ def main() -> None:
         "per_op": per_op,
         "roofline": roofline,
         "copy_reference": res["copy_reference"],
+        "copy_ceiling": copy_ceiling(),
         "parity": parity,
         "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", "?"), "cus": dev.multi_processor_count,
                    "memory": memory_interface()},
