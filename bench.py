@@ -27,9 +27,10 @@ Timing:
   * ``copy_reference``: the HIP runtime's own device-to-device copy of one
     batch-sized tensor, timed the same way: what a plain read+write stream of
     that size achieves on this GPU;
-  * ``copy_ceiling``: the same copy of 1 GiB, where launch costs vanish: what
-    a read+write stream reaches on this GPU at all (context, not the
-    denominator: fractions are of the 8 TB/s spec).
+  * ``copy_ceiling``: a 1 GiB read + 1 GiB write stream by the runtime's
+    elementwise kernel (out = -x), where launch costs vanish: what a plain
+    read+write stream reaches on this GPU (context, not the denominator:
+    fractions are of the 8 TB/s spec).
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
 writes both, (4 R H + H) elements; rms_norm_residual reads x and residual
@@ -434,22 +435,23 @@ def load_traffic(workload: str) -> dict | None:
 
 
 def copy_ceiling(mib: int = 1024, reps: int = 8) -> dict:
-    """The runtime's device-to-device copy of MIB MiB (read MIB, write MIB) on
-    the same stream and clock as the kernels: what a plain read+write stream
-    reaches on this device at a size where launch costs vanish.  Context for
-    the fractions of the 8 TB/s spec, never their denominator."""
+    """A read+write stream of MIB MiB each way by the runtime's elementwise
+    kernel (out = -x over bf16, a shader kernel: the DMA copy behind
+    ``Tensor.copy_`` is slower), on the same clock as the kernels, at a size
+    where launch costs vanish: what a plain read+write stream reaches on this
+    device.  Context for the fractions of the 8 TB/s spec, never their
+    denominator."""
     n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
     dst = torch.empty_like(src)
-    src.fill_(1)
-    dst.copy_(src)
+    torch.neg(src, out=dst)
     torch.cuda.synchronize()
     times = []
     for _ in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / reps)
@@ -457,7 +459,7 @@ def copy_ceiling(mib: int = 1024, reps: int = 8) -> dict:
     del src, dst
     torch.cuda.empty_cache()
     gbps = 2 * n / (ms * 1e-3) / 1e9
-    return {"bytes": 2 * n, "ms_per_copy": round(ms, 4), "gbps": round(gbps, 1),
+    return {"op": "torch.neg, bf16", "bytes": 2 * n, "ms_per_pass": round(ms, 4), "gbps": round(gbps, 1),
             "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
