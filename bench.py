@@ -24,9 +24,9 @@ Timing:
     average launch period includes the short gap between consecutive kernels,
     so it is an upper bound on the kernel's own duration (rocprofv3's kernel
     trace of the same run gives the duration alone);
-  * ``copy_reference``: the HIP runtime's own device-to-device copy of one
-    batch-sized tensor, timed the same way: what a plain read+write stream of
-    that size achieves on this GPU;
+  * ``copy_reference``: one batch-sized tensor streamed through the runtime's
+    elementwise kernel (out = -x: one read, one write), timed the same way:
+    what a plain read+write stream of that size achieves on this GPU;
   * ``copy_ceiling``: a 1 GiB read + 1 GiB write stream by the runtime's
     elementwise kernel (out = -x), where launch costs vanish: what a plain
     read+write stream reaches on this GPU (context, not the denominator:
@@ -314,11 +314,13 @@ class Rig:
         torch.cuda.synchronize()
 
     def copy_reference(self, reps: int) -> dict:
-        """The runtime's device-to-device copy of one batch-sized tensor per launch."""
+        """A read+write stream of one batch-sized tensor per launch by the
+        runtime's elementwise kernel (out = -x; the DMA copy behind
+        ``Tensor.copy_`` is slower)."""
         n = self.nsets
         srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx", s.get("ox", s.get("bx")))))) for s in self.sets]
         dsts = [torch.empty_like(t) for t in srcs]
-        ms = self.timed_graph(lambda i: dsts[i % n].copy_(srcs[i % n]), n, reps)
+        ms = self.timed_graph(lambda i: torch.neg(srcs[i % n], out=dsts[i % n]), n, reps)
         del dsts
         us = ms * 1e3 / (n * reps)
         gbps = 2 * self.tensor_bytes / (us * 1e-6) / 1e9
