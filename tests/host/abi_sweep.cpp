@@ -135,18 +135,28 @@ int main()
     const int vpts[] = {-1, 0, 1, 3, 4, 5, 8, 9};
     const int epas[] = {0, 1, 2, 4, 8, 16};
     const int blocks[] = {0, 64, 256, 512, 1024};
-    const int hints[] = {0, 1, 2};
+    const int hints[] = {0, 1, 2, 3};
     for (int path : paths)
         for (int tpr : tprs)
             for (int vpt : vpts)
                 for (int epa : epas)
                     for (int block : blocks)
-                        for (int h : hints) {
-                            ks_plan_t p{path, tpr, vpt, epa, tpr > 0 ? block / tpr : 0, block, h & 1, h >> 1, h == 2};
+                        for (int h : hints)
+                          for (int rpt : {1, 2, 3, 4}) {
+                            ks_plan_t p{path, tpr, vpt, epa, tpr > 0 ? block / tpr * rpt : 0, block, h & 1, h >> 1,
+                                        h == 2};
                             for (int64_t hidden : {5ll, 1000ll, 4096ll, 40000ll}) {
                                 long before = ks::g_launches;
                                 expect_status(ks_rms_norm_ex(at(0), at(4 * kGiB), at(12 * kGiB), 4, hidden, 1e-6f,
                                                              KS_DTYPE_BFLOAT16, &p, 0), before, 4);
+                                before = ks::g_launches;
+                                expect_status(ks_fused_add_rms_norm_ex(at(4 * kGiB), at(8 * kGiB), at(12 * kGiB), 4,
+                                                                       hidden, 1e-6f, KS_DTYPE_FLOAT16, &p, 0),
+                                              before, 4);
+                                before = ks::g_launches;
+                                expect_status(ks_rms_norm_residual_ex(at(0), at(4 * kGiB), at(8 * kGiB), at(12 * kGiB),
+                                                                      4, hidden, 1e-6f, KS_DTYPE_FLOAT32, &p, 0),
+                                              before, 4);
                                 before = ks::g_launches;
                                 expect_status(ks_softmax_ex(at(0), at(4 * kGiB), 4, hidden, KS_DTYPE_FLOAT32, &p, 0),
                                               before, 4);

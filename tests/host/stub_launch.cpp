@@ -17,17 +17,30 @@ long g_launches = 0;
         return hipSuccess;                 \
     }
 
-KS_STUB(launch_vec_f32_rms, Launch)
-KS_STUB(launch_vec_f32_fused, Launch)
-KS_STUB(launch_vec_f32_residual, Launch)
+// The RMSNorm forms: an accepted plan names a compiled shape (one row per
+// team, so rows_per_block is the workgroup's team count).
+static hipError_t vec_stub(const Launch &l)
+{
+    ++g_launches;
+    const ks_plan_t &p = l.plan;
+    if (p.threads_per_row <= 0 || p.rows_per_block != p.block_threads / p.threads_per_row)
+        abort();
+    return hipSuccess;
+}
+#define KS_VEC_STUB(name) \
+    hipError_t name(const Launch &l) { return vec_stub(l); }
+
+KS_VEC_STUB(launch_vec_f32_rms)
+KS_VEC_STUB(launch_vec_f32_fused)
+KS_VEC_STUB(launch_vec_f32_residual)
 KS_STUB(launch_generic_f32, Launch)
-KS_STUB(launch_vec_f16_rms, Launch)
-KS_STUB(launch_vec_f16_fused, Launch)
-KS_STUB(launch_vec_f16_residual, Launch)
+KS_VEC_STUB(launch_vec_f16_rms)
+KS_VEC_STUB(launch_vec_f16_fused)
+KS_VEC_STUB(launch_vec_f16_residual)
 KS_STUB(launch_generic_f16, Launch)
-KS_STUB(launch_vec_bf16_rms, Launch)
-KS_STUB(launch_vec_bf16_fused, Launch)
-KS_STUB(launch_vec_bf16_residual, Launch)
+KS_VEC_STUB(launch_vec_bf16_rms)
+KS_VEC_STUB(launch_vec_bf16_fused)
+KS_VEC_STUB(launch_vec_bf16_residual)
 KS_STUB(launch_generic_bf16, Launch)
 // Softmax: a split plan must arrive with a workspace.
 static hipError_t softmax_stub(const Launch &l)
