@@ -22,7 +22,9 @@
  *            memory, where a call needs it, is a caller-owned workspace).
  *            weight is only read.  Any alignment is accepted; 16-byte aligned
  *            buffers with hidden * sizeof(element) a multiple of 16 take the
- *            vector path, others a narrower path with identical results.
+ *            vector path, others a narrower path with the same contract
+ *            (its sums run in another order, so a result may differ from the
+ *            vector path's in the last bit).
  * Streams    Work is enqueued on `stream` (0 = the default stream) and the
  *            call returns without waiting.  Calls that overlap in time on
  *            the same buffers race, as with any asynchronous kernel.
@@ -33,16 +35,18 @@
  *            output rounded to the dtype with round-to-nearest-even.  The
  *            summation order depends only on hidden, dtype and alignment, so
  *            a row's result does not depend on how many rows are in the
- *            batch.
+ *            batch (the split plans of ks_softmax_ws aside).
  * Errors     Checked in this order, before any HIP call:
  *              KS_ERROR_UNSUPPORTED_DTYPE  dtype is not one of ks_dtype_t;
- *              KS_ERROR_INVALID_VALUE      rows < 0; hidden <= 0 or
- *                                          hidden > 2^24; rows * hidden *
- *                                          element size > 2^62; eps not
- *                                          finite or eps <= 0; a NULL
- *                                          pointer while rows > 0; a bad plan;
+ *              KS_ERROR_INVALID_VALUE      rows < 0 or rows > 2^31 - 1;
+ *                                          hidden <= 0 or hidden > 2^24;
+ *                                          eps not finite or eps <= 0; a
+ *                                          NULL pointer while rows > 0; a
+ *                                          bad plan; a missing or too small
+ *                                          workspace;
  *              KS_ERROR_OVERLAP            forbidden aliasing (per call);
- *            then rows == 0 returns KS_SUCCESS without touching HIP.
+ *            then rows == 0 returns KS_SUCCESS without touching HIP (the
+ *            backward with a weight gradient still writes dw = 0).
  *            KS_ERROR_HIP reports a failed launch (e.g. no device); the HIP
  *            error code is kept per thread in ks_last_hip_error().
  */

@@ -72,6 +72,10 @@ inline int64_t bwd_workspace_floats(int64_t rows, int64_t hidden)
     return parts * hidden + rows;
 }
 
+// Work-items one launch of a row kernel may hold (its grid counts work-items
+// in 32 bits); the launch code covers larger batches in slices of rows.
+constexpr int64_t kMaxLaunchItems = int64_t(1) << 31;
+
 // Cache-policy bits of a buffer instruction that marks it non-temporal.
 constexpr int kNonTemporal = 2;
 

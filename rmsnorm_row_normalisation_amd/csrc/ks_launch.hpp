@@ -9,14 +9,31 @@
 
 namespace ks {
 
-template <typename Kernel>
+// Rows one launch of a row kernel may cover: its grid stays within 2^31
+// work-items (a dispatch counts work-items in 32 bits); larger batches go out
+// in consecutive slices of rows, each a launch of the same kernel.
+inline int64_t rows_per_launch(int64_t rows_per_block, int block)
+{
+    return (kMaxLaunchItems / block) * rows_per_block;
+}
+
+template <typename T, typename Kernel>
 hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
 {
-    Params p{l.y, l.x, l.res, l.w, l.rows, l.hidden, l.eps};
     const int64_t rpb = block / l.plan.threads_per_row;
-    const dim3 grid((unsigned)((l.rows + rpb - 1) / rpb));
-    hipLaunchKernelGGL(kernel, grid, dim3(block), lds_bytes, l.stream, p);
-    return hipGetLastError();
+    const int64_t slice = rows_per_launch(rpb, block);
+    const size_t row_bytes = (size_t)l.hidden * Pack<T>::kBytes;
+    for (int64_t r0 = 0; r0 < l.rows; r0 += slice) {
+        const int64_t n = l.rows - r0 < slice ? l.rows - r0 : slice;
+        const size_t off = (size_t)r0 * row_bytes;
+        Params p{(char *)l.y + off, (const char *)l.x + off, l.res ? (char *)l.res + off : nullptr, l.w, n,
+                 l.hidden, l.eps};
+        hipLaunchKernelGGL(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), lds_bytes, l.stream, p);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 // The kernel entry point of one op (OP is a ks_op_t: RMSNorm, fused in place,
@@ -56,14 +73,14 @@ hipError_t vec_one(const Launch &l)
     constexpr int NT = kNonTemporal;
     const ks_plan_t &p = l.plan;
     if (!p.load_nt && !p.store_nt && !p.weight_lds)
-        return run(vec_entry<OP, T, TPR, V, B, 0, 0, false>(), l, B);
+        return run<T>(vec_entry<OP, T, TPR, V, B, 0, 0, false>(), l, B);
     if (p.load_nt && p.store_nt && !p.weight_lds)
-        return run(vec_entry<OP, T, TPR, V, B, NT, NT, false>(), l, B);
+        return run<T>(vec_entry<OP, T, TPR, V, B, NT, NT, false>(), l, B);
     if (!p.load_nt && p.store_nt && !p.weight_lds)
-        return run(vec_entry<OP, T, TPR, V, B, 0, NT, false>(), l, B);
+        return run<T>(vec_entry<OP, T, TPR, V, B, 0, NT, false>(), l, B);
     if constexpr (OP != KS_OP_SOFTMAX) {
         if (p.load_nt && p.store_nt && p.weight_lds)
-            return run(vec_entry<OP, T, TPR, V, B, NT, NT, true>(), l, B, (size_t)V * TPR * 16);
+            return run<T>(vec_entry<OP, T, TPR, V, B, NT, NT, true>(), l, B, (size_t)V * TPR * 16);
     }
     return hipErrorInvalidValue;
 }
@@ -104,10 +121,10 @@ template <typename T, int OP, int EPA>
 hipError_t generic_by_tpr(const Launch &l)
 {
     switch (l.plan.threads_per_row) {
-    case 8: return run(generic_entry<OP, T, 8, EPA, 256>(), l, 256);
-    case 64: return run(generic_entry<OP, T, 64, EPA, 256>(), l, 256);
-    case 256: return run(generic_entry<OP, T, 256, EPA, 256>(), l, 256);
-    case 1024: return run(generic_entry<OP, T, 1024, EPA, 1024>(), l, 1024);
+    case 8: return run<T>(generic_entry<OP, T, 8, EPA, 256>(), l, 256);
+    case 64: return run<T>(generic_entry<OP, T, 64, EPA, 256>(), l, 256);
+    case 256: return run<T>(generic_entry<OP, T, 256, EPA, 256>(), l, 256);
+    case 1024: return run<T>(generic_entry<OP, T, 1024, EPA, 1024>(), l, 1024);
     default: return hipErrorInvalidValue;
     }
 }
@@ -160,13 +177,22 @@ hipError_t launch_softmax_typed(const Launch &l)
 // ---------------------------------------------------------------------------
 // SwiGLU
 // ---------------------------------------------------------------------------
-template <typename Kernel>
+template <typename T, typename Kernel>
 hipError_t run_swiglu(Kernel kernel, const SwigluLaunch &l, int block)
 {
-    SwigluParams p{l.out, l.x, l.rows, l.d};
     const int64_t rpb = block / l.plan.threads_per_row;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)((l.rows + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
-    return hipGetLastError();
+    const int64_t slice = rows_per_launch(rpb, block);
+    const size_t out_bytes = (size_t)l.d * Pack<T>::kBytes;   // per row; x rows are twice as long
+    for (int64_t r0 = 0; r0 < l.rows; r0 += slice) {
+        const int64_t n = l.rows - r0 < slice ? l.rows - r0 : slice;
+        SwigluParams p{(char *)l.out + (size_t)r0 * out_bytes, (const char *)l.x + (size_t)r0 * 2 * out_bytes, n,
+                       l.d};
+        hipLaunchKernelGGL(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 template <typename T, int TPR, int V>
@@ -176,11 +202,11 @@ hipError_t swiglu_one(const SwigluLaunch &l)
     constexpr int NT = kNonTemporal;
     const ks_plan_t &p = l.plan;
     if (!p.load_nt && !p.store_nt)
-        return run_swiglu(silu_and_mul_vec<T, TPR, V, B, 0, 0>, l, B);
+        return run_swiglu<T>(silu_and_mul_vec<T, TPR, V, B, 0, 0>, l, B);
     if (p.load_nt && p.store_nt)
-        return run_swiglu(silu_and_mul_vec<T, TPR, V, B, NT, NT>, l, B);
+        return run_swiglu<T>(silu_and_mul_vec<T, TPR, V, B, NT, NT>, l, B);
     if (!p.load_nt && p.store_nt)
-        return run_swiglu(silu_and_mul_vec<T, TPR, V, B, 0, NT>, l, B);
+        return run_swiglu<T>(silu_and_mul_vec<T, TPR, V, B, 0, NT>, l, B);
     return hipErrorInvalidValue;
 }
 
@@ -298,13 +324,24 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
             nparts = (int32_t)(l.rows < kBwdMaxParts ? l.rows : kBwdMaxParts);
             if (l.dw)
                 p.rho = l.work + (size_t)nparts * (size_t)l.hidden;
-            const unsigned grid = (unsigned)((l.rows + rpb - 1) / rpb);
-            if (pl.elems_per_access == 1)
-                err = bwd_generic_by_tpr<T, 1>(p, pl.threads_per_row, grid, l.stream);
-            else if (pl.elems_per_access == Pack<T>::kElems)
-                err = bwd_generic_by_tpr<T, Pack<T>::kElems>(p, pl.threads_per_row, grid, l.stream);
-            else
+            if (pl.elems_per_access != 1 && pl.elems_per_access != Pack<T>::kElems)
                 return hipErrorInvalidValue;
+            const int64_t slice = rows_per_launch(rpb, pl.block_threads);
+            const size_t row_bytes = (size_t)l.hidden * Pack<T>::kBytes;
+            for (int64_t r0 = 0; r0 < l.rows && err == hipSuccess; r0 += slice) {
+                const int64_t n = l.rows - r0 < slice ? l.rows - r0 : slice;
+                const size_t off = (size_t)r0 * row_bytes;
+                BwdParams ps = p;
+                ps.dx = (char *)p.dx + off;
+                ps.dy = (const char *)p.dy + off;
+                ps.x = (const char *)p.x + off;
+                ps.rho = p.rho ? p.rho + r0 : nullptr;
+                ps.rows = n;
+                const unsigned grid = (unsigned)((n + rpb - 1) / rpb);
+                err = pl.elems_per_access == 1
+                          ? bwd_generic_by_tpr<T, 1>(ps, pl.threads_per_row, grid, l.stream)
+                          : bwd_generic_by_tpr<T, Pack<T>::kElems>(ps, pl.threads_per_row, grid, l.stream);
+            }
             if (err == hipSuccess && l.dw) {
                 const dim3 cgrid((unsigned)((l.hidden + 255) / 256), (unsigned)nparts);
                 hipLaunchKernelGGL((rms_norm_backward_colsum<T>), cgrid, dim3(256), 0, l.stream, p);

@@ -83,3 +83,37 @@ def test_backward(dtype):
     mdx, mdw = magnitudes(dy, x, w, 1e-6)
     say(check_gradient(gx.cpu(), rx, mdx))
     say(check_gradient(gw.cpu(), rw, mdw))
+
+
+@pytest.mark.parametrize("op", ["rms_norm", "fused_add_rms_norm", "softmax"])
+def test_batches_beyond_one_launch(op):
+    """Batches whose grid would pass 2^31 work-items go out in slices of rows:
+    2^29 + 4099 rows of 8 bf16 elements (8 GiB per tensor; 16-byte rows, 32
+    rows per 256-thread workgroup, so slices of 2^28 rows, and more than 2^32
+    work-items in all), checked against the oracle on the rows around the
+    slice boundaries, the first and last rows and 2000 sampled rows."""
+    rows, hidden = (1 << 29) + 4099, 8
+    g = torch.Generator(device="cuda").manual_seed(28)
+    x = torch.randn(rows, hidden, dtype=torch.bfloat16, device="cuda", generator=g)
+    w = workloads.random_case((1, hidden), "bfloat16", seed=29)["weight"]
+    edges = [0, 1, (1 << 28) - 1, 1 << 28, (1 << 28) + 1, (1 << 29) - 1, 1 << 29, (1 << 29) + 1, rows - 1]
+    pick = torch.cat([torch.tensor(edges),
+                      torch.randint(0, rows, (2000,), generator=torch.Generator().manual_seed(30))]).cuda()
+    xs = x[pick].cpu()
+    say("limits slices", op, rows, hidden, ks.get_plan(op, torch.bfloat16, hidden, rows).as_dict())
+    if op == "rms_norm":
+        y = ks.rms_norm(x, w.cuda(), 1e-6)
+        torch.cuda.synchronize()
+        say(check_normalised(y[pick].cpu(), oracle.rms_norm(xs, w, 1e-6)))
+    elif op == "softmax":
+        y = ks.softmax(x)
+        torch.cuda.synchronize()
+        say(check_normalised(y[pick].cpu(), oracle.softmax(xs)))
+    else:
+        r = torch.randn(rows, hidden, dtype=torch.bfloat16, device="cuda", generator=g)
+        rs = r[pick].cpu()
+        ks.fused_add_rms_norm(x, r, w.cuda(), 1e-6)
+        torch.cuda.synchronize()
+        ox, orr = oracle.fused_add_rms_norm(xs, rs, w, 1e-6)
+        check_bitexact(r[pick].cpu(), orr)
+        say(check_normalised(x[pick].cpu(), ox))
