@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 OPS = ["rms_norm", "fused_add_rms_norm", "rms_norm_residual", "rms_norm_backward", "silu_and_mul", "softmax"]
 DTYPES = ["bfloat16", "float16", "float32"]
 HIDDEN = [1, 2, 3, 8, 17, 64, 96, 127, 512, 1000, 1536, 2047, 2880, 4096, 5120, 8192, 12288, 16384, 24576,
-          32768, 40000]
+          32768, 40000, 65536, 128256]
 ROWS = [1, 2, 3, 7, 33, 100, 256, 513]
 
 
@@ -51,7 +51,7 @@ def _gpu():
     require_gpu()
 
 
-@pytest.mark.parametrize("i", range(60))
+@pytest.mark.parametrize("i", range(120))
 def test_random_case(i):
     op, dtype, shape, offset, eps, seed = draw(i)
     say("random", i, op, dtype, shape, f"offset={offset}", f"eps={eps}")
