@@ -65,7 +65,8 @@ typedef enum {
     KS_ERROR_INVALID_VALUE = 1,
     KS_ERROR_UNSUPPORTED_DTYPE = 2,
     KS_ERROR_OVERLAP = 3,
-    KS_ERROR_HIP = 4
+    KS_ERROR_HIP = 4,
+    KS_ERROR_SCRATCH_LIMIT = 5      /* ks_softmax_noalloc: the plan needs more scratch than the static array */
 } ks_status_t;
 
 typedef enum {
@@ -328,6 +329,30 @@ ks_status_t ks_softmax_ws(void *out, const void *x, int64_t rows, int64_t hidden
  * block_threads 256, load_nt = store_nt = 1, weight_lds 0). */
 ks_status_t ks_softmax_ws_ex(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
                              void *workspace, size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream);
+
+/*
+ * Softmax for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid allocation.
+ * The contract, arguments, plans and overlap rules are those of
+ * ks_softmax_ws; the split plan's per-chunk statistics go to a device array
+ * that the library itself holds (KS_NOALLOC_SCRATCH_BYTES on each GPU the
+ * library runs on, kept until the process ends), so the caller passes no
+ * workspace.  The call allocates, frees and copies nothing.
+ *   - A plan that needs more than KS_NOALLOC_SCRATCH_BYTES of statistics
+ *     (8 bytes per chunk and row; see ks_softmax_workspace_size) is rejected
+ *     with KS_ERROR_SCRATCH_LIMIT before any HIP call.
+ *   - The array needs no initial contents: a split call writes every
+ *     statistic it reads, and a one-pass plan does not touch the array.
+ *   - All calls on one GPU share that GPU's array and leave their statistics
+ *     in it.  Calls whose work overlaps in time on one GPU (for example on
+ *     two streams without an ordering between them) race on the array;
+ *     order them on one stream, or give one of them ks_softmax_ws.
+ *   - The first call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress, no allocation); a failure there is KS_ERROR_HIP.
+ */
+#define KS_NOALLOC_SCRATCH_BYTES (1u << 20)
+ks_status_t ks_softmax_noalloc(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                               hipStream_t stream);
 
 /* Static description of a status code. */
 const char *ks_status_string(ks_status_t status);

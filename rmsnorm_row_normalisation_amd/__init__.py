@@ -30,6 +30,8 @@ from .binding import (  # noqa: F401
     ks_softmax_workspace_size,
     ks_softmax_ws,
     ks_softmax_ws_ex,
+    ks_softmax_noalloc,
+    KS_NOALLOC_SCRATCH_BYTES,
     KS_PLAN_ALIGNED,
     KS_PLAN_WORKSPACE,
     rms_norm_residual,

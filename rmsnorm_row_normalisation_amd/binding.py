@@ -19,7 +19,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_LIB = os.path.join(_PKG, "libks_norm.so")
 
-KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP = range(5)
+(KS_SUCCESS, KS_ERROR_INVALID_VALUE, KS_ERROR_UNSUPPORTED_DTYPE, KS_ERROR_OVERLAP, KS_ERROR_HIP,
+ KS_ERROR_SCRATCH_LIMIT) = range(6)
+KS_NOALLOC_SCRATCH_BYTES = 1 << 20
 KS_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 (KS_OP_RMS_NORM, KS_OP_FUSED_ADD_RMS_NORM, KS_OP_SILU_AND_MUL, KS_OP_SOFTMAX, KS_OP_RMS_NORM_RESIDUAL,
  KS_OP_RMS_NORM_BACKWARD) = range(6)
@@ -102,6 +104,7 @@ def lib() -> ctypes.CDLL:
         h.ks_softmax_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(Plan), ctypes.POINTER(sz)]
         h.ks_softmax_ws.argtypes = [vp, vp, i64, i64, i32, vp, sz, vp]
         h.ks_softmax_ws_ex.argtypes = [vp, vp, i64, i64, i32, vp, sz, ctypes.POINTER(Plan), vp]
+        h.ks_softmax_noalloc.argtypes = [vp, vp, i64, i64, i32, vp]
         h.ks_status_string.argtypes = [i32]
         h.ks_status_string.restype = ctypes.c_char_p
         h.ks_last_hip_error.argtypes = []
@@ -111,7 +114,7 @@ def lib() -> ctypes.CDLL:
                      "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
                      "ks_softmax_ex", "ks_rms_norm_residual", "ks_rms_norm_residual_ex",
                      "ks_rms_norm_backward_workspace_size", "ks_rms_norm_backward", "ks_rms_norm_backward_ex",
-                     "ks_softmax_workspace_size", "ks_softmax_ws", "ks_softmax_ws_ex"):
+                     "ks_softmax_workspace_size", "ks_softmax_ws", "ks_softmax_ws_ex", "ks_softmax_noalloc"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -123,7 +126,7 @@ def _check(status: int, what: str) -> None:
     msg = f"{what}: {lib().ks_status_string(status).decode()}"
     if status == KS_ERROR_UNSUPPORTED_DTYPE:
         raise KsTypeError(status, msg)
-    if status in (KS_ERROR_INVALID_VALUE, KS_ERROR_OVERLAP):
+    if status in (KS_ERROR_INVALID_VALUE, KS_ERROR_OVERLAP, KS_ERROR_SCRATCH_LIMIT):
         raise KsValueError(status, msg)
     hip = int(lib().ks_last_hip_error())
     raise KsError(status, f"{msg} (hipError {hip})", hip)
@@ -216,6 +219,10 @@ def ks_softmax_ws_ex(out: int, x: int, rows: int, hidden: int, dtype: int, works
                      plan: Plan | None, stream: int) -> int:
     return lib().ks_softmax_ws_ex(out, x, rows, hidden, dtype, workspace, workspace_bytes,
                                   ctypes.byref(plan) if plan is not None else None, stream)
+
+
+def ks_softmax_noalloc(out: int, x: int, rows: int, hidden: int, dtype: int, stream: int) -> int:
+    return lib().ks_softmax_noalloc(out, x, rows, hidden, dtype, stream)
 
 
 KS_PLAN_ALIGNED = 1

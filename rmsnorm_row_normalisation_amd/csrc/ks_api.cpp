@@ -384,6 +384,29 @@ ks_status_t softmax_call(void *out, const void *x, int64_t rows, int64_t hidden,
 
 }  // namespace
 
+namespace ks {
+
+// The checks ks_softmax_ws makes before any HIP call (dtype, sizes, null
+// pointers) and the bytes of workspace the plan it would pick needs for these
+// buffers (0 for a one-pass plan).  No HIP call.
+ks_status_t softmax_ws_need(const void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                            size_t *need)
+{
+    if (!valid_dtype(dtype))
+        return KS_ERROR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
+        return KS_ERROR_INVALID_VALUE;
+    if (rows > 0 && (out == nullptr || x == nullptr))
+        return KS_ERROR_INVALID_VALUE;
+    const ks_plan_t p = policy(KS_OP_SOFTMAX, dtype, rows, hidden, aligned16(out) && aligned16(x), true);
+    *need = softmax_workspace_bytes(p, rows, hidden * elem_size(dtype));
+    return KS_SUCCESS;
+}
+
+void record_hip_error(int err) { g_last_hip_error = err; }
+
+}  // namespace ks
+
 extern "C" {
 
 ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t rows, int64_t hidden, float eps,
@@ -624,6 +647,9 @@ const char *ks_status_string(ks_status_t status)
     case KS_ERROR_UNSUPPORTED_DTYPE: return "KS_ERROR_UNSUPPORTED_DTYPE: dtype must be float32, float16 or bfloat16";
     case KS_ERROR_OVERLAP: return "KS_ERROR_OVERLAP: buffers overlap where the operation forbids it";
     case KS_ERROR_HIP: return "KS_ERROR_HIP: the HIP runtime reported an error (see ks_last_hip_error)";
+    case KS_ERROR_SCRATCH_LIMIT:
+        return "KS_ERROR_SCRATCH_LIMIT: the call needs more scratch than the library's static array holds "
+               "(KS_NOALLOC_SCRATCH_BYTES); pass a workspace to ks_softmax_ws instead";
     default: return "unknown ks_status_t";
     }
 }

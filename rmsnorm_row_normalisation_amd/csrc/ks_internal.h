@@ -119,6 +119,12 @@ inline int64_t split_workspace_floats(int64_t rows, int64_t row_bytes, int vpt)
     return rows * split_chunks(row_bytes, vpt) * 2;
 }
 
+// ks_api.cpp: the pre-HIP checks of ks_softmax_ws and the workspace bytes of
+// its plan for these buffers; the per-thread HIP error behind KS_ERROR_HIP.
+ks_status_t softmax_ws_need(const void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
+                            size_t *need);
+void record_hip_error(int err);
+
 // The one generic SwiGLU plan: a grid-stride loop over elements.
 constexpr int kSwigluGenericBlock = 256;
 

@@ -21,7 +21,7 @@ from rmsnorm_row_normalisation_amd import binding as b
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 F32, F16, BF16 = 0, 1, 2
-OK, INVALID, DTYPE, OVERLAP, HIP = range(5)
+OK, INVALID, DTYPE, OVERLAP, HIP, SCRATCH_LIMIT = range(6)
 A = 0x10000000          # fake, 16-byte aligned device addresses: only compared, never dereferenced
 MB = 1 << 20
 
@@ -51,7 +51,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(5):
+    for code in range(6):
         s = lib.ks_status_string(code).decode()
         assert s.startswith("KS_")
     assert lib.ks_status_string(99).decode().startswith("unknown")
@@ -520,6 +520,29 @@ def test_softmax_ws_statuses_and_overlaps():
     assert b.ks_softmax_ws(None, None, 0, 65536, F16, None, 0, 0) == OK
     # explicit split plans are checked against every other op too
     assert b.ks_rms_norm_ex(out, x, A + 768 * MB, 8, 65536, 1e-6, BF16, p, 0) == INVALID
+
+
+def test_softmax_noalloc_statuses():
+    """The allocation-free softmax checks what ks_softmax_ws checks, and rejects a
+    plan whose statistics would not fit the library's static array, all before
+    any HIP call."""
+    x, out = A, A + 4096 * MB
+    assert b.KS_NOALLOC_SCRATCH_BYTES == 1 << 20
+    assert b.ks_softmax_noalloc(out, x, 8, 4096, 9, 0) == DTYPE
+    assert b.ks_softmax_noalloc(out, x, -1, 4096, BF16, 0) == INVALID
+    assert b.ks_softmax_noalloc(out, x, 8, 0, BF16, 0) == INVALID
+    assert b.ks_softmax_noalloc(out, x, 8, (1 << 24) + 1, BF16, 0) == INVALID
+    assert b.ks_softmax_noalloc(None, x, 8, 4096, BF16, 0) == INVALID
+    assert b.ks_softmax_noalloc(out, None, 8, 4096, BF16, 0) == INVALID
+    assert b.ks_softmax_noalloc(None, None, 0, 65536, F16, 0) == OK          # empty batch: no HIP call
+    # 131072-wide fp32 rows split into 32 chunks: 256 bytes of statistics per
+    # row, so 4096 rows fill the 1 MiB array exactly and 4097 are too many
+    assert b.ks_softmax_workspace_size(4096, 131072, F32) == b.KS_NOALLOC_SCRATCH_BYTES
+    assert b.ks_softmax_workspace_size(4097, 131072, F32) > b.KS_NOALLOC_SCRATCH_BYTES
+    assert b.ks_softmax_noalloc(out, x, 4097, 131072, F32, 0) == SCRATCH_LIMIT
+    assert b.ks_softmax_noalloc(out, x, 65535, 2 ** 20, F16, 0) == SCRATCH_LIMIT
+    with pytest.raises(ks.KsValueError, match="SCRATCH_LIMIT"):
+        b._check(SCRATCH_LIMIT, "ks_softmax_noalloc")
 
 
 def test_softmax_split_policy():
