@@ -1,8 +1,9 @@
 """Benchmark: RMSNorm and fused residual-add RMSNorm on one MI355X (the
 default workload), and the SwiGLU (S*) and softmax (X*) workloads.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b] [--dtype bf16|fp16|fp32]
     python bench.py --sweep-workloads [--out FILE]      # every workload, one table
+    python bench.py --stream-reference                  # reference streams at 16 MiB and 1 GiB
 
 One step is one pass of the whole path over one batch: ks_rms_norm on the
 batch, then ks_fused_add_rms_norm on it (both at 2048 x 4096 bf16 by
@@ -14,23 +15,24 @@ working set, so the steps rotate over enough copies of the batch (1 GiB by
 default) that every step reads data last touched more than a cache's worth
 of traffic ago.  Numbers are therefore HBM numbers, not cache numbers.
 
-Timing:
+Timing (exactly K steps in every timed region):
   * whole job (``value``): one rotation of steps over the copies is captured
     into a HIP graph (no host launch overhead inside the timed region) and
-    replayed until K steps have run, between a synchronize and two events on
-    the launch stream;
-  * per kernel (``per_op``, ``roofline``): the same, with a graph holding only
-    that op's launches, back to back (the median of three timed regions); the
-    average launch period includes the short gap between consecutive kernels,
-    so it is an upper bound on the kernel's own duration (rocprofv3's kernel
-    trace of the same run gives the duration alone);
-  * ``copy_reference``: one batch-sized tensor streamed through the runtime's
-    elementwise kernel (out = -x: one read, one write), timed the same way:
-    what a plain read+write stream of that size achieves on this GPU;
-  * ``copy_ceiling``: a 1 GiB read + 1 GiB write stream by the runtime's
-    elementwise kernel (out = -x), where launch costs vanish: what a plain
-    read+write stream reaches on this GPU (context, not the denominator:
-    fractions are of the 8 TB/s spec).
+    replayed, plus a graph of the remaining K mod (copies) steps, between a
+    synchronize and two events on the launch stream;
+  * per op, launch period (``per_op[op].us_per_call``): the same, with graphs
+    holding only that op's launches back to back (median of three timed
+    regions): what a caller sees per call in a captured sequence;
+  * per op, kernel duration (``per_op[op].kernel_us``, ``roofline``): K calls
+    of that op on the launch stream, each timed by the runtime's
+    kernel-dispatch events (``ks_time_next_call``): min / p50 / p95 / p99 /
+    max / mean of the kernels' own durations.  ``roofline.achieved`` is the
+    dominant kernel's algorithmic bytes over its mean duration;
+  * ``stream_reference``: the library-independent reference streams of
+    ``libks_streamref.so`` timed the same way: an empty kernel (the
+    per-launch floor) and a plain copy (one 16-byte load and store per lane)
+    of one batch-sized tensor and of 1 GiB (context for the fractions, never
+    their denominator, which is the 8 TB/s spec).
 Bytes are the algorithmic bytes the contract must move: rms_norm reads x and
 writes out, (2 R H + H) elements; the fused form reads x and residual and
 writes both, (4 R H + H) elements; rms_norm_residual reads x and residual
@@ -71,6 +73,9 @@ FULL_PARITY_ELEMS = 1 << 24     # above this, the parity gate checks sampled row
 SAMPLED_ROWS = 64
 COPY_REPS = 5
 MAX_SETS = 1024
+STREAMREF_LIB = os.path.join(ROOT, "rmsnorm_row_normalisation_amd", "libks_streamref.so")
+REF_FLOOR_GROUPS = 512          # the empty reference kernel's grid (the headline kernels' workgroup count)
+GIB = 1 << 30
 
 
 def algorithmic_bytes(op: str, rows: int, hidden: int, esize: int) -> int:
@@ -108,12 +113,20 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="C3b", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--dtype", default=None, choices=sorted(workloads.DTYPE_TAGS),
+                    help="run the workload's shape, distributions and seeds in this dtype instead")
+    ap.add_argument("--sweep-dtypes", default="bf16,fp16,fp32",
+                    help="with --sweep-workloads: the dtypes the RMSNorm workloads C1, C2 and C3b also run in")
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="time the reference streams (reads, writes, copies) at 16 MiB and 1 GiB and exit")
     ap.add_argument("--rotate-mib", type=int, default=1024, help="total size of the rotating input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-workloads", action="store_true",
                     help="measure every workload (per op) and print a markdown table instead of the bench line")
-    ap.add_argument("--out", default=None, help="with --sweep-workloads: also write the table to this file")
+    ap.add_argument("--out", default=None,
+                    help="with --sweep-workloads: also write the table to this file; with --trace-summary: write "
+                         "the summary there")
     ap.add_argument("--json-out", default=None, help="also write the per-case results (JSON) to this file")
     ap.add_argument("--baseline", default=None,
                     help="a previous --json-out file: exit with status 2 if any matching case got slower "
@@ -121,6 +134,13 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--max-regression-percent", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run device-to-device copies of MIB MiB (the counter calibration run) and exit")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR", default=None,
+                    help="render a rocprofv3 --kernel-trace output directory of a bench run of --workload "
+                         "(--dtype) as a markdown summary and exit (no GPU needed)")
+    ap.add_argument("--trace-bench", metavar="JSON", default=None,
+                    help="with --trace-summary: the bench line of an uninstrumented run of the same command")
+    ap.add_argument("--trace-command", default=None,
+                    help="with --trace-summary: the command line the trace was taken with, quoted in the summary")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="turn four rocprofv3 --pmc output directories into profiles/hbm_traffic.json and exit")
     return ap.parse_args()
@@ -283,24 +303,61 @@ class Rig:
         else:
             self.ks.silu_and_mul(s["sx"], out=s["sout"])
 
-    def timed_graph(self, body, per_rotation: int, reps: int, repeats: int = 1) -> float:
-        """Capture body(i) for i in range(per_rotation) into a HIP graph and replay
-        it `reps` times between two events on the launch stream; milliseconds.
-        With repeats > 1 the timed region runs that many times and the median
-        is returned."""
-        graph = torch.cuda.CUDAGraph()
-        times = []
+    def raw_call(self, op: str):
+        """call(i): op on copy i through the C entry point itself, with every
+        argument marshalled in advance (a few microseconds of host time per
+        call, so a run of timed calls keeps the launch queue ahead of the GPU).
+        Returns the status."""
+        lib = self.ks.lib()
+        wl, n = self.wl, self.nsets
+        code = self.ks.KS_DTYPE[wl.torch_dtype]
+        rows, hidden = wl.rows, wl.hidden
+        eps = ctypes.c_float(wl.eps)
+        st = self.stream.cuda_stream
+        w = self.w.data_ptr() if self.w is not None else None
+        P = [{k: v.data_ptr() for k, v in s.items()} for s in self.sets]
+        if op == "rms_norm":
+            return lambda i: lib.ks_rms_norm(P[i % n]["out"], P[i % n]["x"], w, rows, hidden, eps, code, st)
+        if op == "fused_add_rms_norm":
+            return lambda i: lib.ks_fused_add_rms_norm(P[i % n]["fx"], P[i % n]["fr"], w, rows, hidden, eps, code, st)
+        if op == "rms_norm_residual":
+            return lambda i: lib.ks_rms_norm_residual(P[i % n]["oout"], P[i % n]["ox"], P[i % n]["or"], w, rows,
+                                                      hidden, eps, code, st)
+        if op == "softmax":
+            ws, wsn = self.softmax_workspace.data_ptr(), self.softmax_workspace.numel()
+            return lambda i: lib.ks_softmax_ws(P[i % n]["mout"], P[i % n]["mx"], rows, hidden, code, ws, wsn, st)
+        if op == "rms_norm_backward":
+            ws, wsn = self.workspace.data_ptr(), self.workspace.numel()
+            return lambda i: lib.ks_rms_norm_backward(P[i % n]["bdx"], P[i % n]["bdw"], P[i % n]["bdy"],
+                                                      P[i % n]["bx"], w, rows, hidden, eps, code, ws, wsn, st)
+        return lambda i: lib.ks_silu_and_mul(P[i % n]["sout"], P[i % n]["sx"], rows, hidden // 2, code, st)
+
+    def timed_graph(self, body, per_rotation: int, steps: int, repeats: int = 1) -> float:
+        """Exactly `steps` calls of body(i): body(i) for i < per_rotation is
+        captured into one HIP graph, body(i) for i < steps mod per_rotation into
+        a second; steps // per_rotation replays of the first and one of the
+        second run between two events on the launch stream.  Milliseconds
+        (the median of `repeats` timed regions)."""
+        reps, tail = divmod(steps, per_rotation)
+        graphs = []
         with torch.cuda.stream(self.stream):
-            with torch.cuda.graph(graph, stream=self.stream):
-                for i in range(per_rotation):
-                    body(i)
-            graph.replay()                                   # untimed
+            for count, n in ((reps, per_rotation), (1 if tail else 0, tail)):
+                if count == 0:
+                    continue
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=self.stream):
+                    for i in range(n):
+                        body(i)
+                g.replay()                                   # untimed
+                graphs.append((g, count))
             torch.cuda.synchronize()
+            times = []
             for _ in range(repeats):
                 ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ev0.record(self.stream)
-                for _ in range(reps):
-                    graph.replay()
+                for g, count in graphs:
+                    for _ in range(count):
+                        g.replay()
                 ev1.record(self.stream)
                 torch.cuda.synchronize()
                 times.append(ev0.elapsed_time(ev1))
@@ -313,60 +370,304 @@ class Rig:
                     self.launch(op, i)
         torch.cuda.synchronize()
 
-    def copy_reference(self, reps: int) -> dict:
-        """A read+write stream of one batch-sized tensor per launch by the
-        runtime's elementwise kernel (out = -x; the DMA copy behind
-        ``Tensor.copy_`` is slower)."""
-        n = self.nsets
-        srcs = [s.get("x", s.get("fx", s.get("sx", s.get("mx", s.get("ox", s.get("bx")))))) for s in self.sets]
-        dsts = [torch.empty_like(t) for t in srcs]
-        ms = self.timed_graph(lambda i: torch.neg(srcs[i % n], out=dsts[i % n]), n, reps)
-        del dsts
-        us = ms * 1e3 / (n * reps)
-        gbps = 2 * self.tensor_bytes / (us * 1e-6) / 1e9
-        return {"bytes": 2 * self.tensor_bytes, "us_per_copy": round(us, 3), "gbps": round(gbps, 1),
-                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+# ---------------------------------------------------------------------------
+# HIP runtime calls the bench makes itself: events and versions
+# ---------------------------------------------------------------------------
+def _hip_runtime_path() -> str:
+    """The HIP runtime library this process already uses (torch's), so that the
+    events the bench creates are the ones the library records."""
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and os.path.basename(parts[-1]).startswith("libamdhip64.so"):
+                    return parts[-1]
+    except OSError:
+        pass
+    return "libamdhip64.so.7"
 
 
-def measure(wl, inp, ks, args) -> dict:
-    """Whole-step and per-op throughput of one workload."""
+class Hip:
+    def __init__(self):
+        torch.cuda.init()
+        self.h = ctypes.CDLL(_hip_runtime_path())
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        self.h.hipEventDestroy.argtypes = [vp]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.h.hipRuntimeGetVersion.argtypes = [ctypes.POINTER(ci)]
+        self.h.hipDriverGetVersion.argtypes = [ctypes.POINTER(ci)]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(e))
+        if rc != 0 or not e.value:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def destroy(self, e: int) -> None:
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+    def elapsed_us(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value * 1e3
+
+    def versions(self) -> dict:
+        rt, drv = ctypes.c_int(0), ctypes.c_int(0)
+        self.h.hipRuntimeGetVersion(ctypes.byref(rt))
+        self.h.hipDriverGetVersion(ctypes.byref(drv))
+        return {"hip_runtime": rt.value, "hip_driver": drv.value, "hip_runtime_library": _hip_runtime_path()}
+
+
+def distribution(vals: list[float]) -> dict:
+    """n, mean, min, p50, p95, p99 and max of a sample (nearest-rank percentiles), rounded to ns."""
+    v = sorted(vals)
+    n = len(v)
+
+    def q(p: float) -> float:
+        return v[min(n - 1, max(0, int(np.ceil(p * n)) - 1))]
+
+    return {"n": n, "mean": round(float(np.mean(v)), 3), "min": round(v[0], 3), "p50": round(q(0.50), 3),
+            "p95": round(q(0.95), 3), "p99": round(q(0.99), 3), "max": round(v[-1], 3)}
+
+
+def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_call=None) -> list[float]:
+    """n calls of call(i) (a raw C entry point on `stream`, returning its status),
+    each timed by the runtime's kernel-dispatch events (from the start of the
+    call's first kernel to the end of its last): microseconds.
+    `timed_call(i, start, stop)` replaces the request through
+    ks_time_next_call for callers that take the events themselves."""
+    import rmsnorm_row_normalisation_amd as ks
+
+    lib = ks.lib()
+    evs = [(hip.event(), hip.event()) for _ in range(n)]
+    try:
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            if timed_call is not None:
+                timed_call(i, a, b)
+            else:
+                lib.ks_time_next_call(a, b)
+                rc = call(i)
+                if rc != 0:
+                    raise RuntimeError(f"timed call failed: {lib.ks_status_string(rc).decode()}")
+        torch.cuda.synchronize()
+        return [hip.elapsed_us(a, b) for a, b in evs]
+    finally:
+        for a, b in evs:
+            hip.destroy(a)
+            hip.destroy(b)
+
+
+KERNEL_TIMED_MAX = 2048
+
+
+def measure(wl, inp, ks, args, hip: Hip) -> dict:
+    """Whole-step throughput and, per op, the launch period and the kernel durations."""
     esize = torch.empty(0, dtype=wl.torch_dtype).element_size()
     op_bytes = {op: algorithmic_bytes(op, wl.rows, wl.hidden, esize) for op in wl.ops}
     rig = Rig(wl, inp, ks, args.rotate_mib)
     log(f"{wl.name}: {rig.nsets} rotating copies, {rig.rotation_mib:.0f} MiB")
-    reps = max(1, -(-args.steps // rig.nsets))
-    steps = reps * rig.nsets
+    steps = args.steps
     rig.warmup(args.warmup)
-    total_ms = rig.timed_graph(lambda i: [rig.launch(op, i) for op in wl.ops], rig.nsets, reps)
+    total_ms = rig.timed_graph(lambda i: [rig.launch(op, i) for op in wl.ops], rig.nsets, steps)
     per_op = {}
     for op in wl.ops:
-        # per-op figures: median of three timed regions (run-to-run spread is a few %)
-        ms = rig.timed_graph(lambda i, op=op: rig.launch(op, i), rig.nsets, reps, repeats=3)
+        # launch period: median of three timed regions (run-to-run spread is a few %)
+        ms = rig.timed_graph(lambda i, op=op: rig.launch(op, i), rig.nsets, steps, repeats=3)
         us = ms * 1e3 / steps
-        gbps = op_bytes[op] / (us * 1e-6) / 1e9
-        per_op[op] = {"us_per_call": round(us, 3), "bytes": op_bytes[op], "gbps": round(gbps, 1),
+        kus = distribution(kernel_durations(hip, rig.raw_call(op), min(steps, KERNEL_TIMED_MAX), rig.stream))
+        gbps = op_bytes[op] / (kus["mean"] * 1e-6) / 1e9
+        per_op[op] = {"us_per_call": round(us, 3), "kernel_us": kus, "bytes": op_bytes[op], "gbps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                      "gbps_per_call": round(op_bytes[op] / (us * 1e-6) / 1e9, 1),
                       "plan": ks.get_plan(op, wl.torch_dtype, wl.hidden // 2 if op == "silu_and_mul" else wl.hidden,
                                           wl.rows, workspace=op == "softmax").as_dict()}
-    copy = rig.copy_reference(reps)
     ms_per_step = total_ms / steps
-    result = {"steps": steps, "reps": reps, "nsets": rig.nsets, "rotation_mib": rig.rotation_mib,
+    result = {"steps": steps, "nsets": rig.nsets, "rotation_mib": rig.rotation_mib,
               "ms_per_step": ms_per_step, "step_bytes": sum(op_bytes.values()),
               "value": sum(op_bytes.values()) / (ms_per_step * 1e-3) / 1e9, "per_op": per_op,
-              "copy_reference": copy}
+              "tensor_bytes": rig.tensor_bytes}
     del rig
     torch.cuda.empty_cache()
     return result
 
 
 # ---------------------------------------------------------------------------
+# reference streams (libks_streamref.so)
+# ---------------------------------------------------------------------------
+class StreamRef:
+    """The benchmark's reference streams: an empty kernel, reads, writes and
+    copies of 16-byte pieces (rmsnorm_row_normalisation_amd/streamref)."""
+
+    def __init__(self):
+        if not os.path.exists(STREAMREF_LIB):
+            raise RuntimeError(f"{STREAMREF_LIB} is not built; run __graft_entry__.build() first")
+        h = ctypes.CDLL(STREAMREF_LIB)
+        vp, u64, ci, cu = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint
+        h.ksref_read.argtypes = [vp, u64, vp, vp, vp, vp]
+        h.ksref_write.argtypes = [vp, u64, ci, vp, vp, vp]
+        h.ksref_copy.argtypes = [vp, vp, u64, ci, vp, vp, vp]
+        h.ksref_copy_rows.argtypes = [vp, vp, u64, ci, vp, vp, vp]
+        h.ksref_inplace4.argtypes = [vp, vp, u64, ci, vp, vp, vp]
+        h.ksref_empty.argtypes = [cu, vp, vp, vp]
+        self.h = h
+
+    @staticmethod
+    def check(rc: int, what: str) -> None:
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+
+
+# name -> (bytes moved per byte of buffer, launcher(ref, src, dst, nbytes, sink, stream, e0, e1))
+STREAMS = {
+    "read": (1, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_read(a, n, k, s, e0, e1)),
+    "write": (1, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_write(b, n, 0, s, e0, e1)),
+    "write nt": (1, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_write(b, n, 1, s, e0, e1)),
+    "write sc0 sc1": (1, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_write(b, n, 2, s, e0, e1)),
+    "copy": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy(a, b, n, 0, s, e0, e1)),
+    "copy nt": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy(a, b, n, 1, s, e0, e1)),
+    "copy sc0 sc1": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy(a, b, n, 2, s, e0, e1)),
+    "rows 1": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy_rows(a, b, n, 1, s, e0, e1)),
+    "rows 2": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy_rows(a, b, n, 2, s, e0, e1)),
+    "rows 4": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy_rows(a, b, n, 4, s, e0, e1)),
+    "rows 8": (2, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_copy_rows(a, b, n, 8, s, e0, e1)),
+    "in place x+r 1": (4, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_inplace4(a, b, n, 1, s, e0, e1)),
+    "in place x+r 2": (4, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_inplace4(a, b, n, 2, s, e0, e1)),
+    "in place x+r 8": (4, lambda r, a, b, n, k, s, e0, e1: r.h.ksref_inplace4(a, b, n, 8, s, e0, e1)),
+}
+STREAM_DESCRIPTIONS = {
+    "read": "one 16-byte load per lane", "write": "one 16-byte store per lane, default cache bits",
+    "write nt": "the same, non-temporal", "write sc0 sc1": "the same, system scope (sc0 sc1)",
+    "copy": "one load and one store per lane", "copy nt": "the same, non-temporal stores",
+    "copy sc0 sc1": "the same, system-scope stores",
+    "rows 1": "the row kernels' layout: a wave owns N KiB (N pieces per lane at a 1 KiB stride), loads, "
+              "a wave-wide sum and double rsqrt, then stores",
+    "rows 2": "", "rows 4": "", "rows 8": "",
+    "in place x+r 1": "the fused form's four streams: read x and r, write both back in place (row layout, "
+                      "N pieces per lane)",
+    "in place x+r 2": "", "in place x+r 8": "",
+}
+
+
+def stream_times(hip: Hip, ref: StreamRef, name: str, nbytes: int, launches: int, graph_calls: int) -> dict:
+    """One reference stream over rotating buffers of nbytes (at least 1 GiB of
+    buffers in the rotation, so every call reads data last touched more than a
+    cache's worth of traffic ago): kernel durations from the kernel-dispatch
+    events, and the launch period of graph-captured back-to-back calls."""
+    mult, fn = STREAMS[name]
+    nsets = max(1, -(-GIB // nbytes)) if nbytes < GIB else 1
+    bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255),
+             torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(nsets)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def call(i: int, e0=None, e1=None) -> None:
+        a, b = bufs[i % nsets]
+        StreamRef.check(fn(ref, a.data_ptr(), b.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream, e0, e1), name)
+
+    for i in range(2 * nsets):
+        call(i)
+    torch.cuda.synchronize()
+    kus = distribution(kernel_durations(hip, None, launches, stream, timed_call=lambda i, a, b: call(i, a, b)))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(graph_calls):
+                call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    period = e0.elapsed_time(e1) * 1e3 / graph_calls
+    moved = mult * nbytes
+    del bufs, g
+    torch.cuda.empty_cache()
+    return {"stream": name, "buffer_bytes": nbytes, "bytes_moved": moved, "kernel_us": kus,
+            "gbps": round(moved / (kus["mean"] * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(moved / (kus["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "us_per_call": round(period, 3), "gbps_per_call": round(moved / (period * 1e-6) / 1e9, 1)}
+
+
+def empty_kernel_floor(hip: Hip, ref: StreamRef, launches: int = 512) -> dict:
+    """A kernel that does nothing (REF_FLOOR_GROUPS workgroups of 256 threads):
+    its launch period back to back in a graph (the per-launch floor of a
+    captured sequence), and its kernel-dispatch event interval (which, for a
+    kernel this short, is mostly the events' own overhead)."""
+    stream = torch.cuda.Stream()
+
+    def call(a=None, b=None) -> None:
+        StreamRef.check(ref.h.ksref_empty(REF_FLOOR_GROUPS, stream.cuda_stream, a, b), "ksref_empty")
+
+    kus = distribution(kernel_durations(hip, None, launches, stream, timed_call=lambda i, a, b: call(a, b)))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(launches):
+                call()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    return {"groups": REF_FLOOR_GROUPS, "us_per_call": round(e0.elapsed_time(e1) * 1e3 / launches, 3),
+            "event_interval_us": kus}
+
+
+def stream_reference(hip: Hip, tensor_bytes: int) -> dict:
+    """The bench line's context: the per-launch floor, and a plain copy (one
+    load and store per lane, system-scope stores: the fastest copy measured)
+    of one batch-sized tensor and of 1 GiB."""
+    ref = StreamRef()
+    size = max(4096, tensor_bytes // 4096 * 4096)
+    return {"empty_kernel": empty_kernel_floor(hip, ref),
+            "copy_tensor": stream_times(hip, ref, "copy sc0 sc1", size, 256 if size <= 64 << 20 else 16, 16),
+            "copy_1gib": stream_times(hip, ref, "copy sc0 sc1", GIB, 16, 4)}
+
+
+def stream_reference_table(hip: Hip) -> None:
+    """Every reference stream at 16 MiB and at 1 GiB, one markdown table (and
+    the JSON cases with --json-out)."""
+    ref = StreamRef()
+    floor = empty_kernel_floor(hip, ref)
+    lines = [f"Empty kernel ({REF_FLOOR_GROUPS} workgroups of 256 threads): {floor['us_per_call']:.2f} us per call "
+             f"back to back in a graph; its kernel-dispatch event interval p50 "
+             f"{floor['event_interval_us']['p50']:.2f} us (mostly the events' own overhead at this length).", "",
+             "| Stream | Buffer | Bytes moved | Kernel p50 us | Kernel mean us | GB/s (mean) | % of 8 TB/s "
+             "| Graph us/call | What it is |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    cases = []
+    for nbytes, launches, graph_calls in ((16 << 20, 256, 64), (GIB, 16, 4)):
+        for name in STREAMS:
+            r = stream_times(hip, ref, name, nbytes, launches, graph_calls)
+            cases.append(r)
+            lines.append(f"| {name} | {nbytes >> 20} MiB | {r['bytes_moved'] >> 20} MiB | {r['kernel_us']['p50']:.2f} "
+                         f"| {r['kernel_us']['mean']:.2f} | {r['gbps']:.0f} | {100 * r['frac_of_peak']:.1f} "
+                         f"| {r['us_per_call']:.2f} | {STREAM_DESCRIPTIONS[name]} |")
+            log(lines[-1])
+    print("\n".join(lines), flush=True)
+    return {"empty_kernel": floor, "cases": cases}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline
 # ---------------------------------------------------------------------------
 def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
-    """The oracle as it stands, single-threaded on a host core, on whole steps of the workload."""
-    t0 = time.perf_counter()
-    steps = 0
+    """The oracle as it stands, single-threaded on a host core, on whole steps of
+    the workload, repeated for about budget_s seconds: the median step time."""
+    times = []
+    t_start = time.perf_counter()
     while True:
+        t0 = time.perf_counter()
         if "rms_norm" in wl.ops:
             oracle_mod.rms_norm(inp["x"], inp["weight"], wl.eps)
         if "fused_add_rms_norm" in wl.ops:
@@ -379,15 +680,16 @@ def cpu_baseline(wl, inp, oracle_mod, budget_s: float, step_bytes: int) -> dict:
             oracle_mod.rms_norm_residual(inp["x"], inp["residual"], inp["weight"], wl.eps)
         if "rms_norm_backward" in wl.ops:
             oracle_mod.rms_norm_backward(inp["residual"], inp["x"], inp["weight"], wl.eps)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s and len(times) >= 3:
             break
-    return {"value": round(steps * step_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} full steps ({' + '.join(wl.ops)} on the whole [{wl.rows},{wl.hidden}] batch) "
-                      f"in {el:.1f} s, single thread",
-            "us_per_step": round(el / steps * 1e6, 1), "host_cpus": os.cpu_count(),
-            "host_cpu": _cpu_model()}
+    med = float(np.median(times))
+    return {"value": round(step_bytes / med / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} full steps ({' + '.join(wl.ops)} on the whole [{wl.rows},{wl.hidden}] batch), "
+                      f"timed one by one, single thread; value from the median step",
+            "us_per_step": {"median": round(med * 1e6, 1), "min": round(min(times) * 1e6, 1),
+                            "max": round(max(times) * 1e6, 1)},
+            "host_cpus": os.cpu_count(), "host_cpu": _cpu_model()}
 
 
 def memory_interface() -> dict | None:
@@ -397,7 +699,7 @@ def memory_interface() -> dict | None:
     HBM3E interface moves several transfers per reported clock (8 TB/s over
     2048 GB/s is about 4)."""
     try:
-        hip = ctypes.CDLL("libamdhip64.so")
+        hip = ctypes.CDLL(_hip_runtime_path())
     except OSError:
         return None
     bus, clk = ctypes.c_int(0), ctypes.c_int(0)
@@ -408,6 +710,36 @@ def memory_interface() -> dict | None:
     gbps = clk.value * 1e3 * bus.value / 8 / 1e9
     return {"bus_width_bits": bus.value, "memory_clock_khz": clk.value, "clock_x_bus_gbps": round(gbps, 1),
             "spec_peak_gbps": HBM_PEAK_GBPS}
+
+
+def source_commit() -> str | None:
+    """The checkout's commit (None where there is no git metadata, as on a
+    machine that received a copy of the tree without it)."""
+    import subprocess
+
+    try:
+        res = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return res.stdout.strip() if res.returncode == 0 else None
+
+
+def environment(hip: Hip, ks) -> dict:
+    """Software versions and the source the library was built from."""
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"python": platform.python_version(), "torch": torch.__version__, "torch_hip": torch.version.hip,
+            "rocm": rocm, **hip.versions(), "library": ks.ks_version(), "commit": source_commit(),
+            "host_cpu": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def seeds(wl) -> dict:
+    return {k: v for k, v in (("x", wl.seed_x), ("residual", wl.seed_r), ("weight", wl.seed_w),
+                              ("outliers", wl.seed_outlier)) if v is not None}
 
 
 def _cpu_model() -> str:
@@ -434,35 +766,6 @@ def load_traffic(workload: str) -> dict | None:
     if data.get("kernel_source_hash") != kernel_source_hash():
         return None
     return data.get("workloads", {}).get(workload)
-
-
-def copy_ceiling(mib: int = 1024, reps: int = 8) -> dict:
-    """A read+write stream of MIB MiB each way by the runtime's elementwise
-    kernel (out = -x over bf16, a shader kernel: the DMA copy behind
-    ``Tensor.copy_`` is slower), on the same clock as the kernels, at a size
-    where launch costs vanish: what a plain read+write stream reaches on this
-    device.  Context for the fractions of the 8 TB/s spec, never their
-    denominator."""
-    n = mib << 20
-    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
-    dst = torch.empty_like(src)
-    torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            torch.neg(src, out=dst)
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / reps)
-    ms = float(np.median(times))
-    del src, dst
-    torch.cuda.empty_cache()
-    gbps = 2 * n / (ms * 1e-3) / 1e9
-    return {"op": "torch.neg, bf16", "bytes": 2 * n, "ms_per_pass": round(ms, 4), "gbps": round(gbps, 1),
-            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def copy_calibration(mib: int) -> None:
@@ -570,6 +873,103 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
 
 
 # ---------------------------------------------------------------------------
+# kernel-trace summaries (rocprofv3 --kernel-trace output of a bench run)
+# ---------------------------------------------------------------------------
+def trace_dispatches(directory: str) -> dict[str, dict]:
+    """Per kernel name (and grid, where one kernel ran at several sizes): the
+    dispatch durations (us) and the first dispatch's resources."""
+    import csv
+    import glob
+
+    out: dict[str, dict] = {}
+    paths = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *kernel_trace.csv under {directory}")
+    for path in paths:
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+            grids: dict[str, set] = {}
+            for r in rows:
+                grids.setdefault(r["Kernel_Name"], set()).add(r.get("Grid_Size_X", ""))
+            for r in rows:
+                name = r["Kernel_Name"]
+                if len(grids[name]) > 1:
+                    name = f"{name} [grid {r.get('Grid_Size_X', '')}]"
+                k = out.setdefault(name, {
+                    "us": [], "resources": {key: r.get(col, "") for key, col in (
+                        ("vgpr", "VGPR_Count"), ("agpr", "Accum_VGPR_Count"), ("sgpr", "SGPR_Count"),
+                        ("lds", "LDS_Block_Size"), ("scratch", "Scratch_Size"), ("workgroup", "Workgroup_Size_X"),
+                        ("grid", "Grid_Size_X"))}})
+                k["us"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    return out
+
+
+def trace_summary(wl, directory: str, bench_json: str | None, command: str | None) -> str:
+    disp = trace_dispatches(directory)
+    esize = wl.torch_dtype.itemsize
+    L = [f"# Kernel trace: {' + '.join(wl.ops)}, {wl.dtype} [{wl.rows},{wl.hidden}]", "",
+         f"Workload `{wl.name}`: {wl.describe()}.", ""]
+    if command:
+        L += ["Command (repository root on the GPU box; the summary is rendered from its output by "
+              "`python bench.py --trace-summary`):", "", "```", "cd /tmp && export TMPDIR=/tmp", command, "```", ""]
+    L += ["Per-dispatch kernel durations (us, end minus start timestamp of each dispatch in the trace) and each "
+          "kernel's resources:", "",
+          "| Kernel | Dispatches | min | p50 | mean | p95 | p99 | max | VGPR | AGPR | SGPR | LDS B | scratch B "
+          "| workgroup | grid threads |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    per_op: dict[str, dict] = {}
+    for name, k in sorted(disp.items(), key=lambda kv: (kernel_op(kv[0]) is None, kv[0])):
+        d = distribution(k["us"])
+        short = name if len(name) < 130 else name[:100] + "..." + name[name.rfind(" ["):] if " [grid" in name else \
+            name if len(name) < 110 else name[:100] + "..."
+        res = k["resources"]
+        L.append(f"| `{short}` | {d['n']} | {d['min']:.2f} | {d['p50']:.2f} | {d['mean']:.2f} | {d['p95']:.2f} | "
+                 f"{d['p99']:.2f} | {d['max']:.2f} | {res['vgpr']} | {res['agpr']} | {res['sgpr']} | {res['lds']} | "
+                 f"{res['scratch']} | {res['workgroup']} | {res['grid']} |")
+        op = kernel_op(name)
+        if op is not None and op in wl.ops:
+            per_op.setdefault(op, {"mean": 0.0, "p50": 0.0, "kernels": 0})
+            per_op[op]["mean"] += d["mean"]   # an op of several kernels takes their sum
+            per_op[op]["p50"] += d["p50"]
+            per_op[op]["kernels"] += 1
+    L += ["", "The library's kernels come first; the rest are the bench's own setup and reference kernels "
+          "(input copies, the empty and copy reference streams)."]
+    line = None
+    if bench_json:
+        with open(bench_json) as f:
+            line = json.loads(f.read().strip().splitlines()[-1])
+    L += ["", "Per op: the trace's durations against the uninstrumented bench run of the same command "
+          "(kernel-dispatch events per call, and the graph launch period):", "",
+          "| Op | algorithmic bytes | trace mean us | trace p50 us | GB/s (trace mean) | bench kernel mean us "
+          "| bench kernel p50 us | bench graph us/call | GB/s (bench kernel mean) | bench vs trace mean |",
+          "|---|---|---|---|---|---|---|---|---|---|"]
+    for op in wl.ops:
+        alg = algorithmic_bytes(op, wl.rows, wl.hidden, esize)
+        t = per_op.get(op)
+        if t is None:
+            continue
+        row = f"| {op} | {alg} | {t['mean']:.3f} | {t['p50']:.3f} | {alg / t['mean'] / 1e3:.0f} |"
+        if line is not None and op in line.get("per_op", {}):
+            b = line["per_op"][op]
+            km = b["kernel_us"]["mean"]
+            row += (f" {km:.3f} | {b['kernel_us']['p50']:.3f} | {b['us_per_call']:.3f} | {alg / km / 1e3:.0f} | "
+                    f"{100 * (km - t['mean']) / t['mean']:+.1f}% |")
+        else:
+            row += " | | | | |"
+        L.append(row)
+    if line is not None:
+        rf = line["roofline"]
+        L += ["", f"The bench line's roofline: dominant kernel {rf['kernel']}, {rf['achieved']} GB/s, frac "
+              f"{rf['frac']} (algorithmic bytes over the mean of the per-call kernel-dispatch event durations).  "
+              f"The same bytes over the trace's mean duration give frac "
+              f"{algorithmic_bytes(rf['kernel'], wl.rows, wl.hidden, esize) / per_op[rf['kernel']]['mean'] / 1e3 / HBM_PEAK_GBPS:.4f}."
+              "  The tracer adds a little to each dispatch, so its durations run slightly longer than the "
+              "uninstrumented ones."]
+        L += ["", f"Library: {line.get('env', {}).get('library', '?')}; kernel sources hash "
+              f"`{line.get('kernel_source_hash', '?')}`."]
+    return "\n".join(L) + "\n"
+
+
+# ---------------------------------------------------------------------------
 # regression gate: cases matched by (op, dtype, rows, hidden)
 # ---------------------------------------------------------------------------
 def case_key(case: dict) -> tuple:
@@ -617,17 +1017,34 @@ def finish_cases(args, cases: list[dict]) -> None:
 # ---------------------------------------------------------------------------
 # modes
 # ---------------------------------------------------------------------------
-def sweep_workloads(args, ks, oracle_mod) -> None:
-    """Every workload of the pages' benchmark set: parity, then per-op timing."""
+def sweep_set(dtypes: list[str]) -> list:
+    """Every workload, plus the RMSNorm workloads C1, C2 and C3b in the other
+    requested dtypes (same shapes, distributions and seeds) where no workload
+    already covers that (op, dtype, shape)."""
+    out = list(workloads.WORKLOADS.values())
+    keys = {(wl.ops, wl.dtype, wl.rows, wl.hidden) for wl in out}
+    for name in ("C1", "C2", "C3b"):
+        for tag in dtypes:
+            v = workloads.with_dtype(workloads.WORKLOADS[name], tag)
+            key = (v.ops, v.dtype, v.rows, v.hidden)
+            if key not in keys:
+                keys.add(key)
+                out.append(v)
+    return out
+
+
+def sweep_workloads(args, ks, oracle_mod, hip: Hip) -> None:
+    """Every workload of the pages' benchmark set (and the dtype variants):
+    parity, then per-op timing."""
     cases = []
-    lines = ["| Workload | Op | dtype | rows x hidden | us/call | GB/s | % of 8 TB/s | copy ref GB/s | rotation MiB "
-             "| plan (team x pieces, hints) | max ulp | exact |",
+    lines = ["| Workload | Op | dtype | rows x hidden | us/call (graph) | kernel p50 us | GB/s (kernel mean) "
+             "| % of 8 TB/s | rotation MiB | plan (team x pieces, hints) | max ulp | exact |",
              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
-    for name, wl in workloads.WORKLOADS.items():
-        log("generating", name, wl.describe())
+    for wl in sweep_set([t for t in args.sweep_dtypes.split(",") if t]):
+        log("generating", wl.name, wl.describe())
         inp = workloads.make_inputs(wl)
         parity = parity_gate(wl, inp, ks, oracle_mod)
-        res = measure(wl, inp, ks, args)
+        res = measure(wl, inp, ks, args, hip)
         cases.extend(cases_from(wl, res["per_op"]))
         for op in wl.ops:
             p = res["per_op"][op]
@@ -635,8 +1052,8 @@ def sweep_workloads(args, ks, oracle_mod) -> None:
             path = {0: "", 1: "generic ", 2: "split "}.get(pl["path"], "?")
             plan = (f"{path}{pl['threads_per_row']}x{pl['vectors_per_thread']} "
                     f"nt{pl['load_nt']}{pl['store_nt']} lds{pl['weight_lds']}")
-            lines.append(f"| {name} | {op} | {DTYPE_TAG[wl.dtype]} | {wl.rows}x{wl.hidden} | {p['us_per_call']:.3f} | "
-                         f"{p['gbps']:.0f} | {100 * p['frac_of_peak']:.1f} | {res['copy_reference']['gbps']:.0f} | "
+            lines.append(f"| {wl.name} | {op} | {DTYPE_TAG[wl.dtype]} | {wl.rows}x{wl.hidden} | {p['us_per_call']:.3f} | "
+                         f"{p['kernel_us']['p50']:.2f} | {p['gbps']:.0f} | {100 * p['frac_of_peak']:.1f} | "
                          f"{res['rotation_mib']:.0f} | {plan} | {parity[op]['max_ulp']} | "
                          f"{parity[op]['exact_match']:.6f} |")
             log(lines[-1])
@@ -651,6 +1068,17 @@ def sweep_workloads(args, ks, oracle_mod) -> None:
 
 def main() -> None:
     args = parse()
+    if args.trace_summary:
+        wl = workloads.WORKLOADS[args.workload]
+        if args.dtype:
+            wl = workloads.with_dtype(wl, args.dtype)
+        text = trace_summary(wl, args.trace_summary, args.trace_bench, args.trace_command)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        else:
+            print(text, end="")
+        return
     if args.traffic_summary:
         traffic_summary(args.workload, *args.traffic_summary)
         return
@@ -669,11 +1097,22 @@ def main() -> None:
 
     dev = torch.cuda.get_device_properties(0)
     log("device", dev.name, getattr(dev, "gcnArchName", "?"), "CUs", dev.multi_processor_count)
+    if args.steps < 1:
+        fail("--steps must be at least 1")
+    hip = Hip()
+    if args.stream_reference:
+        table = stream_reference_table(hip)
+        if args.json_out:
+            with open(args.json_out, "w") as f:
+                json.dump(table, f, indent=1)
+        return
     if args.sweep_workloads:
-        sweep_workloads(args, ks, oracle)
+        sweep_workloads(args, ks, oracle, hip)
         return
 
     wl = workloads.WORKLOADS[args.workload]
+    if args.dtype:
+        wl = workloads.with_dtype(wl, args.dtype)
     log("generating inputs", wl.describe())
     inp = workloads.make_inputs(wl)
     try:
@@ -681,33 +1120,40 @@ def main() -> None:
     except AssertionError as exc:
         fail(f"parity gate failed, nothing timed: {exc}")
     log("parity", parity)
-    res = measure(wl, inp, ks, args)
+    res = measure(wl, inp, ks, args, hip)
     per_op = res["per_op"]
     log("per op", per_op)
 
-    dominant = max(wl.ops, key=lambda op: per_op[op]["us_per_call"])
-    traffic = load_traffic(args.workload)
+    dominant = max(wl.ops, key=lambda op: per_op[op]["kernel_us"]["mean"])
+    traffic = load_traffic(wl.name)
+    kus = per_op[dominant]["kernel_us"]
     roofline = {"bound": "hbm", "kernel": dominant,
                 "achieved": per_op[dominant]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(per_op[dominant]["gbps"] / HBM_PEAK_GBPS, 4),
-                "traffic": (traffic or {}).get(dominant)}
-    timing_mode = (f"HIP graph replay, {res['reps']} replays of {res['nsets']} steps; per op: graphs of "
-                   "back-to-back launches of that op, median of three timed regions")
+                "traffic": (traffic or {}).get(dominant),
+                "bytes": per_op[dominant]["bytes"], "kernel_us_mean": kus["mean"], "kernel_us_p50": kus["p50"],
+                "method": f"algorithmic bytes / mean kernel duration over {kus['n']} calls, each timed by the "
+                          "runtime's kernel-dispatch events (ks_time_next_call) on the launch stream"}
+    reps, tail = divmod(res["steps"], res["nsets"])
+    timing_mode = (f"exactly {res['steps']} steps: HIP graph of {res['nsets']} steps replayed {reps} times"
+                   + (f" plus a graph of {tail}" if tail else "")
+                   + "; per op: the same with that op's launches alone (median of three timed regions) and "
+                     "per-call kernel-dispatch events")
     line = {
         "metric": METRIC, "value": round(res["value"], 1), "unit": "GB/s", "n_gpus": 1, "steps": res["steps"],
         "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_TAG[wl.dtype], "data": "synthetic",
-        "config": {"workload": wl.describe(), "ops": list(wl.ops), "rows": wl.rows, "hidden": wl.hidden,
-                   "eps": wl.eps, "timing": timing_mode,
+        "config": {"workload": wl.describe(), "name": wl.name, "ops": list(wl.ops), "rows": wl.rows,
+                   "hidden": wl.hidden, "eps": wl.eps, "seeds": seeds(wl), "timing": timing_mode,
                    "cache": f"cold: {res['nsets']} rotating copies ({res['rotation_mib']:.0f} MiB)"},
         "frac_of_peak": round(res["value"] / HBM_PEAK_GBPS, 4),
         "per_op": per_op,
         "roofline": roofline,
-        "copy_reference": res["copy_reference"],
-        "copy_ceiling": copy_ceiling(),
+        "stream_reference": stream_reference(hip, res["tensor_bytes"]),
         "parity": parity,
         "device": {"name": dev.name, "arch": getattr(dev, "gcnArchName", "?"), "cus": dev.multi_processor_count,
                    "memory": memory_interface()},
+        "env": environment(hip, ks),
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -36,7 +36,7 @@
  *            summation order depends only on hidden, dtype and alignment, so
  *            a row's result does not depend on how many rows are in the
  *            batch (the split plans of ks_softmax_ws aside).
- * Errors     Checked in this order, before any HIP call:
+ * Errors     Checked in this order, before any kernel launch:
  *              KS_ERROR_UNSUPPORTED_DTYPE  dtype is not one of ks_dtype_t;
  *              KS_ERROR_INVALID_VALUE      rows < 0 or rows > 2^31 - 1;
  *                                          hidden <= 0 or hidden > 2^24;
@@ -45,8 +45,12 @@
  *                                          bad plan; a missing or too small
  *                                          workspace;
  *              KS_ERROR_OVERLAP            forbidden aliasing (per call);
- *            then rows == 0 returns KS_SUCCESS without touching HIP (the
- *            backward with a weight gradient still writes dw = 0).
+ *            rows == 0 returns KS_SUCCESS without touching HIP (the backward
+ *            with a weight gradient still writes dw = 0).  The only HIP calls
+ *            before the checks end are those of the device's compute-unit
+ *            query (hipGetDevice, and hipDeviceGetAttribute once per device),
+ *            which the launch policy reads; with no device visible the
+ *            policy assumes a whole MI355X (256 compute units).
  *            KS_ERROR_HIP reports a failed launch (e.g. no device); the HIP
  *            error code is kept per thread in ks_last_hip_error().
  */
@@ -212,19 +216,39 @@ ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, con
 
 /*
  * The launch plan the calls of this header use for this op, dtype, batch and
- * row size.  All vector-path plans sum a row in one canonical order, so the plan
- * may change with `rows` while every row's result stays the same; the path
- * (vector or generic) depends only on dtype, hidden and alignment.
+ * row size on the current device.  All vector-path plans sum a row in one
+ * canonical order, so the plan may change with `rows` (and with the device's
+ * compute units) while every row's result stays the same; the path (vector
+ * or generic) depends only on dtype, hidden and alignment.
  * `flags`: KS_PLAN_ALIGNED when all buffers are 16-byte aligned;
  * KS_PLAN_WORKSPACE for the plan of a call that passes a workspace
  * (ks_softmax_ws, whose plan may be a split plan; the other ops ignore it).
- * No HIP call.  Returns KS_ERROR_INVALID_VALUE for a NULL plan, a bad row
- * count or hidden size, an unknown op or unknown flag bits.
+ * The policy's batch-size thresholds scale with the device's compute units:
+ * ks_get_plan reads the current device's count (cached per device; 256, a
+ * whole MI355X, when no device is visible); ks_get_plan_cus takes it as an
+ * argument (1..4096) and makes no HIP call.  Returns KS_ERROR_INVALID_VALUE
+ * for a NULL plan, a bad row count, hidden size or compute-unit count, an
+ * unknown op or unknown flag bits.
  */
 #define KS_PLAN_ALIGNED 1
 #define KS_PLAN_WORKSPACE 2
 ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags,
                         ks_plan_t *plan);
+ks_status_t ks_get_plan_cus(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags,
+                            int compute_units, ks_plan_t *plan);
+
+/*
+ * Kernel timing without a profiler, per call.  The next call of this header
+ * made on the calling thread records `start` when its first kernel begins and
+ * `stop` when its last kernel ends (the HIP runtime's kernel-dispatch
+ * events, hipExtLaunchKernel); the request then clears, whether or not that
+ * call launched anything.  Either event may be NULL.  The events belong to
+ * the caller (hipEventCreate, default flags), who reads the interval with
+ * hipEventElapsedTime once the stream has reached them.  Kernel-dispatch
+ * events are not graph nodes: make no timed call under stream capture.
+ * No HIP call here; always KS_SUCCESS.
+ */
+ks_status_t ks_time_next_call(hipEvent_t start, hipEvent_t stop);
 
 /*
  * The two operations with an explicit launch plan (for tuning and for

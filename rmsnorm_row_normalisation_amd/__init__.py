@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     ks_fused_add_rms_norm,
     ks_fused_add_rms_norm_ex,
     ks_get_plan,
+    ks_time_next_call,
     ks_rms_norm,
     ks_rms_norm_ex,
     ks_silu_and_mul,

@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         h.ks_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_fused_add_rms_norm_ex.argtypes = [vp, vp, vp, i64, i64, f32, i32, ctypes.POINTER(Plan), vp]
         h.ks_get_plan.argtypes = [i32, i32, i64, i64, i32, ctypes.POINTER(Plan)]
+        h.ks_get_plan_cus.argtypes = [i32, i32, i64, i64, i32, i32, ctypes.POINTER(Plan)]
+        h.ks_time_next_call.argtypes = [vp, vp]
         h.ks_silu_and_mul.argtypes = [vp, vp, i64, i64, i32, vp]
         h.ks_silu_and_mul_ex.argtypes = [vp, vp, i64, i64, i32, ctypes.POINTER(Plan), vp]
         h.ks_softmax.argtypes = [vp, vp, i64, i64, i32, vp]
@@ -114,7 +116,8 @@ def lib() -> ctypes.CDLL:
                      "ks_get_plan", "ks_last_hip_error", "ks_silu_and_mul", "ks_silu_and_mul_ex", "ks_softmax",
                      "ks_softmax_ex", "ks_rms_norm_residual", "ks_rms_norm_residual_ex",
                      "ks_rms_norm_backward_workspace_size", "ks_rms_norm_backward", "ks_rms_norm_backward_ex",
-                     "ks_softmax_workspace_size", "ks_softmax_ws", "ks_softmax_ws_ex", "ks_softmax_noalloc"):
+                     "ks_softmax_workspace_size", "ks_softmax_ws", "ks_softmax_ws_ex", "ks_softmax_noalloc",
+                     "ks_get_plan_cus", "ks_time_next_call"):
             getattr(h, name).restype = ctypes.c_int
         _lib = h
     return _lib
@@ -229,11 +232,23 @@ KS_PLAN_ALIGNED = 1
 KS_PLAN_WORKSPACE = 2
 
 
-def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True, workspace: bool = False) -> Plan:
+def ks_get_plan(op: int, dtype: int, rows: int, hidden: int, aligned: bool = True, workspace: bool = False,
+                compute_units: int | None = None) -> Plan:
+    """ks_get_plan (the current device's compute units), or ks_get_plan_cus when
+    compute_units is given."""
     plan = Plan()
     flags = (KS_PLAN_ALIGNED if aligned else 0) | (KS_PLAN_WORKSPACE if workspace else 0)
-    _check(lib().ks_get_plan(op, dtype, rows, hidden, flags, ctypes.byref(plan)), "ks_get_plan")
+    if compute_units is None:
+        _check(lib().ks_get_plan(op, dtype, rows, hidden, flags, ctypes.byref(plan)), "ks_get_plan")
+    else:
+        _check(lib().ks_get_plan_cus(op, dtype, rows, hidden, flags, compute_units, ctypes.byref(plan)),
+               "ks_get_plan_cus")
     return plan
+
+
+def ks_time_next_call(start: int | None, stop: int | None) -> int:
+    """Attach two hipEvent_t handles (ints, or None) to the calling thread's next call."""
+    return lib().ks_time_next_call(start, stop)
 
 
 def ks_version() -> str:
@@ -453,11 +468,12 @@ def softmax(x: torch.Tensor, *, out: torch.Tensor | None = None, plan: Plan | No
 
 
 def get_plan(op: str, dtype: torch.dtype, hidden: int, rows: int = 1, aligned: bool = True,
-             workspace: bool = False) -> Plan:
-    """The plan the library picks for this op, dtype, row size and batch (ks_get_plan).
+             workspace: bool = False, compute_units: int | None = None) -> Plan:
+    """The plan the library picks for this op, dtype, row size and batch (ks_get_plan:
+    on the current device, or on a device of ``compute_units`` compute units).
     For silu_and_mul, ``hidden`` is the output width D; ``workspace`` asks for the
     plan of a call that passes one (softmax: ``softmax(split=True)``)."""
     code = {"rms_norm": KS_OP_RMS_NORM, "fused_add_rms_norm": KS_OP_FUSED_ADD_RMS_NORM,
             "silu_and_mul": KS_OP_SILU_AND_MUL, "softmax": KS_OP_SOFTMAX,
             "rms_norm_residual": KS_OP_RMS_NORM_RESIDUAL, "rms_norm_backward": KS_OP_RMS_NORM_BACKWARD}[op]
-    return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned, workspace)
+    return ks_get_plan(code, KS_DTYPE[dtype], rows, hidden, aligned, workspace, compute_units)

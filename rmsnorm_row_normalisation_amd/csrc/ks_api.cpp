@@ -15,6 +15,13 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+thread_local ks::TimingRequest g_timing;
+
+// Clears the calling thread's timing request when an entry point returns, so
+// that a request applies to exactly one call (whether or not it launched).
+struct TimingScope {
+    ~TimingScope() { g_timing = ks::TimingRequest{}; }
+};
 
 constexpr int64_t kMaxHidden = int64_t(1) << 24;   // float(hidden) stays exact
 constexpr int64_t kMaxRows = INT32_MAX;             // one workgroup row index per grid slot at most
@@ -58,19 +65,20 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 //
 // Vector path (aligned buffers, row bytes a multiple of 16, rows up to 128 KiB):
 //   * work units are the row's 16-byte pieces; a batch holds rows * nvec;
-//   * pieces per lane aim at spreading the batch over about 131072 lanes
-//     (8 waves on each of the 256 compute units), between 1 and 8 per lane,
-//     at most 4 for batches of 4M pieces or more (more waves in flight
-//     stream better there);
+//   * pieces per lane aim at spreading the batch over 512 lanes per compute
+//     unit (8 waves on each; 131072 lanes on 256 compute units), between 1
+//     and 8 per lane, at most 4 for batches of 16384 pieces per compute unit
+//     or more (4M on 256; more waves in flight stream better there);
 //   * the team is the power of two of lanes that covers the row with that
 //     many pieces, between 8 and 512 lanes (1024-lane workgroups measured
 //     slower);
 //   * loads and stores are marked non-temporal: the data is streamed once;
-//   * the fused kernel stages the weight in LDS from 2^18 pieces up, where
-//     several rows per compute unit share it; below that the staging barrier
-//     costs more than the L2 re-reads it saves.
+//   * the fused kernel stages the weight in LDS from 1024 pieces per compute
+//     unit up (2^18 on 256), where several rows per compute unit share it;
+//     below that the staging barrier costs more than the L2 re-reads it
+//     saves.
 // The two forms that add a residual (in place and out of place) read two
-// streams per row: from 4M pieces they take at most 2 pieces per lane and
+// streams per row: in large batches they take at most 2 pieces per lane and
 // teams of up to 1024 lanes.  The out-of-place form never stages the weight
 // in LDS (measured slower at every batch size).
 // These rules were fitted to timings of every compiled shape and hint
@@ -89,9 +97,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // team where that covers the row with no more idle piece slots than a
 // 512-lane team does.  Fitted to timings for output widths 1024..14336 and
 // 1..8192 rows (bf16, fp16).
-constexpr int64_t kTargetLanes = 131072;
-constexpr int64_t kLargeBatchPieces = int64_t(1) << 22;
-constexpr int64_t kWeightLdsPieces = int64_t(1) << 18;
+// The batch-size thresholds scale with the device's compute units (a whole
+// MI355X has 256; a partitioned one exposes fewer): per compute unit, 512
+// target lanes (131072 on 256), a large batch from 16384 pieces (4M) and LDS
+// weight staging from 1024 pieces (2^18).
+constexpr int64_t kTargetLanesPerCu = 512;
+constexpr int64_t kLargeBatchPiecesPerCu = 16384;
+constexpr int64_t kWeightLdsPiecesPerCu = 1024;
 constexpr int kPolicyMaxTpr = 512;
 constexpr int64_t kSwigluMaxVpt = 2;
 
@@ -134,22 +146,27 @@ ks_plan_t backward_vector_plan(int64_t nvec, int vec_elems, int max_vpt)
 // Pieces per lane: 1 while a one-piece split has at most 1024 workgroups,
 // 2 up to 4096, else 4 (longer chunks for large grids).
 // Fitted to timings of the one-pass policy plan against every split plan for
-// hidden 4096..131072 and 1..2048 rows (bf16, fp16, fp32).
+// hidden 4096..131072 and 1..2048 rows (bf16, fp16, fp32) on 256 compute
+// units; the row and workgroup counts scale with the compute units (rounded
+// up, so a row count never drops to zero).
 constexpr int64_t kSplitVectorPieces = 8192;
 
-int64_t split_max_rows(int64_t nvec)
+int64_t per_device(int64_t at_256_cus, int64_t cus) { return (at_256_cus * cus + 255) / 256; }
+
+int64_t split_max_rows(int64_t nvec, int64_t cus)
 {
-    return nvec > kSplitVectorPieces ? ks::kSplitMaxRows : nvec >= 6144 ? 32 : nvec >= 5120 ? 16 : nvec >= 4096 ? 4 : 0;
+    const int64_t at256 = nvec >= 6144 ? 32 : nvec >= 5120 ? 16 : nvec >= 4096 ? 4 : 0;
+    return nvec > kSplitVectorPieces ? ks::kSplitMaxRows : per_device(at256, cus);
 }
 
-bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, ks_plan_t *plan)
+bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, int64_t cus, ks_plan_t *plan)
 {
-    if (op != KS_OP_SOFTMAX || !vec_ok || rows > split_max_rows(nvec))
+    if (op != KS_OP_SOFTMAX || !vec_ok || rows > split_max_rows(nvec, cus))
         return false;
     const int64_t groups = rows * ks::split_chunks(nvec * 16, 1);
     plan->path = KS_PATH_SPLIT;
     plan->threads_per_row = ks::kSplitBlock;
-    plan->vectors_per_thread = groups <= 1024 ? 1 : groups <= 4096 ? 2 : 4;
+    plan->vectors_per_thread = groups <= per_device(1024, cus) ? 1 : groups <= per_device(4096, cus) ? 2 : 4;
     plan->rows_per_block = 1;
     plan->block_threads = ks::kSplitBlock;
     plan->load_nt = 1;
@@ -157,7 +174,9 @@ bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, ks_plan_t
     return true;
 }
 
-ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned, bool split_ok = false)
+// cus: the device's compute units (ks::kDefaultComputeUnits when unknown).
+ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned, bool split_ok,
+                 int64_t cus)
 {
     ks_plan_t plan;
     memset(&plan, 0, sizeof(plan));
@@ -166,7 +185,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
     const int vec_elems = (int)(16 / esize);
     const int64_t nvec = row_bytes / 16;
     const int bwd_vpt = ks::bwd_max_vpt((int)esize);
-    if (split_ok && split_policy(op, rows, nvec, aligned && row_bytes % 16 == 0, &plan)) {
+    if (split_ok && split_policy(op, rows, nvec, aligned && row_bytes % 16 == 0, cus, &plan)) {
         plan.elems_per_access = vec_elems;
         return plan;
     }
@@ -176,13 +195,14 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         const int64_t pieces = rows * nvec;
         const bool swiglu = op == KS_OP_SILU_AND_MUL;
         const bool adds_residual = op == KS_OP_FUSED_ADD_RMS_NORM || op == KS_OP_RMS_NORM_RESIDUAL;
-        const bool large = pieces >= kLargeBatchPieces;
+        const bool large = pieces >= kLargeBatchPiecesPerCu * cus;
+        const int64_t target_lanes = kTargetLanesPerCu * cus;
         const int64_t max_vpt = swiglu                  ? kSwigluMaxVpt
                                 : op == KS_OP_SOFTMAX ? (large ? 2 : 4)
                                 : adds_residual && large ? 2
                                 : large                 ? 4
                                                         : ks::kMaxVpt;
-        int64_t vpt = pow2_ceil((pieces + kTargetLanes - 1) / kTargetLanes);
+        int64_t vpt = pow2_ceil((pieces + target_lanes - 1) / target_lanes);
         vpt = vpt < 1 ? 1 : vpt > max_vpt ? max_vpt : vpt;
         int64_t tpr = pow2_ceil((nvec + vpt - 1) / vpt);
         if (swiglu && tpr > kPolicyMaxTpr) {
@@ -206,7 +226,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.rows_per_block = plan.block_threads / (int32_t)tpr;
         plan.load_nt = 1;
         plan.store_nt = 1;
-        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPieces) ? 1 : 0;
+        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPiecesPerCu * cus) ? 1 : 0;
         return plan;
     }
     plan.path = KS_PATH_GENERIC;
@@ -330,17 +350,29 @@ ks_status_t launch(ks::Launch &l, ks_dtype_t dtype)
     return KS_SUCCESS;
 }
 
-ks_status_t select_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden,
-                        bool aligned, ks_plan_t *out, bool split_ok = false)
+// Check an explicit plan (no HIP call).  Without one the policy's plan is
+// taken later, by policy_plan, once every argument check has passed: it
+// needs the device's compute units, which is a HIP query.
+ks_status_t check_plan(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden,
+                       bool aligned, bool split_ok = false)
 {
-    if (requested == nullptr) {
-        *out = policy(op, dtype, rows, hidden, aligned, split_ok);
-        return KS_SUCCESS;
-    }
-    if (!plan_fits(*requested, op, dtype, rows, hidden, aligned, split_ok))
+    if (requested != nullptr && !plan_fits(*requested, op, dtype, rows, hidden, aligned, split_ok))
         return KS_ERROR_INVALID_VALUE;
-    *out = *requested;
     return KS_SUCCESS;
+}
+
+// The device's compute units, or the whole-MI355X default when no device is
+// visible (a query of the plan on a machine without a GPU).
+int64_t compute_units()
+{
+    const int cus = ks::device_compute_units();
+    return cus > 0 ? cus : ks::kDefaultComputeUnits;
+}
+
+ks_plan_t plan_for(const ks_plan_t *requested, ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden,
+                   bool aligned, bool split_ok = false)
+{
+    return requested != nullptr ? *requested : policy(op, dtype, rows, hidden, aligned, split_ok, compute_units());
 }
 
 // Workspace bytes of a softmax plan: a (maximum, sum) pair per chunk on the
@@ -357,6 +389,7 @@ size_t softmax_workspace_bytes(const ks_plan_t &p, int64_t rows, int64_t row_byt
 ks_status_t softmax_call(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype, void *workspace,
                          size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream, bool split_ok)
 {
+    const TimingScope timing;
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
@@ -365,15 +398,14 @@ ks_status_t softmax_call(void *out, const void *x, int64_t rows, int64_t hidden,
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(out) && aligned16(x);
     ks::Launch l{out, x, nullptr, nullptr, rows, (int32_t)hidden, 0.0f, KS_OP_SOFTMAX, {}, stream};
-    ks_status_t st = select_plan(plan, KS_OP_SOFTMAX, dtype, rows, hidden, aligned, &l.plan, split_ok);
-    if (st != KS_SUCCESS)
+    ks_status_t st = check_plan(plan, KS_OP_SOFTMAX, dtype, rows, hidden, aligned, split_ok);
+    if (st != KS_SUCCESS || rows == 0)       // an empty batch needs no workspace
         return st;
+    l.plan = plan_for(plan, KS_OP_SOFTMAX, dtype, rows, hidden, aligned, split_ok);
     const int64_t nbytes = rows * hidden * elem_size(dtype);
     const size_t need = softmax_workspace_bytes(l.plan, rows, hidden * elem_size(dtype));
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 3u) != 0))
         return KS_ERROR_INVALID_VALUE;
-    if (rows == 0)
-        return KS_SUCCESS;
     if (out != x && overlaps(out, nbytes, x, nbytes))
         return KS_ERROR_OVERLAP;
     if (overlaps(workspace, (int64_t)need, out, nbytes) || overlaps(workspace, (int64_t)need, x, nbytes))
@@ -386,9 +418,10 @@ ks_status_t softmax_call(void *out, const void *x, int64_t rows, int64_t hidden,
 
 namespace ks {
 
-// The checks ks_softmax_ws makes before any HIP call (dtype, sizes, null
-// pointers) and the bytes of workspace the plan it would pick needs for these
-// buffers (0 for a one-pass plan).  No HIP call.
+// The checks ks_softmax_ws makes first (dtype, sizes, null pointers) and the
+// bytes of workspace the plan it would pick needs for these buffers (0 for a
+// one-pass plan or an empty batch).  The only HIP call is the device's
+// compute-unit query behind the policy (once per device).
 ks_status_t softmax_ws_need(const void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
                             size_t *need)
 {
@@ -398,12 +431,19 @@ ks_status_t softmax_ws_need(const void *out, const void *x, int64_t rows, int64_
         return KS_ERROR_INVALID_VALUE;
     if (rows > 0 && (out == nullptr || x == nullptr))
         return KS_ERROR_INVALID_VALUE;
-    const ks_plan_t p = policy(KS_OP_SOFTMAX, dtype, rows, hidden, aligned16(out) && aligned16(x), true);
+    if (rows == 0) {
+        *need = 0;
+        return KS_SUCCESS;
+    }
+    const ks_plan_t p = policy(KS_OP_SOFTMAX, dtype, rows, hidden, aligned16(out) && aligned16(x), true,
+                               compute_units());
     *need = softmax_workspace_bytes(p, rows, hidden * elem_size(dtype));
     return KS_SUCCESS;
 }
 
 void record_hip_error(int err) { g_last_hip_error = err; }
+
+TimingRequest &timing_request() { return g_timing; }
 
 }  // namespace ks
 
@@ -412,6 +452,7 @@ extern "C" {
 ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t rows, int64_t hidden, float eps,
                            ks_dtype_t dtype, const ks_plan_t *plan, hipStream_t stream)
 {
+    const TimingScope timing;
     ks_status_t st = check_sizes(dtype, rows, hidden, eps);
     if (st != KS_SUCCESS)
         return st;
@@ -419,7 +460,7 @@ ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(out) && aligned16(x) && aligned16(weight);
     ks::Launch l{out, x, nullptr, weight, rows, (int32_t)hidden, eps, KS_OP_RMS_NORM, {}, stream};
-    st = select_plan(plan, KS_OP_RMS_NORM, dtype, rows, hidden, aligned, &l.plan);
+    st = check_plan(plan, KS_OP_RMS_NORM, dtype, rows, hidden, aligned);
     if (st != KS_SUCCESS || rows == 0)
         return st;
     const int64_t es = elem_size(dtype);
@@ -428,6 +469,7 @@ ks_status_t ks_rms_norm_ex(void *out, const void *x, const void *weight, int64_t
         return KS_ERROR_OVERLAP;
     if (overlaps(out, nbytes, weight, hidden * es))
         return KS_ERROR_OVERLAP;
+    l.plan = plan_for(plan, KS_OP_RMS_NORM, dtype, rows, hidden, aligned);
     return launch(l, dtype);
 }
 
@@ -440,6 +482,7 @@ ks_status_t ks_rms_norm(void *out, const void *x, const void *weight, int64_t ro
 ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight, int64_t rows, int64_t hidden,
                                      float eps, ks_dtype_t dtype, const ks_plan_t *plan, hipStream_t stream)
 {
+    const TimingScope timing;
     ks_status_t st = check_sizes(dtype, rows, hidden, eps);
     if (st != KS_SUCCESS)
         return st;
@@ -447,7 +490,7 @@ ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(x) && aligned16(residual) && aligned16(weight);
     ks::Launch l{x, x, residual, weight, rows, (int32_t)hidden, eps, KS_OP_FUSED_ADD_RMS_NORM, {}, stream};
-    st = select_plan(plan, KS_OP_FUSED_ADD_RMS_NORM, dtype, rows, hidden, aligned, &l.plan);
+    st = check_plan(plan, KS_OP_FUSED_ADD_RMS_NORM, dtype, rows, hidden, aligned);
     if (st != KS_SUCCESS || rows == 0)
         return st;
     const int64_t es = elem_size(dtype);
@@ -455,6 +498,7 @@ ks_status_t ks_fused_add_rms_norm_ex(void *x, void *residual, const void *weight
     if (overlaps(x, nbytes, residual, nbytes) || overlaps(x, nbytes, weight, hidden * es) ||
         overlaps(residual, nbytes, weight, hidden * es))
         return KS_ERROR_OVERLAP;
+    l.plan = plan_for(plan, KS_OP_FUSED_ADD_RMS_NORM, dtype, rows, hidden, aligned);
     return launch(l, dtype);
 }
 
@@ -468,6 +512,7 @@ ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residu
                                    int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype,
                                    const ks_plan_t *plan, hipStream_t stream)
 {
+    const TimingScope timing;
     ks_status_t st = check_sizes(dtype, rows, hidden, eps);
     if (st != KS_SUCCESS)
         return st;
@@ -476,7 +521,7 @@ ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residu
     const bool aligned = aligned16(out) && aligned16(x) && aligned16(residual) && aligned16(weight);
     ks::Launch l{out, x, const_cast<void *>(residual), weight, rows, (int32_t)hidden, eps,
                  KS_OP_RMS_NORM_RESIDUAL, {}, stream};
-    st = select_plan(plan, KS_OP_RMS_NORM_RESIDUAL, dtype, rows, hidden, aligned, &l.plan);
+    st = check_plan(plan, KS_OP_RMS_NORM_RESIDUAL, dtype, rows, hidden, aligned);
     if (st != KS_SUCCESS || rows == 0)
         return st;
     const int64_t es = elem_size(dtype);
@@ -486,6 +531,7 @@ ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residu
     if ((out != x && overlaps(out, nbytes, x, nbytes)) || (out != residual && overlaps(out, nbytes, residual, nbytes)) ||
         overlaps(out, nbytes, weight, hidden * es))
         return KS_ERROR_OVERLAP;
+    l.plan = plan_for(plan, KS_OP_RMS_NORM_RESIDUAL, dtype, rows, hidden, aligned);
     return launch(l, dtype);
 }
 
@@ -507,6 +553,7 @@ ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, con
                                     int64_t rows, int64_t hidden, float eps, ks_dtype_t dtype, void *workspace,
                                     size_t workspace_bytes, const ks_plan_t *plan, hipStream_t stream)
 {
+    const TimingScope timing;
     ks_status_t st = check_sizes(dtype, rows, hidden, eps);
     if (st != KS_SUCCESS)
         return st;
@@ -518,7 +565,7 @@ ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, con
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(dx) && aligned16(dy) && aligned16(x) && aligned16(weight);
     ks::BwdLaunch l{dx, dweight, dy, x, weight, (float *)workspace, rows, (int32_t)hidden, eps, {}, stream};
-    st = select_plan(plan, KS_OP_RMS_NORM_BACKWARD, dtype, rows, hidden, aligned, &l.plan);
+    st = check_plan(plan, KS_OP_RMS_NORM_BACKWARD, dtype, rows, hidden, aligned);
     if (st != KS_SUCCESS || (rows == 0 && dweight == nullptr))
         return st;
     const int64_t es = elem_size(dtype);
@@ -535,6 +582,7 @@ ks_status_t ks_rms_norm_backward_ex(void *dx, void *dweight, const void *dy, con
          overlaps(workspace, kbytes, dy, nbytes) || overlaps(workspace, kbytes, x, nbytes) ||
          overlaps(workspace, kbytes, weight, wbytes)))
         return KS_ERROR_OVERLAP;
+    l.plan = plan_for(plan, KS_OP_RMS_NORM_BACKWARD, dtype, rows, hidden, aligned);
     hipError_t err;
     switch (dtype) {
     case KS_DTYPE_FLOAT32: err = ks::launch_bwd_f32(l); break;
@@ -559,6 +607,7 @@ ks_status_t ks_rms_norm_backward(void *dx, void *dweight, const void *dy, const 
 ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d, ks_dtype_t dtype,
                                const ks_plan_t *plan, hipStream_t stream)
 {
+    const TimingScope timing;
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (rows < 0 || rows > kMaxRows || d <= 0 || d > kMaxHidden)
@@ -567,12 +616,13 @@ ks_status_t ks_silu_and_mul_ex(void *out, const void *x, int64_t rows, int64_t d
         return KS_ERROR_INVALID_VALUE;
     const bool aligned = aligned16(out) && aligned16(x);
     ks::SwigluLaunch l{out, x, rows, (int32_t)d, {}, stream};
-    ks_status_t st = select_plan(plan, KS_OP_SILU_AND_MUL, dtype, rows, d, aligned, &l.plan);
+    ks_status_t st = check_plan(plan, KS_OP_SILU_AND_MUL, dtype, rows, d, aligned);
     if (st != KS_SUCCESS || rows == 0)
         return st;
     const int64_t es = elem_size(dtype);
     if (overlaps(out, rows * d * es, x, rows * 2 * d * es))
         return KS_ERROR_OVERLAP;
+    l.plan = plan_for(plan, KS_OP_SILU_AND_MUL, dtype, rows, d, aligned);
     hipError_t err;
     switch (dtype) {
     case KS_DTYPE_FLOAT32: err = ks::launch_swiglu_f32(l); break;
@@ -609,7 +659,11 @@ ks_status_t ks_softmax_workspace_size(int64_t rows, int64_t hidden, ks_dtype_t d
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (bytes == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden)
         return KS_ERROR_INVALID_VALUE;
-    const ks_plan_t p = plan != nullptr ? *plan : policy(KS_OP_SOFTMAX, dtype, rows, hidden, true, true);
+    if (plan == nullptr && rows == 0) {
+        *bytes = 0;
+        return KS_SUCCESS;
+    }
+    const ks_plan_t p = plan != nullptr ? *plan : policy(KS_OP_SOFTMAX, dtype, rows, hidden, true, true, compute_units());
     *bytes = softmax_workspace_bytes(p, rows, hidden * elem_size(dtype));
     return KS_SUCCESS;
 }
@@ -626,16 +680,34 @@ ks_status_t ks_softmax_ws(void *out, const void *x, int64_t rows, int64_t hidden
     return softmax_call(out, x, rows, hidden, dtype, workspace, workspace_bytes, nullptr, stream, true);
 }
 
-ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags, ks_plan_t *plan)
+ks_status_t ks_get_plan_cus(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags, int compute_units,
+                           ks_plan_t *plan)
 {
     if (!valid_dtype(dtype))
         return KS_ERROR_UNSUPPORTED_DTYPE;
     if (plan == nullptr || rows < 0 || rows > kMaxRows || hidden <= 0 || hidden > kMaxHidden ||
-        (flags & ~(KS_PLAN_ALIGNED | KS_PLAN_WORKSPACE)) != 0 ||
+        (flags & ~(KS_PLAN_ALIGNED | KS_PLAN_WORKSPACE)) != 0 || compute_units < 1 ||
+        compute_units > ks::kMaxComputeUnits ||
         (op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_SILU_AND_MUL &&
          op != KS_OP_SOFTMAX && op != KS_OP_RMS_NORM_RESIDUAL && op != KS_OP_RMS_NORM_BACKWARD))
         return KS_ERROR_INVALID_VALUE;
-    *plan = policy(op, dtype, rows, hidden, (flags & KS_PLAN_ALIGNED) != 0, (flags & KS_PLAN_WORKSPACE) != 0);
+    *plan = policy(op, dtype, rows, hidden, (flags & KS_PLAN_ALIGNED) != 0, (flags & KS_PLAN_WORKSPACE) != 0,
+                   compute_units);
+    return KS_SUCCESS;
+}
+
+ks_status_t ks_get_plan(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, int flags, ks_plan_t *plan)
+{
+    if (!valid_dtype(dtype))
+        return KS_ERROR_UNSUPPORTED_DTYPE;
+    if (plan == nullptr)
+        return KS_ERROR_INVALID_VALUE;
+    return ks_get_plan_cus(op, dtype, rows, hidden, flags, (int)compute_units(), plan);
+}
+
+ks_status_t ks_time_next_call(hipEvent_t start, hipEvent_t stop)
+{
+    ks::timing_request() = ks::TimingRequest{start, stop};
     return KS_SUCCESS;
 }
 
@@ -656,6 +728,9 @@ const char *ks_status_string(ks_status_t status)
 
 int ks_last_hip_error(void) { return g_last_hip_error; }
 
-const char *ks_version(void) { return "ks_norm 0.1.0 gfx950"; }
+#ifndef KS_BUILD_GIT
+#define KS_BUILD_GIT "unknown"
+#endif
+const char *ks_version(void) { return "ks_norm 0.2.0 gfx950 (source " KS_BUILD_GIT ")"; }
 
 }  // extern "C"

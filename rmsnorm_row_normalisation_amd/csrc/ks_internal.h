@@ -119,6 +119,25 @@ inline int64_t split_workspace_floats(int64_t rows, int64_t row_bytes, int vpt)
     return rows * split_chunks(row_bytes, vpt) * 2;
 }
 
+// A pending request for per-call kernel timing (ks_time_next_call): the
+// runtime's kernel-dispatch events for the calling thread's next call.  The
+// launch code attaches `start` to the call's first kernel and `stop` to every
+// kernel of the call (the last record stands); the entry point clears the
+// request when it returns.
+struct TimingRequest {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+TimingRequest &timing_request();   // the calling thread's request (ks_api.cpp)
+
+// Compute units of the current device, queried once per device and cached
+// (ks_device_info.cpp); 0 when no device is visible.  The launch policy scales
+// its batch-size thresholds with it; kDefaultComputeUnits (a whole MI355X)
+// stands in when it is unknown.
+int device_compute_units();
+constexpr int kDefaultComputeUnits = 256;
+constexpr int kMaxComputeUnits = 4096;
+
 // ks_api.cpp: the pre-HIP checks of ks_softmax_ws and the workspace bytes of
 // its plan for these buffers; the per-thread HIP error behind KS_ERROR_HIP.
 ks_status_t softmax_ws_need(const void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,

@@ -2,12 +2,30 @@
 // per-dtype translation unit includes this once and defines its launch_*.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "ks_device.hpp"
 #include "ks_internal.h"
 
 namespace ks {
+
+// Launch one kernel on `stream`.  With a timing request pending
+// (ks_time_next_call) the launch goes through the runtime's kernel-dispatch
+// events: the start event marks the beginning of the call's first kernel,
+// the stop event the end of each kernel (so of the last one).
+template <typename Kernel, typename... Args>
+hipError_t dispatch(Kernel kernel, dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream, Args... args)
+{
+    TimingRequest &t = timing_request();
+    if (t.start == nullptr && t.stop == nullptr) {
+        hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+    } else {
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds_bytes, stream, t.start, t.stop, 0u, args...);
+        t.start = nullptr;
+    }
+    return hipGetLastError();
+}
 
 // Rows one launch of a row kernel may cover: its grid stays within 2^31
 // work-items (a dispatch counts work-items in 32 bits); larger batches go out
@@ -28,8 +46,7 @@ hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
         const size_t off = (size_t)r0 * row_bytes;
         Params p{(char *)l.y + off, (const char *)l.x + off, l.res ? (char *)l.res + off : nullptr, l.w, n,
                  l.hidden, l.eps};
-        hipLaunchKernelGGL(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), lds_bytes, l.stream, p);
-        const hipError_t err = hipGetLastError();
+        const hipError_t err = dispatch(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), lds_bytes, l.stream, p);
         if (err != hipSuccess)
             return err;
     }
@@ -150,12 +167,10 @@ hipError_t softmax_split_one(const Launch &l)
     const int64_t chunks = split_chunks((int64_t)l.hidden * Pack<T>::kBytes, V);
     SplitParams p{l.y, l.x, l.work, l.rows, l.hidden, (int32_t)chunks};
     const dim3 grid((unsigned)chunks, (unsigned)l.rows);
-    hipLaunchKernelGGL((softmax_split_stats<T, V>), grid, dim3(kSplitBlock), 0, l.stream, p);
-    hipError_t err = hipGetLastError();
+    const hipError_t err = dispatch(softmax_split_stats<T, V>, grid, dim3(kSplitBlock), 0, l.stream, p);
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL((softmax_split_norm<T, V>), grid, dim3(kSplitBlock), 0, l.stream, p);
-    return hipGetLastError();
+    return dispatch(softmax_split_norm<T, V>, grid, dim3(kSplitBlock), 0, l.stream, p);
 }
 
 template <typename T>
@@ -187,8 +202,7 @@ hipError_t run_swiglu(Kernel kernel, const SwigluLaunch &l, int block)
         const int64_t n = l.rows - r0 < slice ? l.rows - r0 : slice;
         SwigluParams p{(char *)l.out + (size_t)r0 * out_bytes, (const char *)l.x + (size_t)r0 * 2 * out_bytes, n,
                        l.d};
-        hipLaunchKernelGGL(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
-        const hipError_t err = hipGetLastError();
+        const hipError_t err = dispatch(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
         if (err != hipSuccess)
             return err;
     }
@@ -234,8 +248,7 @@ hipError_t launch_swiglu_typed(const SwigluLaunch &l)
         const int64_t total = l.rows * (int64_t)l.d;
         int64_t blocks = (total + kSwigluGenericBlock - 1) / kSwigluGenericBlock;
         blocks = blocks > 8192 ? 8192 : blocks;   // grid-stride beyond 2M threads
-        hipLaunchKernelGGL(silu_and_mul_generic<T>, dim3((unsigned)blocks), dim3(kSwigluGenericBlock), 0, l.stream, p);
-        return hipGetLastError();
+        return dispatch(silu_and_mul_generic<T>, dim3((unsigned)blocks), dim3(kSwigluGenericBlock), 0, l.stream, p);
     }
     switch (l.plan.threads_per_row) {
     case 8: return swiglu_by_vpt<T, 8>(l);
@@ -256,8 +269,7 @@ hipError_t launch_swiglu_typed(const SwigluLaunch &l)
 template <typename T, int TPR, int V>
 hipError_t bwd_vec_one(const BwdParams &p, unsigned grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((rms_norm_backward_vec<T, TPR, V, kBwdBlock>), dim3(grid), dim3(kBwdBlock), 0, stream, p);
-    return hipGetLastError();
+    return dispatch(rms_norm_backward_vec<T, TPR, V, kBwdBlock>, dim3(grid), dim3(kBwdBlock), 0, stream, p);
 }
 
 template <typename T, int TPR>
@@ -280,8 +292,7 @@ template <typename T, int TPR, int EPA>
 hipError_t bwd_generic_one(const BwdParams &p, unsigned grid, hipStream_t stream)
 {
     constexpr int B = TPR == 1024 ? 1024 : 256;
-    hipLaunchKernelGGL((rms_norm_backward_generic<T, TPR, EPA, B>), dim3(grid), dim3(B), 0, stream, p);
-    return hipGetLastError();
+    return dispatch(rms_norm_backward_generic<T, TPR, EPA, B>, dim3(grid), dim3(B), 0, stream, p);
 }
 
 template <typename T, int EPA>
@@ -344,8 +355,7 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
             }
             if (err == hipSuccess && l.dw) {
                 const dim3 cgrid((unsigned)((l.hidden + 255) / 256), (unsigned)nparts);
-                hipLaunchKernelGGL((rms_norm_backward_colsum<T>), cgrid, dim3(256), 0, l.stream, p);
-                err = hipGetLastError();
+                err = dispatch(rms_norm_backward_colsum<T>, cgrid, dim3(256), 0, l.stream, p);
             }
         }
     }
@@ -353,8 +363,7 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
         return err;
     DwParams d{l.dw, l.work, nparts, l.hidden};
     const dim3 dgrid((unsigned)((l.hidden + kDwCols - 1) / kDwCols));
-    hipLaunchKernelGGL((rms_norm_backward_dw<T>), dgrid, dim3(kDwBlock), 0, l.stream, d);
-    return hipGetLastError();
+    return dispatch(rms_norm_backward_dw<T>, dgrid, dim3(kDwBlock), 0, l.stream, d);
 }
 
 }  // namespace ks

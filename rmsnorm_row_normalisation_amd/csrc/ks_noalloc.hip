@@ -51,11 +51,18 @@ hipError_t scratch_address(void **out)
     return hipSuccess;
 }
 
+// A timing request (ks_time_next_call) applies to this call alone, also when
+// it returns before reaching ks_softmax_ws.
+struct ClearTimingOnReturn {
+    ~ClearTimingOnReturn() { ks::timing_request() = ks::TimingRequest{}; }
+};
+
 }  // namespace
 
 extern "C" ks_status_t ks_softmax_noalloc(void *out, const void *x, int64_t rows, int64_t hidden, ks_dtype_t dtype,
                                           hipStream_t stream)
 {
+    const ClearTimingOnReturn timing;
     size_t need = 0;
     const ks_status_t st = ks::softmax_ws_need(out, x, rows, hidden, dtype, &need);
     if (st != KS_SUCCESS)

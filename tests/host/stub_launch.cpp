@@ -61,3 +61,8 @@ KS_STUB(launch_bwd_f16, BwdLaunch)
 KS_STUB(launch_bwd_bf16, BwdLaunch)
 
 }  // namespace ks
+
+namespace ks {
+// The sweep runs without a device: the whole-MI355X compute-unit count.
+int device_compute_units() { return kDefaultComputeUnits; }
+}  // namespace ks

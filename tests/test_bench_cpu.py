@@ -84,3 +84,68 @@ def test_gpus_above_one_exits_with_message():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                          text=True, cwd=ROOT)
     assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_distribution_nearest_rank():
+    d = bench.distribution([float(v) for v in range(1, 101)])
+    assert (d["n"], d["min"], d["p50"], d["p95"], d["p99"], d["max"]) == (100, 1, 50, 95, 99, 100)
+    assert d["mean"] == pytest.approx(50.5)
+    one = bench.distribution([3.25])
+    assert one["p50"] == one["p99"] == one["min"] == one["max"] == 3.25
+
+
+def test_sweep_set_adds_dtype_variants_once():
+    wls = bench.sweep_set(["bf16", "fp16", "fp32"])
+    names = [w.name for w in wls]
+    for n in ("C1-fp16", "C1-fp32", "C2-fp16", "C2-fp32", "C3b-fp32"):
+        assert n in names
+    # C3 already covers fp16 at 2048x4096, so C3b's fp16 variant would repeat its cases
+    assert "C3b-fp16" not in names
+    keys = [(w.ops, w.dtype, w.rows, w.hidden) for w in wls]
+    assert len(keys) == len(set(keys))
+    v = next(w for w in wls if w.name == "C1-fp32")
+    c1 = bench.workloads.WORKLOADS["C1"]
+    assert (v.rows, v.hidden, v.seed_x, v.seed_w, v.eps, v.dtype) == (c1.rows, c1.hidden, c1.seed_x, c1.seed_w,
+                                                                     c1.eps, "float32")
+
+
+def test_streamref_library_exports_and_rejects_bad_sizes():
+    """The reference streams check sizes before any launch (no GPU needed)."""
+    ref = bench.StreamRef()
+    for name in ("ksref_read", "ksref_write", "ksref_copy", "ksref_copy_rows", "ksref_inplace4", "ksref_empty"):
+        assert hasattr(ref.h, name)
+    a, b = 0x10000000, 0x20000000
+    assert ref.h.ksref_copy(a, b, 4095, 0, None, None, None) == 1          # not a whole 4 KiB block
+    assert ref.h.ksref_copy(a, b, 0, 0, None, None, None) == 1
+    assert ref.h.ksref_copy(a, b, (1 << 31) + 4096, 0, None, None, None) == 1
+    assert ref.h.ksref_copy(a, b, 4096, 3, None, None, None) == 1          # unknown store policy
+    assert ref.h.ksref_write(b, 4096, 7, None, None, None) == 1
+    assert ref.h.ksref_copy_rows(a, b, 4096, 2, None, None, None) == 1     # 2 pieces: blocks of 8 KiB
+    assert ref.h.ksref_copy_rows(a, b, 8192, 3, None, None, None) == 1
+    assert ref.h.ksref_inplace4(a, b, 4096 * 8 + 4096, 8, None, None, None) == 1
+    assert ref.h.ksref_empty(0, None, None, None) == 1
+
+
+def test_streams_table_is_consistent():
+    for name, (mult, _) in bench.STREAMS.items():
+        assert name in bench.STREAM_DESCRIPTIONS
+        assert mult == (1 if name.startswith(("read", "write")) else 4 if name.startswith("in place") else 2)
+
+
+def test_trace_summary_renders_a_kernel_trace(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    hdr = ('"Kind","Kernel_Name","Start_Timestamp","End_Timestamp","LDS_Block_Size","Scratch_Size","VGPR_Count",'
+           '"Accum_VGPR_Count","SGPR_Count","Workgroup_Size_X","Grid_Size_X"\n')
+    k = "void ks::fused_add_rms_norm_vec<ks::bf16, 64, 8, 256, 2, 2, true>(ks::Params)"
+    r = "void ks::rms_norm_vec<ks::bf16, 64, 8, 256, 2, 2, false>(ks::Params)"
+    lines = [f'"KERNEL_DISPATCH","{k}",{1000 * i},{1000 * i + 11000 + 10 * i},0,0,52,0,32,256,131072\n' for i in range(5)]
+    lines += [f'"KERNEL_DISPATCH","{r}",{1000 * i},{1000 * i + 6000},0,0,52,0,48,256,131072\n' for i in range(5)]
+    lines += ['"KERNEL_DISPATCH","copy_one<17>",0,7000,0,0,4,0,32,256,1048576\n',
+              '"KERNEL_DISPATCH","copy_one<17>",0,325000,0,0,4,0,32,256,67108864\n']
+    (d / "b_kernel_trace.csv").write_text(hdr + "".join(lines))
+    wl = bench.workloads.WORKLOADS["C3b"]
+    text = bench.trace_summary(wl, str(d), None, "rocprofv3 --kernel-trace -- python3 bench.py")
+    assert "| fused_add_rms_norm | 67117056 | 11.020 | 11.020 |" in text
+    assert "| rms_norm | 33562624 | 6.000 | 6.000 |" in text
+    assert "[grid 1048576]" in text and "[grid 67108864]" in text

@@ -6,7 +6,7 @@ Bar: the fused residual output is bit-exact; normalised outputs are within
 
 Cases: every benchmark workload of the operator pages (128x1024, 512x4096,
 2048x4096 in fp16 with outliers and in bf16, decode 4x1536 and 1x8192, and the
-large prefills 32768x8192 and 8192x16384, those two checked on sampled rows),
+large prefills 32768x8192 and 8192x16384, every row checked in chunks),
 the kernscope edge shapes, ragged row counts, unaligned buffers, every
 compiled launch plan, and the invariants that hold at any size.
 """
@@ -43,21 +43,29 @@ def test_workload_full(name):
 
 
 @pytest.mark.parametrize("name", ["C5f", "C5r"])
-def test_workload_large_sampled(name):
-    """Full-size launch; the oracle checks 48 sampled rows plus the first and last."""
+def test_workload_large_full(name):
+    """Full-size launch; every row checked against the oracle, in chunks of rows
+    (the bar per element, the exact-match rate over the whole batch)."""
     wl = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(wl)
-    rows = np.random.default_rng(77).choice(wl.rows, size=48, replace=False)
-    rows = np.unique(np.concatenate([rows, [0, wl.rows - 1]]))
-    idx = torch.from_numpy(rows)
     for op in wl.ops:
         say(name, op, "full launch", (wl.rows, wl.hidden))
         y, r = gpu_run(op, inp, wl.eps)
-        sub = {k: (v[idx].contiguous() if v.dim() == 2 else v) for k, v in inp.items()}
-        ref = oracle_run(op, sub, wl.eps)
-        st = check_outputs(op, (y[idx].contiguous(), r[idx].contiguous() if r is not None else None), ref,
-                           exact_rate=True)
-        say(name, op, st)
+        exact = total = worst = 0
+        for r0 in range(0, wl.rows, LARGE_CHUNK_ROWS):
+            sl = slice(r0, min(wl.rows, r0 + LARGE_CHUNK_ROWS))
+            sub = {k: (v[sl] if v.dim() == 2 else v) for k, v in inp.items()}
+            ref = oracle_run(op, sub, wl.eps)
+            st = check_outputs(op, (y[sl], r[sl] if r is not None else None), ref, exact_rate=False)
+            exact += round(st.exact_rate * st.n)
+            total += st.n
+            worst = max(worst, st.max_ulp)
+        say(name, op, f"rows {wl.rows}: max ulp {worst}, exact {exact / total:.6f}")
+        assert total == wl.rows * wl.hidden
+        assert exact / total >= 0.999
+
+
+LARGE_CHUNK_ROWS = 2048
 
 
 # ---------------------------------------------------------------------------

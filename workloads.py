@@ -26,7 +26,7 @@ and 16384, and row counts from one decode token up to long prefills.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -146,6 +146,21 @@ WORKLOADS: dict[str, Workload] = {
     "X4": Workload("X4", (SOFTMAX,), "float16", 8, 65536, normal(0, 1), None, 0.0, 7301, None),
     "X5": Workload("X5", (SOFTMAX,), "bfloat16", 2048, 4096, normal(0, 1), None, 0.0, 7401, None),
 }
+
+
+DTYPE_TAGS = {"bf16": "bfloat16", "fp16": "float16", "fp32": "float32"}
+
+
+def with_dtype(wl: Workload, dtype: str) -> Workload:
+    """The same workload (shape, distributions, seeds) stored in another dtype;
+    named e.g. ``C1-fp32``.  ``dtype`` is a torch name or a tag (bf16, fp16, fp32)."""
+    dtype = DTYPE_TAGS.get(dtype, dtype)
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype}")
+    if dtype == wl.dtype:
+        return wl
+    tag = {v: k for k, v in DTYPE_TAGS.items()}[dtype]
+    return replace(wl, name=f"{wl.name}-{tag}", dtype=dtype)
 
 
 def _to_dtype(values: np.ndarray, dtype: torch.dtype, shape: tuple[int, ...]) -> torch.Tensor:
