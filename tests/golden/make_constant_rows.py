@@ -13,7 +13,8 @@ ulps, from the closed-form value to the nearest rounding boundary: a large
 margin means the fp32 rounding of the intermediate steps cannot move the
 result across a boundary.
 
-Run from the repository root:  python tests/golden/make_constant_rows.py
+Run from the repository root:  python tests/golden/make_constant_rows.py [OUTPUT]
+(default output: tests/golden/constant_rows.txt)
 """
 from __future__ import annotations
 
@@ -91,7 +92,8 @@ def _pattern(value: float, fmt: str) -> int:
     return f32 >> 16
 
 
-def main() -> None:
+def table() -> str:
+    """The table's text."""
     lines = [
         "# RMSNorm of constant rows with unit weight: y = c / sqrt(c^2 + eps), one rounding",
         "# Source: kernscope README, 'Numerical contract' > 'RMSNorm' (closed form for a constant row).",
@@ -114,10 +116,17 @@ def main() -> None:
             assert c2.denominator & (c2.denominator - 1) == 0 and bits_needed <= 24, (fmt, cs, h)
             width = _BITS[fmt] // 4
             lines.append(f"{fmt} {cs} {eps:g} {h} 0x{_pattern(yv, fmt):0{width}x} {_margin(y, fmt):.4f}")
-    with open(OUT, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print(f"wrote {OUT} ({len(lines) - 5} cases)")
+    return "\n".join(lines) + "\n"
+
+
+def main(argv: list[str]) -> None:
+    """Write the table to the path given (default: constant_rows.txt next to this script)."""
+    out = argv[0] if argv else OUT
+    text = table()
+    with open(out, "w") as f:
+        f.write(text)
+    print(f"wrote {out} ({text.count(chr(10)) - 5} cases)")
 
 
 if __name__ == "__main__":
-    main()
+    main(sys.argv[1:])

@@ -10,14 +10,15 @@ def test_pin(pin, oracle_lib):
     pin(oracle_lib)
 
 
-def test_golden_table_is_current():
-    """The stored closed-form table is what its generator writes today."""
+def test_golden_table_is_current(tmp_path):
+    """The stored closed-form table is what its generator writes today (written
+    to a temporary file: the committed table is never rewritten by a test)."""
     import os
     import subprocess
     import sys
 
     golden = pins.GOLDEN
-    before = open(golden).read()
-    subprocess.run([sys.executable, os.path.join(os.path.dirname(golden), "make_constant_rows.py")],
+    fresh = tmp_path / "constant_rows.txt"
+    subprocess.run([sys.executable, os.path.join(os.path.dirname(golden), "make_constant_rows.py"), str(fresh)],
                    check=True, capture_output=True)
-    assert open(golden).read() == before
+    assert fresh.read_text() == open(golden).read()
