@@ -24,10 +24,12 @@ Timing (exactly K steps in every timed region):
     holding only that op's launches back to back (median of three timed
     regions): what a caller sees per call in a captured sequence;
   * per op, kernel duration (``per_op[op].kernel_us``, ``roofline``): K calls
-    of that op on the launch stream, each timed by the runtime's
-    kernel-dispatch events (``ks_time_next_call``): min / p50 / p95 / p99 /
-    max / mean of the kernels' own durations.  ``roofline.achieved`` is the
-    dominant kernel's algorithmic bytes over its mean duration;
+    of that op on the launch stream (at most 2048), each timed by the
+    runtime's kernel-dispatch events (``ks_time_next_call``), enqueued in runs
+    of 32 behind a 300 us spin kernel so that each run executes back to back:
+    min / p50 / p95 / p99 / max / mean of the kernels' own durations.
+    ``roofline.achieved`` is the dominant kernel's algorithmic bytes over its
+    mean duration;
   * ``stream_reference``: the library-independent reference streams of
     ``libks_streamref.so`` timed the same way: an empty kernel (the
     per-launch floor) and a plain copy (one 16-byte load and store per lane)
@@ -435,19 +437,29 @@ def distribution(vals: list[float]) -> dict:
             "p95": round(q(0.95), 3), "p99": round(q(0.99), 3), "max": round(v[-1], 3)}
 
 
+HEAD_START_US = 300      # the spin kernel queued ahead of each run of timed calls
+HEAD_START_CALLS = 32    # timed calls enqueued behind one spin kernel
+
+
 def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_call=None) -> list[float]:
     """n calls of call(i) (a raw C entry point on `stream`, returning its status),
     each timed by the runtime's kernel-dispatch events (from the start of the
-    call's first kernel to the end of its last): microseconds.
-    `timed_call(i, start, stop)` replaces the request through
-    ks_time_next_call for callers that take the events themselves."""
+    call's first kernel to the end of its last): microseconds.  The calls go in
+    runs of HEAD_START_CALLS behind a spin kernel of HEAD_START_US, so the host
+    has enqueued a run before it starts and its calls execute back to back, as
+    they would in a steady stream of work.  `timed_call(i, start, stop)`
+    replaces the request through ks_time_next_call for callers that take the
+    events themselves."""
     import rmsnorm_row_normalisation_amd as ks
 
     lib = ks.lib()
+    ref = StreamRef()
     evs = [(hip.event(), hip.event()) for _ in range(n)]
     try:
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(evs):
+            if i % HEAD_START_CALLS == 0:
+                StreamRef.check(ref.h.ksref_spin(HEAD_START_US, stream.cuda_stream), "ksref_spin")
             if timed_call is not None:
                 timed_call(i, a, b)
             else:
@@ -515,6 +527,7 @@ class StreamRef:
         h.ksref_copy_rows.argtypes = [vp, vp, u64, ci, vp, vp, vp]
         h.ksref_inplace4.argtypes = [vp, vp, u64, ci, vp, vp, vp]
         h.ksref_empty.argtypes = [cu, vp, vp, vp]
+        h.ksref_spin.argtypes = [cu, vp]
         self.h = h
 
     @staticmethod
@@ -905,10 +918,14 @@ def trace_dispatches(directory: str) -> dict[str, dict]:
 
 
 def trace_summary(wl, directory: str, bench_json: str | None, command: str | None) -> str:
+    """Markdown summary of a kernel trace of a bench run of workload `wl` (None:
+    of a --stream-reference run)."""
     disp = trace_dispatches(directory)
-    esize = wl.torch_dtype.itemsize
-    L = [f"# Kernel trace: {' + '.join(wl.ops)}, {wl.dtype} [{wl.rows},{wl.hidden}]", "",
-         f"Workload `{wl.name}`: {wl.describe()}.", ""]
+    if wl is None:
+        L = ["# Kernel trace: the reference streams (`bench.py --stream-reference`)", ""]
+    else:
+        L = [f"# Kernel trace: {' + '.join(wl.ops)}, {wl.dtype} [{wl.rows},{wl.hidden}]", "",
+             f"Workload `{wl.name}`: {wl.describe()}.", ""]
     if command:
         L += ["Command (repository root on the GPU box; the summary is rendered from its output by "
               "`python bench.py --trace-summary`):", "", "```", "cd /tmp && export TMPDIR=/tmp", command, "```", ""]
@@ -926,13 +943,16 @@ def trace_summary(wl, directory: str, bench_json: str | None, command: str | Non
                  f"{d['p99']:.2f} | {d['max']:.2f} | {res['vgpr']} | {res['agpr']} | {res['sgpr']} | {res['lds']} | "
                  f"{res['scratch']} | {res['workgroup']} | {res['grid']} |")
         op = kernel_op(name)
-        if op is not None and op in wl.ops:
+        if wl is not None and op is not None and op in wl.ops:
             per_op.setdefault(op, {"mean": 0.0, "p50": 0.0, "kernels": 0})
             per_op[op]["mean"] += d["mean"]   # an op of several kernels takes their sum
             per_op[op]["p50"] += d["p50"]
             per_op[op]["kernels"] += 1
     L += ["", "The library's kernels come first; the rest are the bench's own setup and reference kernels "
-          "(input copies, the empty and copy reference streams)."]
+          "(input copies, the empty, spin and copy reference streams)."]
+    if wl is None:
+        return "\n".join(L) + "\n"
+    esize = wl.torch_dtype.itemsize
     line = None
     if bench_json:
         with open(bench_json) as f:
@@ -1069,8 +1089,8 @@ def sweep_workloads(args, ks, oracle_mod, hip: Hip) -> None:
 def main() -> None:
     args = parse()
     if args.trace_summary:
-        wl = workloads.WORKLOADS[args.workload]
-        if args.dtype:
+        wl = None if args.stream_reference else workloads.WORKLOADS[args.workload]
+        if wl is not None and args.dtype:
             wl = workloads.with_dtype(wl, args.dtype)
         text = trace_summary(wl, args.trace_summary, args.trace_bench, args.trace_command)
         if args.out:

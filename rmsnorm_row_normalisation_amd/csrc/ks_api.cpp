@@ -215,6 +215,13 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > max_tpr ? max_tpr : tpr;
         if (wide)
             tpr = ks::kMaxTpr;
+        // the in-place fused form in a large batch: a row of a whole multiple
+        // of 1024 pieces (within the piece cap) takes a 1024-lane team, e.g.
+        // one piece per lane for 8192-wide bf16 rows (measured 1-3% faster
+        // than 512 lanes x 2 at 16384..65536 rows of 8192; other widths keep
+        // the rule above, which measured as fast or faster)
+        if (op == KS_OP_FUSED_ADD_RMS_NORM && large && nvec % ks::kMaxTpr == 0 && nvec / ks::kMaxTpr <= max_vpt)
+            tpr = ks::kMaxTpr;
         int64_t pieces_per_lane = (nvec + tpr - 1) / tpr;
         if (op == KS_OP_RMS_NORM_RESIDUAL && tpr == ks::kMaxTpr && pieces_per_lane == 7)
             pieces_per_lane = 8;   // the 7-piece build of this form spills registers

@@ -17,6 +17,11 @@
 //   ksref_inplace4  the fused form's four streams: read x and r, write both
 //                   back in place, with the ksref_copy_rows layout
 //   ksref_empty     a kernel that does nothing: the per-launch floor
+//   ksref_spin      one wave that waits a given number of microseconds on the
+//                   device's constant-rate wall clock, then exits (at most
+//                   100 ms): queued ahead of a run of timed calls, it lets the
+//                   host enqueue them before the first one starts, so they
+//                   run back to back
 // `policy` selects the cache bits of the stores: 0 default, 1 non-temporal,
 // 2 sc0 sc1 (system scope).  Loads are non-temporal.
 //
@@ -124,6 +129,15 @@ template <int V> __global__ __launch_bounds__(256) void inplace4(char *x, char *
 
 __global__ __launch_bounds__(256) void empty_kernel() {}
 
+// waits `ticks` of the constant-rate wall clock (every wave of the one
+// workgroup leaves when the clock has moved that far)
+__global__ __launch_bounds__(64) void spin_kernel(uint64_t ticks)
+{
+    const uint64_t t0 = wall_clock64();
+    while (wall_clock64() - t0 < ticks)
+        __builtin_amdgcn_s_sleep(8);
+}
+
 template <typename Kernel, typename... Args>
 int go(Kernel k, unsigned groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1, Args... args)
 {
@@ -211,6 +225,23 @@ int ksref_inplace4(void *x, void *r, uint64_t bytes, int pieces, hipStream_t s, 
 int ksref_empty(unsigned groups, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
     return groups == 0 ? 1 : go(empty_kernel, groups, s, e0, e1);
+}
+
+int ksref_spin(unsigned microseconds, hipStream_t s)
+{
+    if (microseconds == 0 || microseconds > 100000)
+        return 1;
+    int dev = 0, khz = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (err != hipSuccess)
+        return (int)err;
+    if (khz <= 0)
+        return 1;
+    const uint64_t ticks = (uint64_t)microseconds * (uint64_t)khz / 1000u;
+    hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(64), 0, s, ticks);
+    return (int)hipGetLastError();
 }
 
 }  // extern "C"

@@ -166,7 +166,8 @@ EXPECTED = {
     ("rms_norm", torch.float16, 4096, 2048): (0, 64, 8, 4, 0),
     ("fused_add_rms_norm", torch.bfloat16, 1536, 4): (0, 256, 1, 1, 0),  # decode 4x1536
     ("fused_add_rms_norm", torch.bfloat16, 8192, 1): (0, 512, 2, 1, 0),  # decode 1x8192
-    ("fused_add_rms_norm", torch.bfloat16, 8192, 32768): (0, 512, 2, 1, 1),   # prefill 32768x8192
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 32768): (0, 1024, 1, 1, 1),  # prefill 32768x8192: 1024 pieces fill a team
+    ("fused_add_rms_norm", torch.bfloat16, 6144, 43690): (0, 512, 2, 1, 1),   # 768 pieces: the 512-lane rule
     ("fused_add_rms_norm", torch.bfloat16, 16384, 8192): (0, 1024, 2, 1, 1),  # 4M+ pieces: up to 1024 lanes
     ("fused_add_rms_norm", torch.bfloat16, 4096, 8192): (0, 256, 2, 1, 1),
     ("rms_norm_residual", torch.bfloat16, 4096, 2048): (0, 64, 8, 4, 0),      # never stages the weight
@@ -182,6 +183,48 @@ EXPECTED = {
     ("rms_norm_residual", torch.bfloat16, 57344, 4): (0, 1024, 8, 1, 0),  # 7 pieces per lane would spill: 8
     ("rms_norm", torch.bfloat16, 65544, 4): (1, 1024, 0, 1, 0),          # wider: generic 16-byte path
 }
+
+
+def test_policy_scales_with_compute_units():
+    """The batch-size thresholds are per compute unit: a whole MI355X (256) gives
+    the table above; a partitioned device with fewer compute units reaches the
+    same decisions at proportionally smaller batches."""
+    for key, want in EXPECTED.items():
+        op, dtype, hidden, rows = key
+        p = ks.get_plan(op, dtype, hidden, rows, compute_units=256).as_dict()
+        assert (p["path"], p["threads_per_row"], p["vectors_per_thread"], p["rows_per_block"],
+                p["weight_lds"]) == want
+    bf = torch.bfloat16
+    # 2048x4096 bf16 (1M pieces): 8 pieces per lane on 256 compute units; on 32
+    # it is a large batch (16384 pieces per compute unit), so at most 4 per lane
+    assert ks.get_plan("rms_norm", bf, 4096, 2048, compute_units=256).as_dict()["vectors_per_thread"] == 8
+    p32 = ks.get_plan("rms_norm", bf, 4096, 2048, compute_units=32).as_dict()
+    assert (p32["threads_per_row"], p32["vectors_per_thread"]) == (128, 4)
+    # 512x4096 (256K pieces): 2 per lane on 256 compute units (131072 lanes); 8 on 32 (16384 lanes)
+    assert ks.get_plan("rms_norm", bf, 4096, 512, compute_units=256).as_dict()["vectors_per_thread"] == 2
+    assert ks.get_plan("rms_norm", bf, 4096, 512, compute_units=32).as_dict()["vectors_per_thread"] == 8
+    # LDS weight staging of the fused form from 1024 pieces per compute unit
+    assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=256).as_dict()["weight_lds"] == 0
+    assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=32).as_dict()["weight_lds"] == 1
+    # split softmax: rows of 4096..5119 pieces split in batches of up to 4 rows on
+    # 256 compute units and of 1 row on 32 (thresholds rounded up)
+    for cus, rows, split in ((256, 4, True), (256, 5, False), (32, 1, True), (32, 2, False), (512, 8, True),
+                             (512, 9, False)):
+        p = ks.get_plan("softmax", bf, 32768, rows, workspace=True, compute_units=cus).as_dict()
+        assert (p["path"] == b.KS_PATH_SPLIT) == split, (cus, rows, p)
+    # every plan on any compute-unit count is one the library accepts
+    for cus in (1, 8, 32, 38, 64, 80, 256, 304, 1024, 4096):
+        for op in ("rms_norm", "fused_add_rms_norm", "rms_norm_residual", "softmax", "silu_and_mul"):
+            for hidden, rows in ((1024, 1), (4096, 512), (4096, 2048), (8192, 32768), (16384, 8192), (65536, 4)):
+                p = ks.get_plan(op, bf, hidden, rows, compute_units=cus, workspace=op == "softmax")
+                assert p.threads_per_row * max(p.vectors_per_thread, 1) * 8 >= hidden or p.path != 0
+    # bad counts
+    for bad in (0, -1, 4097):
+        with pytest.raises(ks.KsValueError):
+            ks.get_plan("rms_norm", bf, 4096, 2048, compute_units=bad)
+    # no device here: ks_get_plan assumes a whole MI355X
+    assert ks.get_plan("rms_norm", bf, 4096, 2048).as_dict() == \
+        ks.get_plan("rms_norm", bf, 4096, 2048, compute_units=256).as_dict()
 
 
 @pytest.mark.parametrize("key", list(EXPECTED), ids=[f"{k[0]}-{k[1]}-{k[2]}x{k[3]}" for k in EXPECTED])
@@ -602,13 +645,20 @@ def test_residual_statuses_and_overlaps():
 
 
 def test_residual_plans_follow_the_fused_rule():
-    """Same shapes as the in-place form, without LDS weight staging."""
+    """Same shapes as the in-place form, without LDS weight staging (and without
+    the in-place form's whole-team rule for rows of a multiple of 1024 pieces in
+    large batches, which was measured for the in-place form only)."""
     for hidden in (8, 1000, 1024, 4096, 8192, 16384, 32768, 32769, 70000):
         for rows in (1, 64, 2048, 65536):
             for aligned in (True, False):
                 p = ks.get_plan("rms_norm_residual", torch.bfloat16, hidden, rows, aligned).as_dict()
                 q = ks.get_plan("fused_add_rms_norm", torch.bfloat16, hidden, rows, aligned).as_dict()
-                assert p == {**q, "weight_lds": 0}
+                nvec = hidden * 2 // 16
+                if aligned and rows * nvec >= 1 << 22 and nvec % 1024 == 0 and nvec // 1024 <= 2:
+                    assert (q["threads_per_row"], q["vectors_per_thread"]) == (1024, nvec // 1024)
+                    assert p["threads_per_row"] * p["vectors_per_thread"] >= nvec
+                else:
+                    assert p == {**q, "weight_lds": 0}
                 base = A if aligned else A + 2
                 assert resid(base + 768 * MB, base, base + 256 * MB, base + 512 * MB, 0, hidden,
                              plan=b.Plan.from_dict(p)) == OK

@@ -112,7 +112,8 @@ def test_sweep_set_adds_dtype_variants_once():
 def test_streamref_library_exports_and_rejects_bad_sizes():
     """The reference streams check sizes before any launch (no GPU needed)."""
     ref = bench.StreamRef()
-    for name in ("ksref_read", "ksref_write", "ksref_copy", "ksref_copy_rows", "ksref_inplace4", "ksref_empty"):
+    for name in ("ksref_read", "ksref_write", "ksref_copy", "ksref_copy_rows", "ksref_inplace4", "ksref_empty",
+                 "ksref_spin"):
         assert hasattr(ref.h, name)
     a, b = 0x10000000, 0x20000000
     assert ref.h.ksref_copy(a, b, 4095, 0, None, None, None) == 1          # not a whole 4 KiB block
@@ -124,6 +125,7 @@ def test_streamref_library_exports_and_rejects_bad_sizes():
     assert ref.h.ksref_copy_rows(a, b, 8192, 3, None, None, None) == 1
     assert ref.h.ksref_inplace4(a, b, 4096 * 8 + 4096, 8, None, None, None) == 1
     assert ref.h.ksref_empty(0, None, None, None) == 1
+    assert ref.h.ksref_spin(0, None) == 1 and ref.h.ksref_spin(100001, None) == 1
 
 
 def test_streams_table_is_consistent():
