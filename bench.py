@@ -831,10 +831,12 @@ def kernel_op(name: str) -> str | None:
     return None
 
 
-def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str) -> None:
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                    out: str | None = None) -> None:
     """Counter-derived HBM bytes per launch of each kernel of one workload,
-    scaled so that the calibration copy reads and writes exactly its own size.
-    Entries of other workloads taken on the same kernel sources are kept."""
+    scaled so that the calibration copy reads and writes exactly its own size,
+    into profiles/hbm_traffic.json (entries of other workloads taken on the
+    same kernel sources are kept); with `out`, also a markdown summary there."""
     fetch = _per_kernel_kib(fetch_dir, "FETCH_SIZE")
     write = _per_kernel_kib(write_dir, "WRITE_SIZE")
     cf = _per_kernel_kib(copy_fetch_dir, "FETCH_SIZE")
@@ -883,6 +885,54 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
         json.dump(data, f, indent=1)
     print(json.dumps({"workload": workload, "calibration": data["calibration"][workload], "kernels": kernels},
                      indent=1))
+    if out:
+        with open(out, "w") as f:
+            f.write(traffic_markdown(wl, data["calibration"][workload], kernels, data["kernel_source_hash"],
+                                     (fetch_dir, write_dir, copy_fetch_dir, copy_write_dir)))
+
+
+def traffic_markdown(wl, cal: dict, kernels: dict, source_hash: str, dirs: tuple) -> str:
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    run = f"python3 $REPO/bench.py --workload {wl.name} --no-cpu-baseline --steps 64 --warmup 2"
+    L = [f"# HBM traffic from counters: {' + '.join(wl.ops)}, {wl.dtype} [{wl.rows},{wl.hidden}]", "",
+         f"Workload `{wl.name}`: {wl.describe()}.", "",
+         "Four `rocprofv3 --pmc` passes, one counter each (from /tmp with TMPDIR=/tmp), and the summary:", "", "```",
+         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{fetch_dir} -o fetch -- {run}",
+         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{write_dir} -o write -- {run}",
+         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/{cfetch_dir} -o cfetch -- python3 $REPO/bench.py "
+         "--copy-calibration 256",
+         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/{cwrite_dir} -o cwrite -- python3 $REPO/bench.py "
+         "--copy-calibration 256",
+         f"python bench.py --workload {wl.name} --traffic-summary {fetch_dir} {write_dir} {cfetch_dir} {cwrite_dir} "
+         "--out <this file>",
+         "```", "",
+         f"Calibration: a plain device-to-device copy of {cal['copy_bytes'] >> 20} MiB (`__amd_rocclr_copyBuffer`) "
+         f"reads FETCH_SIZE = {cal['copy_bytes'] / 1024 / cal['fetch_scale']:.0f} KiB and WRITE_SIZE = "
+         f"{cal['copy_bytes'] / 1024 / cal['write_scale']:.0f} KiB per dispatch, so FETCH_SIZE is scaled by "
+         f"{cal['fetch_scale']} and WRITE_SIZE by {cal['write_scale']}.", "",
+         "Per launch (median over the profiled dispatches), scaled:", "",
+         "| Kernel | Dispatches | Fetch bytes | Write bytes | Traffic bytes | Algorithmic bytes | Traffic / algorithmic |",
+         "|---|---|---|---|---|---|---|"]
+    for name, k in kernels.items():
+        L.append(f"| `{name}` | {k['dispatches']} | {k['fetch_bytes']} | {k['write_bytes']} | {k['traffic_bytes']} | "
+                 f"{k['algorithmic_bytes']} | {k['traffic_over_algorithmic']} |")
+    models = {"silu_and_mul": "silu_and_mul reads the [R, 2D] input once and writes the [R, D] output, 3 R D elements.",
+              "rms_norm_backward": "rms_norm_backward reads x and dy and writes dx, reads the weight and writes its "
+                                   "gradient, (3 R H + 2 H) elements; each kernel's row compares its own traffic with "
+                                   "the whole op's algorithmic bytes, and the op's traffic is the sum over its two "
+                                   "kernels (the row kernel also writes fp32 partial sums of dw, one row per "
+                                   "workgroup, which the dw kernel reads back).",
+              "rms_norm_residual": "rms_norm_residual reads x and residual and writes out, (3 R H + H) elements "
+                                   "with the weight.",
+              "softmax": "softmax reads the [R, H] input once and writes the [R, H] output, 2 R H elements."}
+    model = next((v for k, v in models.items() if k in wl.ops),
+                 "rms_norm reads x and writes out, (2 R H + H) elements; the fused form reads x and residual and "
+                 "writes both, (4 R H + H) elements.")
+    L += ["", "Algorithmic bytes: " + model, "",
+          f"`profiles/hbm_traffic.json` holds these figures with the hash of the kernel sources they were taken on "
+          f"(`{source_hash}`, comments and whitespace removed); bench.py reports them as `roofline.traffic` only "
+          "while the sources still hash the same."]
+    return "\n".join(L) + "\n"
 
 
 # ---------------------------------------------------------------------------
@@ -1100,7 +1150,7 @@ def main() -> None:
             print(text, end="")
         return
     if args.traffic_summary:
-        traffic_summary(args.workload, *args.traffic_summary)
+        traffic_summary(args.workload, *args.traffic_summary, out=args.out)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
