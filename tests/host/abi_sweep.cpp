@@ -5,7 +5,10 @@
 //   * every status is one of ks_status_t;
 //   * a call that succeeds with rows > 0 reaches exactly one launch (the
 //     backward: one launch call), a failing or empty call reaches none;
-//   * the plan ks_get_plan returns is accepted by the matching _ex call;
+//   * the plan ks_get_plan returns is accepted by the matching _ex call, and
+//     so is the plan ks_get_plan_cus returns for any compute-unit count (and
+//     it reaches one launch of a compiled shape);
+//   * a timing request (ks_time_next_call) is accepted before any call;
 //   * a split softmax launch carries a workspace (checked by the stand-in).
 #include <math.h>
 #include <stdint.h>
@@ -35,7 +38,7 @@ static const uintptr_t kGiB = 1ull << 30;
 
 static void expect_status(ks_status_t st, long before, int64_t rows)
 {
-    CHECK(st >= KS_SUCCESS && st <= KS_ERROR_HIP);
+    CHECK(st >= KS_SUCCESS && st <= KS_ERROR_SCRATCH_LIMIT);
     const long launched = ks::g_launches - before;
     if (st == KS_SUCCESS && rows > 0)
         CHECK(launched == 1);
@@ -170,6 +173,59 @@ int main()
                                                                at(8 * kGiB), need, &p, 0), before, 4);
                             }
                         }
+    // the policy on devices of other compute-unit counts: every plan is a
+    // compiled shape its own _ex call accepts, and it launches once
+    for (int cus : {1, 2, 7, 32, 38, 80, 128, 256, 304, 1024, 4096})
+        for (int op : ops)
+            for (int dt = 0; dt < 3; ++dt)
+                for (int64_t hidden : {1ll, 8ll, 100ll, 1024ll, 1536ll, 4096ll, 8192ll, 16384ll, 32768ll, 65536ll})
+                    for (int64_t rows : {1ll, 4ll, 512ll, 2048ll, 32768ll})
+                        for (int flags = 0; flags < 4; ++flags) {
+                            ks_plan_t p;
+                            CHECK(ks_get_plan_cus((ks_op_t)op, (ks_dtype_t)dt, rows, hidden, flags, cus, &p) ==
+                                  KS_SUCCESS);
+                            // buffers 64 GiB apart: the largest case here (32768 rows of 65536 fp32) is 8 GiB
+                            const uintptr_t a = (flags & KS_PLAN_ALIGNED) ? 0 : 2;
+                            void *o = at(a), *x = at(64 * kGiB + a), *r = at(128 * kGiB + a), *w = at(192 * kGiB + a);
+                            const ks_dtype_t d = (ks_dtype_t)dt;
+                            const long before = ks::g_launches;
+                            ks_status_t st = KS_ERROR_HIP;
+                            size_t need = 0;
+                            switch (op) {
+                            case KS_OP_RMS_NORM: st = ks_rms_norm_ex(o, x, w, rows, hidden, 1e-6f, d, &p, 0); break;
+                            case KS_OP_FUSED_ADD_RMS_NORM:
+                                st = ks_fused_add_rms_norm_ex(x, r, w, rows, hidden, 1e-6f, d, &p, 0);
+                                break;
+                            case KS_OP_SILU_AND_MUL: st = ks_silu_and_mul_ex(o, x, rows, hidden, d, &p, 0); break;
+                            case KS_OP_SOFTMAX:
+                                CHECK(ks_softmax_workspace_size(rows, hidden, d, &p, &need) == KS_SUCCESS);
+                                st = (flags & KS_PLAN_WORKSPACE)
+                                         ? ks_softmax_ws_ex(o, x, rows, hidden, d, at(256 * kGiB), need, &p, 0)
+                                         : ks_softmax_ex(o, x, rows, hidden, d, &p, 0);
+                                break;
+                            case KS_OP_RMS_NORM_RESIDUAL:
+                                st = ks_rms_norm_residual_ex(o, x, r, w, rows, hidden, 1e-6f, d, &p, 0);
+                                break;
+                            default:
+                                st = ks_rms_norm_backward_ex(o, nullptr, r, x, w, rows, hidden, 1e-6f, d, nullptr, 0,
+                                                             &p, 0);
+                                break;
+                            }
+                            CHECK(st == KS_SUCCESS);
+                            CHECK(ks::g_launches - before == 1);
+                        }
+    for (int cus : {-1, 0, 4097}) {
+        ks_plan_t p;
+        CHECK(ks_get_plan_cus(KS_OP_RMS_NORM, KS_DTYPE_BFLOAT16, 4, 4096, 1, cus, &p) == KS_ERROR_INVALID_VALUE);
+    }
+    // a timing request is accepted and spent by the next call, launched or rejected
+    CHECK(ks_time_next_call(nullptr, nullptr) == KS_SUCCESS);
+    CHECK(ks_rms_norm(at(0), at(4 * kGiB), at(12 * kGiB), 4, 0, 1e-6f, KS_DTYPE_BFLOAT16, 0) == KS_ERROR_INVALID_VALUE);
+    {
+        const long before = ks::g_launches;
+        CHECK(ks_rms_norm(at(0), at(4 * kGiB), at(12 * kGiB), 4, 4096, 1e-6f, KS_DTYPE_BFLOAT16, 0) == KS_SUCCESS);
+        CHECK(ks::g_launches - before == 1);
+    }
     for (int op = -2; op < 8; ++op) {
         ks_plan_t p;
         const ks_status_t st = ks_get_plan((ks_op_t)op, KS_DTYPE_BFLOAT16, 4, 4096, 1, &p);
