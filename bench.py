@@ -117,6 +117,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--workload", default="C3b", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--dtype", default=None, choices=sorted(workloads.DTYPE_TAGS),
                     help="run the workload's shape, distributions and seeds in this dtype instead")
+    ap.add_argument("--op", default=None,
+                    help="measure only this op of the workload (e.g. rms_norm of C3b); it is then the whole step")
     ap.add_argument("--sweep-dtypes", default="bf16,fp16,fp32",
                     help="with --sweep-workloads: the dtypes the RMSNorm workloads C1, C2 and C3b also run in")
     ap.add_argument("--stream-reference", action="store_true",
@@ -1183,6 +1185,10 @@ def main() -> None:
     wl = workloads.WORKLOADS[args.workload]
     if args.dtype:
         wl = workloads.with_dtype(wl, args.dtype)
+    if args.op:
+        if args.op not in wl.ops:
+            fail(f"workload {wl.name} has no op {args.op} (its ops: {', '.join(wl.ops)})", 2)
+        wl = workloads.with_ops(wl, (args.op,))
     log("generating inputs", wl.describe())
     inp = workloads.make_inputs(wl)
     try:

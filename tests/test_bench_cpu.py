@@ -151,3 +151,16 @@ def test_trace_summary_renders_a_kernel_trace(tmp_path):
     assert "| fused_add_rms_norm | 67117056 | 11.020 | 11.020 |" in text
     assert "| rms_norm | 33562624 | 6.000 | 6.000 |" in text
     assert "[grid 1048576]" in text and "[grid 67108864]" in text
+
+
+def test_op_and_dtype_variants_keep_inputs():
+    c3b = bench.workloads.WORKLOADS["C3b"]
+    v = bench.workloads.with_ops(c3b, ("rms_norm",))
+    assert v.ops == ("rms_norm",) and v.name == "C3b/rms_norm"
+    assert (v.seed_x, v.seed_w, v.rows, v.hidden, v.dtype) == (c3b.seed_x, c3b.seed_w, c3b.rows, c3b.hidden, c3b.dtype)
+    assert bench.workloads.with_ops(c3b, c3b.ops) is c3b
+    with pytest.raises(ValueError):
+        bench.workloads.with_ops(c3b, ("softmax",))
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--op", "softmax"], capture_output=True,
+                         text=True, cwd=ROOT)
+    assert res.returncode != 0

@@ -163,6 +163,16 @@ def with_dtype(wl: Workload, dtype: str) -> Workload:
     return replace(wl, name=f"{wl.name}-{tag}", dtype=dtype)
 
 
+def with_ops(wl: Workload, ops: tuple[str, ...]) -> Workload:
+    """The same workload restricted to some of its ops (same inputs and seeds);
+    named e.g. ``C3b/rms_norm``."""
+    if not set(ops) <= set(wl.ops) or not ops:
+        raise ValueError(f"{wl.name} has ops {wl.ops}, not {ops}")
+    if tuple(ops) == wl.ops:
+        return wl
+    return replace(wl, name=f"{wl.name}/{'+'.join(ops)}", ops=tuple(ops))
+
+
 def _to_dtype(values: np.ndarray, dtype: torch.dtype, shape: tuple[int, ...]) -> torch.Tensor:
     return torch.from_numpy(values).reshape(shape).to(dtype)
 
