@@ -64,3 +64,38 @@ def test_noalloc_matches_workspace_entry(first, second):
         check_normalised(got, oracle.softmax(x), 0.999 if x.numel() >= 20000 else None)
     assert needs[0] > 0 and needs[1] < needs[0]
 
+
+
+def test_noalloc_under_graph_capture():
+    """The use it exists for: captured into a HIP graph (no allocation inside the
+    capture), replayed several times with eager calls and synchronisations in
+    between; every replay gives the eager result bit for bit."""
+    x = workloads.random_case((4, 65536), "float16", 37)["x"].cuda()
+    rows, hidden = x.shape
+    code = ks.KS_DTYPE[x.dtype]
+    assert b.ks_softmax_workspace_size(rows, hidden, code) > 0          # a split plan: the array is used
+    stream = torch.cuda.Stream()
+    want = torch.empty_like(x)
+    with torch.cuda.stream(stream):
+        assert b.ks_softmax_noalloc(want.data_ptr(), x.data_ptr(), rows, hidden, code, stream.cuda_stream) == 0
+    stream.synchronize()
+    out = torch.full_like(x, float("nan"))
+    other_in = workloads.random_case((2, 32768), "bfloat16", 38)["x"].cuda()
+    other_out = torch.empty_like(other_in)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            st = b.ks_softmax_noalloc(out.data_ptr(), x.data_ptr(), rows, hidden, code, stream.cuda_stream)
+    assert st == 0
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("noalloc graph replay", rep)
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+        # eager work on the same array between replays (another shape, another dtype)
+        assert b.ks_softmax_noalloc(other_out.data_ptr(), other_in.data_ptr(), 2, 32768, ks.KS_DTYPE[other_in.dtype],
+                                    torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+    check_normalised(out.cpu(), oracle.softmax(x.cpu()), 0.999)
