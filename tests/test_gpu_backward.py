@@ -183,3 +183,28 @@ def test_autograd_wrapper(dtype):
     mdx, mdw = magnitudes(dy, inp["x"], inp["weight"], 1e-6)
     check_gradient(x.grad.cpu(), rx, mdx)
     check_gradient(w.grad.cpu(), rw, mdw)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(2048, 4096), (300, 4096), (5, 1024), (700, 8)], ids=lambda s: "x".join(map(str, s)))
+def test_workspace_alignment(shape, dtype):
+    """A workspace only 4-byte aligned (4 bytes into an allocation) gives the
+    gradients a 256-byte-aligned one gives, bit for bit, both within the bar,
+    and every call the same."""
+    inp = workloads.random_case(shape, dtype, seed=shape[0] + shape[1] + 23, residual=workloads.normal(0, 1))
+    dy, x, w = (inp[k].cuda() for k in ("residual", "x", "weight"))
+    need = ks.ks_rms_norm_backward_workspace_size(*shape)
+    buf = torch.empty(need + 16, dtype=torch.uint8, device="cuda")
+    rx, rw = oracle.rms_norm_backward(inp["residual"], inp["x"], inp["weight"], 1e-5)
+    mdx, mdw = magnitudes(inp["residual"], inp["x"], inp["weight"], 1e-5)
+    outs = []
+    for off in (0, 4, 0, 4):
+        say("backward workspace", shape, dtype, "offset", off)
+        gx, gw = ks.rms_norm_backward(dy, x, w, 1e-5, workspace=buf[off:off + need])
+        torch.cuda.synchronize()
+        outs.append((gx.cpu(), gw.cpu()))
+    check_gradient(outs[0][0], rx, mdx, 0.99 if outs[0][0].numel() >= 20000 else None)
+    check_gradient(outs[0][1], rw, mdw)
+    for gx, gw in outs[1:]:
+        check_bitexact(gx, outs[0][0])
+        check_bitexact(gw, outs[0][1])
