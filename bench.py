@@ -4,6 +4,7 @@ default workload), and the SwiGLU (S*) and softmax (X*) workloads.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3b] [--dtype bf16|fp16|fp32]
     python bench.py --sweep-workloads [--out FILE]      # every workload, one table
     python bench.py --stream-reference                  # reference streams at 16 MiB and 1 GiB
+    python bench.py --wave-timeline                     # per-wave clock stamps of the row layouts at 16 MiB
 
 One step is one pass of the whole path over one batch: ks_rms_norm on the
 batch, then ks_fused_add_rms_norm on it (both at 2048 x 4096 bf16 by
@@ -123,14 +124,17 @@ def parse() -> argparse.Namespace:
                     help="with --sweep-workloads: the dtypes the RMSNorm workloads C1, C2 and C3b also run in")
     ap.add_argument("--stream-reference", action="store_true",
                     help="time the reference streams (reads, writes, copies) at 16 MiB and 1 GiB and exit")
+    ap.add_argument("--wave-timeline", action="store_true",
+                    help="record per-wave clock stamps of the row layouts at 16 MiB (rms_norm's and the fused "
+                         "form's streams) and print a markdown summary (--out, --json-out) and exit")
     ap.add_argument("--rotate-mib", type=int, default=1024, help="total size of the rotating input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep-workloads", action="store_true",
                     help="measure every workload (per op) and print a markdown table instead of the bench line")
     ap.add_argument("--out", default=None,
-                    help="with --sweep-workloads: also write the table to this file; with --trace-summary: write "
-                         "the summary there")
+                    help="with --sweep-workloads: also write the table to this file; with --trace-summary or "
+                         "--wave-timeline: write the summary there")
     ap.add_argument("--json-out", default=None, help="also write the per-case results (JSON) to this file")
     ap.add_argument("--baseline", default=None,
                     help="a previous --json-out file: exit with status 2 if any matching case got slower "
@@ -530,6 +534,8 @@ class StreamRef:
         h.ksref_inplace4.argtypes = [vp, vp, u64, ci, vp, vp, vp]
         h.ksref_empty.argtypes = [cu, vp, vp, vp]
         h.ksref_spin.argtypes = [cu, vp]
+        h.ksref_timeline.argtypes = [vp, vp, u64, ci, ci, vp, u64, vp, vp, vp]
+        h.ksref_wall_clock_khz.argtypes = [ctypes.POINTER(ci)]
         self.h = h
 
     @staticmethod
@@ -671,6 +677,156 @@ def stream_reference_table(hip: Hip) -> None:
             log(lines[-1])
     print("\n".join(lines), flush=True)
     return {"empty_kernel": floor, "cases": cases}
+
+
+TIMELINE_BYTES = 16 << 20       # one 2048 x 4096 bf16 tensor
+TIMELINE_CALLS = 64
+TIMELINE_STAMPS = ("start", "first", "loaded", "scaled", "issued", "acked", "hw_id", "xcc_id")
+# (layout, store policy, name, what it is, histogram in the summary); the
+# kernels' own stores are non-temporal (policy 1)
+TIMELINE_LAYOUTS = (
+    (2, 0, "stamps only", "no loads or stores: the launch and the waves alone", False),
+    (0, 1, "rows 8", "rms_norm's layout: read x, write y, non-temporal stores", True),
+    (0, 2, "rows 8 sc0 sc1", "the same with stores written through (system scope)", False),
+    (1, 1, "in place x+r 8", "the fused form's: read x and r, write both in place, non-temporal stores", True),
+    (1, 2, "in place x+r 8 sc0 sc1", "the same with stores written through", False),
+)
+
+
+def timeline_call_stats(st: np.ndarray, tick_us: float, event_us: float) -> dict:
+    """One call's wave records (waves x 8 words) reduced to where its time went:
+    offsets from the first wave's start, per-wave phase lengths, residency."""
+    t0, tf, t1, t2, t3, t4 = (st[:, k].astype(np.int64) for k in range(6))
+    base = t0.min()
+    us = lambda v: v.astype(np.float64) * tick_us  # noqa: E731
+    load, reduce_, issue, ack = us(t1 - t0), us(t2 - t1), us(t3 - t2), us(t4 - t3)
+    span = float(us(t4.max() - base))
+    edges = np.concatenate([t0, t4])
+    order = np.argsort(edges, kind="stable")
+    alive = np.cumsum(np.where(order < len(t0), 1, -1))
+    return {
+        "event_us": event_us, "span_us": span, "outside_waves_us": event_us - span,
+        "start_ramp_us": float(us(t0.max() - base)),
+        "first_data_us": float(us(tf.min() - base)), "first_data_p50_us": float(np.median(us(tf - base))),
+        "first_loaded_us": float(us(t1.min() - base)), "last_loaded_us": float(us(t1.max() - base)),
+        "first_issued_us": float(us(t3.min() - base)), "last_issued_us": float(us(t3.max() - base)),
+        "last_acked_us": span,
+        "first_load_p50_us": float(np.median(us(tf - t0))), "load_p50_us": float(np.median(load)), "load_p90_us": float(np.quantile(load, 0.9)),
+        "load_max_us": float(load.max()), "reduce_p50_us": float(np.median(reduce_)),
+        "issue_p50_us": float(np.median(issue)), "ack_p50_us": float(np.median(ack)),
+        "ack_max_us": float(ack.max()), "max_resident_waves": int(alive.max()),
+    }
+
+
+def timeline_histogram(st: np.ndarray, tick_us: float, bucket_us: float = 0.5) -> list[dict]:
+    """Waves that started, had their loads arrive, issued their last store and
+    had their stores acknowledged in each bucket of time from the first start."""
+    base = st[:, 0].astype(np.int64).min()
+    rel = (st[:, :6].astype(np.int64) - base) * tick_us
+    nb = int(rel.max() // bucket_us) + 1
+    rows = []
+    for b in range(nb):
+        lo, hi = b * bucket_us, (b + 1) * bucket_us
+        n = lambda k: int(((rel[:, k] >= lo) & (rel[:, k] < hi)).sum())  # noqa: E731
+        rows.append({"from_us": lo, "started": n(0), "first": n(1), "loaded": n(2), "issued": n(4), "acked": n(5)})
+    return rows
+
+
+def wave_timeline(hip: Hip) -> dict:
+    """ksref_timeline over rotating 16 MiB buffers (1 GiB in the rotation, every
+    call cold), TIMELINE_CALLS calls back to back behind a head-start spin, each
+    also timed by its kernel-dispatch events; per layout the medians over calls
+    of each call's statistics, the spread of the dispatch events, the waves per
+    XCD and compute unit, and the histogram of the median call."""
+    ref = StreamRef()
+    khz = ctypes.c_int(0)
+    StreamRef.check(ref.h.ksref_wall_clock_khz(ctypes.byref(khz)), "ksref_wall_clock_khz")
+    if khz.value <= 0:
+        raise RuntimeError("the device reports no wall clock rate")
+    tick_us = 1e3 / khz.value
+    nbytes, calls = TIMELINE_BYTES, TIMELINE_CALLS
+    waves = nbytes // 8192
+    nsets = GIB // nbytes
+    stream = torch.cuda.Stream()
+    out = {"bytes_per_tensor": nbytes, "waves": waves, "calls": calls, "wall_clock_khz": khz.value, "layouts": []}
+    for layout, policy, name, what, hist in TIMELINE_LAYOUTS:
+        bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255),
+                 torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)) for _ in range(nsets)]
+        stamps = torch.zeros(calls, waves, len(TIMELINE_STAMPS), dtype=torch.int64, device="cuda")
+
+        def call(i: int, e0=None, e1=None) -> None:
+            x, y = bufs[i % nsets]
+            row = stamps[i % calls]
+            StreamRef.check(ref.h.ksref_timeline(x.data_ptr(), y.data_ptr(), nbytes, layout, policy, row.data_ptr(),
+                                                 row.numel() * row.element_size(), stream.cuda_stream, e0, e1),
+                            "ksref_timeline")
+
+        for i in range(2 * nsets):
+            call(i)
+        torch.cuda.synchronize()
+        ev = kernel_durations(hip, None, calls, stream, timed_call=lambda i, a, b: call(i, a, b))
+        st = stamps.cpu().numpy()
+        per_call = [timeline_call_stats(st[c], tick_us, ev[c]) for c in range(calls)]
+        med = {k: round(float(np.median([p[k] for p in per_call])), 3) for k in per_call[0]}
+        mid = int(np.argsort([p["event_us"] for p in per_call])[calls // 2])
+        hw = st[:, :, 6].astype(np.int64)
+        cu_key = (st[:, :, 7].astype(np.int64) << 16) | (((hw >> 13) & 7) << 8) | (((hw >> 12) & 1) << 4) | ((hw >> 8) & 15)
+        xcc = st[mid, :, 7].astype(np.int64)
+        start_by_xcc = {int(x): round(float(np.median((st[mid, xcc == x, 0] - st[mid, :, 0].min()) * tick_us)), 3)
+                        for x in np.unique(xcc)}
+        out["layouts"].append({
+            "stream": name, "what": what, "bytes_moved": {0: 2, 1: 4, 2: 0}[layout] * nbytes,
+            "event_us": distribution(ev), "median": med,
+            "distinct_cus": int(len(np.unique(cu_key[mid]))), "waves_per_xcc": {int(x): int((xcc == x).sum())
+                                                                             for x in np.unique(xcc)},
+            "median_start_by_xcc_us": start_by_xcc, "median_call": mid,
+            "histogram": timeline_histogram(st[mid], tick_us) if hist else None})
+        del bufs, stamps
+        torch.cuda.empty_cache()
+    return out
+
+
+def wave_timeline_markdown(res: dict) -> str:
+    L = ["| Quantity (median over calls; µs from the first wave's start) | " +
+         " | ".join(f"{l['stream']}" for l in res["layouts"]) + " |",
+         "|---|" + "---|" * len(res["layouts"])]
+    rows = [("kernel-dispatch events (whole kernel)", "event_us"), ("waves' span: first start to last ack", "span_us"),
+            ("outside the waves (events minus span)", "outside_waves_us"),
+            ("wave starts spread over", "start_ramp_us"), ("first data back (any wave's first load)", "first_data_us"),
+            ("waves' first load back, p50", "first_data_p50_us"), ("first wave's loads all arrived", "first_loaded_us"),
+            ("last wave's loads all arrived", "last_loaded_us"), ("first wave's stores all issued", "first_issued_us"),
+            ("last wave's stores all issued", "last_issued_us"), ("last wave's stores acknowledged", "last_acked_us"),
+            ("per wave: start to first load back, p50", "first_load_p50_us"),
+            ("per wave: start to loads arrived, p50", "load_p50_us"), ("per wave: the same, p90", "load_p90_us"),
+            ("per wave: the same, max", "load_max_us"), ("per wave: sum, shuffles and rsqrt, p50", "reduce_p50_us"),
+            ("per wave: store issue, p50", "issue_p50_us"), ("per wave: issue to acknowledged, p50", "ack_p50_us"),
+            ("per wave: the same, max", "ack_max_us"), ("most waves resident at once", "max_resident_waves")]
+    for label, key in rows:
+        L.append(f"| {label} | " + " | ".join(f"{l['median'][key]}" for l in res["layouts"]) + " |")
+    L.append("| kernel-dispatch events p50 / p95 / max | " + " | ".join(
+        f"{l['event_us']['p50']} / {l['event_us']['p95']} / {l['event_us']['max']}" for l in res["layouts"]) + " |")
+    L.append("| distinct compute units (one call) | " + " | ".join(str(l["distinct_cus"]) for l in res["layouts"]) + " |")
+    L.append("| median wave start by XCD (one call) | " + " | ".join(
+        ", ".join(f"{x}: {v}" for x, v in l["median_start_by_xcc_us"].items()) for l in res["layouts"]) + " |")
+    out = ["# Wave timeline: the row kernels' layouts at 16 MiB (`bench.py --wave-timeline`)", "",
+           "Command (repository root on the GPU box):", "", "```",
+           "python bench.py --wave-timeline --out <this file> --json-out <stamps summary JSON>", "```", "",
+           "ksref_timeline (rmsnorm_row_normalisation_amd/streamref) runs the reference streams' row layouts with "
+           "lane 0 of every wave reading the device's constant-rate wall clock at the wave's start, when its first "
+           "load is back, when all its loads are back, when the row's scale is ready, when its last store has "
+           "issued and when its stores are acknowledged; the kernel-dispatch events time the whole kernel.  "
+           "Times are from the first wave's start.",
+           "", f"{res['waves']} waves of one 8 KiB row each, 16 MiB per tensor, {res['calls']} calls back to back "
+           f"(each cold: 1 GiB of buffers in the rotation); wall clock {res['wall_clock_khz']} kHz.", ""] + L
+    for l in res["layouts"]:
+        if l["histogram"] is None:
+            continue
+        out += ["", f"Waves per 0.5 µs of the median call (#{l['median_call']}), {l['stream']} ({l['what']}):", "",
+                "| from µs | started | first load back | all loads back | last store issued | stores acknowledged |",
+                "|---|---|---|---|---|---|"]
+        out += [f"| {h['from_us']:.1f} | {h['started']} | {h['first']} | {h['loaded']} | {h['issued']} | {h['acked']} |"
+                for h in l["histogram"]]
+    return "\n".join(out) + "\n"
 
 
 # ---------------------------------------------------------------------------
@@ -1177,6 +1333,17 @@ def main() -> None:
         if args.json_out:
             with open(args.json_out, "w") as f:
                 json.dump(table, f, indent=1)
+        return
+    if args.wave_timeline:
+        res = wave_timeline(hip)
+        text = wave_timeline_markdown(res)
+        print(text, end="", flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        if args.json_out:
+            with open(args.json_out, "w") as f:
+                json.dump(res, f, indent=1)
         return
     if args.sweep_workloads:
         sweep_workloads(args, ks, oracle, hip)

@@ -7,6 +7,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import bench
@@ -113,7 +114,7 @@ def test_streamref_library_exports_and_rejects_bad_sizes():
     """The reference streams check sizes before any launch (no GPU needed)."""
     ref = bench.StreamRef()
     for name in ("ksref_read", "ksref_write", "ksref_copy", "ksref_copy_rows", "ksref_inplace4", "ksref_empty",
-                 "ksref_spin"):
+                 "ksref_spin", "ksref_timeline", "ksref_wall_clock_khz"):
         assert hasattr(ref.h, name)
     a, b = 0x10000000, 0x20000000
     assert ref.h.ksref_copy(a, b, 4095, 0, None, None, None) == 1          # not a whole 4 KiB block
@@ -126,6 +127,43 @@ def test_streamref_library_exports_and_rejects_bad_sizes():
     assert ref.h.ksref_inplace4(a, b, 4096 * 8 + 4096, 8, None, None, None) == 1
     assert ref.h.ksref_empty(0, None, None, None) == 1
     assert ref.h.ksref_spin(0, None) == 1 and ref.h.ksref_spin(100001, None) == 1
+    st, need = 0x30000000, 4 * 64                                          # one 32 KiB block: 4 waves of 64 B
+    assert ref.h.ksref_timeline(a, b, 32768, 0, 1, st, need - 8, None, None, None) == 1   # stamps too small
+    assert ref.h.ksref_timeline(a, b, 32768, 0, 1, None, need, None, None, None) == 1
+    assert ref.h.ksref_timeline(a, b, 32768, 0, 1, st + 4, need, None, None, None) == 1   # not 8-byte aligned
+    assert ref.h.ksref_timeline(a, b, 32768, 3, 1, st, need, None, None, None) == 1       # unknown layout
+    assert ref.h.ksref_timeline(a, b, 32768, 1, 3, st, need, None, None, None) == 1       # unknown store policy
+    assert ref.h.ksref_timeline(a, b, 16384, 0, 1, st, need, None, None, None) == 1       # not a whole 32 KiB block
+    assert ref.h.ksref_wall_clock_khz(None) == 1
+
+
+def test_wave_timeline_statistics():
+    """Per-call statistics of the wave records, on a hand-made call: 4 waves,
+    clock ticks of 10 ns."""
+    tick_us = 0.01
+    st = np.zeros((4, 8), dtype=np.int64)
+    #          start first loaded scaled issued acked
+    st[:, :6] = [[100, 150, 200, 210, 215, 300],
+                 [110, 240, 250, 260, 262, 330],
+                 [120, 130, 220, 225, 230, 280],
+                 [130, 300, 400, 402, 404, 500]]
+    s = bench.timeline_call_stats(st, tick_us, 5.0)
+    assert s["span_us"] == pytest.approx(4.0) and s["outside_waves_us"] == pytest.approx(1.0)
+    assert s["start_ramp_us"] == pytest.approx(0.3)
+    assert s["first_data_us"] == pytest.approx(0.3) and s["first_data_p50_us"] == pytest.approx((0.5 + 1.4) / 2)
+    assert s["first_load_p50_us"] == pytest.approx((0.5 + 1.3) / 2)
+    assert s["first_loaded_us"] == pytest.approx(1.0) and s["last_loaded_us"] == pytest.approx(3.0)
+    assert s["first_issued_us"] == pytest.approx(1.15) and s["last_issued_us"] == pytest.approx(3.04)
+    assert s["load_max_us"] == pytest.approx(2.7) and s["load_p50_us"] == pytest.approx(1.2)
+    assert s["ack_p50_us"] == pytest.approx((0.68 + 0.85) / 2)
+    assert s["max_resident_waves"] == 4
+    h = bench.timeline_histogram(st, tick_us, bucket_us=1.0)
+    assert [r["started"] for r in h] == [4, 0, 0, 0, 0]
+    assert [r["first"] for r in h] == [2, 1, 1, 0, 0]
+    assert [r["loaded"] for r in h] == [0, 3, 0, 1, 0]
+    assert [r["acked"] for r in h] == [0, 1, 2, 0, 1]
+    st[3, :6] = [400, 420, 450, 451, 452, 460]     # starts after the others have finished
+    assert bench.timeline_call_stats(st, tick_us, 5.0)["max_resident_waves"] == 3
 
 
 def test_streams_table_is_consistent():
