@@ -809,7 +809,7 @@ def wave_timeline_markdown(res: dict) -> str:
     L.append("| median wave start by XCD (one call) | " + " | ".join(
         ", ".join(f"{x}: {v}" for x, v in l["median_start_by_xcc_us"].items()) for l in res["layouts"]) + " |")
     out = ["# Wave timeline: the row kernels' layouts at 16 MiB (`bench.py --wave-timeline`)", "",
-           "Command (repository root on the GPU box):", "", "```",
+           "Command (from the repository root, on an MI355X):", "", "```",
            "python bench.py --wave-timeline --out <this file> --json-out <stamps summary JSON>", "```", "",
            "ksref_timeline (rmsnorm_row_normalisation_amd/streamref) runs the reference streams' row layouts with "
            "lane 0 of every wave reading the device's constant-rate wall clock at the wave's start, when its first "
@@ -1135,7 +1135,7 @@ def trace_summary(wl, directory: str, bench_json: str | None, command: str | Non
         L = [f"# Kernel trace: {' + '.join(wl.ops)}, {wl.dtype} [{wl.rows},{wl.hidden}]", "",
              f"Workload `{wl.name}`: {wl.describe()}.", ""]
     if command:
-        L += ["Command (repository root on the GPU box; the summary is rendered from its output by "
+        L += ["Command (from the repository root, on an MI355X; the summary is rendered from its output by "
               "`python bench.py --trace-summary`):", "", "```", "cd /tmp && export TMPDIR=/tmp", command, "```", ""]
     L += ["Per-dispatch kernel durations (us, end minus start timestamp of each dispatch in the trace) and each "
           "kernel's resources:", "",
