@@ -19,7 +19,8 @@
  *            All buffers hold the same dtype.  There are no stride arguments.
  * Memory     Every pointer is a device pointer owned by the caller.  The
  *            library never allocates, frees, copies or synchronises (scratch
- *            memory, where a call needs it, is a caller-owned workspace).
+ *            memory, where a call needs it, is a caller-owned workspace, or
+ *            for ks_softmax_noalloc a static device array of the library's).
  *            weight is only read.  Any alignment is accepted; 16-byte aligned
  *            buffers with hidden * sizeof(element) a multiple of 16 take the
  *            vector path, others a narrower path with the same contract
@@ -384,7 +385,8 @@ const char *ks_status_string(ks_status_t status);
 /* hipError_t behind the calling thread's last KS_ERROR_HIP (0 if none). */
 int ks_last_hip_error(void);
 
-/* Library version string, e.g. "ks_norm 0.1.0 gfx950". */
+/* Library version string: name, version, target and the source revision it
+ * was built from, e.g. "ks_norm 0.2.0 gfx950 (source 3e7a201c0ba1)". */
 const char *ks_version(void);
 
 #ifdef __cplusplus
