@@ -1109,57 +1109,73 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
             dyo[k] = __builtin_amdgcn_raw_buffer_load_b128(rdy, off[k], 0, kNt);
     };
 
-    // Software pipeline: the next group's loads are in flight while this
-    // group is reduced and written.
-    u32x4 xv[kVpt], dv[kVpt];
-    int64_t g = blockIdx.x;
-    if (g < ngroups)
-        load_group(g, xv, dv);
-    while (g < ngroups) {
-        const int64_t gn = g + gridDim.x;
-        u32x4 xn[kVpt], dn[kVpt];
-        if (gn < ngroups)
-            load_group(gn, xn, dn);
-
-        float ps[kVpt], pc[kVpt];   // per-piece sums of x^2 and of g * x, elements in index order
+    // The two row sums of a group (per piece, elements in index order, then
+    // the canonical fold within the lane).
+    auto sums = [&](const u32x4 *xg, const u32x4 *dg, float &ss, float &dot) {
+        float ps[kVpt], pc[kVpt];
 #pragma unroll
         for (int k = 0; k < kVpt; ++k) {
             float a = 0.0f, b = 0.0f;
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
-                const float xe = Pack<T>::get(xv[k], e);
-                const float ge = Pack<T>::get(dv[k], e) * Pack<T>::get(wv[k], e);
+                const float xe = Pack<T>::get(xg[k], e);
+                const float ge = Pack<T>::get(dg[k], e) * Pack<T>::get(wv[k], e);
                 a = __builtin_fmaf(xe, xe, a);
                 b = __builtin_fmaf(ge, xe, b);
             }
             ps[k] = a;
             pc[k] = b;
         }
-        float ss = local_fold<kVpt>(ps);
-        float dot = local_fold<kVpt>(pc);
+        ss = local_fold<kVpt>(ps);
+        dot = local_fold<kVpt>(pc);
+    };
+    // The team sums, dx of the group, and its dw terms added to acc.
+    auto finish = [&](int64_t grp, const u32x4 *xg, const u32x4 *dg, float ss, float dot) {
         team_fold2<kTpr, kBlock>(ss, dot);
         const float rho = row_scale(ss, p.hidden, p.eps);
         const float c = ((dot / (float)p.hidden) * rho) * rho;
-        const auto rdx = make_rsrc((char *)p.dx + (size_t)g * kRpb * row_bytes, group_bytes(g));
+        const auto rdx = make_rsrc((char *)p.dx + (size_t)grp * kRpb * row_bytes, group_bytes(grp));
 #pragma unroll
         for (int k = 0; k < kVpt; ++k) {
             float o[kE];
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
-                const float xe = Pack<T>::get(xv[k], e);
-                const float de = Pack<T>::get(dv[k], e);
+                const float xe = Pack<T>::get(xg[k], e);
+                const float de = Pack<T>::get(dg[k], e);
                 const float ge = de * Pack<T>::get(wv[k], e);
                 o[e] = __builtin_fmaf(-c, xe, ge) * rho;
                 acc[k][e] = __builtin_fmaf(de, xe * rho, acc[k][e]);
             }
             __builtin_amdgcn_raw_buffer_store_b128(Pack<T>::put(o), rdx, off[k], 0, kNt);
         }
+    };
+
+    // Software pipeline: while a group is reduced and written, the next
+    // group's loads are in flight.  They issue only once the group's own data
+    // is back (its sums are formed), so that the memory system returns the
+    // groups in turn and a group's dx stores overlap the next group's reads;
+    // the last group issues no loads.  g is the same for the whole workgroup,
+    // so every thread reaches the barriers in team_fold2 equally often.
+    int64_t g = blockIdx.x;
+    if (g < ngroups) {
+        u32x4 xv[kVpt], dv[kVpt];
+        load_group(g, xv, dv);
+        for (int64_t gn = g + gridDim.x; gn < ngroups; g = gn, gn += gridDim.x) {
+            float ss, dot;
+            sums(xv, dv, ss, dot);
+            asm volatile("" ::"v"(ss), "v"(dot) : "memory");   // the loads below stay after the sums
+            u32x4 xn[kVpt], dn[kVpt];
+            load_group(gn, xn, dn);
+            finish(g, xv, dv, ss, dot);
 #pragma unroll
-        for (int k = 0; k < kVpt; ++k) {
-            xv[k] = xn[k];
-            dv[k] = dn[k];
+            for (int k = 0; k < kVpt; ++k) {
+                xv[k] = xn[k];
+                dv[k] = dn[k];
+            }
         }
-        g = gn;
+        float ss, dot;
+        sums(xv, dv, ss, dot);
+        finish(g, xv, dv, ss, dot);
     }
     if (p.part == nullptr)
         return;
