@@ -27,7 +27,8 @@ Timing (exactly K steps in every timed region):
   * per op, kernel duration (``per_op[op].kernel_us``, ``roofline``): K calls
     of that op on the launch stream (at most 2048), each timed by the
     runtime's kernel-dispatch events (``ks_time_next_call``), enqueued in runs
-    of 32 behind a 300 us spin kernel so that each run executes back to back:
+    of 32 behind a 1 ms spin kernel and one untimed lead call, so that each
+    run executes back to back and every timed call follows another one:
     min / p50 / p95 / p99 / max / mean of the kernels' own durations.
     ``roofline.achieved`` is the dominant kernel's algorithmic bytes over its
     mean duration;
@@ -443,7 +444,7 @@ def distribution(vals: list[float]) -> dict:
             "p95": round(q(0.95), 3), "p99": round(q(0.99), 3), "max": round(v[-1], 3)}
 
 
-HEAD_START_US = 300      # the spin kernel queued ahead of each run of timed calls
+HEAD_START_US = 1000     # the spin kernel queued ahead of each run of timed calls
 HEAD_START_CALLS = 32    # timed calls enqueued behind one spin kernel
 
 
@@ -452,10 +453,14 @@ def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_ca
     each timed by the runtime's kernel-dispatch events (from the start of the
     call's first kernel to the end of its last): microseconds.  The calls go in
     runs of HEAD_START_CALLS behind a spin kernel of HEAD_START_US, so the host
-    has enqueued a run before it starts and its calls execute back to back, as
-    they would in a steady stream of work.  `timed_call(i, start, stop)`
-    replaces the request through ks_time_next_call for callers that take the
-    events themselves."""
+    has enqueued a run before it starts (a Python enqueue takes 10-20 us per
+    call) and its calls execute back to back, as they would in a steady stream
+    of work.  Each run opens with one untimed call on the previous copy: the
+    first call after the idle spin runs slower (about 0.8 us for rms_norm at
+    2048x4096), and every timed call should follow another one as in a
+    stream.  `timed_call(i, start, stop)` replaces the request through
+    ks_time_next_call for callers that take the events themselves (start and
+    stop None: untimed)."""
     import rmsnorm_row_normalisation_amd as ks
 
     lib = ks.lib()
@@ -466,6 +471,12 @@ def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_ca
         for i, (a, b) in enumerate(evs):
             if i % HEAD_START_CALLS == 0:
                 StreamRef.check(ref.h.ksref_spin(HEAD_START_US, stream.cuda_stream), "ksref_spin")
+                if timed_call is not None:     # the untimed lead call
+                    timed_call(i - 1, None, None)
+                else:
+                    rc = call(i - 1)
+                    if rc != 0:
+                        raise RuntimeError(f"lead call failed: {lib.ks_status_string(rc).decode()}")
             if timed_call is not None:
                 timed_call(i, a, b)
             else:
