@@ -405,6 +405,8 @@ class Hip:
         self.h.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
         self.h.hipEventDestroy.argtypes = [vp]
         self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.h.hipEventRecord.argtypes = [vp, vp]
+        self.h.hipEventQuery.argtypes = [vp]
         self.h.hipRuntimeGetVersion.argtypes = [ctypes.POINTER(ci)]
         self.h.hipDriverGetVersion.argtypes = [ctypes.POINTER(ci)]
 
@@ -417,6 +419,18 @@ class Hip:
 
     def destroy(self, e: int) -> None:
         self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+    def record(self, e: int, stream: int) -> None:
+        rc = self.h.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def done(self, e: int) -> bool:
+        """Whether the stream has reached event e (hipEventQuery)."""
+        rc = self.h.hipEventQuery(ctypes.c_void_p(e))
+        if rc not in (0, 600):   # hipSuccess, hipErrorNotReady
+            raise RuntimeError(f"hipEventQuery failed ({rc})")
+        return rc == 0
 
     def elapsed_us(self, a: int, b: int) -> float:
         ms = ctypes.c_float()
@@ -444,18 +458,25 @@ def distribution(vals: list[float]) -> dict:
             "p95": round(q(0.95), 3), "p99": round(q(0.99), 3), "max": round(v[-1], 3)}
 
 
-HEAD_START_US = 1000     # the spin kernel queued ahead of each run of timed calls
+HEAD_START_US = 1000     # the first spin kernel queued ahead of a run of timed calls
+HEAD_START_MAX_US = 20000
 HEAD_START_CALLS = 32    # timed calls enqueued behind one spin kernel
 
 
-def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_call=None) -> list[float]:
+def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_call=None,
+                     info: dict | None = None) -> list[float]:
     """n calls of call(i) (a raw C entry point on `stream`, returning its status),
     each timed by the runtime's kernel-dispatch events (from the start of the
     call's first kernel to the end of its last): microseconds.  The calls go in
-    runs of HEAD_START_CALLS behind a spin kernel of HEAD_START_US, so the host
-    has enqueued a run before it starts (a Python enqueue takes 10-20 us per
-    call) and its calls execute back to back, as they would in a steady stream
-    of work.  Each run opens with one untimed call on the previous copy: the
+    runs of HEAD_START_CALLS behind a spin kernel, so the host has enqueued a
+    run before it starts and its calls execute back to back, as they would in
+    a steady stream of work.  The first spin lasts HEAD_START_US; each later
+    one at least twice the host time the previous run took to enqueue (10-20
+    us per call from Python, several times that under a tracer), up to
+    HEAD_START_MAX_US.  A run is late when its spin had already ended by the
+    time its last call was enqueued (the GPU may then have idled between
+    calls); `info`, if given, receives runs, late_runs and the last spin's
+    length.  Each run opens with one untimed call on the previous copy: the
     first call after the idle spin runs slower (about 0.8 us for rms_norm at
     2048x4096), and every timed call should follow another one as in a
     stream.  `timed_call(i, start, stop)` replaces the request through
@@ -466,17 +487,32 @@ def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_ca
     lib = ks.lib()
     ref = StreamRef()
     evs = [(hip.event(), hip.event()) for _ in range(n)]
+    marks: list[int] = []
+    spin_us, late, t_run = HEAD_START_US, 0, None
+
+    def close_run() -> None:
+        nonlocal spin_us, late
+        enqueue_us = (time.perf_counter() - t_run) * 1e6
+        if hip.done(marks[-1]):
+            late += 1
+        spin_us = min(HEAD_START_MAX_US, max(spin_us, int(2 * enqueue_us)))
+
     try:
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(evs):
             if i % HEAD_START_CALLS == 0:
-                StreamRef.check(ref.h.ksref_spin(HEAD_START_US, stream.cuda_stream), "ksref_spin")
+                if t_run is not None:
+                    close_run()
+                StreamRef.check(ref.h.ksref_spin(spin_us, stream.cuda_stream), "ksref_spin")
+                marks.append(hip.event())
+                hip.record(marks[-1], stream.cuda_stream)
                 if timed_call is not None:     # the untimed lead call
                     timed_call(i - 1, None, None)
                 else:
                     rc = call(i - 1)
                     if rc != 0:
                         raise RuntimeError(f"lead call failed: {lib.ks_status_string(rc).decode()}")
+                t_run = time.perf_counter()
             if timed_call is not None:
                 timed_call(i, a, b)
             else:
@@ -484,12 +520,18 @@ def kernel_durations(hip: Hip, call, n: int, stream: torch.cuda.Stream, timed_ca
                 rc = call(i)
                 if rc != 0:
                     raise RuntimeError(f"timed call failed: {lib.ks_status_string(rc).decode()}")
+        if t_run is not None:
+            close_run()
         torch.cuda.synchronize()
+        if info is not None:
+            info.update({"runs": len(marks), "late_runs": late, "head_start_us": spin_us})
         return [hip.elapsed_us(a, b) for a, b in evs]
     finally:
         for a, b in evs:
             hip.destroy(a)
             hip.destroy(b)
+        for e in marks:
+            hip.destroy(e)
 
 
 KERNEL_TIMED_MAX = 2048
@@ -509,7 +551,10 @@ def measure(wl, inp, ks, args, hip: Hip) -> dict:
         # launch period: median of three timed regions (run-to-run spread is a few %)
         ms = rig.timed_graph(lambda i, op=op: rig.launch(op, i), rig.nsets, steps, repeats=3)
         us = ms * 1e3 / steps
-        kus = distribution(kernel_durations(hip, rig.raw_call(op), min(steps, KERNEL_TIMED_MAX), rig.stream))
+        timing: dict = {}
+        kus = distribution(kernel_durations(hip, rig.raw_call(op), min(steps, KERNEL_TIMED_MAX), rig.stream,
+                                            info=timing))
+        kus.update(timing)
         gbps = op_bytes[op] / (kus["mean"] * 1e-6) / 1e9
         per_op[op] = {"us_per_call": round(us, 3), "kernel_us": kus, "bytes": op_bytes[op], "gbps": round(gbps, 1),
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
@@ -1136,6 +1181,40 @@ def trace_dispatches(directory: str) -> dict[str, dict]:
     return out
 
 
+def _dispatch_kind(name: str) -> str:
+    op = kernel_op(name)
+    if op is not None:
+        return op
+    for key, kind in (("spin_kernel", "spin (head start)"), ("empty_kernel", "empty (reference)"),
+                      ("copy", "copy (setup, reference)")):
+        if key in name:
+            return kind
+    return "other"
+
+
+def trace_contexts(directory: str) -> dict[str, dict]:
+    """The library's dispatches per op, grouped by the kind of dispatch that
+    ran just before on the device and by the idle gap between the two (under
+    2 us: back to back, as in a graph replay; else the host or the tracer
+    kept the device waiting): n, mean and p50 (us)."""
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows += [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(f)]
+    rows.sort()
+    groups: dict[tuple, list] = {}
+    for (_, e0, n0), (s1, e1, n1) in zip(rows, rows[1:]):
+        op = kernel_op(n1)
+        if op is None:
+            continue
+        gap = "< 2 us" if (s1 - e0) < 2000 else ">= 2 us"
+        groups.setdefault((op, _dispatch_kind(n0), gap), []).append((e1 - s1) / 1000.0)
+    return {k: {"n": len(v), "mean": float(np.mean(v)), "p50": float(np.median(v))} for k, v in sorted(groups.items())}
+
+
 def trace_summary(wl, directory: str, bench_json: str | None, command: str | None) -> str:
     """Markdown summary of a kernel trace of a bench run of workload `wl` (None:
     of a --stream-reference run)."""
@@ -1203,6 +1282,18 @@ def trace_summary(wl, directory: str, bench_json: str | None, command: str | Non
               f"{algorithmic_bytes(rf['kernel'], wl.rows, wl.hidden, esize) / per_op[rf['kernel']]['mean'] / 1e3 / HBM_PEAK_GBPS:.4f}."
               "  The tracer adds a little to each dispatch, so its durations run slightly longer than the "
               "uninstrumented ones."]
+    ctx = trace_contexts(directory)
+    if ctx:
+        L += ["", "The library's dispatches by what ran just before them on the device (a kernel of an op, the "
+              "head-start spin, the setup and reference kernels) and by the idle gap in between.  The graph "
+              "replays run back to back (gap under 2 us); the per-call timed calls follow another call of the "
+              "same op, with the gaps the tracer's own work adds; the untimed lead call of each timed run "
+              "follows the spin and reads a copy that is still in the Infinity Cache.  The trace's mean mixes "
+              "these; the bench's kernel mean is the timed calls alone:", "",
+              "| Op | after | gap | dispatches | mean us | p50 us |", "|---|---|---|---|---|---|"]
+        L += [f"| {op} | {prev} | {gap} | {v['n']} | {v['mean']:.3f} | {v['p50']:.3f} |"
+              for (op, prev, gap), v in ctx.items() if v["n"] >= 8]
+    if line is not None:
         L += ["", f"Library: {line.get('env', {}).get('library', '?')}; kernel sources hash "
               f"`{line.get('kernel_source_hash', '?')}`."]
     return "\n".join(L) + "\n"

@@ -191,6 +191,30 @@ def test_trace_summary_renders_a_kernel_trace(tmp_path):
     assert "[grid 1048576]" in text and "[grid 67108864]" in text
 
 
+def test_trace_contexts_group_by_predecessor_and_gap(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    hdr = '"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"\n'
+    r = "void ks::rms_norm_vec<ks::bf16, 64, 8, 256, 2, 2, false>(ks::Params)"
+    f = "void ks::fused_add_rms_norm_vec<ks::bf16, 64, 8, 256, 2, 2, true>(ks::Params)"
+    ev = [("spin_kernel(unsigned long)", 0, 300000),     # head start
+          (r, 300500, 305500),                          # after the spin, 0.5 us gap: 5 us
+          (r, 306000, 312000),                          # back to back: 6 us
+          (r, 312500, 318500),                          # back to back: 6 us
+          (r, 330000, 337000),                          # 11.5 us gap: 7 us
+          (f, 337500, 348500),                          # fused after rms, back to back: 11 us
+          (r, 349000, 355400)]                          # rms after fused: 6.4 us
+    rows = [f'"KERNEL_DISPATCH","{n}",{s0},{e0}\n' for n, s0, e0 in ev]
+    (d / "b_kernel_trace.csv").write_text(hdr + "".join(reversed(rows)))    # order comes from the timestamps
+    ctx = bench.trace_contexts(str(d))
+    assert ctx[("rms_norm", "spin (head start)", "< 2 us")] == {"n": 1, "mean": 5.0, "p50": 5.0}
+    assert ctx[("rms_norm", "rms_norm", "< 2 us")]["n"] == 2 and ctx[("rms_norm", "rms_norm", "< 2 us")]["mean"] == 6.0
+    assert ctx[("rms_norm", "rms_norm", ">= 2 us")]["mean"] == 7.0
+    assert ctx[("fused_add_rms_norm", "rms_norm", "< 2 us")]["mean"] == 11.0
+    assert ctx[("rms_norm", "fused_add_rms_norm", "< 2 us")]["mean"] == pytest.approx(6.4)
+    assert len(ctx) == 5
+
+
 def test_op_and_dtype_variants_keep_inputs():
     c3b = bench.workloads.WORKLOADS["C3b"]
     v = bench.workloads.with_ops(c3b, ("rms_norm",))
