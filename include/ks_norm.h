@@ -116,7 +116,8 @@ typedef enum {
 typedef struct {
     int32_t path;               /* ks_path_t */
     int32_t threads_per_row;    /* 8, 16, 32, 64, 128, 256, 512 or 1024 */
-    int32_t vectors_per_thread; /* vector path: 1..8; split path: 1, 2 or 4; generic path: 0 */
+    int32_t vectors_per_thread; /* vector path: 1..8, and 16 for RMSNorm and its residual forms
+                                   on teams of 32..128 lanes; split path: 1, 2 or 4; generic path: 0 */
     int32_t elems_per_access;   /* generic path: 1 or 16 / element size; vector path: 16 / element size */
     int32_t rows_per_block;     /* rows handled by one workgroup */
     int32_t block_threads;      /* workgroup size */

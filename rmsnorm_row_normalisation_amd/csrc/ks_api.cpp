@@ -174,6 +174,25 @@ bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, int64_t c
     return true;
 }
 
+// RMSNorm on rows of 1024..2048 pieces (16..32 KiB) in a batch that is not
+// large: 16 pieces per lane on a one- or two-wave team (64 or 128 lanes), when
+// that plan's grid comes to 1.75..2 workgroups of 4 (2) rows per compute unit.
+// There the 8-piece plan (two or four waves per row, joined through LDS and a
+// barrier) measured 10-22% slower per call (fp32 4096 and bf16 8192 wide at
+// 1792..2048 rows, fp32 8192 and bf16 16384 wide at 1024 rows); at other grids
+// the 16-piece plan ranged from 18% slower to 7% faster, and the two residual
+// forms gained 0-10% at best, so they keep the rules above.  The weight sits
+// in LDS for 16-bit dtypes (fewer VGPRs: 164 against 218), not for fp32
+// (10-19% against 0-12% faster).
+bool wide_rms_norm(ks_op_t op, int64_t rows, int64_t nvec, bool large, int64_t cus)
+{
+    if (op != KS_OP_RMS_NORM || large || nvec < 1024 || nvec > 2048)
+        return false;
+    const int64_t rows_per_group = nvec <= 1024 ? 4 : 2;
+    const int64_t groups = (rows + rows_per_group - 1) / rows_per_group;
+    return 4 * groups >= 7 * cus && groups <= 2 * cus;
+}
+
 // cus: the device's compute units (ks::kDefaultComputeUnits when unknown).
 ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, bool aligned, bool split_ok,
                  int64_t cus)
@@ -225,6 +244,12 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         int64_t pieces_per_lane = (nvec + tpr - 1) / tpr;
         if (op == KS_OP_RMS_NORM_RESIDUAL && tpr == ks::kMaxTpr && pieces_per_lane == 7)
             pieces_per_lane = 8;   // the 7-piece build of this form spills registers
+        bool weight_lds = op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPiecesPerCu * cus;
+        if (wide_rms_norm(op, rows, nvec, large, cus)) {
+            tpr = nvec <= 1024 ? 64 : 128;
+            pieces_per_lane = ks::kWideVpt;
+            weight_lds = esize == 2;
+        }
         plan.path = KS_PATH_VECTOR;
         plan.threads_per_row = (int32_t)tpr;
         plan.vectors_per_thread = (int32_t)pieces_per_lane;
@@ -233,7 +258,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.rows_per_block = plan.block_threads / (int32_t)tpr;
         plan.load_nt = 1;
         plan.store_nt = 1;
-        plan.weight_lds = (op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPiecesPerCu * cus) ? 1 : 0;
+        plan.weight_lds = weight_lds ? 1 : 0;
         return plan;
     }
     plan.path = KS_PATH_GENERIC;
@@ -301,7 +326,9 @@ bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t rows, i
     if (p.path == KS_PATH_VECTOR) {
         if (!vec_ok || !is_pow2_team(p.threads_per_row) || !hints_compiled(p))
             return false;
-        if (p.vectors_per_thread < 1 || p.vectors_per_thread > ks::kMaxVpt)
+        if (p.vectors_per_thread < 1 ||
+            (p.vectors_per_thread > ks::kMaxVpt &&
+             !(p.vectors_per_thread == ks::kWideVpt && ks::wide_vpt_compiled(op, p.threads_per_row))))
             return false;
         if ((int64_t)p.threads_per_row * p.vectors_per_thread * 16 < row_bytes)
             return false;

@@ -236,8 +236,8 @@ template <int kWidth, typename Op = SumOp> __device__ __forceinline__ float butt
 // missing slots count as zero); returns the fold of all of them.
 template <int kSlots> __device__ __forceinline__ float local_fold(float *part)
 {
-    constexpr int kP2 = kSlots <= 1 ? 1 : kSlots <= 2 ? 2 : kSlots <= 4 ? 4 : 8;
-    static_assert(kSlots <= 8, "at most 8 slots per lane");
+    constexpr int kP2 = kSlots <= 1 ? 1 : kSlots <= 2 ? 2 : kSlots <= 4 ? 4 : kSlots <= 8 ? 8 : 16;
+    static_assert(kSlots <= 16, "at most 16 slots per lane");
 #pragma unroll
     for (int n = kP2; n > 1; n /= 2)
 #pragma unroll

@@ -155,6 +155,15 @@ constexpr int kSwigluGenericBlock = 256;
 constexpr int kMinTpr = 8;
 constexpr int kMaxTpr = 1024;
 constexpr int kMaxVpt = 8;
+// Besides 1..kMaxVpt, RMSNorm and its two residual forms compile 16 pieces
+// per lane for teams of 32..128 lanes: a 16 KiB row on one wave (fp32 4096,
+// 16-bit 8192 wide) instead of two joined by an LDS exchange and a barrier.
+constexpr int kWideVpt = 16;
+constexpr bool wide_vpt_compiled(int op, int tpr)
+{
+    return op != KS_OP_SOFTMAX && op != KS_OP_SILU_AND_MUL && op != KS_OP_RMS_NORM_BACKWARD && tpr >= 32 &&
+           tpr <= 128;
+}
 
 inline int block_threads_for(int tpr) { return tpr < 256 ? 256 : tpr; }
 

@@ -114,6 +114,10 @@ hipError_t vec_by_vpt(const Launch &l)
     case 6: return vec_one<T, OP, TPR, 6>(l);
     case 7: return vec_one<T, OP, TPR, 7>(l);
     case 8: return vec_one<T, OP, TPR, 8>(l);
+    case kWideVpt:
+        if constexpr (wide_vpt_compiled(OP, TPR))
+            return vec_one<T, OP, TPR, kWideVpt>(l);
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }

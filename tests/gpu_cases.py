@@ -83,8 +83,13 @@ def check_case(name: str, op: str, inp: dict, eps: float, plan=None, offset: int
 HINTS = ((0, 0, 0), (1, 1, 0), (0, 1, 0), (1, 1, 1))   # compiled (load_nt, store_nt, weight_lds)
 
 
+WIDE_VPT = 16            # the 16-piece builds (RMSNorm and its residual forms, teams of 32..128 lanes)
+WIDE_VPT_TPRS = (32, 64, 128)
+
+
 def all_plans(dtype: torch.dtype, hidden: int, aligned: bool = True) -> list:
-    """Every compiled plan that covers rows of this size (the library rejects the rest)."""
+    """Every compiled plan of rms_norm and the fused form that covers rows of
+    this size (the library rejects the rest)."""
     es = torch.empty(0, dtype=dtype).element_size()
     row_bytes = hidden * es
     vec_elems = 16 // es
@@ -93,7 +98,7 @@ def all_plans(dtype: torch.dtype, hidden: int, aligned: bool = True) -> list:
         tpr = 8
         while tpr <= 1024:
             maxv = 8
-            for vpt in range(1, maxv + 1):
+            for vpt in list(range(1, maxv + 1)) + ([WIDE_VPT] if tpr in WIDE_VPT_TPRS else []):
                 if tpr * vpt * 16 >= row_bytes:
                     block = max(256, tpr)
                     for lnt, snt, wlds in HINTS:

@@ -136,6 +136,15 @@ def test_explicit_plans_are_checked():
                                             block_threads=1024)) == INVALID
     assert rms(y, x, w, 4, 65544, plan=_plan(threads_per_row=1024, vectors_per_thread=8, rows_per_block=1,
                                              block_threads=1024)) == INVALID     # 131088-byte rows do not fit
+    # 16 pieces per lane: RMSNorm and its residual forms, teams of 32..128 lanes only
+    assert rms(y, x, w, 0, 8192, plan=_plan(vectors_per_thread=16)) == OK          # 64 x 16 x 16 B = 16 KiB
+    assert fused(x, y, w, 0, 8192, plan=_plan(vectors_per_thread=16, weight_lds=1, load_nt=1, store_nt=1)) == OK
+    assert rms(y, x, w, 0, 16384, plan=_plan(threads_per_row=128, vectors_per_thread=16, rows_per_block=2)) == OK
+    assert rms(y, x, w, 4, 16384, plan=_plan(threads_per_row=256, vectors_per_thread=16, rows_per_block=1)) == INVALID
+    assert rms(y, x, w, 4, 2048, plan=_plan(threads_per_row=16, vectors_per_thread=16, rows_per_block=16)) == INVALID
+    assert rms(y, x, w, 4, 8192, plan=_plan(vectors_per_thread=12)) == INVALID
+    sm16 = _plan(vectors_per_thread=16, load_nt=1, store_nt=1)
+    assert b.ks_softmax_ex(y, x, 4, 8192, BF16, sm16, 0) == INVALID
     # the vector path needs 16-byte aligned buffers
     assert rms(y + 2, x, w, 4, 4096, plan=_plan()) == INVALID
     # generic plans
@@ -173,7 +182,14 @@ EXPECTED = {
     ("rms_norm_residual", torch.bfloat16, 4096, 2048): (0, 64, 8, 4, 0),      # never stages the weight
     ("rms_norm_residual", torch.bfloat16, 16384, 8192): (0, 1024, 2, 1, 0),
     ("rms_norm", torch.bfloat16, 16384, 8192): (0, 512, 4, 1, 0),        # prefill 8192x16384
-    ("rms_norm", torch.float32, 4096, 2048): (0, 128, 8, 2, 0),
+    ("rms_norm", torch.float32, 4096, 2048): (0, 64, 16, 4, 0),          # 16 KiB rows, 2 groups per CU: one wave per row
+    ("rms_norm", torch.bfloat16, 8192, 2048): (0, 64, 16, 4, 1),         # the same for 16-bit dtypes, weight in LDS
+    ("rms_norm", torch.bfloat16, 8192, 1792): (0, 64, 16, 4, 1),         # 1.75 groups per CU
+    ("rms_norm", torch.bfloat16, 8192, 1788): (0, 128, 8, 2, 0),         # 447 groups: just below the band
+    ("rms_norm", torch.bfloat16, 8192, 2049): (0, 128, 8, 2, 0),         # just above it
+    ("rms_norm", torch.bfloat16, 16384, 1024): (0, 128, 16, 2, 1),       # 32 KiB rows: two waves per row
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 2048): (0, 128, 8, 2, 1),   # the residual forms keep 8 pieces
+    ("rms_norm_residual", torch.float32, 4096, 2048): (0, 128, 8, 2, 0),
     ("rms_norm", torch.bfloat16, 5, 3): (1, 8, 0, 32, 0),                # odd sizes: generic scalar path
     ("rms_norm", torch.bfloat16, 1000, 3): (0, 128, 1, 2, 0),            # 2000-byte rows are 16-byte multiples
     ("rms_norm", torch.bfloat16, 1001, 3): (1, 64, 0, 4, 0),
@@ -203,6 +219,12 @@ def test_policy_scales_with_compute_units():
     # 512x4096 (256K pieces): 2 per lane on 256 compute units (131072 lanes); 8 on 32 (16384 lanes)
     assert ks.get_plan("rms_norm", bf, 4096, 512, compute_units=256).as_dict()["vectors_per_thread"] == 2
     assert ks.get_plan("rms_norm", bf, 4096, 512, compute_units=32).as_dict()["vectors_per_thread"] == 8
+    # 16 pieces per lane for rms_norm on 16 KiB rows where the grid of 4-row
+    # groups comes to 1.75..2 per compute unit: 1792..2048 rows on 256, 896..1024 on 128
+    for cus, rows, wide in ((256, 1792, True), (256, 2048, True), (256, 1024, False), (128, 896, True),
+                            (128, 1024, True), (128, 1025, False), (128, 2048, False)):
+        p = ks.get_plan("rms_norm", bf, 8192, rows, compute_units=cus).as_dict()
+        assert (p["vectors_per_thread"] == 16) == wide, (cus, rows, p)
     # LDS weight staging of the fused form from 1024 pieces per compute unit
     assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=256).as_dict()["weight_lds"] == 0
     assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=32).as_dict()["weight_lds"] == 1
@@ -242,7 +264,9 @@ def test_policy_table(key):
 def test_policy_rule():
     """The vector plan follows the stated rule: about 131072 lanes of work,
     pieces per lane a power of two in [1, 8] (at most 4 from 4M pieces), team a
-    power of two in [8, 512]; the path itself never depends on rows."""
+    power of two in [8, 512]; except 16 pieces on 64 or 128 lanes for rows of
+    1024..2048 pieces when those plans' 4-row (2-row) groups come to 1.75..2
+    per compute unit; the path itself never depends on rows."""
     for hidden in (8, 64, 1024, 1536, 4096, 5120, 8192, 16384, 32768):
         nvec = hidden * 2 // 16
         paths = set()
@@ -250,6 +274,11 @@ def test_policy_rule():
             p = ks.get_plan("rms_norm", torch.bfloat16, hidden, rows).as_dict()
             paths.add(p["path"])
             pieces = rows * nvec
+            if 1024 <= nvec <= 2048 and pieces < 2**22:
+                groups = -(-rows // (4 if nvec <= 1024 else 2))
+                if 4 * groups >= 7 * 256 and groups <= 512:
+                    assert (p["threads_per_row"], p["vectors_per_thread"]) == (64 if nvec <= 1024 else 128, 16), p
+                    continue
             target = 1
             while target * 131072 < pieces:
                 target *= 2

@@ -15,7 +15,7 @@ import oracle
 import rmsnorm_row_normalisation_amd as ks
 import workloads
 from compare import check_bitexact, check_normalised
-from gpu_cases import HINTS, require_gpu, say
+from gpu_cases import WIDE_VPT, WIDE_VPT_TPRS, HINTS, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 DTYPES = ["bfloat16", "float16", "float32"]
@@ -95,7 +95,7 @@ def test_every_plan(dtype, hidden):
     n = 0
     while tpr <= 1024:
         maxv = 8
-        for vpt in range(1, maxv + 1):
+        for vpt in list(range(1, maxv + 1)) + ([WIDE_VPT] if tpr in WIDE_VPT_TPRS else []):
             if tpr * vpt * 16 >= hidden * es:
                 block = max(256, tpr)
                 for lnt, snt, wl in HINTS:
