@@ -174,19 +174,22 @@ bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, int64_t c
     return true;
 }
 
-// RMSNorm on rows of 1024..2048 pieces (16..32 KiB) in a batch that is not
-// large: 16 pieces per lane on a one- or two-wave team (64 or 128 lanes), when
-// that plan's grid comes to 1.75..2 workgroups of 4 (2) rows per compute unit.
-// There the 8-piece plan (two or four waves per row, joined through LDS and a
-// barrier) measured 10-22% slower per call (fp32 4096 and bf16 8192 wide at
-// 1792..2048 rows, fp32 8192 and bf16 16384 wide at 1024 rows); at other grids
-// the 16-piece plan ranged from 18% slower to 7% faster, and the two residual
-// forms gained 0-10% at best, so they keep the rules above.  The weight sits
-// in LDS for 16-bit dtypes (fewer VGPRs: 164 against 218), not for fp32
-// (10-19% against 0-12% faster).
-bool wide_rms_norm(ks_op_t op, int64_t rows, int64_t nvec, bool large, int64_t cus)
+// RMSNorm and its two residual forms on rows of 1024..2048 pieces (16..32
+// KiB) in a batch that is not large: 16 pieces per lane on a one- or two-wave
+// team (64 or 128 lanes), when that plan's grid comes to 1.75..2 workgroups of
+// 4 (2) rows per compute unit.  There the 8-piece plan (two or four waves per
+// row, joined through LDS and a barrier) measured slower per call: rms_norm by
+// 10-24% (fp32 4096 and 16-bit 8192 wide at 1792..2048 rows, fp32 8192 and
+// 16-bit 16384 wide at 920..1024 rows), the fused form by 4-12% (weight in
+// LDS, as its rule above gives it) and the out-of-place form by 2-6% (weight
+// not in LDS, as its rule gives it).  At other grids the 16-piece plans ranged
+// from 19% slower to 7% faster, so they stay in this band.  rms_norm stages the
+// weight in LDS for 16-bit dtypes (164 VGPRs against 218; 18-22% against
+// 13-16% faster), not for fp32 (10-19% against 0-12%).
+bool wide_row_plan(ks_op_t op, int64_t rows, int64_t nvec, bool large, int64_t cus)
 {
-    if (op != KS_OP_RMS_NORM || large || nvec < 1024 || nvec > 2048)
+    if ((op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_RMS_NORM_RESIDUAL) || large ||
+        nvec < 1024 || nvec > 2048)
         return false;
     const int64_t rows_per_group = nvec <= 1024 ? 4 : 2;
     const int64_t groups = (rows + rows_per_group - 1) / rows_per_group;
@@ -245,10 +248,11 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         if (op == KS_OP_RMS_NORM_RESIDUAL && tpr == ks::kMaxTpr && pieces_per_lane == 7)
             pieces_per_lane = 8;   // the 7-piece build of this form spills registers
         bool weight_lds = op == KS_OP_FUSED_ADD_RMS_NORM && pieces >= kWeightLdsPiecesPerCu * cus;
-        if (wide_rms_norm(op, rows, nvec, large, cus)) {
+        if (wide_row_plan(op, rows, nvec, large, cus)) {
             tpr = nvec <= 1024 ? 64 : 128;
             pieces_per_lane = ks::kWideVpt;
-            weight_lds = esize == 2;
+            if (op == KS_OP_RMS_NORM)
+                weight_lds = esize == 2;
         }
         plan.path = KS_PATH_VECTOR;
         plan.threads_per_row = (int32_t)tpr;

@@ -188,8 +188,9 @@ EXPECTED = {
     ("rms_norm", torch.bfloat16, 8192, 1788): (0, 128, 8, 2, 0),         # 447 groups: just below the band
     ("rms_norm", torch.bfloat16, 8192, 2049): (0, 128, 8, 2, 0),         # just above it
     ("rms_norm", torch.bfloat16, 16384, 1024): (0, 128, 16, 2, 1),       # 32 KiB rows: two waves per row
-    ("fused_add_rms_norm", torch.bfloat16, 8192, 2048): (0, 128, 8, 2, 1),   # the residual forms keep 8 pieces
-    ("rms_norm_residual", torch.float32, 4096, 2048): (0, 128, 8, 2, 0),
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 2048): (0, 64, 16, 4, 1),   # the residual forms too, with their
+    ("rms_norm_residual", torch.float32, 4096, 2048): (0, 64, 16, 4, 0),     # own weight staging rules
+    ("fused_add_rms_norm", torch.bfloat16, 8192, 2560): (0, 128, 8, 2, 1),   # 640 groups: outside the band
     ("rms_norm", torch.bfloat16, 5, 3): (1, 8, 0, 32, 0),                # odd sizes: generic scalar path
     ("rms_norm", torch.bfloat16, 1000, 3): (0, 128, 1, 2, 0),            # 2000-byte rows are 16-byte multiples
     ("rms_norm", torch.bfloat16, 1001, 3): (1, 64, 0, 4, 0),
@@ -223,8 +224,10 @@ def test_policy_scales_with_compute_units():
     # groups comes to 1.75..2 per compute unit: 1792..2048 rows on 256, 896..1024 on 128
     for cus, rows, wide in ((256, 1792, True), (256, 2048, True), (256, 1024, False), (128, 896, True),
                             (128, 1024, True), (128, 1025, False), (128, 2048, False)):
-        p = ks.get_plan("rms_norm", bf, 8192, rows, compute_units=cus).as_dict()
-        assert (p["vectors_per_thread"] == 16) == wide, (cus, rows, p)
+        for op in ("rms_norm", "fused_add_rms_norm", "rms_norm_residual"):
+            p = ks.get_plan(op, bf, 8192, rows, compute_units=cus).as_dict()
+            assert (p["vectors_per_thread"] == 16) == wide, (op, cus, rows, p)
+        assert ks.get_plan("softmax", bf, 8192, rows, compute_units=cus).as_dict()["vectors_per_thread"] <= 8
     # LDS weight staging of the fused form from 1024 pieces per compute unit
     assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=256).as_dict()["weight_lds"] == 0
     assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=32).as_dict()["weight_lds"] == 1

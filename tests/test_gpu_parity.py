@@ -148,23 +148,26 @@ SIXTEEN_CASES = [("float32", 4096, 2048), ("bfloat16", 8192, 1856), ("float16", 
 
 @pytest.mark.parametrize("dtype,hidden,rows", SIXTEEN_CASES, ids=[f"{d}-{r}x{h}" for d, h, r in SIXTEEN_CASES])
 def test_sixteen_piece_plans_at_full_size(dtype, hidden, rows):
-    """The batches where the policy (on a whole MI355X) gives rms_norm 16 pieces
-    per lane: every row against the oracle, and the same bits as the 8-piece
-    plan the policy gave these batches before."""
+    """The batches where the policy (on a whole MI355X) gives rms_norm and the
+    fused form 16 pieces per lane: every row against the oracle, and the same
+    bits as the 8-piece plans the policy gave these batches before."""
     inp = workloads.random_case((rows, hidden), dtype, seed=rows + hidden)
     dt = inp["x"].dtype
-    p16 = ks.get_plan("rms_norm", dt, hidden, rows, compute_units=256)
-    assert p16.vectors_per_thread == 16, p16.as_dict()
     es = inp["x"].element_size()
     nvec = hidden * es // 16
     tpr8 = 128 if nvec <= 1024 else 256
-    p8 = ks.Plan(path=0, threads_per_row=tpr8, vectors_per_thread=8, elems_per_access=16 // es,
-                 rows_per_block=256 // tpr8, block_threads=256, load_nt=1, store_nt=1, weight_lds=0)
-    say("sixteen pieces", dtype, rows, hidden, p16.as_dict())
-    got16 = gpu_run("rms_norm", inp, 1e-6, plan=p16)
-    got8 = gpu_run("rms_norm", inp, 1e-6, plan=p8)
-    check_outputs("rms_norm", got16, oracle_run("rms_norm", inp, 1e-6), exact_rate=True)
-    check_bitexact(got16[0], got8[0])
+    for op in ("rms_norm", "fused_add_rms_norm"):
+        p16 = ks.get_plan(op, dt, hidden, rows, compute_units=256)
+        assert p16.vectors_per_thread == 16, p16.as_dict()
+        p8 = ks.Plan(path=0, threads_per_row=tpr8, vectors_per_thread=8, elems_per_access=16 // es,
+                     rows_per_block=256 // tpr8, block_threads=256, load_nt=1, store_nt=1, weight_lds=p16.weight_lds)
+        say("sixteen pieces", op, dtype, rows, hidden, p16.as_dict())
+        got16 = gpu_run(op, inp, 1e-6, plan=p16)
+        got8 = gpu_run(op, inp, 1e-6, plan=p8)
+        check_outputs(op, got16, oracle_run(op, inp, 1e-6), exact_rate=True)
+        check_bitexact(got16[0], got8[0])
+        if got16[1] is not None:
+            check_bitexact(got16[1], got8[1])
 
 
 # ---------------------------------------------------------------------------
