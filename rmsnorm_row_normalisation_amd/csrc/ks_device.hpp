@@ -40,6 +40,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace ks {
 
@@ -1088,19 +1089,22 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
 
     // Row group g covers rows [g * kRpb, g * kRpb + kRpb); rows past the batch
     // fall outside the group's descriptors (zero reads, dropped stores).
+    // A group past the batch has zero-size descriptors: its loads read zeros
+    // and move no data.
     const int64_t ngroups = (p.rows + kRpb - 1) / kRpb;
     auto group_bytes = [&](int64_t grp) {
         const int64_t left = p.rows - grp * kRpb;
-        return (left < kRpb ? (uint32_t)left : (uint32_t)kRpb) * row_bytes;
+        return left <= 0 ? 0u : (left < kRpb ? (uint32_t)left : (uint32_t)kRpb) * row_bytes;
     };
     uint32_t off[kVpt];
 #pragma unroll
     for (int k = 0; k < kVpt; ++k)
         off[k] = in_row[k] ? (uint32_t)team * row_bytes + (uint32_t)(k * kTpr + lane) * 16u : kOutOfRange;
     auto load_group = [&](int64_t grp, u32x4 *xo, u32x4 *dyo) {
-        const size_t base = (size_t)grp * kRpb * row_bytes;
-        const auto rx = make_rsrc((const char *)p.x + base, group_bytes(grp));
-        const auto rdy = make_rsrc((const char *)p.dy + base, group_bytes(grp));
+        const uint32_t bytes = group_bytes(grp);
+        const size_t base = bytes == 0 ? 0 : (size_t)grp * kRpb * row_bytes;
+        const auto rx = make_rsrc((const char *)p.x + base, bytes);
+        const auto rdy = make_rsrc((const char *)p.dy + base, bytes);
 #pragma unroll
         for (int k = 0; k < kVpt; ++k)
             xo[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, off[k], 0, kNt);
@@ -1153,29 +1157,39 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
     // Software pipeline: while a group is reduced and written, the next
     // group's loads are in flight.  They issue only once the group's own data
     // is back (its sums are formed), so that the memory system returns the
-    // groups in turn and a group's dx stores overlap the next group's reads;
-    // the last group issues no loads.  g is the same for the whole workgroup,
-    // so every thread reaches the barriers in team_fold2 equally often.
+    // groups in turn and a group's dx stores overlap the next group's reads.
+    // The first group is peeled off the loop and always issues the next
+    // group's loads (a group past the batch has zero-size descriptors), so
+    // the loop is entered, as it repeats, with one group's loads followed by
+    // the previous group's stores outstanding: the wait for a group's data
+    // then counts its loads only and leaves the stores in flight.  The last
+    // group issues no loads.  g is the same for the whole workgroup, so every
+    // thread reaches the barriers in team_fold2 equally often.
     int64_t g = blockIdx.x;
     if (g < ngroups) {
-        u32x4 xv[kVpt], dv[kVpt];
+        u32x4 xv[kVpt], dv[kVpt], xn[kVpt], dn[kVpt];
         load_group(g, xv, dv);
-        for (int64_t gn = g + gridDim.x; gn < ngroups; g = gn, gn += gridDim.x) {
-            float ss, dot;
-            sums(xv, dv, ss, dot);
-            asm volatile("" ::"v"(ss), "v"(dot) : "memory");   // the loads below stay after the sums
-            u32x4 xn[kVpt], dn[kVpt];
-            load_group(gn, xn, dn);
-            finish(g, xv, dv, ss, dot);
-#pragma unroll
-            for (int k = 0; k < kVpt; ++k) {
-                xv[k] = xn[k];
-                dv[k] = dn[k];
-            }
-        }
+        int64_t gn = g + gridDim.x;
         float ss, dot;
         sums(xv, dv, ss, dot);
+        asm volatile("" ::"v"(ss), "v"(dot) : "memory");   // the loads below stay after the sums
+        load_group(gn, xn, dn);
         finish(g, xv, dv, ss, dot);
+        if (gn < ngroups) {
+            for (g = gn, gn += gridDim.x; gn < ngroups; g = gn, gn += gridDim.x) {
+#pragma unroll
+                for (int k = 0; k < kVpt; ++k) {
+                    xv[k] = xn[k];
+                    dv[k] = dn[k];
+                }
+                sums(xv, dv, ss, dot);
+                asm volatile("" ::"v"(ss), "v"(dot) : "memory");
+                load_group(gn, xn, dn);
+                finish(g, xv, dv, ss, dot);
+            }
+            sums(xn, dn, ss, dot);
+            finish(g, xn, dn, ss, dot);
+        }
     }
     if (p.part == nullptr)
         return;
@@ -1315,13 +1329,15 @@ __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
 // dw[j] = the nparts partial rows added in a fixed order.  A 256-thread block
 // owns kDwCols consecutive columns; thread (slice v, column c) adds rows
 // v, v + kDwSlices, v + 2 kDwSlices, ... of its column in turn (loads issued
-// sixteen at a time, so their latencies overlap), then the kDwSlices sums of
-// a column are folded in half (v with v + 4, then v + 2, v + 1) and rounded
-// to the dtype.  32-column blocks spread a 4096-wide dw over 128 compute
-// units (64-column, 1024-thread blocks measured 10% slower).
+// 32, then 16 at a time, so their latencies overlap: with 256 partial rows,
+// all of a thread's loads are in flight at once), then the kDwSlices
+// sums of a column are folded in half (v with v + 4, then v + 2, v + 1) and
+// rounded to the dtype.  32-column blocks spread a 4096-wide dw over 128
+// compute units (64-column, 1024-thread blocks measured 10% slower).
 constexpr int kDwCols = 32;
 constexpr int kDwSlices = 8;
 constexpr int kDwBlock = kDwCols * kDwSlices;
+constexpr int kDwBatch = 32;
 
 struct DwParams {
     void *dw;
@@ -1342,15 +1358,20 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
         const float *col = p.part + j;
         const size_t step = (size_t)kDwSlices * (size_t)p.hidden;
         int q = v;
-        for (; q + 15 * kDwSlices < p.nparts; q += 16 * kDwSlices) {
-            float t[16];
+        auto batch = [&](auto n) {
+            constexpr int kN = decltype(n)::value;
+            for (; q + (kN - 1) * kDwSlices < p.nparts; q += kN * kDwSlices) {
+                float t[kN];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                t[u] = col[(size_t)q * p.hidden + u * step];
+                for (int u = 0; u < kN; ++u)
+                    t[u] = col[(size_t)q * p.hidden + u * step];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                s = s + t[u];
-        }
+                for (int u = 0; u < kN; ++u)
+                    s = s + t[u];
+            }
+        };
+        batch(std::integral_constant<int, kDwBatch>{});
+        batch(std::integral_constant<int, kDwBatch / 2>{});
         for (; q < p.nparts; q += kDwSlices)
             s = s + col[(size_t)q * p.hidden];
     }

@@ -751,8 +751,16 @@ def test_backward_plans():
                 code = {4: F32, 2: F16 if dtype == torch.float16 else BF16}[es]
                 assert bwd(base, None, base + 256 * MB, base + 512 * MB, base + 768 * MB, 0, hidden, None, 0,
                            dtype=code, plan=b.Plan.from_dict(p)) == OK
+    # one piece per lane for rows of 256..1024 pieces from 2048 rows, else the fewest lanes
+    for dtype, hidden, rows, want in ((torch.bfloat16, 4096, 2048, (512, 1)), (torch.bfloat16, 4096, 2047, (256, 2)),
+                                      (torch.bfloat16, 2048, 2048, (256, 1)), (torch.bfloat16, 1024, 8192, (64, 2)),
+                                      (torch.float16, 8192, 32768, (1024, 1)), (torch.bfloat16, 16384, 8192, (1024, 2)),
+                                      (torch.float32, 4096, 2048, (1024, 1)), (torch.float32, 1024, 2048, (256, 1)),
+                                      (torch.float32, 8192, 2048, (1024, 2)), (torch.float32, 4096, 512, (512, 2))):
+        p = ks.get_plan("rms_norm_backward", dtype, hidden, rows).as_dict()
+        assert (p["threads_per_row"], p["vectors_per_thread"]) == want, (dtype, hidden, rows, p)
+        assert p["rows_per_block"] * p["threads_per_row"] == 1024
     p = ks.get_plan("rms_norm_backward", torch.bfloat16, 4096, 2048).as_dict()
-    assert (p["threads_per_row"], p["vectors_per_thread"]) == (256, 2)
     bad = [{**p, "vectors_per_thread": 3, "threads_per_row": 256}, {**p, "block_threads": 256, "rows_per_block": 1},
            {**p, "weight_lds": 1}, {**p, "load_nt": 0}]
     for q in bad:
