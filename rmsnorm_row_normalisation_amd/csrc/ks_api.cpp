@@ -196,6 +196,36 @@ bool split_policy(ks_op_t op, int64_t rows, int64_t nvec, bool vec_ok, int64_t c
 // from 19% slower to 7% faster, so they stay in this band.  rms_norm stages the
 // weight in LDS for 16-bit dtypes (164 VGPRs against 218; 18-22% against
 // 13-16% faster), not for fp32 (10-19% against 0-12%).
+// rms_norm in batches of at least 32 rows per compute unit (8192 on 256):
+// rows of exactly 1024 pieces (16 KiB) take 512 lanes x 2 pieces with the
+// weight staged in LDS, 16-bit rows of exactly 2048 pieces (32 KiB) 128
+// lanes x 16 pieces.  Against the large-batch plans (256 x 4, 512 x 4) they
+// measured 1-2% faster at 8192 rows and 2.4-7% at 16384..32768 rows (hidden
+// 8192 and 16384 in bf16 and fp16, 4096 in fp32; graph-timed, two passes
+// each, bf16 on two boxes); at 4096 rows they were even or up to 1% slower, and
+// fp32 rows of 2048 pieces were slower on 16 pieces per lane.
+constexpr int64_t kHugeRmsRowsPerCu = 32;
+
+bool huge_rms_plan(ks_op_t op, int64_t rows, int64_t nvec, int64_t esize, int64_t cus, int64_t *tpr, int64_t *vpt,
+                   bool *weight_lds)
+{
+    if (op != KS_OP_RMS_NORM || rows < kHugeRmsRowsPerCu * cus)
+        return false;
+    if (nvec == 1024) {
+        *tpr = 512;
+        *vpt = 2;
+        *weight_lds = true;
+        return true;
+    }
+    if (nvec == 2048 && esize == 2) {
+        *tpr = 128;
+        *vpt = ks::kWideVpt;
+        *weight_lds = false;
+        return true;
+    }
+    return false;
+}
+
 bool wide_row_plan(ks_op_t op, int64_t rows, int64_t nvec, bool large, int64_t cus)
 {
     if ((op != KS_OP_RMS_NORM && op != KS_OP_FUSED_ADD_RMS_NORM && op != KS_OP_RMS_NORM_RESIDUAL) || large ||
@@ -264,6 +294,7 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
             if (op == KS_OP_RMS_NORM)
                 weight_lds = esize == 2;
         }
+        huge_rms_plan(op, rows, nvec, esize, cus, &tpr, &pieces_per_lane, &weight_lds);
         plan.path = KS_PATH_VECTOR;
         plan.threads_per_row = (int32_t)tpr;
         plan.vectors_per_thread = (int32_t)pieces_per_lane;

@@ -181,7 +181,13 @@ EXPECTED = {
     ("fused_add_rms_norm", torch.bfloat16, 4096, 8192): (0, 256, 2, 1, 1),
     ("rms_norm_residual", torch.bfloat16, 4096, 2048): (0, 64, 8, 4, 0),      # never stages the weight
     ("rms_norm_residual", torch.bfloat16, 16384, 8192): (0, 1024, 2, 1, 0),
-    ("rms_norm", torch.bfloat16, 16384, 8192): (0, 512, 4, 1, 0),        # prefill 8192x16384
+    ("rms_norm", torch.bfloat16, 16384, 8192): (0, 128, 16, 2, 0),       # prefill 8192x16384: 32 KiB rows from
+    ("rms_norm", torch.bfloat16, 16384, 8191): (0, 512, 4, 1, 0),        # 8192 rows on two waves, 16 pieces
+    ("rms_norm", torch.float32, 8192, 8192): (0, 512, 4, 1, 0),          # (16-bit dtypes only)
+    ("rms_norm", torch.bfloat16, 8192, 8192): (0, 512, 2, 1, 1),         # 16 KiB rows from 8192 rows: 512 x 2,
+    ("rms_norm", torch.float32, 4096, 32768): (0, 512, 2, 1, 1),         # weight in LDS
+    ("rms_norm", torch.bfloat16, 8192, 8191): (0, 256, 4, 1, 0),
+    ("rms_norm_residual", torch.bfloat16, 8192, 8192): (0, 512, 2, 1, 0),  # rms_norm only
     ("rms_norm", torch.float32, 4096, 2048): (0, 64, 16, 4, 0),          # 16 KiB rows, 2 groups per CU: one wave per row
     ("rms_norm", torch.bfloat16, 8192, 2048): (0, 64, 16, 4, 1),         # the same for 16-bit dtypes, weight in LDS
     ("rms_norm", torch.bfloat16, 8192, 1792): (0, 64, 16, 4, 1),         # 1.75 groups per CU
@@ -228,6 +234,12 @@ def test_policy_scales_with_compute_units():
             p = ks.get_plan(op, bf, 8192, rows, compute_units=cus).as_dict()
             assert (p["vectors_per_thread"] == 16) == wide, (op, cus, rows, p)
         assert ks.get_plan("softmax", bf, 8192, rows, compute_units=cus).as_dict()["vectors_per_thread"] <= 8
+    # rms_norm's plans for 16 and 32 KiB rows from 32 rows per compute unit
+    for cus, rows, huge in ((256, 8192, True), (256, 8191, False), (128, 4096, True), (128, 4095, False)):
+        p = ks.get_plan("rms_norm", bf, 8192, rows, compute_units=cus).as_dict()
+        assert ((p["threads_per_row"], p["vectors_per_thread"], p["weight_lds"]) == (512, 2, 1)) == huge, (cus, rows)
+        p = ks.get_plan("rms_norm", bf, 16384, rows, compute_units=cus).as_dict()
+        assert ((p["threads_per_row"], p["vectors_per_thread"]) == (128, 16)) == huge, (cus, rows)
     # LDS weight staging of the fused form from 1024 pieces per compute unit
     assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=256).as_dict()["weight_lds"] == 0
     assert ks.get_plan("fused_add_rms_norm", bf, 4096, 256, compute_units=32).as_dict()["weight_lds"] == 1
@@ -269,7 +281,8 @@ def test_policy_rule():
     pieces per lane a power of two in [1, 8] (at most 4 from 4M pieces), team a
     power of two in [8, 512]; except 16 pieces on 64 or 128 lanes for rows of
     1024..2048 pieces when those plans' 4-row (2-row) groups come to 1.75..2
-    per compute unit; the path itself never depends on rows."""
+    per compute unit, and from 8192 rows 512 x 2 for rows of 1024 pieces and
+    128 x 16 for rows of 2048; the path itself never depends on rows."""
     for hidden in (8, 64, 1024, 1536, 4096, 5120, 8192, 16384, 32768):
         nvec = hidden * 2 // 16
         paths = set()
@@ -282,6 +295,9 @@ def test_policy_rule():
                 if 4 * groups >= 7 * 256 and groups <= 512:
                     assert (p["threads_per_row"], p["vectors_per_thread"]) == (64 if nvec <= 1024 else 128, 16), p
                     continue
+            if rows >= 8192 and nvec in (1024, 2048):
+                assert (p["threads_per_row"], p["vectors_per_thread"]) == ((512, 2) if nvec == 1024 else (128, 16)), p
+                continue
             target = 1
             while target * 131072 < pieces:
                 target *= 2

@@ -170,6 +170,39 @@ def test_sixteen_piece_plans_at_full_size(dtype, hidden, rows):
             check_bitexact(got16[1], got8[1])
 
 
+HUGE_CASES = [("bfloat16", 8192, 8192), ("float32", 4096, 8192), ("float16", 16384, 8192)]
+
+
+@pytest.mark.parametrize("dtype,hidden,rows", HUGE_CASES, ids=[f"{d}-{r}x{h}" for d, h, r in HUGE_CASES])
+def test_large_batch_rms_plans_at_full_size(dtype, hidden, rows):
+    """rms_norm from 8192 rows of 16 KiB (512 lanes x 2 pieces, weight in LDS)
+    or 16-bit rows of 32 KiB (128 lanes x 16 pieces): every row against the
+    oracle, in chunks, and the same bits as the large-batch plan of 4 pieces
+    per lane that the policy gives one row fewer."""
+    inp = workloads.random_case((rows, hidden), dtype, seed=rows ^ hidden)
+    dt = inp["x"].dtype
+    es = inp["x"].element_size()
+    nvec = hidden * es // 16
+    p = ks.get_plan("rms_norm", dt, hidden, rows, compute_units=256)
+    assert (p.threads_per_row, p.vectors_per_thread) == ((512, 2) if nvec == 1024 else (128, 16)), p.as_dict()
+    q = ks.get_plan("rms_norm", dt, hidden, rows - 1, compute_units=256)
+    assert q.vectors_per_thread == 4, q.as_dict()
+    say("large-batch rms plans", dtype, rows, hidden, p.as_dict(), q.as_dict())
+    y, _ = gpu_run("rms_norm", inp, 1e-6, plan=p)
+    y4, _ = gpu_run("rms_norm", inp, 1e-6, plan=q)
+    check_bitexact(y, y4)
+    exact = total = 0
+    for r0 in range(0, rows, LARGE_CHUNK_ROWS):
+        sl = slice(r0, min(rows, r0 + LARGE_CHUNK_ROWS))
+        sub = {k: (v[sl] if v.dim() == 2 else v) for k, v in inp.items()}
+        st = check_outputs("rms_norm", (y[sl], None), oracle_run("rms_norm", sub, 1e-6), exact_rate=False)
+        exact += round(st.exact_rate * st.n)
+        total += st.n
+    assert total == rows * hidden
+    if dtype != "float32":
+        assert exact / total >= 0.999
+
+
 # ---------------------------------------------------------------------------
 # invariants that hold at any size
 # ---------------------------------------------------------------------------
