@@ -131,6 +131,26 @@ def test_every_plan(dtype, hidden):
             check_gradient(gw, rw, mdw)
 
 
+ONE_PIECE_CASES = [("bfloat16", 4096, 8192), ("float16", 8192, 4096), ("float32", 4096, 2048)]
+
+
+@pytest.mark.parametrize("dtype,hidden,rows", ONE_PIECE_CASES, ids=[f"{d}-{r}x{h}" for d, h, r in ONE_PIECE_CASES])
+def test_one_piece_plans_at_full_size(dtype, hidden, rows):
+    """Batches where the policy gives the backward one piece per lane on twice
+    the team: both gradients against the oracle, and dx the same bits as with
+    the fewest-lane plan the policy gives a smaller batch."""
+    inp = workloads.random_case((rows, hidden), dtype, seed=rows + 7 * hidden)
+    dy, x, w = inp["residual"], inp["x"], inp["weight"]
+    p1 = ks.get_plan("rms_norm_backward", x.dtype, hidden, rows, compute_units=256)
+    assert p1.vectors_per_thread == 1, p1.as_dict()
+    p2 = ks.get_plan("rms_norm_backward", x.dtype, hidden, 512, compute_units=256)
+    assert p2.vectors_per_thread > 1 and p2.threads_per_row * 2 == p1.threads_per_row, p2.as_dict()
+    st, gx, _ = check(f"one piece {dtype}", dy, x, w, 1e-6, plan=p1)
+    say("one-piece backward", dtype, rows, hidden, st)
+    gx2, _ = run(dy, x, w, 1e-6, p2)
+    check_bitexact(gx, gx2)
+
+
 def test_dx_batch_invariance_and_dw_determinism():
     wl = workloads.WORKLOADS["B1"]
     inp = workloads.make_inputs(wl, rows=700)
