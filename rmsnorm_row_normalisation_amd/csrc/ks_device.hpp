@@ -1162,8 +1162,8 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
     // group's loads (a group past the batch has zero-size descriptors), so
     // the loop is entered, as it repeats, with one group's loads followed by
     // the previous group's stores outstanding: the wait for a group's data
-    // then counts its loads only and leaves the stores in flight.  The last
-    // group issues no loads.  g is the same for the whole workgroup, so every
+    // then counts its loads only and leaves the stores in flight.  Any later
+    // last group issues no loads.  g is the same for the whole workgroup, so every
     // thread reaches the barriers in team_fold2 equally often.
     int64_t g = blockIdx.x;
     if (g < ngroups) {
