@@ -1329,8 +1329,8 @@ __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
 // dw[j] = the nparts partial rows added in a fixed order.  A 256-thread block
 // owns kDwCols consecutive columns; thread (slice v, column c) adds rows
 // v, v + kDwSlices, v + 2 kDwSlices, ... of its column in turn (loads issued
-// 32, then 16 at a time, so their latencies overlap: with 256 partial rows,
-// all of a thread's loads are in flight at once), then the kDwSlices
+// in batches, so their latencies overlap: with at most 256 partial rows, a
+// thread waits for at most three rounds of loads), then the kDwSlices
 // sums of a column are folded in half (v with v + 4, then v + 2, v + 1) and
 // rounded to the dtype.  32-column blocks spread a 4096-wide dw over 128
 // compute units (64-column, 1024-thread blocks measured 10% slower).
@@ -1357,6 +1357,12 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
     if (j < p.hidden) {
         const float *col = p.part + j;
         const size_t step = (size_t)kDwSlices * (size_t)p.hidden;
+        // kDwBatch, then kDwBatch / 2 rows of the column at a time, so their
+        // loads are in flight together; the rows left after that (fewer than
+        // kDwBatch / 2) go in one more batch of that size, whose loads past
+        // the last partial row read the batch's first row again and whose
+        // terms past it are not added (a plain loop over them waited for each
+        // load in turn).  The rows are added in order either way.
         int q = v;
         auto batch = [&](auto n) {
             constexpr int kN = decltype(n)::value;
@@ -1372,8 +1378,18 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
         };
         batch(std::integral_constant<int, kDwBatch>{});
         batch(std::integral_constant<int, kDwBatch / 2>{});
-        for (; q < p.nparts; q += kDwSlices)
-            s = s + col[(size_t)q * p.hidden];
+        if (q < p.nparts) {
+            constexpr int kN = kDwBatch / 2;
+            float t[kN];
+#pragma unroll
+            for (int u = 0; u < kN; ++u) {
+                const int r = q + u * kDwSlices < p.nparts ? q + u * kDwSlices : q;
+                t[u] = col[(size_t)r * p.hidden];
+            }
+#pragma unroll
+            for (int u = 0; u < kN; ++u)
+                s = q + u * kDwSlices < p.nparts ? s + t[u] : s;
+        }
     }
     red[v][c] = s;
     __syncthreads();
