@@ -202,8 +202,8 @@ ks_status_t ks_rms_norm_residual_ex(void *out, const void *x, const void *residu
  * (deterministic for a given plan and batch size).  A workspace that is
  * missing or too small is KS_ERROR_INVALID_VALUE.  Errors, streams and plans
  * as above (op KS_OP_RMS_NORM_BACKWARD: vector plans use 1024-thread
- * workgroups, at most 3 pieces per lane for fp32 and 2 for 16-bit dtypes,
- * non-temporal hints on).
+ * workgroups with at most 3 pieces per lane for fp32 and 2 for 16-bit
+ * dtypes, or 512-thread workgroups with at most 4, non-temporal hints on).
  */
 ks_status_t ks_rms_norm_backward_workspace_size(int64_t rows, int64_t hidden, size_t *bytes);
 

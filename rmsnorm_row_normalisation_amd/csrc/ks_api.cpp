@@ -115,32 +115,45 @@ int64_t pow2_ceil(int64_t v)
     return p;
 }
 
-// RMSNorm backward (vector path): 1024-thread workgroups that walk row
-// groups, the team the power of two covering the row (8..1024 lanes) at the
-// fewest lanes, at most 3 (fp32) or 2 (16-bit) pieces per lane; x and dy
-// loads and dx stores non-temporal.  Rows of 256..1024 pieces in batches of
-// at least 2048 rows take one piece per lane instead: each workgroup then
-// walks twice as many groups of half the size, and the pipeline overlaps
-// more of them (measured 0.4-8% faster over 2048-8192-wide rows, 2048-32768
-// rows and all three dtypes; narrower rows and smaller batches were even or
-// slower).
-constexpr int64_t kBwdOnePieceMinRows = 2048;
-constexpr int64_t kBwdOnePieceMinPieces = 256;
+// RMSNorm backward (vector path).  Workgroups walk row groups (at most 256
+// workgroups, one fp32 partial row of dw each); x and dy loads and dx
+// stores non-temporal.  Fitted to graph-timed sweeps of every compiled plan
+// (1024-thread workgroups with up to 3 (fp32) or 2 pieces per lane, 512-thread
+// ones with up to 4) over hidden 512..16384, 64..32768 rows, bf16 and fp32
+// with fp16 spot checks: 0.8% slower than the best plan per case on average
+// (worst 9%), against 10% (worst 44%) for the fewest lanes on 1024 threads.
+//   * below 2048 rows: 512-thread workgroups, the team the power of two
+//     covering the row (up to 512 lanes) with one piece per lane, so the
+//     batch spreads over as many workgroups as it can;
+//   * 2048..32767 rows: 512-thread workgroups, rows of up to 512 pieces on
+//     teams of up to 128 lanes (up to 4 pieces per lane), rows of 513..1024
+//     pieces on 512 lanes with 2;
+//   * from 32768 rows: 1024-thread workgroups with one piece per lane for
+//     rows of up to 1024 pieces;
+//   * rows over 1024 pieces: 512 lanes of 512-thread workgroups with up to 4
+//     pieces per lane; fp32 rows over 2048 pieces (up to 3072): 1024 lanes
+//     with 3.
+constexpr int64_t kBwdMidRows = 2048;
+constexpr int64_t kBwdHugeRows = 32768;
+constexpr int64_t kBwdMidTeam = 128;
 
-ks_plan_t backward_vector_plan(int64_t rows, int64_t nvec, int vec_elems, int max_vpt)
+ks_plan_t backward_vector_plan(int64_t rows, int64_t nvec, int vec_elems)
 {
     ks_plan_t plan;
     memset(&plan, 0, sizeof(plan));
-    if (rows >= kBwdOnePieceMinRows && nvec >= kBwdOnePieceMinPieces && nvec <= ks::kMaxTpr)
-        max_vpt = 1;
-    int64_t tpr = pow2_ceil((nvec + max_vpt - 1) / max_vpt);
-    tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > ks::kMaxTpr ? ks::kMaxTpr : tpr;
+    int64_t block = ks::kBwdBlockHalf;
+    int64_t tpr = pow2_ceil(nvec);
+    if ((nvec <= ks::kMaxTpr && rows >= kBwdHugeRows) || nvec > (int64_t)ks::kBwdBlockHalf * ks::kBwdMaxVptHalf)
+        block = ks::kBwdBlock;
+    else if (nvec <= ks::kBwdBlockHalf && rows >= kBwdMidRows && tpr > kBwdMidTeam)
+        tpr = kBwdMidTeam;
+    tpr = tpr < ks::kMinTpr ? ks::kMinTpr : tpr > block ? block : tpr;
     plan.path = KS_PATH_VECTOR;
     plan.threads_per_row = (int32_t)tpr;
     plan.vectors_per_thread = (int32_t)((nvec + tpr - 1) / tpr);
     plan.elems_per_access = vec_elems;
-    plan.block_threads = ks::kBwdBlock;
-    plan.rows_per_block = ks::kBwdBlock / (int32_t)tpr;
+    plan.block_threads = (int32_t)block;
+    plan.rows_per_block = (int32_t)(block / tpr);
     plan.load_nt = 1;
     plan.store_nt = 1;
     return plan;
@@ -251,8 +264,9 @@ ks_plan_t policy(ks_op_t op, ks_dtype_t dtype, int64_t rows, int64_t hidden, boo
         plan.elems_per_access = vec_elems;
         return plan;
     }
-    if (op == KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * bwd_vpt)
-        return backward_vector_plan(rows, nvec, vec_elems, bwd_vpt);
+    if (op == KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 &&
+        (nvec <= (int64_t)ks::kBwdBlockHalf * ks::kBwdMaxVptHalf || nvec <= (int64_t)ks::kBwdBlock * bwd_vpt))
+        return backward_vector_plan(rows, nvec, vec_elems);
     if (op != KS_OP_RMS_NORM_BACKWARD && aligned && row_bytes % 16 == 0 && nvec <= (int64_t)ks::kMaxTpr * ks::kMaxVpt) {
         const int64_t pieces = rows * nvec;
         const bool swiglu = op == KS_OP_SILU_AND_MUL;
@@ -359,14 +373,15 @@ bool plan_fits(const ks_plan_t &p, ks_op_t op, ks_dtype_t dtype, int64_t rows, i
     const int vec_elems = (int)(16 / esize);
     const bool vec_ok = aligned && row_bytes % 16 == 0;
     if (op == KS_OP_RMS_NORM_BACKWARD && p.path == KS_PATH_VECTOR) {
-        if (!vec_ok || !is_pow2_team(p.threads_per_row) || p.vectors_per_thread < 1 ||
-            p.vectors_per_thread > ks::bwd_max_vpt((int)esize))
+        if (p.block_threads != ks::kBwdBlock && p.block_threads != ks::kBwdBlockHalf)
+            return false;
+        if (!vec_ok || !is_pow2_team(p.threads_per_row) || p.threads_per_row > p.block_threads ||
+            p.vectors_per_thread < 1 || p.vectors_per_thread > ks::bwd_max_vpt((int)esize, p.block_threads))
             return false;
         if ((int64_t)p.threads_per_row * p.vectors_per_thread * 16 < row_bytes)
             return false;
-        return p.elems_per_access == vec_elems && p.block_threads == ks::kBwdBlock &&
-               p.rows_per_block == ks::kBwdBlock / p.threads_per_row && p.load_nt == 1 && p.store_nt == 1 &&
-               p.weight_lds == 0;
+        return p.elems_per_access == vec_elems && p.rows_per_block == p.block_threads / p.threads_per_row &&
+               p.load_nt == 1 && p.store_nt == 1 && p.weight_lds == 0;
     }
     if (p.path == KS_PATH_VECTOR) {
         if (!vec_ok || !is_pow2_team(p.threads_per_row) || !hints_compiled(p))

@@ -53,16 +53,22 @@ struct BwdLaunch {
 };
 
 // Backward: at most this many fp32 partial rows of dw (vector path: one per
-// workgroup; generic path: one per chunk of rows); 1024-thread workgroups
-// (128 VGPRs per lane) on the vector path, where x, dy, the next group's x
-// and dy, the weight and the dw sums of a lane's pieces stay in VGPRs: at
-// most 3 pieces per lane for fp32 and 2 for 16-bit dtypes (whose pieces hold
-// 8 sums each); one more spills.
+// workgroup; generic path: one per chunk of rows).  The vector path runs
+// 1024- or 512-thread workgroups, where x, dy, the next group's x and dy, the
+// weight and the dw sums of a lane's pieces stay in VGPRs: with 1024 threads
+// (128 VGPRs per lane) at most 3 pieces per lane for fp32 and 2 for 16-bit
+// dtypes (whose pieces hold 8 sums each), one more spills; with 512 threads
+// (256 VGPRs per lane) up to 4 pieces for every dtype.
 constexpr int kBwdMaxParts = 256;
 constexpr int kBwdBlock = 1024;
+constexpr int kBwdBlockHalf = 512;
 constexpr int kBwdMaxVpt32 = 3;
 constexpr int kBwdMaxVpt16 = 2;
-inline int bwd_max_vpt(int elem_bytes) { return elem_bytes == 4 ? kBwdMaxVpt32 : kBwdMaxVpt16; }
+constexpr int kBwdMaxVptHalf = 4;
+inline int bwd_max_vpt(int elem_bytes, int block = kBwdBlock)
+{
+    return block == kBwdBlockHalf ? kBwdMaxVptHalf : elem_bytes == 4 ? kBwdMaxVpt32 : kBwdMaxVpt16;
+}
 
 // fp32 elements of workspace a backward call needs: the partial rows and, on
 // the generic path, one rho per row.

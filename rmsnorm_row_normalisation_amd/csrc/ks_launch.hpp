@@ -270,23 +270,39 @@ hipError_t launch_swiglu_typed(const SwigluLaunch &l)
 // ---------------------------------------------------------------------------
 // RMSNorm backward
 // ---------------------------------------------------------------------------
-template <typename T, int TPR, int V>
+template <typename T, int TPR, int V, int B>
 hipError_t bwd_vec_one(const BwdParams &p, unsigned grid, hipStream_t stream)
 {
-    return dispatch(rms_norm_backward_vec<T, TPR, V, kBwdBlock>, dim3(grid), dim3(kBwdBlock), 0, stream, p);
+    return dispatch(rms_norm_backward_vec<T, TPR, V, B>, dim3(grid), dim3(B), 0, stream, p);
 }
 
+// The compiled backward plans: 1024-thread workgroups with 1..3 (fp32) or 1..2
+// pieces per lane, 512-thread workgroups (teams up to 512 lanes) with 1..4.
 template <typename T, int TPR>
-hipError_t bwd_vec_by_vpt(const BwdParams &p, int vpt, unsigned grid, hipStream_t stream)
+hipError_t bwd_vec_by_vpt(const BwdParams &p, int vpt, int block, unsigned grid, hipStream_t stream)
 {
+    if (block == kBwdBlockHalf) {
+        if constexpr (TPR <= kBwdBlockHalf) {
+            switch (vpt) {
+            case 1: return bwd_vec_one<T, TPR, 1, kBwdBlockHalf>(p, grid, stream);
+            case 2: return bwd_vec_one<T, TPR, 2, kBwdBlockHalf>(p, grid, stream);
+            case 3: return bwd_vec_one<T, TPR, 3, kBwdBlockHalf>(p, grid, stream);
+            case 4: return bwd_vec_one<T, TPR, 4, kBwdBlockHalf>(p, grid, stream);
+            default: break;
+            }
+        }
+        return hipErrorInvalidValue;
+    }
+    if (block != kBwdBlock)
+        return hipErrorInvalidValue;
     switch (vpt) {
-    case 1: return bwd_vec_one<T, TPR, 1>(p, grid, stream);
-    case 2: return bwd_vec_one<T, TPR, 2>(p, grid, stream);
+    case 1: return bwd_vec_one<T, TPR, 1, kBwdBlock>(p, grid, stream);
+    case 2: return bwd_vec_one<T, TPR, 2, kBwdBlock>(p, grid, stream);
     default: break;
     }
     if constexpr (Pack<T>::kBytes == 4) {
         if (vpt == 3)
-            return bwd_vec_one<T, TPR, 3>(p, grid, stream);
+            return bwd_vec_one<T, TPR, 3, kBwdBlock>(p, grid, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -325,14 +341,14 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
             const unsigned grid = (unsigned)(groups < kBwdMaxParts ? groups : kBwdMaxParts);
             nparts = (int32_t)grid;
             switch (pl.threads_per_row) {
-            case 8: err = bwd_vec_by_vpt<T, 8>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 16: err = bwd_vec_by_vpt<T, 16>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 32: err = bwd_vec_by_vpt<T, 32>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 64: err = bwd_vec_by_vpt<T, 64>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 128: err = bwd_vec_by_vpt<T, 128>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 256: err = bwd_vec_by_vpt<T, 256>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 512: err = bwd_vec_by_vpt<T, 512>(p, pl.vectors_per_thread, grid, l.stream); break;
-            case 1024: err = bwd_vec_by_vpt<T, 1024>(p, pl.vectors_per_thread, grid, l.stream); break;
+            case 8: err = bwd_vec_by_vpt<T, 8>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 16: err = bwd_vec_by_vpt<T, 16>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 32: err = bwd_vec_by_vpt<T, 32>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 64: err = bwd_vec_by_vpt<T, 64>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 128: err = bwd_vec_by_vpt<T, 128>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 256: err = bwd_vec_by_vpt<T, 256>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 512: err = bwd_vec_by_vpt<T, 512>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
+            case 1024: err = bwd_vec_by_vpt<T, 1024>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
             default: return hipErrorInvalidValue;
             }
         } else {

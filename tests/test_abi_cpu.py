@@ -752,36 +752,46 @@ def test_backward_statuses_and_overlaps():
 
 def test_backward_plans():
     for dtype, es in ((torch.float32, 4), (torch.float16, 2), (torch.bfloat16, 2)):
-        maxv = 3 if es == 4 else 2
         for hidden in (8, 1000, 1001, 4096, 8192, 16384, 32768, 40000):
-            for aligned in (True, False):
-                p = ks.get_plan("rms_norm_backward", dtype, hidden, 2048, aligned).as_dict()
-                nvec = hidden * es // 16
-                if aligned and (hidden * es) % 16 == 0 and nvec <= 1024 * maxv:
-                    assert p["path"] == 0 and p["block_threads"] == 1024
-                    assert p["vectors_per_thread"] <= maxv and p["threads_per_row"] * p["vectors_per_thread"] >= nvec
-                    assert p["rows_per_block"] * p["threads_per_row"] == 1024
-                else:
-                    assert p["path"] == 1
-                base = A if aligned else A + 2
-                code = {4: F32, 2: F16 if dtype == torch.float16 else BF16}[es]
-                assert bwd(base, None, base + 256 * MB, base + 512 * MB, base + 768 * MB, 0, hidden, None, 0,
-                           dtype=code, plan=b.Plan.from_dict(p)) == OK
-    # one piece per lane for rows of 256..1024 pieces from 2048 rows, else the fewest lanes
-    for dtype, hidden, rows, want in ((torch.bfloat16, 4096, 2048, (512, 1)), (torch.bfloat16, 4096, 2047, (256, 2)),
-                                      (torch.bfloat16, 2048, 2048, (256, 1)), (torch.bfloat16, 1024, 8192, (64, 2)),
-                                      (torch.float16, 8192, 32768, (1024, 1)), (torch.bfloat16, 16384, 8192, (1024, 2)),
-                                      (torch.float32, 4096, 2048, (1024, 1)), (torch.float32, 1024, 2048, (256, 1)),
-                                      (torch.float32, 8192, 2048, (1024, 2)), (torch.float32, 4096, 512, (512, 2))):
-        p = ks.get_plan("rms_norm_backward", dtype, hidden, rows).as_dict()
-        assert (p["threads_per_row"], p["vectors_per_thread"]) == want, (dtype, hidden, rows, p)
-        assert p["rows_per_block"] * p["threads_per_row"] == 1024
+            for rows in (64, 2048, 32768):
+                for aligned in (True, False):
+                    p = ks.get_plan("rms_norm_backward", dtype, hidden, rows, aligned).as_dict()
+                    nvec = hidden * es // 16
+                    vector = aligned and (hidden * es) % 16 == 0 and (nvec <= 512 * 4 or (es == 4 and nvec <= 1024 * 3))
+                    if vector:
+                        assert p["path"] == 0 and p["block_threads"] in (512, 1024), p
+                        maxv = 4 if p["block_threads"] == 512 else (3 if es == 4 else 2)
+                        assert p["vectors_per_thread"] <= maxv and p["threads_per_row"] * p["vectors_per_thread"] >= nvec
+                        assert p["rows_per_block"] * p["threads_per_row"] == p["block_threads"]
+                    else:
+                        assert p["path"] == 1
+                    base = A if aligned else A + 2
+                    code = {4: F32, 2: F16 if dtype == torch.float16 else BF16}[es]
+                    assert bwd(base, None, base + 256 * MB, base + 512 * MB, base + 768 * MB, 0, hidden, None, 0,
+                               dtype=code, plan=b.Plan.from_dict(p)) == OK
+    # (team, pieces per lane, workgroup threads): one piece per lane on 512 threads below 2048 rows; teams of
+    # up to 128 lanes (rows of up to 512 pieces) or 512 lanes x 2 (513..1024) from 2048 rows; one piece on 1024
+    # threads from 32768 rows; 512 x up to 4 for wider rows, fp32 rows over 2048 pieces 1024 x 3
+    for dtype, hidden, rows, want in ((torch.bfloat16, 4096, 2048, (128, 4, 512)), (torch.bfloat16, 4096, 2047, (512, 1, 512)),
+                                      (torch.bfloat16, 4096, 32767, (128, 4, 512)), (torch.bfloat16, 4096, 32768, (512, 1, 1024)),
+                                      (torch.bfloat16, 2048, 8192, (128, 2, 512)), (torch.bfloat16, 1024, 8192, (128, 1, 512)),
+                                      (torch.bfloat16, 512, 64, (64, 1, 512)), (torch.float16, 8192, 512, (512, 2, 512)),
+                                      (torch.float16, 8192, 32768, (1024, 1, 1024)), (torch.bfloat16, 16384, 8192, (512, 4, 512)),
+                                      (torch.bfloat16, 16384, 32768, (512, 4, 512)), (torch.float32, 4096, 2048, (512, 2, 512)),
+                                      (torch.float32, 2048, 2048, (128, 4, 512)), (torch.float32, 8192, 64, (512, 4, 512)),
+                                      (torch.float32, 12288, 2048, (1024, 3, 1024)), (torch.bfloat16, 1536, 2048, (128, 2, 512))):
+        p = ks.get_plan("rms_norm_backward", dtype, hidden, rows, compute_units=256).as_dict()
+        assert (p["threads_per_row"], p["vectors_per_thread"], p["block_threads"]) == want, (dtype, hidden, rows, p)
+        assert p["rows_per_block"] * p["threads_per_row"] == p["block_threads"]
     p = ks.get_plan("rms_norm_backward", torch.bfloat16, 4096, 2048).as_dict()
-    bad = [{**p, "vectors_per_thread": 3, "threads_per_row": 256}, {**p, "block_threads": 256, "rows_per_block": 1},
-           {**p, "weight_lds": 1}, {**p, "load_nt": 0}]
+    bad = [{**p, "vectors_per_thread": 5, "threads_per_row": 128}, {**p, "block_threads": 256, "rows_per_block": 2},
+           {**p, "weight_lds": 1}, {**p, "load_nt": 0}, {**p, "threads_per_row": 1024, "vectors_per_thread": 1,
+                                                        "rows_per_block": 1},
+           {**p, "block_threads": 1024, "rows_per_block": 8, "vectors_per_thread": 4},
+           {**p, "rows_per_block": 8}]
     for q in bad:
         assert bwd(A, None, A + 256 * MB, A + 512 * MB, A + 768 * MB, 0, 4096, None, 0,
-                   plan=b.Plan.from_dict(q)) == INVALID
+                   plan=b.Plan.from_dict(q)) == INVALID, q
 
 
 def test_autograd_wrapper_checks_devices():

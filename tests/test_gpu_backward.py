@@ -90,15 +90,18 @@ def test_unaligned_no_dw_and_empty(dtype):
 
 
 def _vector_plans(hidden, es):
-    maxv = 3 if es == 4 else 2
+    """Every compiled vector plan that covers the row: 1024-thread workgroups with
+    up to 3 (fp32) or 2 pieces per lane, 512-thread ones with up to 4."""
     nvec = hidden * es // 16
-    out, tpr = [], 8
-    while tpr <= 1024:
-        for vpt in range(1, maxv + 1):
-            if tpr * vpt >= nvec:
-                out.append(ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt, elems_per_access=16 // es,
-                                   rows_per_block=1024 // tpr, block_threads=1024, load_nt=1, store_nt=1))
-        tpr *= 2
+    out = []
+    for block, maxv in ((1024, 3 if es == 4 else 2), (512, 4)):
+        tpr = 8
+        while tpr <= block:
+            for vpt in range(1, maxv + 1):
+                if tpr * vpt >= nvec:
+                    out.append(ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=vpt, elems_per_access=16 // es,
+                                       rows_per_block=block // tpr, block_threads=block, load_nt=1, store_nt=1))
+            tpr *= 2
     return out
 
 
@@ -131,23 +134,31 @@ def test_every_plan(dtype, hidden):
             check_gradient(gw, rw, mdw)
 
 
-ONE_PIECE_CASES = [("bfloat16", 4096, 8192), ("float16", 8192, 4096), ("float32", 4096, 2048)]
+POLICY_CASES = [("bfloat16", 4096, 2048), ("bfloat16", 2048, 4096), ("bfloat16", 1024, 64), ("float16", 8192, 512),
+                ("float32", 2048, 2048), ("float32", 8192, 256)]
 
 
-@pytest.mark.parametrize("dtype,hidden,rows", ONE_PIECE_CASES, ids=[f"{d}-{r}x{h}" for d, h, r in ONE_PIECE_CASES])
-def test_one_piece_plans_at_full_size(dtype, hidden, rows):
-    """Batches where the policy gives the backward one piece per lane on twice
-    the team: both gradients against the oracle, and dx the same bits as with
-    the fewest-lane plan the policy gives a smaller batch."""
+@pytest.mark.parametrize("dtype,hidden,rows", POLICY_CASES, ids=[f"{d}-{r}x{h}" for d, h, r in POLICY_CASES])
+def test_policy_plans_at_full_size(dtype, hidden, rows):
+    """The policy's plans of each kind (one piece per lane on 512 threads, teams
+    of up to 128 lanes with up to 4 pieces, 512 lanes x 2 or 4) at full size:
+    both gradients against the oracle, and dx the same bits as with the
+    fewest lanes on 1024 threads."""
     inp = workloads.random_case((rows, hidden), dtype, seed=rows + 7 * hidden)
     dy, x, w = inp["residual"], inp["x"], inp["weight"]
-    p1 = ks.get_plan("rms_norm_backward", x.dtype, hidden, rows, compute_units=256)
-    assert p1.vectors_per_thread == 1, p1.as_dict()
-    p2 = ks.get_plan("rms_norm_backward", x.dtype, hidden, 512, compute_units=256)
-    assert p2.vectors_per_thread > 1 and p2.threads_per_row * 2 == p1.threads_per_row, p2.as_dict()
-    st, gx, _ = check(f"one piece {dtype}", dy, x, w, 1e-6, plan=p1)
-    say("one-piece backward", dtype, rows, hidden, st)
-    gx2, _ = run(dy, x, w, 1e-6, p2)
+    es = x.element_size()
+    nvec = hidden * es // 16
+    p = ks.get_plan("rms_norm_backward", x.dtype, hidden, rows, compute_units=256)
+    assert p.block_threads == 512, p.as_dict()
+    st, gx, _ = check(f"policy {dtype}", dy, x, w, 1e-6, plan=p)
+    say("backward policy plan", dtype, rows, hidden, p.as_dict(), st)
+    maxv = 3 if es == 4 else 2
+    tpr = 8
+    while tpr * maxv < nvec:
+        tpr *= 2
+    q = ks.Plan(path=0, threads_per_row=tpr, vectors_per_thread=-(-nvec // tpr), elems_per_access=16 // es,
+                rows_per_block=1024 // tpr, block_threads=1024, load_nt=1, store_nt=1)
+    gx2, _ = run(dy, x, w, 1e-6, q)
     check_bitexact(gx, gx2)
 
 
