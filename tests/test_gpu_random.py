@@ -19,7 +19,7 @@ OPS = ["rms_norm", "fused_add_rms_norm", "rms_norm_residual", "rms_norm_backward
 DTYPES = ["bfloat16", "float16", "float32"]
 HIDDEN = [1, 2, 3, 8, 17, 64, 96, 127, 512, 1000, 1536, 2047, 2880, 4096, 5120, 8192, 12288, 16384, 24576,
           32768, 40000, 65536, 128256]
-ROWS = [1, 2, 3, 7, 33, 100, 256, 513]
+ROWS = [1, 2, 3, 7, 33, 100, 256, 513, 2048, 4100]
 
 
 def draw(i: int):
