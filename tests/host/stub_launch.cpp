@@ -56,9 +56,23 @@ hipError_t launch_softmax_bf16(const Launch &l) { return softmax_stub(l); }
 KS_STUB(launch_swiglu_f32, SwigluLaunch)
 KS_STUB(launch_swiglu_f16, SwigluLaunch)
 KS_STUB(launch_swiglu_bf16, SwigluLaunch)
-KS_STUB(launch_bwd_f32, BwdLaunch)
-KS_STUB(launch_bwd_f16, BwdLaunch)
-KS_STUB(launch_bwd_bf16, BwdLaunch)
+// The backward: an accepted vector plan names a compiled shape (1024-thread
+// workgroups with up to 3 (fp32) or 2 pieces per lane, 512-thread ones with up
+// to 4, one row per team).
+static hipError_t bwd_stub(const BwdLaunch &l, int elem_bytes)
+{
+    ++g_launches;
+    const ks_plan_t &p = l.plan;
+    if (p.path == KS_PATH_VECTOR &&
+        ((p.block_threads != kBwdBlock && p.block_threads != kBwdBlockHalf) || p.threads_per_row <= 0 ||
+         p.threads_per_row > p.block_threads || p.rows_per_block != p.block_threads / p.threads_per_row ||
+         p.vectors_per_thread < 1 || p.vectors_per_thread > bwd_max_vpt(elem_bytes, p.block_threads)))
+        abort();
+    return hipSuccess;
+}
+hipError_t launch_bwd_f32(const BwdLaunch &l) { return bwd_stub(l, 4); }
+hipError_t launch_bwd_f16(const BwdLaunch &l) { return bwd_stub(l, 2); }
+hipError_t launch_bwd_bf16(const BwdLaunch &l) { return bwd_stub(l, 2); }
 
 }  // namespace ks
 
