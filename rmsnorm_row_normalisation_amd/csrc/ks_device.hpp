@@ -1018,7 +1018,29 @@ struct BwdParams {
     int64_t rows;
     int32_t hidden;
     float eps;
+    int32_t part_nt;    // nonzero: the partial rows are stored non-temporal
 };
+
+// kN consecutive fp32 partial sums of dw from v to a, stored plainly or
+// non-temporal.  The empty asm statements keep the two branches apart: a
+// branch over two C++ stores that differ only in the hint is otherwise folded
+// into one plain store.  (Buffer stores, whose hint is an immediate, measured
+// 10% slower for the 32-byte pieces of 16-bit dtypes.)
+template <int kN>
+__device__ __forceinline__ void store_part(float *a, const float *v, int32_t nt)
+{
+    if (nt) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < kN; ++e)
+            __builtin_nontemporal_store(v[e], a + e);
+    } else {
+#pragma unroll
+        for (int e = 0; e < kN; ++e)
+            a[e] = v[e];
+        asm volatile("" ::: "memory");
+    }
+}
 
 // Two team sums in the canonical fold, safe to call repeatedly in one kernel:
 // barriers on both sides of the LDS exchange.  Every thread of the block
@@ -1199,9 +1221,7 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
 #pragma unroll
         for (int k = 0; k < kVpt; ++k)
             if (in_row[k])
-#pragma unroll
-                for (int e = 0; e < kE; ++e)
-                    prow[(k * kTpr + lane) * kE + e] = acc[k][e];
+                store_part<kE>(&prow[(k * kTpr + lane) * kE], acc[k], p.part_nt);
     } else {
         __shared__ float red[kBlock * kE];
 #pragma unroll
@@ -1217,7 +1237,7 @@ __device__ __forceinline__ void bwd_vec_body(const BwdParams &p)
                     sum = sum + red[t * kTpr * kE + q];
                 const int piece = k * kTpr + q / kE;
                 if ((uint32_t)piece * 16u < row_bytes)
-                    prow[piece * kE + q % kE] = sum;
+                    store_part<1>(&prow[piece * kE + q % kE], &sum, p.part_nt);
             }
         }
     }
@@ -1323,7 +1343,8 @@ __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
         const int64_t i = r * p.hidden + j;
         acc.add(Scalar<T>::get(p.dy, i) * (Scalar<T>::get(p.x, i) * p.rho[r]));
     }
-    p.part[(size_t)blockIdx.y * (size_t)p.hidden + j] = acc.value();
+    const float v = acc.value();
+    store_part<1>(&p.part[(size_t)blockIdx.y * (size_t)p.hidden + j], &v, p.part_nt);
 }
 
 // dw[j] = the nparts partial rows added in a fixed order.  A 256-thread block
@@ -1333,7 +1354,8 @@ __device__ __forceinline__ void bwd_colsum_body(const BwdParams &p)
 // thread waits for at most three rounds of loads), then the kDwSlices
 // sums of a column are folded in half (v with v + 4, then v + 2, v + 1) and
 // rounded to the dtype.  32-column blocks spread a 4096-wide dw over 128
-// compute units (64-column, 1024-thread blocks measured 10% slower).
+// compute units (64-column, 1024-thread blocks measured 10% slower).  With
+// kNt the partial rows are read non-temporal, as they were written.
 constexpr int kDwCols = 32;
 constexpr int kDwSlices = 8;
 constexpr int kDwBlock = kDwCols * kDwSlices;
@@ -1346,7 +1368,16 @@ struct DwParams {
     int32_t hidden;
 };
 
-template <typename T>
+template <bool kNt>
+__device__ __forceinline__ float load_part(const float *a)
+{
+    if constexpr (kNt)
+        return __builtin_nontemporal_load(a);
+    else
+        return *a;
+}
+
+template <typename T, bool kNt>
 __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
 {
     __shared__ float red[kDwSlices][kDwCols];
@@ -1370,7 +1401,7 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
                 float t[kN];
 #pragma unroll
                 for (int u = 0; u < kN; ++u)
-                    t[u] = col[(size_t)q * p.hidden + u * step];
+                    t[u] = load_part<kNt>(&col[(size_t)q * p.hidden + u * step]);
 #pragma unroll
                 for (int u = 0; u < kN; ++u)
                     s = s + t[u];
@@ -1384,7 +1415,7 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
 #pragma unroll
             for (int u = 0; u < kN; ++u) {
                 const int r = q + u * kDwSlices < p.nparts ? q + u * kDwSlices : q;
-                t[u] = col[(size_t)r * p.hidden];
+                t[u] = load_part<kNt>(&col[(size_t)r * p.hidden]);
             }
 #pragma unroll
             for (int u = 0; u < kN; ++u)
@@ -1472,10 +1503,10 @@ __global__ __launch_bounds__(256) void rms_norm_backward_colsum(BwdParams p)
     bwd_colsum_body<T>(p);
 }
 
-template <typename T>
+template <typename T, bool kNt>
 __global__ __launch_bounds__(kDwBlock) void rms_norm_backward_dw(DwParams p)
 {
-    bwd_dw_body<T>(p);
+    bwd_dw_body<T, kNt>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>

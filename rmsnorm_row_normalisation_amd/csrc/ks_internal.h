@@ -60,6 +60,12 @@ struct BwdLaunch {
 // dtypes (whose pieces hold 8 sums each), one more spills; with 512 threads
 // (256 VGPRs per lane) up to 4 pieces for every dtype.
 constexpr int kBwdMaxParts = 256;
+// Partial-row arrays of at least this many bytes are written and read
+// non-temporal: from 2 MiB (a 2048-wide row's 256 partial rows) a graph-timed
+// sweep of bf16 and fp32, 1024..8192 wide, 64..2048 rows, measured 0..19%
+// faster calls; below it, plain stores and loads were 3..5% faster (the
+// column sum then finds the rows in the caches).
+constexpr int64_t kBwdPartNtBytes = 2 << 20;
 constexpr int kBwdBlock = 1024;
 constexpr int kBwdBlockHalf = 512;
 constexpr int kBwdMaxVpt32 = 3;

@@ -327,6 +327,12 @@ hipError_t bwd_generic_by_tpr(const BwdParams &p, int tpr, unsigned grid, hipStr
     }
 }
 
+// Whether nparts fp32 partial rows of dw are written and read non-temporal.
+inline int32_t part_nt(int64_t nparts, int64_t hidden)
+{
+    return nparts * hidden * (int64_t)sizeof(float) >= kBwdPartNtBytes ? 1 : 0;
+}
+
 template <typename T>
 hipError_t launch_bwd_typed(const BwdLaunch &l)
 {
@@ -335,11 +341,12 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
     int32_t nparts = 0;
     hipError_t err = hipSuccess;
     if (l.rows > 0) {
-        BwdParams p{l.dx, l.dy, l.x, l.w, l.dw ? l.work : nullptr, nullptr, l.rows, l.hidden, l.eps};
+        BwdParams p{l.dx, l.dy, l.x, l.w, l.dw ? l.work : nullptr, nullptr, l.rows, l.hidden, l.eps, 0};
         if (pl.path == KS_PATH_VECTOR) {
             const int64_t groups = (l.rows + rpb - 1) / rpb;
             const unsigned grid = (unsigned)(groups < kBwdMaxParts ? groups : kBwdMaxParts);
             nparts = (int32_t)grid;
+            p.part_nt = part_nt(nparts, l.hidden);
             switch (pl.threads_per_row) {
             case 8: err = bwd_vec_by_vpt<T, 8>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
             case 16: err = bwd_vec_by_vpt<T, 16>(p, pl.vectors_per_thread, pl.block_threads, grid, l.stream); break;
@@ -353,6 +360,7 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
             }
         } else {
             nparts = (int32_t)(l.rows < kBwdMaxParts ? l.rows : kBwdMaxParts);
+            p.part_nt = part_nt(nparts, l.hidden);
             if (l.dw)
                 p.rho = l.work + (size_t)nparts * (size_t)l.hidden;
             if (pl.elems_per_access != 1 && pl.elems_per_access != Pack<T>::kElems)
@@ -383,7 +391,9 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
         return err;
     DwParams d{l.dw, l.work, nparts, l.hidden};
     const dim3 dgrid((unsigned)((l.hidden + kDwCols - 1) / kDwCols));
-    return dispatch(rms_norm_backward_dw<T>, dgrid, dim3(kDwBlock), 0, l.stream, d);
+    return part_nt(nparts, l.hidden)
+               ? dispatch(rms_norm_backward_dw<T, true>, dgrid, dim3(kDwBlock), 0, l.stream, d)
+               : dispatch(rms_norm_backward_dw<T, false>, dgrid, dim3(kDwBlock), 0, l.stream, d);
 }
 
 }  // namespace ks
