@@ -585,8 +585,9 @@ struct SwigluParams {
 
 // sigmoid(g) for outputs rounded to 16 bits.  e^-g comes from the hardware
 // base-2 exponential, with -g * log2(e) carried as hi + lo (log2(e) split into
-// an fp32 head and tail, the head product's error recovered by an FMA) and
-// 2^lo applied to first order; 1 / (1 + e) is the hardware reciprocal with one
+// an fp32 head and tail, as in Cody and Waite's argument reduction, and the
+// head product's rounding error recovered exactly by an FMA, the error-free
+// product of Ogita, Rump and Oishi) and 2^lo applied to first order; 1 / (1 + e) is the hardware reciprocal with one
 // Newton step.  Within a few fp32 ulps of the exact value, far below half an
 // ulp of bf16 or fp16.  -g is clamped to [-20, 88]: from g >= 20 the result is
 // exactly 1, as the exact value rounds to 1 in fp32; below g = -88 (exact
