@@ -33,9 +33,13 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # -ffp-contract=off: every multiply and add in the kernels rounds as written
 #   (the one fused step, the sum of squares, is an explicit fmaf).
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
+# -amdgpu-kernarg-preload-count=16: kernels whose arguments are scalars get
+#   up to 16 SGPRs of them preloaded at wave launch (the row kernels' 48 bytes
+#   fit); a kernel taking a struct is unaffected.
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

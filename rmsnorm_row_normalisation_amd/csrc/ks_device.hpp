@@ -1436,101 +1436,140 @@ __device__ __forceinline__ void bwd_dw_body(const DwParams &p)
 }
 
 // ---------------------------------------------------------------------------
-// Kernel entry points, one name per operation and path.
+// Kernel entry points, one name per operation and path.  Every kernel takes
+// its arguments as scalars (the fields of its parameter struct; the
+// backward's sizes ahead of its partial-row pointers) rather than the
+// struct: built with kernel-argument preloading, gfx950 then starts every
+// wave with them already in SGPRs, where a struct argument would be read
+// from the kernel-argument segment first, one memory round trip before the
+// first data load can issue.
 // ---------------------------------------------------------------------------
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
-__global__ __launch_bounds__(kBlock) void rms_norm_vec(Params p)
+__global__ __launch_bounds__(kBlock) void rms_norm_vec(void *y, const void *x, void *res, const void *w, int64_t rows,
+                                                       int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     vec_body<T, false, false, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
-__global__ __launch_bounds__(kBlock) void fused_add_rms_norm_vec(Params p)
+__global__ __launch_bounds__(kBlock) void fused_add_rms_norm_vec(void *y, const void *x, void *res, const void *w,
+                                                                 int64_t rows, int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     vec_body<T, true, true, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol, bool kWeightLds>
-__global__ __launch_bounds__(kBlock) void rms_norm_residual_vec(Params p)
+__global__ __launch_bounds__(kBlock) void rms_norm_residual_vec(void *y, const void *x, void *res, const void *w,
+                                                                int64_t rows, int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     vec_body<T, true, false, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol, kWeightLds>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
-__global__ __launch_bounds__(kBlock) void rms_norm_generic(Params p)
+__global__ __launch_bounds__(kBlock) void rms_norm_generic(void *y, const void *x, void *res, const void *w,
+                                                           int64_t rows, int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     generic_body<T, false, false, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
-__global__ __launch_bounds__(kBlock) void fused_add_rms_norm_generic(Params p)
+__global__ __launch_bounds__(kBlock) void fused_add_rms_norm_generic(void *y, const void *x, void *res, const void *w,
+                                                                     int64_t rows, int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     generic_body<T, true, true, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
-__global__ __launch_bounds__(kBlock) void rms_norm_residual_generic(Params p)
+__global__ __launch_bounds__(kBlock) void rms_norm_residual_generic(void *y, const void *x, void *res, const void *w,
+                                                                    int64_t rows, int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     generic_body<T, true, false, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>
-__global__ __launch_bounds__(kBlock) void silu_and_mul_vec(SwigluParams p)
+__global__ __launch_bounds__(kBlock) void silu_and_mul_vec(void *out, const void *x, int64_t rows, int32_t d)
 {
+    const SwigluParams p{out, x, rows, d};
     swiglu_vec_body<T, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol>(p);
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void silu_and_mul_generic(SwigluParams p)
+__global__ __launch_bounds__(256) void silu_and_mul_generic(void *out, const void *x, int64_t rows, int32_t d)
 {
+    const SwigluParams p{out, x, rows, d};
     swiglu_generic_body<T>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock>
-__global__ __launch_bounds__(kBlock) void rms_norm_backward_vec(BwdParams p)
+__global__ __launch_bounds__(kBlock) void rms_norm_backward_vec(void *dx, const void *dy, const void *x, const void *w,
+                                                                int64_t rows, int32_t hidden, float eps, float *part,
+                                                                float *rho, int32_t part_nt)
 {
+    const BwdParams p{dx, dy, x, w, part, rho, rows, hidden, eps, part_nt};
     bwd_vec_body<T, kTpr, kVpt, kBlock>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
-__global__ __launch_bounds__(kBlock) void rms_norm_backward_generic(BwdParams p)
+__global__ __launch_bounds__(kBlock) void rms_norm_backward_generic(void *dx, const void *dy, const void *x,
+                                                                    const void *w, int64_t rows, int32_t hidden,
+                                                                    float eps, float *part, float *rho, int32_t part_nt)
 {
+    const BwdParams p{dx, dy, x, w, part, rho, rows, hidden, eps, part_nt};
     bwd_generic_body<T, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void rms_norm_backward_colsum(BwdParams p)
+__global__ __launch_bounds__(256) void rms_norm_backward_colsum(void *dx, const void *dy, const void *x, const void *w,
+                                                                int64_t rows, int32_t hidden, float eps, float *part,
+                                                                float *rho, int32_t part_nt)
 {
+    const BwdParams p{dx, dy, x, w, part, rho, rows, hidden, eps, part_nt};
     bwd_colsum_body<T>(p);
 }
 
 template <typename T, bool kNt>
-__global__ __launch_bounds__(kDwBlock) void rms_norm_backward_dw(DwParams p)
+__global__ __launch_bounds__(kDwBlock) void rms_norm_backward_dw(void *dw, const float *part, int32_t nparts,
+                                                               int32_t hidden)
 {
+    const DwParams p{dw, part, nparts, hidden};
     bwd_dw_body<T, kNt>(p);
 }
 
 template <typename T, int kTpr, int kVpt, int kBlock, int kLoadCpol, int kStoreCpol>
-__global__ __launch_bounds__(kBlock) void softmax_vec(Params p)
+__global__ __launch_bounds__(kBlock) void softmax_vec(void *y, const void *x, void *res, const void *w, int64_t rows,
+                                                      int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     softmax_vec_body<T, kTpr, kVpt, kBlock, kLoadCpol, kStoreCpol>(p);
 }
 
 template <typename T, int kTpr, int kEpa, int kBlock>
-__global__ __launch_bounds__(kBlock) void softmax_generic(Params p)
+__global__ __launch_bounds__(kBlock) void softmax_generic(void *y, const void *x, void *res, const void *w,
+                                                          int64_t rows, int32_t hidden, float eps)
 {
+    const Params p{y, x, res, w, rows, hidden, eps};
     softmax_generic_body<T, kTpr, kEpa, kBlock>(p);
 }
 
 template <typename T, int kVpt>
-__global__ __launch_bounds__(kSplitLanes) void softmax_split_stats(SplitParams p)
+__global__ __launch_bounds__(kSplitLanes) void softmax_split_stats(void *y, const void *x, float *stats, int64_t rows,
+                                                                   int32_t hidden, int32_t chunks)
 {
+    const SplitParams p{y, x, stats, rows, hidden, chunks};
     softmax_split_stats_body<T, kVpt>(p);
 }
 
 template <typename T, int kVpt>
-__global__ __launch_bounds__(kSplitLanes) void softmax_split_norm(SplitParams p)
+__global__ __launch_bounds__(kSplitLanes) void softmax_split_norm(void *y, const void *x, float *stats, int64_t rows,
+                                                                  int32_t hidden, int32_t chunks)
 {
+    const SplitParams p{y, x, stats, rows, hidden, chunks};
     softmax_split_norm_body<T, kVpt>(p);
 }
 

@@ -27,6 +27,38 @@ hipError_t dispatch(Kernel kernel, dim3 grid, dim3 block, size_t lds_bytes, hipS
     return hipGetLastError();
 }
 
+// A kernel launch with the fields of its parameter struct as the kernel's
+// scalar arguments (the kernel entry points rebuild the struct; scalar
+// arguments are preloaded into SGPRs at wave launch, up to 14 SGPRs).
+template <typename Kernel>
+hipError_t dispatch_fields(Kernel k, dim3 g, dim3 b, size_t lds, hipStream_t s, const Params &p)
+{
+    return dispatch(k, g, b, lds, s, p.y, p.x, p.res, p.w, p.rows, p.hidden, p.eps);
+}
+template <typename Kernel>
+hipError_t dispatch_fields(Kernel k, dim3 g, dim3 b, size_t lds, hipStream_t s, const SwigluParams &p)
+{
+    return dispatch(k, g, b, lds, s, p.out, p.x, p.rows, p.d);
+}
+template <typename Kernel>
+hipError_t dispatch_fields(Kernel k, dim3 g, dim3 b, size_t lds, hipStream_t s, const SplitParams &p)
+{
+    return dispatch(k, g, b, lds, s, p.y, p.x, p.stats, p.rows, p.hidden, p.chunks);
+}
+template <typename Kernel>
+hipError_t dispatch_fields(Kernel k, dim3 g, dim3 b, size_t lds, hipStream_t s, const BwdParams &p)
+{
+    // the sizes before the partial-row pointers: 14 SGPRs of arguments are
+    // preloaded, and the sizes are needed before the first load, the
+    // pointers only at the end
+    return dispatch(k, g, b, lds, s, p.dx, p.dy, p.x, p.w, p.rows, p.hidden, p.eps, p.part, p.rho, p.part_nt);
+}
+template <typename Kernel>
+hipError_t dispatch_fields(Kernel k, dim3 g, dim3 b, size_t lds, hipStream_t s, const DwParams &p)
+{
+    return dispatch(k, g, b, lds, s, p.dw, p.part, p.nparts, p.hidden);
+}
+
 // Rows one launch of a row kernel may cover: its grid stays within 2^31
 // work-items (a dispatch counts work-items in 32 bits); larger batches go out
 // in consecutive slices of rows, each a launch of the same kernel.
@@ -46,7 +78,8 @@ hipError_t run(Kernel kernel, const Launch &l, int block, size_t lds_bytes = 0)
         const size_t off = (size_t)r0 * row_bytes;
         Params p{(char *)l.y + off, (const char *)l.x + off, l.res ? (char *)l.res + off : nullptr, l.w, n,
                  l.hidden, l.eps};
-        const hipError_t err = dispatch(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), lds_bytes, l.stream, p);
+        const hipError_t err =
+            dispatch_fields(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), lds_bytes, l.stream, p);
         if (err != hipSuccess)
             return err;
     }
@@ -171,10 +204,10 @@ hipError_t softmax_split_one(const Launch &l)
     const int64_t chunks = split_chunks((int64_t)l.hidden * Pack<T>::kBytes, V);
     SplitParams p{l.y, l.x, l.work, l.rows, l.hidden, (int32_t)chunks};
     const dim3 grid((unsigned)chunks, (unsigned)l.rows);
-    const hipError_t err = dispatch(softmax_split_stats<T, V>, grid, dim3(kSplitBlock), 0, l.stream, p);
+    const hipError_t err = dispatch_fields(softmax_split_stats<T, V>, grid, dim3(kSplitBlock), 0, l.stream, p);
     if (err != hipSuccess)
         return err;
-    return dispatch(softmax_split_norm<T, V>, grid, dim3(kSplitBlock), 0, l.stream, p);
+    return dispatch_fields(softmax_split_norm<T, V>, grid, dim3(kSplitBlock), 0, l.stream, p);
 }
 
 template <typename T>
@@ -206,7 +239,7 @@ hipError_t run_swiglu(Kernel kernel, const SwigluLaunch &l, int block)
         const int64_t n = l.rows - r0 < slice ? l.rows - r0 : slice;
         SwigluParams p{(char *)l.out + (size_t)r0 * out_bytes, (const char *)l.x + (size_t)r0 * 2 * out_bytes, n,
                        l.d};
-        const hipError_t err = dispatch(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
+        const hipError_t err = dispatch_fields(kernel, dim3((unsigned)((n + rpb - 1) / rpb)), dim3(block), 0, l.stream, p);
         if (err != hipSuccess)
             return err;
     }
@@ -252,7 +285,7 @@ hipError_t launch_swiglu_typed(const SwigluLaunch &l)
         const int64_t total = l.rows * (int64_t)l.d;
         int64_t blocks = (total + kSwigluGenericBlock - 1) / kSwigluGenericBlock;
         blocks = blocks > 8192 ? 8192 : blocks;   // grid-stride beyond 2M threads
-        return dispatch(silu_and_mul_generic<T>, dim3((unsigned)blocks), dim3(kSwigluGenericBlock), 0, l.stream, p);
+        return dispatch_fields(silu_and_mul_generic<T>, dim3((unsigned)blocks), dim3(kSwigluGenericBlock), 0, l.stream, p);
     }
     switch (l.plan.threads_per_row) {
     case 8: return swiglu_by_vpt<T, 8>(l);
@@ -273,7 +306,7 @@ hipError_t launch_swiglu_typed(const SwigluLaunch &l)
 template <typename T, int TPR, int V, int B>
 hipError_t bwd_vec_one(const BwdParams &p, unsigned grid, hipStream_t stream)
 {
-    return dispatch(rms_norm_backward_vec<T, TPR, V, B>, dim3(grid), dim3(B), 0, stream, p);
+    return dispatch_fields(rms_norm_backward_vec<T, TPR, V, B>, dim3(grid), dim3(B), 0, stream, p);
 }
 
 // The compiled backward plans: 1024-thread workgroups with 1..3 (fp32) or 1..2
@@ -312,7 +345,7 @@ template <typename T, int TPR, int EPA>
 hipError_t bwd_generic_one(const BwdParams &p, unsigned grid, hipStream_t stream)
 {
     constexpr int B = TPR == 1024 ? 1024 : 256;
-    return dispatch(rms_norm_backward_generic<T, TPR, EPA, B>, dim3(grid), dim3(B), 0, stream, p);
+    return dispatch_fields(rms_norm_backward_generic<T, TPR, EPA, B>, dim3(grid), dim3(B), 0, stream, p);
 }
 
 template <typename T, int EPA>
@@ -383,7 +416,7 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
             }
             if (err == hipSuccess && l.dw) {
                 const dim3 cgrid((unsigned)((l.hidden + 255) / 256), (unsigned)nparts);
-                err = dispatch(rms_norm_backward_colsum<T>, cgrid, dim3(256), 0, l.stream, p);
+                err = dispatch_fields(rms_norm_backward_colsum<T>, cgrid, dim3(256), 0, l.stream, p);
             }
         }
     }
@@ -392,8 +425,8 @@ hipError_t launch_bwd_typed(const BwdLaunch &l)
     DwParams d{l.dw, l.work, nparts, l.hidden};
     const dim3 dgrid((unsigned)((l.hidden + kDwCols - 1) / kDwCols));
     return part_nt(nparts, l.hidden)
-               ? dispatch(rms_norm_backward_dw<T, true>, dgrid, dim3(kDwBlock), 0, l.stream, d)
-               : dispatch(rms_norm_backward_dw<T, false>, dgrid, dim3(kDwBlock), 0, l.stream, d);
+               ? dispatch_fields(rms_norm_backward_dw<T, true>, dgrid, dim3(kDwBlock), 0, l.stream, d)
+               : dispatch_fields(rms_norm_backward_dw<T, false>, dgrid, dim3(kDwBlock), 0, l.stream, d);
 }
 
 }  // namespace ks
