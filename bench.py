@@ -1274,15 +1274,23 @@ def trace_summary(wl, directory: str, bench_json: str | None, command: str | Non
         else:
             row += " | | | | |"
         L.append(row)
+    ctx = trace_contexts(directory)
     if line is not None:
         rf = line["roofline"]
-        L += ["", f"The bench line's roofline: dominant kernel {rf['kernel']}, {rf['achieved']} GB/s, frac "
-              f"{rf['frac']} (algorithmic bytes over the mean of the per-call kernel-dispatch event durations).  "
-              f"The same bytes over the trace's mean duration give frac "
-              f"{algorithmic_bytes(rf['kernel'], wl.rows, wl.hidden, esize) / per_op[rf['kernel']]['mean'] / 1e3 / HBM_PEAK_GBPS:.4f}."
-              "  The tracer adds a little to each dispatch, so its durations run slightly longer than the "
-              "uninstrumented ones."]
-    ctx = trace_contexts(directory)
+        alg = algorithmic_bytes(rf["kernel"], wl.rows, wl.hidden, esize)
+        text = (f"The bench line's roofline: dominant kernel {rf['kernel']}, {rf['achieved']} GB/s, frac "
+                f"{rf['frac']} (algorithmic bytes over the mean of the per-call kernel-dispatch event durations).  "
+                f"The same bytes over the trace's mean duration give frac "
+                f"{alg / per_op[rf['kernel']]['mean'] / 1e3 / HBM_PEAK_GBPS:.4f}.")
+        timed = ctx.get((rf["kernel"], rf["kernel"], ">= 2 us"))
+        kernels = [n for n in disp if kernel_op(n) == rf["kernel"]]
+        if timed is not None and timed["n"] >= 8 and len(kernels) == 1:   # an op of one kernel per call
+            text += (f"  Over the dispatches of the kind the bench times (a call after a call of the same op, "
+                     f"with an idle gap of 2 us or more: {timed['n']} dispatches, mean {timed['mean']:.3f} us) "
+                     f"they give frac {alg / timed['mean'] / 1e3 / HBM_PEAK_GBPS:.4f}.")
+        text += ("  The tracer adds a little to each dispatch, so its durations run slightly longer than the "
+                 "uninstrumented ones.")
+        L += ["", text]
     if ctx:
         L += ["", "The library's dispatches by what ran just before them on the device (a kernel of an op, the "
               "head-start spin, the setup and reference kernels) and by the idle gap in between.  The graph "
